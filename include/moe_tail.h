@@ -1,0 +1,171 @@
+/*
+ * moe_tail.h -- C ABI of the MI355X (gfx950) latent-MoE layer tail.
+ *
+ * The tail (pages: "[Kimi K3][Kernel] Fuse BF16 shared experts into latent
+ * MegaMoE tail", Summary and "Sequence-parallel implementation"; DeepGEMM PR
+ * 416 mirror, Summary and Implementation; tokenspeed PR 1062, Summary):
+ *
+ *   route:    logits = x_lat . W_g^T (+ bias); top-k; softmax over the k
+ *             selected logits; tokens permuted into per-expert row segments
+ *   forward:  x_lat -> e4m3 codes with one fp32 scale per 1x128 block;
+ *             routed L1 gate/up (FP8 128x128 block-scaled or MXFP4 weights),
+ *             SwiGLU, h -> e4m3 per 1x128, routed L2 down to the latent;
+ *             top-k weighted combine in FP32 fused with RMSNorm -> bf16;
+ *             shared BF16 SwiGLU MLP on x_hid (its own token count Ms >= Mr);
+ *             out = bf16(up(RMSNorm(routed)) + f32(shared)) for t < Mr, with
+ *             the up-projection accumulated in FP32 and one final rounding;
+ *             shared rows t >= Mr go to shared_out.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major with the reduction
+ *     (K) dimension contiguous, 16-byte aligned.  bf16 travels as uint16_t
+ *     bit patterns.
+ *   - The caller allocates and owns every buffer.  The library allocates no
+ *     device memory, keeps no pointer after returning, never synchronizes,
+ *     and enqueues all work on `stream` (a hipStream_t; NULL = null stream).
+ *   - Every argument check runs on the host before anything is enqueued.  On
+ *     any error nothing has been enqueued ("fail closed").  A launch failure
+ *     reported by the runtime returns MOE_TAIL_ERR_DEVICE.
+ *   - The library is stateless and re-entrant; concurrent calls need
+ *     disjoint workspaces and outputs.
+ *   - Behaviour is undefined for non-finite inputs and for a routing that
+ *     moe_tail_route did not produce for the same x_lat / Mr.
+ */
+#ifndef MOE_TAIL_H
+#define MOE_TAIL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_TAIL_OK = 0,
+  MOE_TAIL_ERR_INVALID = 1,      /* null/misaligned pointer, bad count, bad dims */
+  MOE_TAIL_ERR_UNSUPPORTED = 2,  /* dims or format outside what the kernels implement */
+  MOE_TAIL_ERR_WORKSPACE = 3,    /* ws_bytes smaller than moe_tail_workspace_bytes() */
+  MOE_TAIL_ERR_DEVICE = 4        /* the HIP runtime rejected a launch */
+} moe_tail_status;
+
+typedef enum {
+  MOE_TAIL_W_FP8_BLOCK128 = 0,   /* e4m3 codes + fp32 scale per 128 (N) x 128 (K) block */
+  MOE_TAIL_W_MXFP4 = 1           /* e2m1 pairs (even K in the low nibble) + e8m0 scale per 32 along K */
+} moe_tail_wfmt;
+
+/* Sizes of one tail.  hidden (H) and latent (L) are the shared and routed
+ * widths (7168 and 3584 in the served model), inter (I) and shared_inter
+ * (I_s) the routed and shared intermediate sizes.
+ * Valid: all sizes > 0, 1 <= top_k <= num_experts, finite rms_eps > 0.
+ * Supported by the kernels: H and L multiples of 256 with L <= 8192; I and
+ * I_s multiples of 128 with I <= 8192; num_experts <= 1024; top_k <= 16. */
+typedef struct {
+  int32_t hidden;
+  int32_t latent;
+  int32_t num_experts;
+  int32_t top_k;
+  int32_t inter;
+  int32_t shared_inter;
+  int32_t wfmt;          /* moe_tail_wfmt */
+  float rms_eps;
+} moe_tail_dims;
+
+/* Weights (device, read-only).  Row r of w1 for r < I is the gate projection,
+ * r >= I the up projection; the same split holds for ws1 with I_s. */
+typedef struct {
+  const float *gate;          /* [E, L] fp32 router weights */
+  const float *gate_bias;     /* [E] fp32 router bias, or NULL for none */
+  const uint8_t *w1;          /* FP8: [E, 2I, L] e4m3      | MXFP4: [E, 2I, L/2] packed e2m1 */
+  const void *w1_scale;       /* FP8: [E, 2I/128, L/128] f32 | MXFP4: [E, 2I, L/32] e8m0 */
+  const uint8_t *w2;          /* FP8: [E, L, I] e4m3       | MXFP4: [E, L, I/2] packed e2m1 */
+  const void *w2_scale;       /* FP8: [E, L/128, I/128] f32  | MXFP4: [E, L, I/32] e8m0 */
+  const uint16_t *rms_gamma;  /* [L] bf16 */
+  const uint16_t *w_up;       /* [H, L] bf16 up-projection */
+  const uint16_t *ws1;        /* [2 I_s, H] bf16 shared gate/up */
+  const uint16_t *ws2;        /* [H, I_s] bf16 shared down */
+} moe_tail_weights;
+
+/* Routing produced by moe_tail_route (device buffers owned by the caller). */
+typedef struct {
+  int32_t *topk_ids;        /* [Mr, k]: experts by (logit desc, index asc) */
+  float *topk_weights;      /* [Mr, k]: softmax over the k selected logits */
+  int32_t *expert_offsets;  /* [E + 1]: exclusive prefix of per-expert row counts */
+  int32_t *sorted_pair;     /* [Mr * k]: row -> pair t*k + j, tokens ascending within an expert */
+  int32_t *pair_to_row;     /* [Mr * k]: pair t*k + j -> row (inverse of sorted_pair) */
+} moe_tail_routing;
+
+/* Bytes of device workspace that moe_tail_route and moe_tail_forward need
+ * for these sizes (one workspace serves both calls).  Returns 0 when the
+ * dims or counts are invalid or unsupported. */
+size_t moe_tail_workspace_bytes(const moe_tail_dims *dims, int32_t Mr, int32_t Ms);
+
+/* Indices into moe_tail_workspace_layout's offsets[]: the intermediates the
+ * forward pass materializes, exposed so tests can read them. */
+enum {
+  MOE_TAIL_WS_XQ = 0,   /* [Mr, L] u8 e4m3 codes of x_lat */
+  MOE_TAIL_WS_SX = 1,   /* [Mr, L/128] f32 scales of x_lat */
+  MOE_TAIL_WS_HQ = 2,   /* [Mr*k, I] u8 e4m3 codes of h, rows in sorted order */
+  MOE_TAIL_WS_SH = 3,   /* [Mr*k, I/128] f32 scales of h */
+  MOE_TAIL_WS_Y = 4,    /* [Mr*k, L] f32 routed L2 output, rows in sorted order */
+  MOE_TAIL_WS_RN = 5,   /* [Mr, L] bf16 normalized combined latent */
+  MOE_TAIL_WS_HS = 6,   /* [Ms, I_s] bf16 shared intermediate */
+  MOE_TAIL_WS_S = 7,    /* [Mr, H] bf16 shared output rows 0..Mr-1 */
+  MOE_TAIL_WS_NUM = 8
+};
+
+/* Byte offsets of the intermediates above inside the workspace.
+ * Returns MOE_TAIL_OK or MOE_TAIL_ERR_INVALID / _UNSUPPORTED. */
+int moe_tail_workspace_layout(const moe_tail_dims *dims, int32_t Mr, int32_t Ms, size_t offsets[MOE_TAIL_WS_NUM]);
+
+/* Routing of Mr tokens (0 <= Mr <= 2^20).  Reads x_lat [Mr, L] bf16 and
+ * weights->gate / gate_bias; writes every array of *out.
+ * Logits use a fixed FP32 summation order (64 strided partial sums, each a
+ * sequential fused multiply-add chain, combined by an xor butterfly over
+ * 32,16,8,4,2,1), so expert ids are reproducible bit for bit.  Ties between
+ * equal logits go to the lower expert index. */
+int moe_tail_route(const moe_tail_dims *dims, const moe_tail_weights *weights, const uint16_t *x_lat, int32_t Mr,
+                   const moe_tail_routing *out, void *workspace, size_t ws_bytes, void *stream);
+
+/* The tail for Mr routed tokens and Ms >= Mr shared tokens (0 <= Mr <= Ms <= 2^20).
+ * Routed token t is shared token t (t < Mr).
+ *   x_lat  [Mr, L] bf16 routed latent input
+ *   x_hid  [Ms, H] bf16 shared-expert input
+ *   routing  from moe_tail_route for this x_lat (read only)
+ *   out        [Mr, H] bf16: bf16(up(RMSNorm(routed)) + f32(shared)) for t < Mr
+ *   shared_out [Ms-Mr, H] bf16: shared rows t >= Mr at row t-Mr; NULL iff Ms == Mr */
+int moe_tail_forward(const moe_tail_dims *dims, const moe_tail_weights *weights, const uint16_t *x_lat, int32_t Mr,
+                     const uint16_t *x_hid, int32_t Ms, const moe_tail_routing *routing, uint16_t *out,
+                     uint16_t *shared_out, void *workspace, size_t ws_bytes, void *stream);
+
+/* Number of stages moe_tail_forward_profiled brackets with events. */
+#define MOE_TAIL_NUM_STAGES 7
+/* Stage order: 0 quantize x_lat, 1 routed L1 (+SwiGLU + h quantization),
+ * 2 routed L2, 3 combine + RMSNorm, 4 shared L1 (+SwiGLU), 5 shared L2,
+ * 6 up-projection + shared add.  A stage with no work records its events
+ * back to back. */
+
+/* moe_tail_forward that also records stage_events[i] (hipEvent_t) on `stream`
+ * right before stage i and stage_events[MOE_TAIL_NUM_STAGES] after the last
+ * one.  stage_events must hold MOE_TAIL_NUM_STAGES + 1 created events. */
+int moe_tail_forward_profiled(const moe_tail_dims *dims, const moe_tail_weights *weights, const uint16_t *x_lat,
+                              int32_t Mr, const uint16_t *x_hid, int32_t Ms, const moe_tail_routing *routing,
+                              uint16_t *out, uint16_t *shared_out, void *workspace, size_t ws_bytes, void *stream,
+                              void *const *stage_events);
+
+/* The device 1x128 FP8 quantizer the forward pass uses, exported for tests:
+ * per row and 128-wide block, s = amax / 448 (1.0 for an all-zero block),
+ * code = e4m3(x / s) rounded to nearest even, saturating at +-448, sign of
+ * zero kept.  x is [rows, cols] bf16 (x_is_bf16 = 1) or fp32; cols % 128 == 0.
+ * codes [rows, cols] u8, scales [rows, cols/128] f32. */
+int moe_tail_quant_fp8_1x128(const void *x, int32_t x_is_bf16, int32_t rows, int32_t cols, uint8_t *codes,
+                             float *scales, void *stream);
+
+/* Static description of a status code. */
+const char *moe_tail_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_TAIL_H */

@@ -1,0 +1,159 @@
+"""ctypes binding of ``libmoe_tail.so`` (the C ABI in include/moe_tail.h).
+
+Argument marshalling only: every step of the tail runs in the HIP kernels
+behind the C ABI.  Pointers may be given as torch tensors (their data_ptr is
+used) or as plain integers; streams as torch.cuda.Stream, an integer handle, or
+None for the null stream.  A non-zero status raises ``MoeTailError``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_tail.so")
+
+MOE_TAIL_OK = 0
+MOE_TAIL_ERR_INVALID = 1
+MOE_TAIL_ERR_UNSUPPORTED = 2
+MOE_TAIL_ERR_WORKSPACE = 3
+MOE_TAIL_ERR_DEVICE = 4
+
+MOE_TAIL_W_FP8_BLOCK128 = 0
+MOE_TAIL_W_MXFP4 = 1
+
+MOE_TAIL_WS_XQ, MOE_TAIL_WS_SX, MOE_TAIL_WS_HQ, MOE_TAIL_WS_SH, MOE_TAIL_WS_Y, MOE_TAIL_WS_RN, \
+    MOE_TAIL_WS_HS, MOE_TAIL_WS_S = range(8)
+MOE_TAIL_WS_NUM = 8
+MOE_TAIL_NUM_STAGES = 7
+
+EXPORTED = ("moe_tail_workspace_bytes", "moe_tail_workspace_layout", "moe_tail_route", "moe_tail_forward",
+            "moe_tail_forward_profiled", "moe_tail_quant_fp8_1x128", "moe_tail_strerror")
+
+
+class MoeTailError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+class Dims(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("latent", C.c_int32), ("num_experts", C.c_int32), ("top_k", C.c_int32),
+                ("inter", C.c_int32), ("shared_inter", C.c_int32), ("wfmt", C.c_int32), ("rms_eps", C.c_float)]
+
+
+class Weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("gate", "gate_bias", "w1", "w1_scale", "w2", "w2_scale", "rms_gamma",
+                                          "w_up", "ws1", "ws2")]
+
+
+class Routing(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("topk_ids", "topk_weights", "expert_offsets", "sorted_pair",
+                                          "pair_to_row")]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load the HIP library; fails loudly when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = C.CDLL(LIB_PATH)
+        L.moe_tail_workspace_bytes.restype = C.c_size_t
+        L.moe_tail_workspace_bytes.argtypes = [C.POINTER(Dims), C.c_int32, C.c_int32]
+        L.moe_tail_workspace_layout.restype = C.c_int
+        L.moe_tail_workspace_layout.argtypes = [C.POINTER(Dims), C.c_int32, C.c_int32, C.POINTER(C.c_size_t)]
+        L.moe_tail_route.restype = C.c_int
+        L.moe_tail_route.argtypes = [C.POINTER(Dims), C.POINTER(Weights), C.c_void_p, C.c_int32,
+                                     C.POINTER(Routing), C.c_void_p, C.c_size_t, C.c_void_p]
+        fwd = [C.POINTER(Dims), C.POINTER(Weights), C.c_void_p, C.c_int32, C.c_void_p, C.c_int32,
+               C.POINTER(Routing), C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+        L.moe_tail_forward.restype = C.c_int
+        L.moe_tail_forward.argtypes = fwd
+        L.moe_tail_forward_profiled.restype = C.c_int
+        L.moe_tail_forward_profiled.argtypes = fwd + [C.POINTER(C.c_void_p)]
+        L.moe_tail_quant_fp8_1x128.restype = C.c_int
+        L.moe_tail_quant_fp8_1x128.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                               C.c_void_p, C.c_void_p]
+        L.moe_tail_strerror.restype = C.c_char_p
+        L.moe_tail_strerror.argtypes = [C.c_int]
+        _lib = L
+    return _lib
+
+
+def ptr(x) -> int | None:
+    """Device address of a torch tensor / integer / None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def stream_handle(stream) -> int | None:
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def strerror(status: int) -> str:
+    return lib().moe_tail_strerror(status).decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != MOE_TAIL_OK:
+        raise MoeTailError(rc, where)
+
+
+def make_dims(hidden, latent, num_experts, top_k, inter, shared_inter, wfmt, rms_eps) -> Dims:
+    return Dims(hidden, latent, num_experts, top_k, inter, shared_inter, wfmt, rms_eps)
+
+
+def make_weights(**kw) -> Weights:
+    return Weights(**{k: ptr(v) for k, v in kw.items()})
+
+
+def make_routing(**kw) -> Routing:
+    return Routing(**{k: ptr(v) for k, v in kw.items()})
+
+
+def moe_tail_workspace_bytes(dims: Dims, Mr: int, Ms: int) -> int:
+    return lib().moe_tail_workspace_bytes(C.byref(dims), Mr, Ms)
+
+
+def moe_tail_workspace_layout(dims: Dims, Mr: int, Ms: int) -> list[int]:
+    offs = (C.c_size_t * MOE_TAIL_WS_NUM)()
+    _check(lib().moe_tail_workspace_layout(C.byref(dims), Mr, Ms, offs), "moe_tail_workspace_layout")
+    return list(offs)
+
+
+def moe_tail_route(dims: Dims, weights: Weights, x_lat, Mr: int, routing: Routing, workspace, ws_bytes: int,
+                   stream=None) -> None:
+    _check(lib().moe_tail_route(C.byref(dims), C.byref(weights), ptr(x_lat), Mr, C.byref(routing), ptr(workspace),
+                                ws_bytes, stream_handle(stream)), "moe_tail_route")
+
+
+def moe_tail_forward(dims: Dims, weights: Weights, x_lat, Mr: int, x_hid, Ms: int, routing: Routing, out,
+                     shared_out, workspace, ws_bytes: int, stream=None) -> None:
+    _check(lib().moe_tail_forward(C.byref(dims), C.byref(weights), ptr(x_lat), Mr, ptr(x_hid), Ms,
+                                  C.byref(routing), ptr(out), ptr(shared_out), ptr(workspace), ws_bytes,
+                                  stream_handle(stream)), "moe_tail_forward")
+
+
+def moe_tail_forward_profiled(dims: Dims, weights: Weights, x_lat, Mr: int, x_hid, Ms: int, routing: Routing, out,
+                              shared_out, workspace, ws_bytes: int, stream, events) -> None:
+    """``events``: MOE_TAIL_NUM_STAGES + 1 hipEvent_t handles (integers)."""
+    arr = (C.c_void_p * len(events))(*events)
+    _check(lib().moe_tail_forward_profiled(C.byref(dims), C.byref(weights), ptr(x_lat), Mr, ptr(x_hid), Ms,
+                                           C.byref(routing), ptr(out), ptr(shared_out), ptr(workspace), ws_bytes,
+                                           stream_handle(stream), arr), "moe_tail_forward_profiled")
+
+
+def moe_tail_quant_fp8_1x128(x, x_is_bf16: bool, rows: int, cols: int, codes, scales, stream=None) -> None:
+    _check(lib().moe_tail_quant_fp8_1x128(ptr(x), int(bool(x_is_bf16)), rows, cols, ptr(codes), ptr(scales),
+                                          stream_handle(stream)), "moe_tail_quant_fp8_1x128")

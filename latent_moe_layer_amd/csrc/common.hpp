@@ -1,0 +1,77 @@
+// Device helpers shared by the tail's kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe_tail {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// fp32 -> e4m3 ("fn": bias 7, max 448, no infinities) code, round to nearest
+// even, saturating to +-448; the sign bit of the input is kept.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a >= 448.0f) return sign | 0x7eu;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
+    return sign | static_cast<uint32_t>(rintf(a * 512.0f));
+  }
+  const int ex = static_cast<int>((__float_as_uint(a) >> 23) & 0xff) - 127;  // -6..8
+  // a * 2^(3 - ex) lies in [8, 16): its integer part carries the implicit bit
+  const float scaled = a * __uint_as_float(static_cast<uint32_t>(127 + 3 - ex) << 23);
+  const uint32_t q = static_cast<uint32_t>(rintf(scaled));                 // 8..16
+  return sign | ((static_cast<uint32_t>(ex + 7) << 3) + (q - 8u));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// max over the 16 lanes that share lane / 16
+__device__ __forceinline__ float group16_max(float v) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ __forceinline__ float silu_mul(float gate, float up) { return (gate / (1.0f + expf(-gate))) * up; }
+
+// 16x16x128 FP8 x FP8 block product (e4m3 both sides, unit scales).
+__device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 127, 0, 127);
+}
+
+// 16x16x128 FP8 (A) x FP4 e2m1 (B) with one e8m0 scale per lane on B.
+__device__ __forceinline__ f32x4 mfma_fp8_fp4(const i32x8& a, const i32x8& b, int scale_b) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 4, 0, 127, 0, scale_b);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace moe_tail

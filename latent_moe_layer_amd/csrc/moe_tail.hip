@@ -1,0 +1,364 @@
+// Host side of the latent-MoE tail library: argument checks, workspace
+// layout, launch planning.  Every check runs before the first HIP call, so a
+// rejected call enqueues nothing (the pages' "fail closed" rule for
+// unsupported layouts and token counts: vLLM PR 53556, "Sequence-parallel
+// implementation"; DeepGEMM PR 416 mirror, Compatibility).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/moe_tail.h"
+#include "dense_gemm.hpp"
+#include "quant_norm.hpp"
+#include "route.hpp"
+#include "routed_gemm.hpp"
+
+using namespace moe_tail;
+
+namespace {
+
+constexpr int32_t kMaxTokens = 1 << 20;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// required pointer: non-null and 16-byte aligned when the tensor is non-empty
+bool ptr_ok(const void* p, size_t bytes) { return bytes == 0 || (p != nullptr && aligned16(p)); }
+
+int check_dims(const moe_tail_dims* d) {
+  if (d == nullptr) return MOE_TAIL_ERR_INVALID;
+  if (d->hidden <= 0 || d->latent <= 0 || d->inter <= 0 || d->shared_inter <= 0 || d->num_experts <= 0)
+    return MOE_TAIL_ERR_INVALID;
+  if (d->top_k < 1 || d->top_k > d->num_experts) return MOE_TAIL_ERR_INVALID;
+  if (!(d->rms_eps > 0.0f) || !std::isfinite(d->rms_eps)) return MOE_TAIL_ERR_INVALID;
+  if (d->wfmt != MOE_TAIL_W_FP8_BLOCK128 && d->wfmt != MOE_TAIL_W_MXFP4) return MOE_TAIL_ERR_UNSUPPORTED;
+  if (d->hidden % 256 || d->latent % 256 || d->latent > 256 * kNormMaxCols) return MOE_TAIL_ERR_UNSUPPORTED;
+  if (d->inter % 128 || d->shared_inter % 128 || d->inter > 128 * kMaxKBlocks) return MOE_TAIL_ERR_UNSUPPORTED;
+  if (d->latent > 128 * kMaxKBlocks) return MOE_TAIL_ERR_UNSUPPORTED;
+  if (d->num_experts > 1024 || d->top_k > 16) return MOE_TAIL_ERR_UNSUPPORTED;
+  return MOE_TAIL_OK;
+}
+
+int check_counts(int32_t Mr, int32_t Ms) {
+  if (Mr < 0 || Ms < 0 || Mr > Ms || Ms > kMaxTokens) return MOE_TAIL_ERR_INVALID;
+  return MOE_TAIL_OK;
+}
+
+// Split-K plan of one dense BF16 GEMM: enough workgroups to cover the chip
+// (256 CUs) several times over when the row count is small.
+struct DensePlan {
+  int mt, nt, splits, kps;
+};
+
+DensePlan plan_dense(int M, int ntiles, int K) {
+  DensePlan p;
+  p.mt = (M + kDM - 1) / kDM;
+  p.nt = ntiles;
+  const int nk = K / 128;
+  const int base = p.mt * p.nt;
+  int s = 1;
+  if (base > 0 && base < 512) s = std::min(nk, (1024 + base - 1) / base);
+  p.kps = (nk + s - 1) / s;
+  p.splits = (nk + p.kps - 1) / p.kps;
+  return p;
+}
+
+struct Plans {
+  DensePlan s1, s2, up;
+};
+
+Plans plan_all(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
+  Plans p;
+  p.s1 = plan_dense(Ms, d.shared_inter / 64, d.hidden);
+  p.s2 = plan_dense(Ms, d.hidden / 128, d.shared_inter);
+  p.up = plan_dense(Mr, d.hidden / 128, d.latent);
+  return p;
+}
+
+struct Layout {
+  size_t logits, hist, masks;                       // routing scratch
+  size_t xq, sx, hq, sh, y, rn, hs, s, partial;     // forward intermediates
+  size_t total;
+};
+
+Layout layout_of(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
+  const size_t L = d.latent, H = d.hidden, I = d.inter, Is = d.shared_inter, E = d.num_experts, k = d.top_k;
+  const size_t R = static_cast<size_t>(Mr) * k;
+  const size_t ng = (static_cast<size_t>(Mr) + kGroup - 1) / kGroup;
+  const Plans p = plan_all(d, Mr, Ms);
+  size_t partial = 0;
+  if (p.s1.splits > 1) partial = std::max(partial, static_cast<size_t>(p.s1.splits) * Ms * 2 * Is * 4);
+  if (p.s2.splits > 1) partial = std::max(partial, static_cast<size_t>(p.s2.splits) * Ms * H * 4);
+  if (p.up.splits > 1) partial = std::max(partial, static_cast<size_t>(p.up.splits) * Mr * H * 4);
+  Layout l;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  l.logits = take(static_cast<size_t>(Mr) * E * 4);
+  l.hist = take(E * ng * 4);
+  l.masks = take(ng * E * 8);
+  l.xq = take(static_cast<size_t>(Mr) * L);
+  l.sx = take(static_cast<size_t>(Mr) * (L / 128) * 4);
+  l.hq = take(R * I);
+  l.sh = take(R * (I / 128) * 4);
+  l.y = take(R * L * 4);
+  l.rn = take(static_cast<size_t>(Mr) * L * 2);
+  l.hs = take(static_cast<size_t>(Ms) * Is * 2);
+  l.s = take(static_cast<size_t>(Mr) * H * 2);
+  l.partial = take(partial);
+  l.total = o;
+  return l;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? MOE_TAIL_OK : MOE_TAIL_ERR_DEVICE; }
+
+int check_weights(const moe_tail_dims& d, const moe_tail_weights* w, bool need_router, bool need_routed,
+                  bool need_shared, bool need_up) {
+  if (w == nullptr) return MOE_TAIL_ERR_INVALID;
+  const size_t E = d.num_experts, L = d.latent, H = d.hidden, I = d.inter, Is = d.shared_inter;
+  if (need_router) {
+    if (!ptr_ok(w->gate, E * L * 4)) return MOE_TAIL_ERR_INVALID;
+    if (w->gate_bias != nullptr && !aligned16(w->gate_bias)) return MOE_TAIL_ERR_INVALID;
+  }
+  if (need_routed) {
+    if (!ptr_ok(w->w1, 1) || !ptr_ok(w->w1_scale, 1) || !ptr_ok(w->w2, 1) || !ptr_ok(w->w2_scale, 1))
+      return MOE_TAIL_ERR_INVALID;
+    if (!ptr_ok(w->rms_gamma, L * 2)) return MOE_TAIL_ERR_INVALID;
+  }
+  if (need_shared && (!ptr_ok(w->ws1, 2 * Is * H * 2) || !ptr_ok(w->ws2, H * Is * 2))) return MOE_TAIL_ERR_INVALID;
+  if (need_up && !ptr_ok(w->w_up, H * L * 2)) return MOE_TAIL_ERR_INVALID;
+  (void)I;
+  return MOE_TAIL_OK;
+}
+
+int check_routing(const moe_tail_routing* r, int32_t Mr, int k, int E) {
+  if (r == nullptr) return MOE_TAIL_ERR_INVALID;
+  const size_t R = static_cast<size_t>(Mr) * k;
+  if (!ptr_ok(r->topk_ids, R * 4) || !ptr_ok(r->topk_weights, R * 4) || !ptr_ok(r->sorted_pair, R * 4) ||
+      !ptr_ok(r->pair_to_row, R * 4) || !ptr_ok(r->expert_offsets, static_cast<size_t>(E + 1) * 4))
+    return MOE_TAIL_ERR_INVALID;
+  return MOE_TAIL_OK;
+}
+
+template <int kEpi>
+void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int M, int N, int K, float* partial,
+                  const DenseEpi& ep, hipStream_t st) {
+  if (M == 0) return;
+  dim3 grid(p.mt, p.nt, p.splits);
+  hipLaunchKernelGGL(k_dense_bf16<kEpi>, grid, dim3(256), 0, st, A, B, M, N, K, p.kps, partial, ep);
+  if (p.splits > 1) {
+    const int ncols = (kEpi == EPI_SWIGLU) ? ep.half : N;
+    const long n = static_cast<long>(M) * ncols;
+    hipLaunchKernelGGL(k_dense_reduce<kEpi>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+                       partial, M, N, p.splits, ep);
+  }
+}
+
+int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
+                 const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, uint16_t* out,
+                 uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  rc = check_counts(Mr, Ms);
+  if (rc) return rc;
+  const moe_tail_dims& d = *dims;
+  const int L = d.latent, H = d.hidden, I = d.inter, Is = d.shared_inter, E = d.num_experts, k = d.top_k;
+  rc = check_weights(d, w, false, Mr > 0, Ms > 0, Mr > 0);
+  if (rc) return rc;
+  if (Mr > 0 && (rc = check_routing(routing, Mr, k, E))) return rc;
+  if (!ptr_ok(x_lat, static_cast<size_t>(Mr) * L * 2) || !ptr_ok(x_hid, static_cast<size_t>(Ms) * H * 2) ||
+      !ptr_ok(out, static_cast<size_t>(Mr) * H * 2))
+    return MOE_TAIL_ERR_INVALID;
+  if ((Ms > Mr) != (shared_out != nullptr)) return MOE_TAIL_ERR_INVALID;
+  if (shared_out != nullptr && !aligned16(shared_out)) return MOE_TAIL_ERR_INVALID;
+  const Layout lay = layout_of(d, Mr, Ms);
+  if (ws_bytes < lay.total) return MOE_TAIL_ERR_WORKSPACE;
+  if (lay.total > 0 && !ptr_ok(ws, 1)) return MOE_TAIL_ERR_INVALID;
+  if (events != nullptr)
+    for (int i = 0; i <= MOE_TAIL_NUM_STAGES; ++i)
+      if (events[i] == nullptr) return MOE_TAIL_ERR_INVALID;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // launch errors below are ours, not an earlier call's
+  auto mark = [&](int i) {
+    if (events) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+  };
+  const Plans plans = plan_all(d, Mr, Ms);
+  const size_t R = static_cast<size_t>(Mr) * k;
+  uint8_t* xq = at<uint8_t>(ws, lay.xq);
+  float* sx = at<float>(ws, lay.sx);
+  uint8_t* hq = at<uint8_t>(ws, lay.hq);
+  float* sh = at<float>(ws, lay.sh);
+  float* y = at<float>(ws, lay.y);
+  uint16_t* rn = at<uint16_t>(ws, lay.rn);
+  uint16_t* hs = at<uint16_t>(ws, lay.hs);
+  uint16_t* s = at<uint16_t>(ws, lay.s);
+  float* partial = at<float>(ws, lay.partial);
+
+  // 0: quantize x_lat
+  mark(0);
+  if (Mr > 0) {
+    const long blocks = static_cast<long>(Mr) * (L / 128);
+    hipLaunchKernelGGL(k_quant_1x128<true>, dim3(static_cast<unsigned>((blocks + 3) / 4)), dim3(256), 0, st, x_lat,
+                       xq, sx, Mr, L);
+  }
+  // 1, 2: routed L1 and L2
+  const unsigned max_tiles = static_cast<unsigned>((R + kBM - 1) / kBM + E);
+  mark(1);
+  if (Mr > 0) {
+    if (d.wfmt == MOE_TAIL_W_FP8_BLOCK128)
+      hipLaunchKernelGGL(k_routed_l1<FMT_FP8>, dim3(max_tiles, I / 128), dim3(256), 0, st, xq, sx,
+                         routing->sorted_pair, routing->expert_offsets, w->w1, w->w1_scale, hq, sh, E, k, L, I);
+    else
+      hipLaunchKernelGGL(k_routed_l1<FMT_MXFP4>, dim3(max_tiles, I / 128), dim3(256), 0, st, xq, sx,
+                         routing->sorted_pair, routing->expert_offsets, w->w1, w->w1_scale, hq, sh, E, k, L, I);
+  }
+  mark(2);
+  if (Mr > 0) {
+    if (d.wfmt == MOE_TAIL_W_FP8_BLOCK128)
+      hipLaunchKernelGGL(k_routed_l2<FMT_FP8>, dim3(max_tiles, L / 128), dim3(256), 0, st, hq, sh,
+                         routing->expert_offsets, w->w2, w->w2_scale, y, E, L, I);
+    else
+      hipLaunchKernelGGL(k_routed_l2<FMT_MXFP4>, dim3(max_tiles, L / 128), dim3(256), 0, st, hq, sh,
+                         routing->expert_offsets, w->w2, w->w2_scale, y, E, L, I);
+  }
+  // 3: combine + RMSNorm
+  mark(3);
+  if (Mr > 0)
+    hipLaunchKernelGGL(k_combine_rmsnorm, dim3(Mr), dim3(256), 0, st, y, routing->topk_weights, routing->pair_to_row,
+                       w->rms_gamma, rn, L, k, d.rms_eps);
+  // 4: shared L1 + SwiGLU
+  mark(4);
+  {
+    DenseEpi ep{Mr, Is, hs, nullptr, nullptr};
+    launch_dense<EPI_SWIGLU>(plans.s1, x_hid, w->ws1, Ms, Is, H, partial, ep, st);
+  }
+  // 5: shared L2 -> s (rows < Mr) and shared_out (rows >= Mr)
+  mark(5);
+  {
+    DenseEpi ep{Mr, Is, s, shared_out, nullptr};
+    launch_dense<EPI_SHARED>(plans.s2, hs, w->ws2, Ms, H, Is, partial, ep, st);
+  }
+  // 6: up-projection + FP32 shared add
+  mark(6);
+  {
+    DenseEpi ep{Mr, Is, out, nullptr, s};
+    launch_dense<EPI_UPADD>(plans.up, rn, w->w_up, Mr, H, L, partial, ep, st);
+  }
+  mark(7);
+  return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_tail_strerror(int status) {
+  switch (status) {
+    case MOE_TAIL_OK: return "ok";
+    case MOE_TAIL_ERR_INVALID: return "invalid argument";
+    case MOE_TAIL_ERR_UNSUPPORTED: return "unsupported dims or format";
+    case MOE_TAIL_ERR_WORKSPACE: return "workspace too small";
+    case MOE_TAIL_ERR_DEVICE: return "device launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_tail_workspace_bytes(const moe_tail_dims* dims, int32_t Mr, int32_t Ms) {
+  if (check_dims(dims) || check_counts(Mr, Ms)) return 0;
+  return layout_of(*dims, Mr, Ms).total;
+}
+
+int moe_tail_workspace_layout(const moe_tail_dims* dims, int32_t Mr, int32_t Ms, size_t offsets[MOE_TAIL_WS_NUM]) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if ((rc = check_counts(Mr, Ms))) return rc;
+  if (offsets == nullptr) return MOE_TAIL_ERR_INVALID;
+  const Layout l = layout_of(*dims, Mr, Ms);
+  offsets[MOE_TAIL_WS_XQ] = l.xq;
+  offsets[MOE_TAIL_WS_SX] = l.sx;
+  offsets[MOE_TAIL_WS_HQ] = l.hq;
+  offsets[MOE_TAIL_WS_SH] = l.sh;
+  offsets[MOE_TAIL_WS_Y] = l.y;
+  offsets[MOE_TAIL_WS_RN] = l.rn;
+  offsets[MOE_TAIL_WS_HS] = l.hs;
+  offsets[MOE_TAIL_WS_S] = l.s;
+  return MOE_TAIL_OK;
+}
+
+int moe_tail_route(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
+                   const moe_tail_routing* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (Mr < 0 || Mr > kMaxTokens) return MOE_TAIL_ERR_INVALID;
+  const moe_tail_dims& d = *dims;
+  const int L = d.latent, E = d.num_experts, k = d.top_k;
+  if ((rc = check_weights(d, w, true, false, false, false))) return rc;
+  if ((rc = check_routing(out, Mr, k, E))) return rc;
+  if (!ptr_ok(x_lat, static_cast<size_t>(Mr) * L * 2)) return MOE_TAIL_ERR_INVALID;
+  // the routing scratch sits at the front of the workspace and depends on Mr only
+  const Layout lay = layout_of(d, Mr, Mr);
+  if (ws_bytes < lay.xq) return MOE_TAIL_ERR_WORKSPACE;
+  if (lay.xq > 0 && !ptr_ok(ws, 1)) return MOE_TAIL_ERR_INVALID;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // launch errors below are ours, not an earlier call's
+  const int ng = (Mr + kGroup - 1) / kGroup;
+  float* logits = at<float>(ws, lay.logits);
+  int32_t* hist = at<int32_t>(ws, lay.hist);
+  unsigned long long* masks = at<unsigned long long>(ws, lay.masks);
+  if (Mr > 0) {
+    const int egroups = (E + 4 * kLogitExpPerWave - 1) / (4 * kLogitExpPerWave);
+    hipLaunchKernelGGL(k_router_logits, dim3((Mr + kLogitTok - 1) / kLogitTok, egroups), dim3(256), 0, st, x_lat,
+                       w->gate, w->gate_bias, logits, Mr, L, E);
+    hipLaunchKernelGGL(k_router_topk, dim3(ng), dim3(1024), 0, st, logits, out->topk_ids, out->topk_weights, hist,
+                       masks, Mr, E, k, ng);
+  }
+  hipLaunchKernelGGL(k_router_scan, dim3(1), dim3(1024), 0, st, hist, out->expert_offsets, E, ng);
+  if (Mr > 0)
+    hipLaunchKernelGGL(k_router_scatter, dim3(ng), dim3(64), 0, st, out->topk_ids, hist, masks, out->sorted_pair,
+                       out->pair_to_row, Mr, E, k, ng);
+  return launched();
+}
+
+int moe_tail_forward(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
+                     const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, uint16_t* out,
+                     uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, out, shared_out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_tail_forward_profiled(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat,
+                              int32_t Mr, const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing,
+                              uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream,
+                              void* const* stage_events) {
+  if (stage_events == nullptr) return MOE_TAIL_ERR_INVALID;
+  return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, out, shared_out, ws, ws_bytes, stream, stage_events);
+}
+
+int moe_tail_quant_fp8_1x128(const void* x, int32_t x_is_bf16, int32_t rows, int32_t cols, uint8_t* codes,
+                             float* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 128) return MOE_TAIL_ERR_INVALID;
+  const size_t n = static_cast<size_t>(rows) * cols;
+  if (!ptr_ok(x, n) || !ptr_ok(codes, n) || !ptr_ok(scales, n / 32)) return MOE_TAIL_ERR_INVALID;
+  if (rows == 0) return MOE_TAIL_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const long blocks = static_cast<long>(rows) * (cols / 128);
+  const dim3 grid(static_cast<unsigned>((blocks + 3) / 4));
+  if (x_is_bf16)
+    hipLaunchKernelGGL(k_quant_1x128<true>, grid, dim3(256), 0, st, x, codes, scales, rows, cols);
+  else
+    hipLaunchKernelGGL(k_quant_1x128<false>, grid, dim3(256), 0, st, x, codes, scales, rows, cols);
+  return launched();
+}
+
+}  // extern "C"

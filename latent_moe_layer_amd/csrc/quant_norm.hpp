@@ -1,0 +1,83 @@
+// 1x128 FP8 activation quantizer and the fused top-k combine + RMSNorm.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe_tail {
+
+// One wave per (row, 128-wide block); each lane owns two neighbouring
+// elements.  s = amax / 448 (IEEE division), 1.0 for an all-zero block;
+// code = e4m3(x / s).  Activations are quantized per 1x128 block with fp32
+// scales, matching the 128-wide K blocks of the weights.
+template <bool kBf16In>
+__global__ __launch_bounds__(256) void k_quant_1x128(const void* __restrict__ x, uint8_t* __restrict__ codes,
+                                                     float* __restrict__ scales, int rows, int cols) {
+  const int lane = threadIdx.x & 63;
+  const long blk = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int nb = cols / 128;
+  if (blk >= static_cast<long>(rows) * nb) return;
+  const long r = blk / nb;
+  const int b = static_cast<int>(blk % nb);
+  const size_t base = static_cast<size_t>(r) * cols + 128 * b + 2 * lane;
+  float v0, v1;
+  if (kBf16In) {
+    const uint32_t pair = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(x) + base);
+    v0 = bf16_bits_to_f32(pair & 0xffffu);
+    v1 = bf16_bits_to_f32(pair >> 16);
+  } else {
+    const float2 p = *reinterpret_cast<const float2*>(static_cast<const float*>(x) + base);
+    v0 = p.x;
+    v1 = p.y;
+  }
+  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  const uint32_t q = f32_to_e4m3(v0 / s) | (f32_to_e4m3(v1 / s) << 8);
+  *reinterpret_cast<uint16_t*>(codes + base) = static_cast<uint16_t>(q);
+  if (lane == 0) scales[static_cast<size_t>(r) * nb + b] = s;
+}
+
+// One workgroup (256 threads) per routed token: z = sum_j w_j * y[row(t, j)]
+// in FP32 (slot order), then RMSNorm with FP32 statistics:
+// rn = bf16((z / sqrt(mean(z^2) + eps)) * gamma).  The routed latent is
+// normalised before the up-projection ("[Kimi K3][Kernel] Fuse BF16 shared
+// experts into latent MegaMoE tail", Summary); FP32-internal statistics follow
+// the bias study in tokenspeed PR 1062.
+constexpr int kNormMaxCols = 32;  // L <= 256 * 32
+
+__global__ __launch_bounds__(256) void k_combine_rmsnorm(const float* __restrict__ y, const float* __restrict__ topk_w,
+                                                         const int32_t* __restrict__ pair_to_row,
+                                                         const uint16_t* __restrict__ gamma,
+                                                         uint16_t* __restrict__ rn, int L, int k, float eps) {
+  __shared__ float s_part[4];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  float z[kNormMaxCols];
+  const int nc = L / 256;
+#pragma unroll
+  for (int c = 0; c < kNormMaxCols; ++c) z[c] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const float w = topk_w[static_cast<size_t>(t) * k + j];
+    const float* yr = y + static_cast<size_t>(pair_to_row[static_cast<size_t>(t) * k + j]) * L + tid;
+#pragma unroll
+    for (int c = 0; c < kNormMaxCols; ++c)
+      if (c < nc) z[c] = z[c] + w * yr[256 * c];
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kNormMaxCols; ++c)
+    if (c < nc) ss += z[c] * z[c];
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) s_part[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+  const float r = 1.0f / sqrtf(tot / static_cast<float>(L) + eps);
+#pragma unroll
+  for (int c = 0; c < kNormMaxCols; ++c)
+    if (c < nc) {
+      const int col = tid + 256 * c;
+      rn[static_cast<size_t>(t) * L + col] =
+          static_cast<uint16_t>(f32_to_bf16_bits((z[c] * r) * bf16_bits_to_f32(gamma[col])));
+    }
+}
+
+}  // namespace moe_tail

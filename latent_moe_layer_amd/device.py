@@ -1,0 +1,97 @@
+"""Device-side buffers for one tail: uploads a seeded ``synth.Inputs`` with
+torch (device memory and streams only) and calls the C ABI through
+``binding``.  No arithmetic of the tail happens here."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+from . import synth
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class DeviceTail:
+    """Weights, inputs, routing, outputs and workspace of one tail on one GPU."""
+
+    def __init__(self, inp: synth.Inputs, device="cuda:0", Mr: int | None = None, Ms: int | None = None):
+        wl = inp.wl
+        self.inp = inp
+        self.device = torch.device(device)
+        self.Mr = inp.x_lat.shape[0] if Mr is None else Mr
+        self.Ms = inp.x_hid.shape[0] if Ms is None else Ms
+        self.dims = B.make_dims(wl.H, wl.L, wl.E, wl.k, wl.I, wl.Is, wl.wfmt, wl.rms_eps)
+        d = self.device
+        self.t = {name: _dev(getattr(inp, name), d) for name in
+                  ("x_lat", "x_hid", "gate", "gate_bias", "w1", "w1_scale", "w2", "w2_scale", "gamma", "w_up",
+                   "ws1", "ws2")}
+        t = self.t
+        self.weights = B.make_weights(gate=t["gate"], gate_bias=t["gate_bias"], w1=t["w1"], w1_scale=t["w1_scale"],
+                                      w2=t["w2"], w2_scale=t["w2_scale"], rms_gamma=t["gamma"], w_up=t["w_up"],
+                                      ws1=t["ws1"], ws2=t["ws2"])
+        self.alloc(self.Mr, self.Ms)
+
+    def alloc(self, Mr: int, Ms: int) -> None:
+        """(Re)allocate routing, outputs and workspace for Mr routed / Ms shared tokens."""
+        wl, d = self.inp.wl, self.device
+        self.Mr, self.Ms = Mr, Ms
+        R = Mr * wl.k
+        self.topk_ids = torch.empty((Mr, wl.k), dtype=torch.int32, device=d)
+        self.topk_w = torch.empty((Mr, wl.k), dtype=torch.float32, device=d)
+        self.offsets = torch.empty(wl.E + 1, dtype=torch.int32, device=d)
+        self.sorted_pair = torch.empty(R, dtype=torch.int32, device=d)
+        self.pair_to_row = torch.empty(R, dtype=torch.int32, device=d)
+        self.routing = B.make_routing(topk_ids=self.topk_ids, topk_weights=self.topk_w,
+                                      expert_offsets=self.offsets, sorted_pair=self.sorted_pair,
+                                      pair_to_row=self.pair_to_row)
+        self.out = torch.empty((Mr, wl.H), dtype=torch.int16, device=d)
+        self.shared_out = torch.empty((Ms - Mr, wl.H), dtype=torch.int16, device=d) if Ms > Mr else None
+        self.ws_bytes = B.moe_tail_workspace_bytes(self.dims, Mr, Ms)
+        if self.ws_bytes == 0 and (Mr or Ms):
+            raise ValueError("dims or token counts rejected by moe_tail_workspace_bytes")
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=d)
+        self.layout = B.moe_tail_workspace_layout(self.dims, Mr, Ms)
+
+    def route(self, stream=None) -> None:
+        B.moe_tail_route(self.dims, self.weights, self.t["x_lat"], self.Mr, self.routing, self.ws, self.ws_bytes,
+                         stream)
+
+    def forward(self, stream=None, events=None) -> None:
+        args = (self.dims, self.weights, self.t["x_lat"], self.Mr, self.t["x_hid"], self.Ms, self.routing, self.out,
+                self.shared_out, self.ws, self.ws_bytes, stream)
+        if events is None:
+            B.moe_tail_forward(*args)
+        else:
+            B.moe_tail_forward_profiled(*args, events)
+
+    # -------- views of the materialized intermediates (tests) --------
+    def _view(self, idx: int, dtype, shape):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        off = self.layout[idx]
+        return self.ws[off:off + n].view(dtype).view(*shape)
+
+    def intermediates(self) -> dict:
+        wl = self.inp.wl
+        Mr, Ms, R = self.Mr, self.Ms, self.Mr * wl.k
+        return {
+            "xq": self._view(B.MOE_TAIL_WS_XQ, torch.uint8, (Mr, wl.L)),
+            "sx": self._view(B.MOE_TAIL_WS_SX, torch.float32, (Mr, wl.L // 128)),
+            "hq": self._view(B.MOE_TAIL_WS_HQ, torch.uint8, (R, wl.I)),
+            "sh": self._view(B.MOE_TAIL_WS_SH, torch.float32, (R, wl.I // 128)),
+            "y": self._view(B.MOE_TAIL_WS_Y, torch.float32, (R, wl.L)),
+            "rn": self._view(B.MOE_TAIL_WS_RN, torch.int16, (Mr, wl.L)),
+            "hs": self._view(B.MOE_TAIL_WS_HS, torch.int16, (Ms, wl.Is)),
+            "s": self._view(B.MOE_TAIL_WS_S, torch.int16, (Mr, wl.H)),
+        }
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    if a.dtype == np.int16:
+        a = a.view(np.uint16)
+    return a

@@ -114,16 +114,13 @@ def _quant_fp8_block128(w: np.ndarray):
     return codes, scale
 
 
-# e2m1 magnitudes by code and the midpoints between neighbours
-_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32)
-_E2M1_MID = (_E2M1_MAG[:-1] + _E2M1_MAG[1:]) / 2
-
-
 def _quant_mxfp4(w: np.ndarray):
     """w [N, K] fp32 -> (packed [N, K/2] u8, e8m0 scales [N, K/32] u8).
 
     OCP MX v1.0: shared exponent X = floor(log2(amax)) - emax(e2m1)=2, element =
     w / 2^X rounded to nearest e2m1 (ties to even code), saturating at 6.
+    The e2m1 grid has spacing 0.5 below 2, 1 in [2, 4) and 2 from 4 on, so the
+    nearest code is an integer rounding (numpy's rint: ties to even) per range.
     """
     n, kk = w.shape
     blocks = w.reshape(n, kk // 32, 32)
@@ -134,11 +131,8 @@ def _quant_mxfp4(w: np.ndarray):
     e8m0 = (X + 127).astype(np.uint8)
     v = blocks * np.ldexp(np.float32(1.0), -X)[:, :, None].astype(np.float32)
     mag = np.abs(v)
-    code = np.zeros(mag.shape, dtype=np.uint8)
-    for i, m in enumerate(_E2M1_MID):
-        above = mag > m
-        tie_up = (mag == m) & (((i + 1) & 1) == 0)   # tie goes to the even code
-        code += (above | tie_up).astype(np.uint8)
+    code = np.where(mag < 2, np.rint(mag * 2),
+                    np.where(mag < 4, np.rint(mag) + 2, np.minimum(np.rint(mag * 0.5), 3) + 4)).astype(np.uint8)
     code |= (np.signbit(v).astype(np.uint8) << 3)
     code = code.reshape(n, kk)
     packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
@@ -182,9 +176,11 @@ def _expert_weights(wl: Workload, tag: int, e: int, n: int, kk: int, out_codes, 
     out_scales[e] = s
 
 
-def make_inputs(wl: Workload | str, Mr: int | None = None, Ms: int | None = None) -> Inputs:
+def make_inputs(wl: Workload | str, Mr: int | None = None, Ms: int | None = None,
+                routing_only: bool = False) -> Inputs:
     """Draw every input of one workload.  ``Mr``/``Ms`` override token counts
-    (the streams of x_lat / x_hid are then a prefix-compatible redraw)."""
+    (the streams of x_lat / x_hid are then a prefix-compatible redraw).
+    ``routing_only`` draws x_lat and the router only (other tensors empty)."""
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
     if Mr is not None or Ms is not None:
@@ -200,6 +196,10 @@ def make_inputs(wl: Workload | str, Mr: int | None = None, Ms: int | None = None
         gate_bias = (-wl.zipf_s * np.log(np.arange(1, E + 1, dtype=np.float64))).astype(np.float32)
     else:
         gate_bias = np.zeros(E, np.float32)
+    if routing_only:
+        e8, e16 = np.zeros(0, np.uint8), np.zeros(0, np.uint16)
+        return Inputs(wl, x_lat, e16, gate, gate_bias, e8, np.zeros(0, np.float32), e8, np.zeros(0, np.float32),
+                      e16, e16, e16, e16)
     if wl.wfmt == WFMT_FP8:
         w1 = np.empty((E, 2 * I, L), np.uint8)
         w1s = np.empty((E, 2 * I // 128, L // 128), np.float32)

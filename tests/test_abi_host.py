@@ -1,0 +1,164 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/moe_tail.h declares, sizes its workspace, and rejects
+bad arguments before touching the device ("fail closed")."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from latent_moe_layer_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(moe_tail_\w+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = B.lib()
+    declared = _declared_functions()
+    assert declared >= set(B.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+DIMS = dict(hidden=7168, latent=3584, num_experts=64, top_k=8, inter=2048, shared_inter=2048, wfmt=0, rms_eps=1e-6)
+
+
+def dims(**kw):
+    d = dict(DIMS)
+    d.update(kw)
+    return B.make_dims(**d)
+
+
+def test_workspace_bytes_and_layout():
+    d = dims()
+    n = B.moe_tail_workspace_bytes(d, 128, 128)
+    offs = B.moe_tail_workspace_layout(d, 128, 128)
+    assert n > 0 and all(o % 256 == 0 for o in offs) and max(offs) < n
+    assert sorted(offs) == offs
+    # y holds Mr*k rows of fp32 latent
+    assert offs[B.MOE_TAIL_WS_RN] - offs[B.MOE_TAIL_WS_Y] >= 128 * 8 * 3584 * 4
+    # the independent-count case (more shared than routed tokens)
+    assert B.moe_tail_workspace_bytes(dims(num_experts=384), 2048, 8192) > 0
+    assert B.moe_tail_workspace_bytes(d, 0, 0) >= 0
+
+
+@pytest.mark.parametrize("kw,Mr,Ms", [
+    (dict(top_k=0), 16, 16),
+    (dict(top_k=9, num_experts=8), 16, 16),
+    (dict(rms_eps=0.0), 16, 16),
+    (dict(rms_eps=float("nan")), 16, 16),
+    (dict(hidden=-7168), 16, 16),
+    ({}, 17, 16),          # Mr > Ms
+    ({}, -1, 16),
+    ({}, 16, (1 << 20) + 1),
+])
+def test_invalid_args_size_zero(kw, Mr, Ms):
+    assert B.moe_tail_workspace_bytes(dims(**kw), Mr, Ms) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(hidden=7000), dict(latent=3600), dict(inter=2000), dict(shared_inter=100),
+                                dict(num_experts=1025), dict(top_k=17, num_experts=64), dict(wfmt=2),
+                                dict(latent=16384)])
+def test_unsupported_dims(kw):
+    offs = (C.c_size_t * B.MOE_TAIL_WS_NUM)()
+    rc = B.lib().moe_tail_workspace_layout(C.byref(dims(**kw)), 16, 16, offs)
+    assert rc == B.MOE_TAIL_ERR_UNSUPPORTED
+
+
+def _fake_weights(align=256):
+    # host addresses that are never dereferenced: every call below fails its checks first
+    base = 1 << 40
+    names = ("gate", "gate_bias", "w1", "w1_scale", "w2", "w2_scale", "rms_gamma", "w_up", "ws1", "ws2")
+    return B.Weights(**{n: base + i * (1 << 30) + (0 if align else 8) for i, n in enumerate(names)})
+
+
+def _fake_routing(null=None, misalign=None):
+    base = 1 << 41
+    names = ("topk_ids", "topk_weights", "expert_offsets", "sorted_pair", "pair_to_row")
+    vals = {n: base + i * (1 << 30) for i, n in enumerate(names)}
+    if null:
+        vals[null] = None
+    if misalign:
+        vals[misalign] += 4
+    return B.Routing(**vals)
+
+
+def _route(d, w, x, Mr, r, ws, nbytes):
+    return B.lib().moe_tail_route(C.byref(d), C.byref(w), x, Mr, C.byref(r), ws, nbytes, None)
+
+
+def _fwd(d, w, x_lat, Mr, x_hid, Ms, r, out, shared_out, ws, nbytes):
+    return B.lib().moe_tail_forward(C.byref(d), C.byref(w), x_lat, Mr, x_hid, Ms, C.byref(r), out, shared_out, ws,
+                                    nbytes, None)
+
+
+X = 1 << 42
+OUT = 1 << 43
+SOUT = 1 << 44
+WS = 1 << 45
+
+
+def test_route_rejections():
+    d, w = dims(), _fake_weights()
+    need = B.moe_tail_workspace_bytes(d, 16, 16)
+    assert _route(d, w, X, 16, _fake_routing(null="sorted_pair"), WS, need) == B.MOE_TAIL_ERR_INVALID
+    assert _route(d, w, X, 16, _fake_routing(misalign="topk_ids"), WS, need) == B.MOE_TAIL_ERR_INVALID
+    assert _route(d, w, None, 16, _fake_routing(), WS, need) == B.MOE_TAIL_ERR_INVALID
+    assert _route(d, w, X + 2, 16, _fake_routing(), WS, need) == B.MOE_TAIL_ERR_INVALID
+    assert _route(d, w, X, -3, _fake_routing(), WS, need) == B.MOE_TAIL_ERR_INVALID
+    assert _route(d, w, X, 16, _fake_routing(), WS, 0) == B.MOE_TAIL_ERR_WORKSPACE
+    assert _route(dims(wfmt=5), w, X, 16, _fake_routing(), WS, need) == B.MOE_TAIL_ERR_UNSUPPORTED
+    wn = _fake_weights()
+    wn.gate = None
+    assert _route(d, wn, X, 16, _fake_routing(), WS, need) == B.MOE_TAIL_ERR_INVALID
+
+
+def test_forward_rejections():
+    d, w, r = dims(), _fake_weights(), _fake_routing()
+    need = B.moe_tail_workspace_bytes(d, 16, 32)
+    # shared_out must be given exactly when Ms > Mr
+    assert _fwd(d, w, X, 16, X, 32, r, OUT, None, WS, need) == B.MOE_TAIL_ERR_INVALID
+    need16 = B.moe_tail_workspace_bytes(d, 16, 16)
+    assert _fwd(d, w, X, 16, X, 16, r, OUT, SOUT, WS, need16) == B.MOE_TAIL_ERR_INVALID
+    assert _fwd(d, w, X, 17, X, 16, r, OUT, None, WS, need16) == B.MOE_TAIL_ERR_INVALID
+    assert _fwd(d, w, X, 16, X, 32, r, OUT, SOUT, WS, need - 1) == B.MOE_TAIL_ERR_WORKSPACE
+    assert _fwd(d, w, X, 16, X, 32, r, None, SOUT, WS, need) == B.MOE_TAIL_ERR_INVALID
+    assert _fwd(d, w, X, 16, X, 32, r, OUT + 8, SOUT, WS, need) == B.MOE_TAIL_ERR_INVALID
+    assert _fwd(d, w, X, 16, X, 32, _fake_routing(null="pair_to_row"), OUT, SOUT, WS, need) == B.MOE_TAIL_ERR_INVALID
+    assert _fwd(d, _fake_weights(align=0), X, 16, X, 32, r, OUT, SOUT, WS, need) == B.MOE_TAIL_ERR_INVALID
+    assert _fwd(dims(hidden=7040), w, X, 16, X, 32, r, OUT, SOUT, WS, need) == B.MOE_TAIL_ERR_UNSUPPORTED
+    wn = _fake_weights()
+    wn.ws2 = None
+    assert _fwd(d, wn, X, 16, X, 32, r, OUT, SOUT, WS, need) == B.MOE_TAIL_ERR_INVALID
+    assert B.lib().moe_tail_forward_profiled(C.byref(d), C.byref(w), X, 16, X, 32, C.byref(r), OUT, SOUT, WS, need,
+                                             None, None) == B.MOE_TAIL_ERR_INVALID
+
+
+def test_quant_rejections():
+    q = B.lib().moe_tail_quant_fp8_1x128
+    assert q(X, 1, 4, 100, OUT, SOUT, None) == B.MOE_TAIL_ERR_INVALID
+    assert q(X, 1, -1, 128, OUT, SOUT, None) == B.MOE_TAIL_ERR_INVALID
+    assert q(None, 1, 4, 128, OUT, SOUT, None) == B.MOE_TAIL_ERR_INVALID
+    assert q(X, 1, 4, 128, OUT + 1, SOUT, None) == B.MOE_TAIL_ERR_INVALID
+
+
+def test_strerror():
+    assert B.strerror(0) == "ok"
+    assert "workspace" in B.strerror(B.MOE_TAIL_ERR_WORKSPACE)
+    assert B.strerror(99) == "unknown status"
+
+
+def test_status_error_type():
+    with pytest.raises(B.MoeTailError) as e:
+        B._check(B.MOE_TAIL_ERR_UNSUPPORTED, "x")
+    assert e.value.status == B.MOE_TAIL_ERR_UNSUPPORTED

@@ -1,0 +1,241 @@
+"""Parity of the HIP path against the CPU oracle on small and ragged tails,
+edge cases and invariants.  Runs on an MI355X only (marker ``gpu``)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from latent_moe_layer_amd import binding as B
+from latent_moe_layer_amd import synth
+from latent_moe_layer_amd.device import DeviceTail, to_np
+from oracle import oracle as orc
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()  # a missing library fails loudly here
+
+
+def run(inp, Mr=None, Ms=None):
+    dev = DeviceTail(inp, "cuda:0", Mr=Mr, Ms=Ms)
+    dev.route()
+    dev.forward()
+    torch.cuda.synchronize()
+    return dev
+
+
+def check_routing(dev, inp):
+    Mr, wl = dev.Mr, inp.wl
+    ids, w = to_np(dev.topk_ids), to_np(dev.topk_w)
+    oids, ow = orc.route(inp.x_lat[:Mr], inp.gate, inp.gate_bias, wl.k)
+    assert np.array_equal(ids, oids), "expert ids differ"
+    assert np.max(np.abs(w - ow), initial=0.0) <= 1e-6, "routing weights differ"
+    off, sp, p2r = orc.permute(oids, wl.E)
+    assert np.array_equal(to_np(dev.offsets), off)
+    assert np.array_equal(to_np(dev.sorted_pair), sp)
+    assert np.array_equal(to_np(dev.pair_to_row), p2r)
+    return oids, ow, p2r
+
+
+def check_forward(dev, inp, sel=None, report=None):
+    """Compare outputs and intermediates on the tokens in `sel` (default all)."""
+    wl, Mr, Ms = inp.wl, dev.Mr, dev.Ms
+    oids, ow, p2r = check_routing(dev, inp)
+    if sel is None:
+        sel = np.arange(Ms, dtype=np.int32)
+    sel = np.asarray(sel, np.int32)
+    ref = orc.forward(inp, oids, ow, sel=sel, Mr=Mr, Ms=Ms)
+    inter = {k: to_np(v) for k, v in dev.intermediates().items()}
+    rsel = np.flatnonzero(sel < Mr)
+    ssel = np.flatnonzero(sel >= Mr)
+    stats = {}
+    if rsel.size:
+        toks = sel[rsel]
+        # x codes and scales: bit-exact
+        assert np.array_equal(inter["xq"][toks], ref.xq[rsel]), "x codes differ"
+        assert np.array_equal(inter["sx"][toks], ref.sx[rsel]), "x scales differ"
+        # h codes: the midpoint rule
+        rows = p2r.reshape(Mr, wl.k)[toks]                      # [n, k]
+        n_mis, n_tot = P.check_h_codes(inter["hq"][rows], inter["sh"][rows], ref.hq[rsel], ref.sh[rsel],
+                                       ref.h[rsel])
+        stats["h_flips"] = (n_mis, n_tot)
+        # routed L2 output and the normalized latent
+        ymax, ymean = P.rel_errors(inter["y"][rows], ref.y[rsel])
+        assert ymax <= 2e-2 and ymean <= 3e-3, (ymax, ymean)
+        rmax, rmean = P.rel_errors(P.bf16_to_f32(inter["rn"][toks]), P.bf16_to_f32(ref.rn[rsel]))
+        assert rmax <= 2e-2 and rmean <= 3e-3, (rmax, rmean)
+        # final output against the oracle's FP32 value
+        got = P.bf16_to_f32(to_np(dev.out)[toks])
+        omax, omean = P.rel_errors(got, ref.out_f32[rsel])
+        stats["out"] = (omax, omean)
+        stats["out_bitwise_frac"] = float(np.mean(to_np(dev.out)[toks] == ref.out_bf16[rsel]))
+        assert omax <= P.MAX_REL and omean <= P.MEAN_REL, stats
+    if ssel.size:
+        got = P.bf16_to_f32(to_np(dev.shared_out)[sel[ssel] - Mr])
+        smax, smean = P.rel_errors(got, ref.out_f32[ssel])
+        stats["shared_out"] = (smax, smean)
+        assert smax <= P.MAX_REL and smean <= P.MEAN_REL, stats
+    if report is not None:
+        report.update(stats)
+    print(stats)
+    return stats
+
+
+# ------------------------------------------------------------------ tests --
+
+def test_quantizer_bit_exact():
+    rng = np.random.default_rng(0)
+    rows, cols = 97, 1024
+    x = (rng.standard_normal((rows, cols)) * rng.choice([1e-4, 1e-2, 1, 50, 3e4], (rows, 1))).astype(np.float32)
+    x[1, :128] = 0.0
+    x[2, 128:256] = -0.0
+    x[3, :] = np.float32(448.0)
+    vals = P.e4m3_value(np.arange(127))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    # block amax 448 -> scale exactly 1: every midpoint between codes, and one ulp below it
+    x[4:6, :] = 0.0
+    x[4, :126] = mids[:126]
+    x[4, 127] = 448.0
+    x[5, :126] = np.nextafter(mids[:126], np.float32(0))
+    x[5, 127] = 448.0
+    xd = torch.from_numpy(x).cuda()
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    s = torch.empty((rows, cols // 128), dtype=torch.float32, device="cuda")
+    B.moe_tail_quant_fp8_1x128(xd, False, rows, cols, q, s)
+    oq, os_ = orc.quant_1x128(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(q), oq)
+    assert np.array_equal(to_np(s), os_)
+    # bf16 input path
+    xb = synth.f32_to_bf16_bits(x)
+    B.moe_tail_quant_fp8_1x128(torch.from_numpy(xb.view(np.int16)).cuda(), True, rows, cols, q, s)
+    oq, os_ = orc.quant_1x128(P.bf16_to_f32(xb))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(q), oq)
+    assert np.array_equal(to_np(s), os_)
+
+
+@pytest.mark.parametrize("E,k,Mr,zipf", [(8, 2, 16, 0.0), (64, 8, 128, 0.0), (64, 8, 4096, 0.0), (128, 8, 1024, 1.2),
+                                         (384, 8, 2048, 0.0), (1024, 16, 200, 0.0), (5, 5, 70, 0.0), (9, 3, 1, 0.0),
+                                         (16, 4, 130, 0.0)])
+def test_route_bit_exact(E, k, Mr, zipf):
+    wl = synth.Workload("r", Mr=Mr, Ms=Mr, E=E, k=k, I=128, Is=128, wfmt=0, seed=100 + E, zipf_s=zipf)
+    inp = synth.make_inputs(wl, routing_only=True)
+    dev = DeviceTail(inp, "cuda:0")
+    dev.route()
+    torch.cuda.synchronize()
+    check_routing(dev, inp)
+
+
+def test_route_all_equal_logits():
+    wl = synth.Workload("r", Mr=70, Ms=70, E=16, k=4, I=128, Is=128, wfmt=0, seed=5, zero_router=True)
+    inp = synth.make_inputs(wl, routing_only=True)
+    dev = DeviceTail(inp, "cuda:0")
+    dev.route()
+    torch.cuda.synchronize()
+    ids = to_np(dev.topk_ids)
+    assert np.array_equal(ids, np.tile(np.arange(4, dtype=np.int32), (70, 1)))
+    assert np.all(to_np(dev.topk_w) == np.float32(0.25))
+    check_routing(dev, inp)
+
+
+def test_forward_tiny_full():
+    inp = synth.make_inputs("tiny")
+    dev = run(inp)
+    check_forward(dev, inp)
+
+
+@pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4])
+def test_forward_ragged(wfmt):
+    # several tiles and a ragged tail in every dimension the grid splits
+    wl = synth.Workload("ragged", Mr=37, Ms=53, E=8, k=3, I=384, Is=256, wfmt=wfmt, seed=21,
+                        zipf_s=1.2 if wfmt else 0.0)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    check_forward(dev, inp)
+
+
+def test_forward_heavy_expert_many_row_tiles():
+    # all-equal logits: every token goes to experts 0..k-1, 100 rows each (4 row tiles per expert)
+    wl = synth.Workload("heavy", Mr=100, Ms=100, E=6, k=2, I=256, Is=128, wfmt=0, seed=22, zero_router=True)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    check_forward(dev, inp)
+
+
+def test_forward_no_routed_tokens():
+    wl = synth.Workload("mr0", Mr=0, Ms=20, E=4, k=2, I=128, Is=256, wfmt=0, seed=23)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    check_forward(dev, inp)
+
+
+def test_forward_single_token_all_experts():
+    wl = synth.Workload("e_eq_k", Mr=1, Ms=1, E=4, k=4, I=128, Is=128, wfmt=0, seed=24)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    check_forward(dev, inp)
+
+
+def test_zero_shared_weights():
+    wl = replace(synth.WORKLOADS["tiny"], zero_shared=True, seed=25)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    assert np.all(to_np(dev.intermediates()["s"]) == 0)
+    check_forward(dev, inp)
+
+
+def test_identical_experts_match_dense():
+    wl = replace(synth.WORKLOADS["tiny"], identical_experts=True, zero_router=True, k=2, seed=26)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    check_forward(dev, inp)
+    dense = synth.make_inputs(replace(wl, E=1, k=1))
+    ddev = run(dense)
+    a = P.bf16_to_f32(to_np(dev.intermediates()["rn"]))
+    b = P.bf16_to_f32(to_np(ddev.intermediates()["rn"]))
+    mx, mean = P.rel_errors(a, b)
+    assert mx <= 2e-2 and mean <= 3e-3
+
+
+def test_deterministic_bitwise():
+    inp = synth.make_inputs(synth.Workload("det", Mr=45, Ms=60, E=16, k=4, I=256, Is=256, wfmt=0, seed=27))
+    a = run(inp)
+    out1, so1, hq1 = to_np(a.out).copy(), to_np(a.shared_out).copy(), to_np(a.intermediates()["hq"]).copy()
+    a.route()
+    a.forward()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(a.out), out1)
+    assert np.array_equal(to_np(a.shared_out), so1)
+    assert np.array_equal(to_np(a.intermediates()["hq"]), hq1)
+
+
+def test_shared_rows_independent_of_routed_count():
+    wl = synth.Workload("t5", Mr=24, Ms=40, E=8, k=2, I=128, Is=256, wfmt=0, seed=28)
+    inp = synth.make_inputs(wl)
+    a = run(inp)
+    b = run(inp, Mr=0, Ms=40)
+    assert np.array_equal(to_np(a.shared_out), to_np(b.shared_out)[24:])
+    # and rows < Mr of the shared output equal the Mr=0 run's rows
+    assert np.array_equal(to_np(a.intermediates()["s"]), to_np(b.shared_out)[:24])
+
+
+def test_token_permutation():
+    wl = synth.Workload("perm", Mr=33, Ms=33, E=8, k=2, I=256, Is=128, wfmt=0, seed=29)
+    inp = synth.make_inputs(wl)
+    a = run(inp)
+    perm = np.random.default_rng(1).permutation(33)
+    inp2 = synth.make_inputs(wl)
+    inp2.x_lat = inp.x_lat[perm].copy()
+    inp2.x_hid = inp.x_hid[perm].copy()
+    b = run(inp2)
+    ga, gb = P.bf16_to_f32(to_np(a.out)[perm]), P.bf16_to_f32(to_np(b.out))
+    mx, mean = P.rel_errors(gb, ga)
+    assert mx <= 2e-2 and mean <= 3e-3
+    print("bitwise-equal fraction under permutation:", float(np.mean(to_np(a.out)[perm] == to_np(b.out))))
