@@ -45,20 +45,30 @@ int check_counts(int32_t Mr, int32_t Ms) {
   return MOE_TAIL_OK;
 }
 
-// Split-K plan of one dense BF16 GEMM: enough workgroups to cover the chip
-// (256 CUs) several times over when the row count is small.
+// Plan of one dense BF16 GEMM.  Up to kSmallMaxM rows: k_dense_small (all
+// rows per workgroup, 128 B rows per workgroup) with K split until the grid
+// holds about 256 workgroups, always through FP32 partials.  More rows: the
+// tiled kernel, split only when the grid is too small to fill the chip.
 struct DensePlan {
+  bool small;
   int mt, nt, splits, kps;
 };
 
-DensePlan plan_dense(int M, int ntiles, int K) {
+DensePlan plan_dense(int M, int nbrows, int ntiles, int K) {
   DensePlan p;
-  p.mt = (M + kDM - 1) / kDM;
-  p.nt = ntiles;
   const int nk = K / 128;
-  const int base = p.mt * p.nt;
+  p.small = M <= kSmallMaxM;
   int s = 1;
-  if (base > 0 && base < 512) s = std::min(nk, (1024 + base - 1) / base);
+  if (p.small) {
+    p.mt = 1;
+    p.nt = nbrows / 128;
+    if (p.nt > 0) s = std::min(nk, std::max(1, (256 + p.nt - 1) / p.nt));
+  } else {
+    p.mt = (M + kDM - 1) / kDM;
+    p.nt = ntiles;
+    const int base = p.mt * p.nt;
+    if (base > 0 && base < 512) s = std::min(nk, (1024 + base - 1) / base);
+  }
   p.kps = (nk + s - 1) / s;
   p.splits = (nk + p.kps - 1) / p.kps;
   return p;
@@ -70,14 +80,14 @@ struct Plans {
 
 Plans plan_all(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   Plans p;
-  p.s1 = plan_dense(Ms, d.shared_inter / 64, d.hidden);
-  p.s2 = plan_dense(Ms, d.hidden / 128, d.shared_inter);
-  p.up = plan_dense(Mr, d.hidden / 128, d.latent);
+  p.s1 = plan_dense(Ms, 2 * d.shared_inter, d.shared_inter / 64, d.hidden);
+  p.s2 = plan_dense(Ms, d.hidden, d.hidden / 128, d.shared_inter);
+  p.up = plan_dense(Mr, d.hidden, d.hidden / 128, d.latent);
   return p;
 }
 
 struct Layout {
-  size_t logits, hist, masks;                       // routing scratch
+  size_t logits, hist;                              // routing scratch
   size_t xq, sx, hq, sh, y, rn, hs, s, partial;     // forward intermediates
   size_t total;
 };
@@ -88,9 +98,10 @@ Layout layout_of(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   const size_t ng = (static_cast<size_t>(Mr) + kGroup - 1) / kGroup;
   const Plans p = plan_all(d, Mr, Ms);
   size_t partial = 0;
-  if (p.s1.splits > 1) partial = std::max(partial, static_cast<size_t>(p.s1.splits) * Ms * 2 * Is * 4);
-  if (p.s2.splits > 1) partial = std::max(partial, static_cast<size_t>(p.s2.splits) * Ms * H * 4);
-  if (p.up.splits > 1) partial = std::max(partial, static_cast<size_t>(p.up.splits) * Mr * H * 4);
+  auto need = [](const DensePlan& q) { return q.small || q.splits > 1; };
+  if (need(p.s1)) partial = std::max(partial, static_cast<size_t>(p.s1.splits) * Ms * 2 * Is * 4);
+  if (need(p.s2)) partial = std::max(partial, static_cast<size_t>(p.s2.splits) * Ms * H * 4);
+  if (need(p.up)) partial = std::max(partial, static_cast<size_t>(p.up.splits) * Mr * H * 4);
   Layout l;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -100,7 +111,6 @@ Layout layout_of(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   };
   l.logits = take(static_cast<size_t>(Mr) * E * 4);
   l.hist = take(E * ng * 4);
-  l.masks = take(ng * E * 8);
   l.xq = take(static_cast<size_t>(Mr) * L);
   l.sx = take(static_cast<size_t>(Mr) * (L / 128) * 4);
   l.hq = take(R * I);
@@ -153,11 +163,16 @@ template <int kEpi>
 void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int M, int N, int K, float* partial,
                   const DenseEpi& ep, hipStream_t st) {
   if (M == 0) return;
-  dim3 grid(p.mt, p.nt, p.splits);
-  hipLaunchKernelGGL(k_dense_bf16<kEpi>, grid, dim3(256), 0, st, A, B, M, N, K, p.kps, partial, ep);
-  if (p.splits > 1) {
+  const int nbrows = (kEpi == EPI_SWIGLU) ? 2 * ep.half : N;
+  if (p.small) {
+    hipLaunchKernelGGL(k_dense_small<2>, dim3(p.nt, p.splits), dim3(256), 0, st, A, B, M, nbrows, K, p.kps, partial);
+  } else {
+    hipLaunchKernelGGL(k_dense_bf16<kEpi>, dim3(p.mt, p.nt, p.splits), dim3(256), 0, st, A, B, M, N, K, p.kps,
+                       partial, ep);
+  }
+  if (p.small || p.splits > 1) {
     const int ncols = (kEpi == EPI_SWIGLU) ? ep.half : N;
-    const long n = static_cast<long>(M) * ncols;
+    const long n = static_cast<long>(M) * (ncols / 4);
     hipLaunchKernelGGL(k_dense_reduce<kEpi>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
                        partial, M, N, p.splits, ep);
   }
@@ -233,9 +248,12 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   }
   // 3: combine + RMSNorm
   mark(3);
-  if (Mr > 0)
-    hipLaunchKernelGGL(k_combine_rmsnorm, dim3(Mr), dim3(256), 0, st, y, routing->topk_weights, routing->pair_to_row,
+  if (Mr > 0) {
+    const int nc = L / 256;
+    auto kern = (nc == 14) ? k_combine_rmsnorm<14> : (nc <= 16) ? k_combine_rmsnorm<16> : k_combine_rmsnorm<32>;
+    hipLaunchKernelGGL(kern, dim3(Mr), dim3(256), 0, st, y, routing->topk_weights, routing->pair_to_row,
                        w->rms_gamma, rn, L, k, d.rms_eps);
+  }
   // 4: shared L1 + SwiGLU
   mark(4);
   {
@@ -315,17 +333,17 @@ int moe_tail_route(const moe_tail_dims* dims, const moe_tail_weights* w, const u
   const int ng = (Mr + kGroup - 1) / kGroup;
   float* logits = at<float>(ws, lay.logits);
   int32_t* hist = at<int32_t>(ws, lay.hist);
-  unsigned long long* masks = at<unsigned long long>(ws, lay.masks);
   if (Mr > 0) {
     const int egroups = (E + 4 * kLogitExpPerWave - 1) / (4 * kLogitExpPerWave);
     hipLaunchKernelGGL(k_router_logits, dim3((Mr + kLogitTok - 1) / kLogitTok, egroups), dim3(256), 0, st, x_lat,
                        w->gate, w->gate_bias, logits, Mr, L, E);
-    hipLaunchKernelGGL(k_router_topk, dim3(ng), dim3(1024), 0, st, logits, out->topk_ids, out->topk_weights, hist,
-                       masks, Mr, E, k, ng);
+    hipLaunchKernelGGL(k_router_topk, dim3((Mr + 3) / 4), dim3(256), 0, st, logits, out->topk_ids,
+                       out->topk_weights, Mr, E, k);
+    hipLaunchKernelGGL(k_router_hist, dim3(ng), dim3(64), 0, st, out->topk_ids, hist, Mr, E, k, ng);
   }
   hipLaunchKernelGGL(k_router_scan, dim3(1), dim3(1024), 0, st, hist, out->expert_offsets, E, ng);
   if (Mr > 0)
-    hipLaunchKernelGGL(k_router_scatter, dim3(ng), dim3(64), 0, st, out->topk_ids, hist, masks, out->sorted_pair,
+    hipLaunchKernelGGL(k_router_scatter, dim3(ng), dim3(64), 0, st, out->topk_ids, hist, out->sorted_pair,
                        out->pair_to_row, Mr, E, k, ng);
   return launched();
 }

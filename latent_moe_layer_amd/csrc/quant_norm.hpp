@@ -44,6 +44,9 @@ __global__ __launch_bounds__(256) void k_quant_1x128(const void* __restrict__ x,
 // the bias study in tokenspeed PR 1062.
 constexpr int kNormMaxCols = 32;  // L <= 256 * 32
 
+// NC = columns per thread (L / 256, or an upper bound of it: extra columns are
+// clamped and unused).
+template <int NC>
 __global__ __launch_bounds__(256) void k_combine_rmsnorm(const float* __restrict__ y, const float* __restrict__ topk_w,
                                                          const int32_t* __restrict__ pair_to_row,
                                                          const uint16_t* __restrict__ gamma,
@@ -51,20 +54,36 @@ __global__ __launch_bounds__(256) void k_combine_rmsnorm(const float* __restrict
   __shared__ float s_part[4];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  float z[kNormMaxCols];
+  float z[NC];
   const int nc = L / 256;
 #pragma unroll
-  for (int c = 0; c < kNormMaxCols; ++c) z[c] = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const float w = topk_w[static_cast<size_t>(t) * k + j];
-    const float* yr = y + static_cast<size_t>(pair_to_row[static_cast<size_t>(t) * k + j]) * L + tid;
+  for (int c = 0; c < NC; ++c) z[c] = 0.0f;
+  // row pointers and weights of the k slots first, so the y loads issue
+  // together (columns past L are clamped, loaded and never used)
+  const float* yr[16];
+  float w[16];
 #pragma unroll
-    for (int c = 0; c < kNormMaxCols; ++c)
-      if (c < nc) z[c] = z[c] + w * yr[256 * c];
+  for (int j = 0; j < 16; ++j) {
+    const int jj = min(j, k - 1);
+    w[j] = topk_w[static_cast<size_t>(t) * k + jj];
+    yr[j] = y + static_cast<size_t>(pair_to_row[static_cast<size_t>(t) * k + jj]) * L;
+  }
+  int colc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) colc[c] = min(tid + 256 * c, L - 1);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < k) {
+      float v[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) v[c] = yr[j][colc[c]];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) z[c] = z[c] + w[j] * v[c];
+    }
   }
   float ss = 0.0f;
 #pragma unroll
-  for (int c = 0; c < kNormMaxCols; ++c)
+  for (int c = 0; c < NC; ++c)
     if (c < nc) ss += z[c] * z[c];
   ss = wave_sum(ss);
   if ((tid & 63) == 0) s_part[tid >> 6] = ss;
@@ -72,7 +91,7 @@ __global__ __launch_bounds__(256) void k_combine_rmsnorm(const float* __restrict
   const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
   const float r = 1.0f / sqrtf(tot / static_cast<float>(L) + eps);
 #pragma unroll
-  for (int c = 0; c < kNormMaxCols; ++c)
+  for (int c = 0; c < NC; ++c)
     if (c < nc) {
       const int col = tid + 256 * c;
       rn[static_cast<size_t>(t) * L + col] =

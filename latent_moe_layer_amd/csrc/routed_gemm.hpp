@@ -13,11 +13,11 @@
 //
 // Each of the 4 waves of a workgroup owns its own output columns and streams
 // its weight rows straight from HBM into MFMA operand registers (no weight
-// byte is used by two waves).  Operand layout of the 16x16x128 MFMA used
-// here: lane l holds row (l % 16) of A (column (l % 16) of B) and K elements
-// [32 (l / 16), 32 (l / 16) + 32) of the 128-wide step -- 32 e4m3 bytes, or
-// 16 bytes of e2m1 pairs whose e8m0 scale covers exactly those 32 elements.
-// The f32 result holds rows 4 (l / 16) + i (i = 0..3) of column l % 16.
+// byte is used by two waves); the next K step's fragments are loaded before
+// the current step's MFMAs issue.  In the 16x16x128 MFMA lane l holds row
+// (l % 16) of A (column (l % 16) of B); the K elements a lane holds depend on
+// the operand width (see load_fp8_frag / load_weight_frag).  The f32 result
+// holds rows 4 (l / 16) + i (i = 0..3) of column l % 16.
 //
 // Block scales: one MFMA covers one 128-wide K block, so its FP32 result is
 // promoted with (activation scale of the row) x (weight scale of the 128x128
@@ -76,17 +76,29 @@ __device__ __forceinline__ bool find_routed_tile(const int32_t* __restrict__ off
   return true;
 }
 
+// FP8 operand fragment of one 128-wide K step.  The 16x16x128 MFMA takes an
+// 8-bit operand's K elements as two halves: lane group g holds K [16 g, 16 g + 16)
+// in its first four registers and K [64 + 16 g, 64 + 16 g + 16) in the last four.
+__device__ __forceinline__ i32x8 load_fp8_frag(const uint8_t* __restrict__ row_ptr, int k0) {
+  const int g = (threadIdx.x & 63) >> 4;
+  const uint4 lo = *reinterpret_cast<const uint4*>(row_ptr + k0 + 16 * g);
+  const uint4 hi = *reinterpret_cast<const uint4*>(row_ptr + k0 + 64 + 16 * g);
+  return i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+               static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+}
+
+// Weight fragment of one 128-wide K step of row `row` of a [N, K] matrix.
+// FP8: the two-half layout above.  MXFP4: the 4-bit operand takes 32
+// consecutive K elements per lane group, K [32 g, 32 g + 32) = 16 packed bytes,
+// and the lane's e8m0 scale covers exactly those 32 elements.
 template <int kFmt>
 __device__ __forceinline__ void load_weight_frag(const uint8_t* __restrict__ w, const void* __restrict__ ws,
                                                  size_t row, int K, int k0, i32x8& frag, int& scale) {
-  const int g = (threadIdx.x & 63) >> 4;
   if (kFmt == FMT_FP8) {
-    const uint4* p = reinterpret_cast<const uint4*>(w + row * K + k0 + 32 * g);
-    const uint4 lo = p[0], hi = p[1];
-    frag = i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                 static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+    frag = load_fp8_frag(w + row * K, k0);
     scale = 127;
   } else {
+    const int g = (threadIdx.x & 63) >> 4;
     const uint4 v = *reinterpret_cast<const uint4*>(w + row * (K / 2) + (k0 + 32 * g) / 2);
     frag = i32x8{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w), 0, 0, 0, 0};
     scale = static_cast<const uint8_t*>(ws)[row * (K / 32) + (k0 + 32 * g) / 32];
@@ -94,12 +106,8 @@ __device__ __forceinline__ void load_weight_frag(const uint8_t* __restrict__ w, 
 }
 
 __device__ __forceinline__ i32x8 load_act_frag(const uint8_t* __restrict__ row_ptr, int k0, bool valid) {
-  const int g = (threadIdx.x & 63) >> 4;
   if (!valid) return i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-  const uint4* p = reinterpret_cast<const uint4*>(row_ptr + k0 + 32 * g);
-  const uint4 lo = p[0], hi = p[1];
-  return i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-               static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+  return load_fp8_frag(row_ptr, k0);
 }
 
 template <int kFmt>
@@ -113,7 +121,7 @@ __device__ __forceinline__ f32x4 mfma_lowp(const i32x8& a, const i32x8& b, int s
 // then h = silu(gate) * up and h -> e4m3 codes with one fp32 scale per 1x128
 // block (the 128 h columns of this tile).  Grid: (R / kBM + E, I / 128).
 template <int kFmt>
-__global__ __launch_bounds__(256) void k_routed_l1(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
+__global__ __launch_bounds__(256, 2) void k_routed_l1(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                                                    const int32_t* __restrict__ sorted_pair,
                                                    const int32_t* __restrict__ expert_offsets,
                                                    const uint8_t* __restrict__ w1, const void* __restrict__ w1s,
@@ -174,14 +182,17 @@ __global__ __launch_bounds__(256) void k_routed_l1(const uint8_t* __restrict__ x
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int k0 = kb * 128;
-    i32x8 a[2], b[4];
-    int bs[4];
+  // Two fragment sets used in turn (no register copies, so the loads of one
+  // set stay in flight while the other set's MFMAs issue).
+  i32x8 fa[2][2], fb[2][4];
+  int fs[2][4];
+  auto load_step = [&](int set, int kb) {
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) load_weight_frag<kFmt>(w1, w1s, brow[ns], L, k0, b[ns], bs[ns]);
+    for (int ns = 0; ns < 4; ++ns) load_weight_frag<kFmt>(w1, w1s, brow[ns], L, kb * 128, fb[set][ns], fs[set][ns]);
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) a[ms] = load_act_frag(arow[ms], k0, avalid[ms]);
+    for (int ms = 0; ms < 2; ++ms) fa[set][ms] = load_act_frag(arow[ms], kb * 128, avalid[ms]);
+  };
+  auto mma_step = [&](int set, int kb) {
     float swg = 1.0f, swu = 1.0f;
     if (kFmt == FMT_FP8) {
       swg = S1[static_cast<size_t>(nb) * nkb + kb];
@@ -194,12 +205,19 @@ __global__ __launch_bounds__(256) void k_routed_l1(const uint8_t* __restrict__ x
       for (int i = 0; i < 4; ++i) sa[i] = s_sx[(16 * ms + 4 * g + i) * nkb + kb];
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns) {
-        const f32x4 p = mfma_lowp<kFmt>(a[ms], b[ns], bs[ns]);
+        const f32x4 p = mfma_lowp<kFmt>(fa[set][ms], fb[set][ns], fs[set][ns]);
         const float sw = (ns < 2) ? swg : swu;
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[ms][ns][i] += p[i] * (sa[i] * sw);
       }
     }
+  };
+  load_step(0, 0);
+  for (int kb = 0; kb < nkb; kb += 2) {
+    if (kb + 1 < nkb) load_step(1, kb + 1);
+    mma_step(0, kb);
+    if (kb + 2 < nkb) load_step(0, kb + 2);
+    if (kb + 1 < nkb) mma_step(1, kb + 1);
   }
 
   // SwiGLU + per-row amax over this tile's 128 h columns
@@ -243,7 +261,7 @@ __global__ __launch_bounds__(256) void k_routed_l1(const uint8_t* __restrict__ x
 // y = h_hat . W2_hat^T for one tile of kBM rows x 128 latent columns, FP32
 // output in sorted row order.  Grid: (R / kBM + E, L / 128).
 template <int kFmt>
-__global__ __launch_bounds__(256) void k_routed_l2(const uint8_t* __restrict__ hq, const float* __restrict__ sh,
+__global__ __launch_bounds__(256, 2) void k_routed_l2(const uint8_t* __restrict__ hq, const float* __restrict__ sh,
                                                    const int32_t* __restrict__ expert_offsets,
                                                    const uint8_t* __restrict__ w2, const void* __restrict__ w2s,
                                                    float* __restrict__ y, int E, int L, int I) {
@@ -292,14 +310,15 @@ __global__ __launch_bounds__(256) void k_routed_l2(const uint8_t* __restrict__ h
 #pragma unroll
     for (int ns = 0; ns < 2; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int k0 = kb * 128;
-    i32x8 a[2], b[2];
-    int bs[2];
+  i32x8 fa[2][2], fb[2][2];
+  int fs[2][2];
+  auto load_step = [&](int set, int kb) {
 #pragma unroll
-    for (int ns = 0; ns < 2; ++ns) load_weight_frag<kFmt>(w2, w2s, brow[ns], I, k0, b[ns], bs[ns]);
+    for (int ns = 0; ns < 2; ++ns) load_weight_frag<kFmt>(w2, w2s, brow[ns], I, kb * 128, fb[set][ns], fs[set][ns]);
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) a[ms] = load_act_frag(arow[ms], k0, avalid[ms]);
+    for (int ms = 0; ms < 2; ++ms) fa[set][ms] = load_act_frag(arow[ms], kb * 128, avalid[ms]);
+  };
+  auto mma_step = [&](int set, int kb) {
     const float sw = (kFmt == FMT_FP8) ? S2[kb] : 1.0f;
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms) {
@@ -308,11 +327,18 @@ __global__ __launch_bounds__(256) void k_routed_l2(const uint8_t* __restrict__ h
       for (int i = 0; i < 4; ++i) sa[i] = s_sh[(16 * ms + 4 * g + i) * nkb + kb] * sw;
 #pragma unroll
       for (int ns = 0; ns < 2; ++ns) {
-        const f32x4 p = mfma_lowp<kFmt>(a[ms], b[ns], bs[ns]);
+        const f32x4 p = mfma_lowp<kFmt>(fa[set][ms], fb[set][ns], fs[set][ns]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[ms][ns][i] += p[i] * sa[i];
       }
     }
+  };
+  load_step(0, 0);
+  for (int kb = 0; kb < nkb; kb += 2) {
+    if (kb + 1 < nkb) load_step(1, kb + 1);
+    mma_step(0, kb);
+    if (kb + 2 < nkb) load_step(0, kb + 2);
+    if (kb + 1 < nkb) mma_step(1, kb + 1);
   }
 #pragma unroll
   for (int ms = 0; ms < 2; ++ms)

@@ -11,6 +11,11 @@ import numpy as np
 
 MAX_REL = 2e-2
 MEAN_REL = 3e-3
+# Intermediates downstream of h (the routed L2 output y and the normalized
+# latent) inherit the legitimate h-code flips: one flip of a top-binade code
+# moves h by up to 1/14 of the block amax, i.e. about 1-2 % of rms(y) at
+# I = 384.  They get a looser max bound; the mean bound is unchanged.
+MAX_REL_INTERMEDIATE = 5e-2
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -34,11 +39,34 @@ def e4m3_value(code: np.ndarray) -> np.ndarray:
     return np.where(s == 1, -mag, mag)
 
 
-def check_h_codes(gpu_hq, gpu_sh, orc_hq, orc_sh, orc_h, tol=1e-5):
-    """The rule for re-quantized activations computed by two different FP32
-    summation orders: scales agree to `tol` relative; codes agree except where
-    the oracle's h lies within tol * block amax of a rounding midpoint, and
-    then by exactly one code step.  Returns (n_mismatch, n_total)."""
+# h is computed twice by different summation procedures: the oracle's
+# sequential FP32 loop and the matrix cores, whose FP8 products are summed in
+# groups with an internal precision of about 2^-14 of the group's largest
+# product (measured on gfx950: 2^-9 addends beside a 448 product are dropped,
+# 2^-5 ones kept).  Over K = 3584 that moves h by a few 1e-5 of the block
+# amax (observed up to 7e-5 on the scales); the bar below leaves 7x margin.
+H_TOL = 5e-4
+
+
+def e4m3_encode_np(x: np.ndarray) -> np.ndarray:
+    """Nearest e4m3 code (ties to even), saturating at 448, sign kept."""
+    vals = e4m3_value(np.arange(127))
+    x = np.asarray(x, np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.searchsorted(vals, a, side="left").clip(0, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    code = np.where(dhi < dlo, hi, np.where(dlo < dhi, lo, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(vals[hi] == a, hi, code)
+    return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def check_h_codes(gpu_hq, gpu_sh, orc_hq, orc_sh, orc_h, tol=H_TOL):
+    """The rule for re-quantized activations computed by two different
+    summation procedures: scales agree to `tol` relative, and every GPU code
+    is the rounding (with the GPU's scale) of some value within tol * block
+    amax of the oracle's h -- so codes differ only where h sits that close to
+    a rounding midpoint.  Returns (n_mismatch, n_total)."""
     gpu_hq = np.asarray(gpu_hq)
     orc_hq = np.asarray(orc_hq)
     rs = np.abs(np.asarray(gpu_sh, np.float64) - orc_sh) / np.abs(orc_sh)
@@ -46,18 +74,15 @@ def check_h_codes(gpu_hq, gpu_sh, orc_hq, orc_sh, orc_h, tol=1e-5):
     mism = gpu_hq != orc_hq
     n = int(mism.sum())
     if n:
-        rows, cols = np.nonzero(mism.reshape(-1, gpu_hq.shape[-1]))
-        g = gpu_hq.reshape(-1, gpu_hq.shape[-1])[rows, cols]
-        o = orc_hq.reshape(-1, orc_hq.shape[-1])[rows, cols]
-        h = np.asarray(orc_h, np.float64).reshape(-1, orc_hq.shape[-1])[rows, cols]
-        s = np.asarray(orc_sh, np.float64).reshape(-1, orc_sh.shape[-1])[rows, cols // 128]
-        gv, ov = e4m3_value(g), e4m3_value(o)
-        # adjacent codes of the same sign (or +-0 around zero)
-        step = np.abs(g.astype(np.int64) & 0x7F) - np.abs(o.astype(np.int64) & 0x7F)
-        same_sign = ((g ^ o) & 0x80) == 0
-        assert np.all((np.abs(step) == 1) & (same_sign | (np.minimum(g & 0x7F, o & 0x7F) == 0))), \
-            "h code differs by more than one step"
-        mid = (gv + ov) / 2 * s
-        amax = 448.0 * s
-        assert np.all(np.abs(h - mid) <= tol * amax), "h code flip away from a rounding midpoint"
+        ncol = gpu_hq.shape[-1]
+        rows, cols = np.nonzero(mism.reshape(-1, ncol))
+        g = gpu_hq.reshape(-1, ncol)[rows, cols]
+        h = np.asarray(orc_h, np.float64).reshape(-1, ncol)[rows, cols]
+        s_orc = np.asarray(orc_sh, np.float64).reshape(-1, ncol // 128)[rows, cols // 128]
+        s_gpu = np.asarray(gpu_sh, np.float64).reshape(-1, ncol // 128)[rows, cols // 128]
+        band = tol * 448.0 * s_orc
+        lo = e4m3_value(e4m3_encode_np((h - band) / s_gpu))
+        hi = e4m3_value(e4m3_encode_np((h + band) / s_gpu))
+        gv = e4m3_value(g)
+        assert np.all((gv >= lo) & (gv <= hi)), "h code flip away from a rounding midpoint"
     return n, gpu_hq.size

@@ -1,0 +1,62 @@
+"""The parity rules themselves, on CPU: the h-code rule accepts codes that
+round a value near a midpoint and rejects anything else."""
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from tests import parity as P
+
+
+def test_encode_np_matches_oracle():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(100000) * rng.choice([1e-3, 1, 100], 100000)).astype(np.float32)
+    x = np.concatenate([x, P.e4m3_value(np.arange(127)).astype(np.float32), [0.0, -0.0, 500.0]]).astype(np.float32)
+    assert np.array_equal(P.e4m3_encode_np(x), orc.e4m3_encode(x))
+
+
+def _block(seed):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((4, 256)).astype(np.float32)
+    q, s = orc.quant_1x128(h)
+    return h, q, s
+
+
+def test_h_rule_accepts_identical_and_midpoint_flips():
+    h, q, s = _block(1)
+    assert P.check_h_codes(q, s, q, s, h) == (0, q.size)
+    # move one value exactly onto a midpoint and flip it to the other side
+    vals = P.e4m3_value(np.arange(127))
+    h2 = h.copy()
+    r, c = 1, 5
+    mid = (vals[60] + vals[61]) / 2 * s[r, c // 128]
+    h2[r, c] = mid
+    q2, _ = orc.quant_1x128(h2)
+    g = q2.copy()
+    g[r, c] = q2[r, c] ^ 1 if (q2[r, c] & 0x7F) in (60, 61) else q2[r, c]
+    assert P.check_h_codes(g, s, q2, s, h2)[0] <= 1
+    # across zero: a tiny h may land on +0 / -0 / the smallest codes
+    h3 = h.copy()
+    h3[2, 7] = 1e-9
+    q3, _ = orc.quant_1x128(h3)
+    g3 = q3.copy()
+    g3[2, 7] = 0x80
+    assert P.check_h_codes(g3, s, q3, s, h3)[0] == 1
+
+
+def test_h_rule_rejects_far_flips_and_scale_drift():
+    h, q, s = _block(2)
+    g = q.copy()
+    i = np.argmax(np.abs(h[0, :128]))
+    g[0, i] = (g[0, i] & 0x80) | ((g[0, i] & 0x7F) - 2)
+    with pytest.raises(AssertionError):
+        P.check_h_codes(g, s, q, s, h)
+    with pytest.raises(AssertionError):
+        P.check_h_codes(q, s * 1.01, q, s, h)
+
+
+def test_rel_errors_definition():
+    o = np.array([1.0, -1.0, 0.0, 1e-6])
+    g = o + np.array([0.01, 0.0, 0.001, 0.0])
+    mx, mean = P.rel_errors(g, o)
+    rms = np.sqrt(np.mean(o ** 2))
+    assert np.isclose(mx, 0.01) and np.isclose(mean, (0.01 + 0.001 / rms) / 4)
