@@ -71,6 +71,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "mxfp4", "indep"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs the tail on one GPU only; --gpus {args.gpus} is not supported "
@@ -92,27 +93,44 @@ def main() -> int:
     nst = len(STAGES)
     hev = HipEvents((args.steps + 1) * (nst + 1) + 2)
 
-    def step(events=None):
-        dev.route(stream)
-        dev.forward(stream, events)
+    def step(st, events=None):
+        dev.route(st)
+        dev.forward(st, events)
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
-            step()
+            step(stream)
     torch.cuda.synchronize()
 
-    # timed region: K steps, stage events recorded by the library on `stream`
+    if args.eager:
+        run_step = lambda: step(stream)  # noqa: E731
+    else:
+        # one step (route + forward, all kernels) captured as a HIP graph
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        for _ in range(3):
+            graph.replay()
+        run_step = graph.replay
+
+    # timed region: exactly K steps
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        step(hev.ev[i * (nst + 1):(i + 1) * (nst + 1)])
-    stop.record(stream)
+    start.record(torch.cuda.current_stream() if not args.eager else stream)
+    for _ in range(args.steps):
+        run_step()
+    stop.record(torch.cuda.current_stream() if not args.eager else stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
 
+    # per-stage durations: K more eager steps, the library recording HIP events
+    # on the stream its kernels run on
+    for i in range(args.steps):
+        step(stream, hev.ev[i * (nst + 1):(i + 1) * (nst + 1)])
+    torch.cuda.synchronize()
     stage_ms = np.zeros(nst)
     for i in range(args.steps):
         base = i * (nst + 1)
@@ -168,6 +186,7 @@ def main() -> int:
         "tflops_lowp": flops["lowp"] / (ms_per_step * 1e-3) / 1e12,
         "tflops_bf16": flops["bf16"] / (ms_per_step * 1e-3) / 1e12,
         "hbm_frac": gbs / HBM_PEAK_GBS,
+        "timing": "eager launches" if args.eager else "HIP graph replay of route + forward",
         "stage_us": {n: float(v * 1e3) for n, v in zip(STAGES, stage_ms)},
         "roofline": roof, "cpu_baseline": cpu, "input_gen_s": gen_s,
     }

@@ -13,9 +13,11 @@ MAX_REL = 2e-2
 MEAN_REL = 3e-3
 # Intermediates downstream of h (the routed L2 output y and the normalized
 # latent) inherit the legitimate h-code flips: one flip of a top-binade code
-# moves h by up to 1/14 of the block amax, i.e. about 1-2 % of rms(y) at
-# I = 384.  They get a looser max bound; the mean bound is unchanged.
-MAX_REL_INTERMEDIATE = 5e-2
+# moves that h element by 1/14 of the block amax (amax ~ 6 rms(h)), which moves
+# y[n] by that times W2[n, i] -- up to about 0.07 * 6 * 3.5 / sqrt(I) of
+# rms(y), i.e. 6-7 % at I = 512.  They get this looser max bound; the mean
+# bound is unchanged.
+MAX_REL_INTERMEDIATE = 1e-1
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:

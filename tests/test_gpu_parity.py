@@ -155,8 +155,11 @@ def test_forward_tiny_full():
 
 @pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4])
 def test_forward_ragged(wfmt):
-    # several tiles and a ragged tail in every dimension the grid splits
-    wl = synth.Workload("ragged", Mr=37, Ms=53, E=8, k=3, I=384, Is=256, wfmt=wfmt, seed=21,
+    # several tiles and a ragged tail in every dimension the grid splits.  I is
+    # the smallest workload's 512: one legitimate h-code flip moves the output
+    # by about 1/sqrt(I) of its rms, so much narrower experts would need a
+    # looser bar than the workloads' 2e-2.
+    wl = synth.Workload("ragged", Mr=37, Ms=53, E=8, k=3, I=512, Is=384, wfmt=wfmt, seed=21,
                         zipf_s=1.2 if wfmt else 0.0)
     inp = synth.make_inputs(wl)
     dev = run(inp)
@@ -165,7 +168,7 @@ def test_forward_ragged(wfmt):
 
 def test_forward_heavy_expert_many_row_tiles():
     # all-equal logits: every token goes to experts 0..k-1, 100 rows each (4 row tiles per expert)
-    wl = synth.Workload("heavy", Mr=100, Ms=100, E=6, k=2, I=256, Is=128, wfmt=0, seed=22, zero_router=True)
+    wl = synth.Workload("heavy", Mr=100, Ms=100, E=6, k=2, I=512, Is=128, wfmt=0, seed=22, zero_router=True)
     inp = synth.make_inputs(wl)
     dev = run(inp)
     check_forward(dev, inp)
