@@ -66,22 +66,24 @@ def check_forward(dev, inp, sel=None, report=None):
                                        ref.h[rsel])
         stats["h_flips"] = (n_mis, n_tot)
         # routed L2 output and the normalized latent
-        ymax, ymean = P.rel_errors(inter["y"][rows], ref.y[rsel])
+        ymax, ymean = P.row_rel_errors(inter["y"][rows], ref.y[rsel])
         assert ymax <= P.MAX_REL_INTERMEDIATE and ymean <= P.MEAN_REL, (ymax, ymean)
-        rmax, rmean = P.rel_errors(P.bf16_to_f32(inter["rn"][toks]), P.bf16_to_f32(ref.rn[rsel]))
+        rmax, rmean = P.row_rel_errors(P.bf16_to_f32(inter["rn"][toks]), P.bf16_to_f32(ref.rn[rsel]))
         assert rmax <= P.MAX_REL_INTERMEDIATE and rmean <= P.MEAN_REL, (rmax, rmean)
         stats["y"] = (ymax, ymean)
         stats["rn"] = (rmax, rmean)
         # final output against the oracle's FP32 value
         got = P.bf16_to_f32(to_np(dev.out)[toks])
-        omax, omean = P.rel_errors(got, ref.out_f32[rsel])
+        omax, omean = P.row_rel_errors(got, ref.out_f32[rsel])
         stats["out"] = (omax, omean)
+        stats["out_elementwise"] = P.rel_errors(got, ref.out_f32[rsel])
         stats["out_bitwise_frac"] = float(np.mean(to_np(dev.out)[toks] == ref.out_bf16[rsel]))
         assert omax <= P.MAX_REL and omean <= P.MEAN_REL, stats
     if ssel.size:
         got = P.bf16_to_f32(to_np(dev.shared_out)[sel[ssel] - Mr])
-        smax, smean = P.rel_errors(got, ref.out_f32[ssel])
+        smax, smean = P.row_rel_errors(got, ref.out_f32[ssel])
         stats["shared_out"] = (smax, smean)
+        stats["shared_out_elementwise"] = P.rel_errors(got, ref.out_f32[ssel])
         assert smax <= P.MAX_REL and smean <= P.MEAN_REL, stats
     if report is not None:
         report.update(stats)
@@ -205,7 +207,7 @@ def test_identical_experts_match_dense():
     ddev = run(dense)
     a = P.bf16_to_f32(to_np(dev.intermediates()["rn"]))
     b = P.bf16_to_f32(to_np(ddev.intermediates()["rn"]))
-    mx, mean = P.rel_errors(a, b)
+    mx, mean = P.row_rel_errors(a, b)
     assert mx <= 2e-2 and mean <= 3e-3
 
 
@@ -241,6 +243,6 @@ def test_token_permutation():
     inp2.x_hid = inp.x_hid[perm].copy()
     b = run(inp2)
     ga, gb = P.bf16_to_f32(to_np(a.out)[perm]), P.bf16_to_f32(to_np(b.out))
-    mx, mean = P.rel_errors(gb, ga)
+    mx, mean = P.row_rel_errors(gb, ga)
     assert mx <= 2e-2 and mean <= 3e-3
     print("bitwise-equal fraction under permutation:", float(np.mean(to_np(a.out)[perm] == to_np(b.out))))

@@ -60,3 +60,10 @@ def test_rel_errors_definition():
     mx, mean = P.rel_errors(g, o)
     rms = np.sqrt(np.mean(o ** 2))
     assert np.isclose(mx, 0.01) and np.isclose(mean, (0.01 + 0.001 / rms) / 4)
+
+
+def test_row_rel_errors_definition():
+    o = np.array([[3.0, 4.0], [1.0, 0.0]])
+    g = o + np.array([[0.05, 0.0], [0.0, 0.01]])
+    mx, mean = P.row_rel_errors(g, o)
+    assert np.isclose(mx, 0.01) and np.isclose(mean, 0.01)
