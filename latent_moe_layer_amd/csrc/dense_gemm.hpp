@@ -7,21 +7,18 @@
 // ("[Kimi K3][Kernel] Fuse BF16 shared experts into latent MegaMoE tail",
 // Summary; DeepGEMM PR 416 mirror, Summary).
 //
-// C[M, N] = A[M, K] . B[N, K]^T, both operands K-contiguous.  A workgroup
-// owns kDM rows x 4 waves x (2 x 16) B rows; each wave streams its own B rows
-// from HBM into registers.  Operand layout of the 16x16x32 MFMA: lane l holds
-// row l % 16 and 8 consecutive K elements of group l / 16; one 128-wide K step
-// is four MFMAs, lane group g covering elements [32 g, 32 g + 32) of the step
-// in both operands.  When the grid is too small to fill the chip, K is split
-// over gridDim.z and FP32 partials go to a workspace that a second kernel
-// reduces in split order (deterministic), applying the same epilogue.
+// C[M, N] = A[M, K] . B[N, K]^T, both operands K-contiguous.  Operand layout
+// of the 16x16x32 MFMA: lane l holds row l % 16 and 8 consecutive K elements
+// of group l / 16; one 128-wide K step is four MFMAs, lane group g covering
+// elements [32 g, 32 g + 32) of the step in both operands.  Decode-sized M
+// uses k_dense_small below (K split over the grid, FP32 partials reduced in
+// split order by k_dense_reduce, which applies the epilogue); larger M the
+// LDS-tiled kernel of tile_gemm.hpp with the epilogue fused.
 #pragma once
 
 #include "common.hpp"
 
 namespace moe_tail {
-
-constexpr int kDM = 32;  // rows per dense tile
 
 enum { EPI_SWIGLU = 0, EPI_SHARED = 1, EPI_UPADD = 2 };
 
@@ -57,75 +54,6 @@ __device__ __forceinline__ void load_bf16_frag(const uint16_t* __restrict__ row_
     const uint4 v = p[j];
     f[j] = __builtin_bit_cast(bf16x8, v);
   }
-}
-
-// Grid: (ceil(M / kDM), n_tiles, splits).  n_tiles = N / 128, or I_s / 64 for
-// SWIGLU (each tile: 64 gate + 64 up B rows).  Split z covers K steps
-// [z * kps, min((z + 1) * kps, K / 128)).  With splits > 1 the raw FP32 sums go
-// to partial[z][row][brow] (row stride nraw = number of B rows).
-template <int kEpi>
-__global__ __launch_bounds__(256) void k_dense_bf16(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                                                    int M, int N, int K, int kps, float* __restrict__ partial,
-                                                    DenseEpi ep) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int m0 = blockIdx.x * kDM;
-  const int nraw = (kEpi == EPI_SWIGLU) ? 2 * ep.half : N;
-  int brow[2];
-  if (kEpi == EPI_SWIGLU) {
-    brow[0] = 64 * blockIdx.y + 16 * wave + l16;
-    brow[1] = ep.half + brow[0];
-  } else {
-    brow[0] = 128 * blockIdx.y + 32 * wave + l16;
-    brow[1] = brow[0] + 16;
-  }
-  const uint16_t* arow[2];
-#pragma unroll
-  for (int ms = 0; ms < 2; ++ms) arow[ms] = A + static_cast<size_t>(min(m0 + 16 * ms + l16, M - 1)) * K;
-  const uint16_t* bptr[2];
-#pragma unroll
-  for (int ns = 0; ns < 2; ++ns) bptr[ns] = B + static_cast<size_t>(brow[ns]) * K;
-
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-    for (int ns = 0; ns < 2; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = K / 128;
-  const int kb0 = blockIdx.z * kps, kb1 = min(kb0 + kps, nk);
-  for (int kb = kb0; kb < kb1; ++kb) {
-    const int k0 = kb * 128;
-    bf16x8 a[2][4], b[2][4];
-#pragma unroll
-    for (int ns = 0; ns < 2; ++ns) load_bf16_frag(bptr[ns], k0, b[ns]);
-#pragma unroll
-    for (int ms = 0; ms < 2; ++ms) load_bf16_frag(arow[ms], k0, a[ms]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-        for (int ns = 0; ns < 2; ++ns) acc[ms][ns] = mfma_bf16(a[ms][j], b[ns][j], acc[ms][ns]);
-  }
-
-#pragma unroll
-  for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + 16 * ms + 4 * g + i;
-      if (row >= M) continue;
-      if (gridDim.z > 1) {
-        float* pr = partial + (static_cast<size_t>(blockIdx.z) * M + row) * nraw;
-#pragma unroll
-        for (int ns = 0; ns < 2; ++ns) pr[brow[ns]] = acc[ms][ns][i];
-      } else if (kEpi == EPI_SWIGLU) {
-        dense_epilogue<kEpi>(ep, N, row, brow[0], acc[ms][0][i], acc[ms][1][i]);
-      } else {
-#pragma unroll
-        for (int ns = 0; ns < 2; ++ns) dense_epilogue<kEpi>(ep, N, row, brow[ns], acc[ms][ns][i], 0.0f);
-      }
-    }
 }
 
 // ---------------------------------------------------------- small M --

@@ -13,6 +13,7 @@
 #include "quant_norm.hpp"
 #include "route.hpp"
 #include "routed_gemm.hpp"
+#include "tile_gemm.hpp"
 
 using namespace moe_tail;
 
@@ -48,7 +49,7 @@ int check_counts(int32_t Mr, int32_t Ms) {
 // Plan of one dense BF16 GEMM.  Up to kSmallMaxM rows: k_dense_small (all
 // rows per workgroup, 128 B rows per workgroup) with K split until the grid
 // holds about 256 workgroups, always through FP32 partials.  More rows: the
-// tiled kernel, split only when the grid is too small to fill the chip.
+// LDS-tiled kernel (128 x 256 tiles, epilogue fused, no split).
 struct DensePlan {
   bool small;
   int mt, nt, splits, kps;
@@ -64,10 +65,8 @@ DensePlan plan_dense(int M, int nbrows, int ntiles, int K) {
     p.nt = nbrows / 128;
     if (p.nt > 0) s = std::min(nk, std::max(1, (256 + p.nt - 1) / p.nt));
   } else {
-    p.mt = (M + kDM - 1) / kDM;
+    p.mt = (M + kTM - 1) / kTM;
     p.nt = ntiles;
-    const int base = p.mt * p.nt;
-    if (base > 0 && base < 512) s = std::min(nk, (1024 + base - 1) / base);
   }
   p.kps = (nk + s - 1) / s;
   p.splits = (nk + p.kps - 1) / p.kps;
@@ -98,7 +97,7 @@ Layout layout_of(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   const size_t ng = (static_cast<size_t>(Mr) + kGroup - 1) / kGroup;
   const Plans p = plan_all(d, Mr, Ms);
   size_t partial = 0;
-  auto need = [](const DensePlan& q) { return q.small || q.splits > 1; };
+  auto need = [](const DensePlan& q) { return q.small; };
   if (need(p.s1)) partial = std::max(partial, static_cast<size_t>(p.s1.splits) * Ms * 2 * Is * 4);
   if (need(p.s2)) partial = std::max(partial, static_cast<size_t>(p.s2.splits) * Ms * H * 4);
   if (need(p.up)) partial = std::max(partial, static_cast<size_t>(p.up.splits) * Mr * H * 4);
@@ -159,6 +158,13 @@ int check_routing(const moe_tail_routing* r, int32_t Mr, int k, int E) {
   return MOE_TAIL_OK;
 }
 
+template <int KIND, int FMT, int EPI>
+void launch_tile(const TileArgs& a, hipStream_t st) {
+  const unsigned T = static_cast<unsigned>(a.nslots) * static_cast<unsigned>(a.ntn);
+  if (T == 0) return;
+  hipLaunchKernelGGL((k_tile<KIND, FMT, EPI>), dim3(T), dim3(256), 0, st, a);
+}
+
 template <int kEpi>
 void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int M, int N, int K, float* partial,
                   const DenseEpi& ep, hipStream_t st) {
@@ -166,16 +172,23 @@ void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int 
   const int nbrows = (kEpi == EPI_SWIGLU) ? 2 * ep.half : N;
   if (p.small) {
     hipLaunchKernelGGL(k_dense_small<2>, dim3(p.nt, p.splits), dim3(256), 0, st, A, B, M, nbrows, K, p.kps, partial);
-  } else {
-    hipLaunchKernelGGL(k_dense_bf16<kEpi>, dim3(p.mt, p.nt, p.splits), dim3(256), 0, st, A, B, M, N, K, p.kps,
-                       partial, ep);
-  }
-  if (p.small || p.splits > 1) {
     const int ncols = (kEpi == EPI_SWIGLU) ? ep.half : N;
     const long n = static_cast<long>(M) * (ncols / 4);
     hipLaunchKernelGGL(k_dense_reduce<kEpi>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
                        partial, M, N, p.splits, ep);
+    return;
   }
+  TileArgs a{};
+  a.a = reinterpret_cast<const uint8_t*>(A);
+  a.b = reinterpret_cast<const uint8_t*>(B);
+  a.ep = ep;
+  a.M = M;
+  a.K = K;
+  a.N = N;
+  a.half = ep.half;
+  a.ntn = (kEpi == EPI_SWIGLU) ? ep.half / 128 : N / kTN;
+  a.nslots = (M + kTM - 1) / kTM;
+  launch_tile<TK_DENSE, TF_BF16, kEpi>(a, st);
 }
 
 int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
@@ -226,25 +239,67 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
     hipLaunchKernelGGL(k_quant_1x128<true>, dim3(static_cast<unsigned>((blocks + 3) / 4)), dim3(256), 0, st, x_lat,
                        xq, sx, Mr, L);
   }
-  // 1, 2: routed L1 and L2
+  // 1, 2: routed L1 and L2.  Experts with at least kBigMinRows rows go to the
+  // LDS-tiled kernel when the batch is large enough for any to be likely; the
+  // rest (and everything at decode sizes) to the row-streaming kernel.
+  const bool use_big = R >= static_cast<size_t>(kBigMinRows) * 16;
+  const int skip_at = use_big ? kBigMinRows : 0x7fffffff;
   const unsigned max_tiles = static_cast<unsigned>((R + kBM - 1) / kBM + E);
+  const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
+  TileArgs ta{};
+  ta.sorted_pair = routing ? routing->sorted_pair : nullptr;
+  ta.expert_offsets = routing ? routing->expert_offsets : nullptr;
+  ta.E = E;
+  ta.k = k;
+  ta.nslots = static_cast<int>(R / (kTM / 2));  // an expert with c >= 128 rows has ceil(c/128) <= c/64 tiles
   mark(1);
   if (Mr > 0) {
-    if (d.wfmt == MOE_TAIL_W_FP8_BLOCK128)
+    if (fp8)
       hipLaunchKernelGGL(k_routed_l1<FMT_FP8>, dim3(max_tiles, I / 128), dim3(256), 0, st, xq, sx,
-                         routing->sorted_pair, routing->expert_offsets, w->w1, w->w1_scale, hq, sh, E, k, L, I);
+                         routing->sorted_pair, routing->expert_offsets, w->w1, w->w1_scale, hq, sh, E, k, L, I,
+                         skip_at);
     else
       hipLaunchKernelGGL(k_routed_l1<FMT_MXFP4>, dim3(max_tiles, I / 128), dim3(256), 0, st, xq, sx,
-                         routing->sorted_pair, routing->expert_offsets, w->w1, w->w1_scale, hq, sh, E, k, L, I);
+                         routing->sorted_pair, routing->expert_offsets, w->w1, w->w1_scale, hq, sh, E, k, L, I,
+                         skip_at);
+    if (use_big) {
+      TileArgs a1 = ta;
+      a1.a = xq;
+      a1.a_scale = sx;
+      a1.b = w->w1;
+      a1.b_scale = w->w1_scale;
+      a1.hq = hq;
+      a1.sh = sh;
+      a1.K = L;
+      a1.N = 2 * I;
+      a1.half = I;
+      a1.ntn = I / 128;
+      if (fp8) launch_tile<TK_L1, TF_FP8, 0>(a1, st);
+      else launch_tile<TK_L1, TF_FP4, 0>(a1, st);
+    }
   }
   mark(2);
   if (Mr > 0) {
-    if (d.wfmt == MOE_TAIL_W_FP8_BLOCK128)
+    if (fp8)
       hipLaunchKernelGGL(k_routed_l2<FMT_FP8>, dim3(max_tiles, L / 128), dim3(256), 0, st, hq, sh,
-                         routing->expert_offsets, w->w2, w->w2_scale, y, E, L, I);
+                         routing->expert_offsets, w->w2, w->w2_scale, y, E, L, I, skip_at);
     else
       hipLaunchKernelGGL(k_routed_l2<FMT_MXFP4>, dim3(max_tiles, L / 128), dim3(256), 0, st, hq, sh,
-                         routing->expert_offsets, w->w2, w->w2_scale, y, E, L, I);
+                         routing->expert_offsets, w->w2, w->w2_scale, y, E, L, I, skip_at);
+    if (use_big) {
+      TileArgs a2 = ta;
+      a2.a = hq;
+      a2.a_scale = sh;
+      a2.b = w->w2;
+      a2.b_scale = w->w2_scale;
+      a2.y = y;
+      a2.K = I;
+      a2.N = L;
+      a2.half = 0;
+      a2.ntn = L / kTN;
+      if (fp8) launch_tile<TK_L2, TF_FP8, 0>(a2, st);
+      else launch_tile<TK_L2, TF_FP4, 0>(a2, st);
+    }
   }
   // 3: combine + RMSNorm
   mark(3);

@@ -34,15 +34,20 @@ constexpr int kMaxKBlocks = 64;   // K <= 8192 for the LDS copy of activation sc
 
 enum { FMT_FP8 = 0, FMT_MXFP4 = 1 };
 
-// Finds the tile `mt` among the experts' row tiles.  Run by one wave; returns
-// false when mt is past the last tile.
-__device__ __forceinline__ bool find_routed_tile(const int32_t* __restrict__ off, int E, int mt, int& e_out,
-                                                 int& row0_out, int& rows_out) {
+// Finds the tile `mt` among the row tiles of the experts with fewer than
+// `skip_at` rows (the others go to the tiled kernel).  Run by one wave;
+// returns false when mt is past the last tile.
+__device__ __forceinline__ bool find_routed_tile(const int32_t* __restrict__ off, int E, int mt, int skip_at,
+                                                 int& e_out, int& row0_out, int& rows_out) {
   const int lane = threadIdx.x & 63;
   const int per = (E + 63) / 64;
   const int eb = min(lane * per, E), ee = min(eb + per, E);
+  auto ntile = [&](int e) {
+    const int c = off[e + 1] - off[e];
+    return c < skip_at ? (c + kBM - 1) / kBM : 0;
+  };
   int local = 0;
-  for (int e = eb; e < ee; ++e) local += (off[e + 1] - off[e] + kBM - 1) / kBM;
+  for (int e = eb; e < ee; ++e) local += ntile(e);
   int incl = local;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -56,8 +61,7 @@ __device__ __forceinline__ bool find_routed_tile(const int32_t* __restrict__ off
   if (mt >= excl && mt < incl) {
     int acc = excl;
     for (int e = eb; e < ee; ++e) {
-      const int cnt = off[e + 1] - off[e];
-      const int n = (cnt + kBM - 1) / kBM;
+      const int n = ntile(e);
       if (mt < acc + n) {
         found_e = e;
         found_row0 = off[e] + (mt - acc) * kBM;
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(256, 2) void k_routed_l1(const uint8_t* __restrict_
                                                    const int32_t* __restrict__ expert_offsets,
                                                    const uint8_t* __restrict__ w1, const void* __restrict__ w1s,
                                                    uint8_t* __restrict__ hq, float* __restrict__ sh, int E, int k,
-                                                   int L, int I) {
+                                                   int L, int I, int skip_at) {
   __shared__ int s_tile[3];
   __shared__ int s_tok[kBM];
   __shared__ float s_sx[kBM * kMaxKBlocks];
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void k_routed_l1(const uint8_t* __restrict_
   const int nb = blockIdx.y;
   if (wave == 0) {
     int e, row0, rows;
-    const bool ok = find_routed_tile(expert_offsets, E, blockIdx.x, e, row0, rows);
+    const bool ok = find_routed_tile(expert_offsets, E, blockIdx.x, skip_at, e, row0, rows);
     if (lane == 0) {
       s_tile[0] = ok ? e : -1;
       s_tile[1] = row0;
@@ -264,7 +268,7 @@ template <int kFmt>
 __global__ __launch_bounds__(256, 2) void k_routed_l2(const uint8_t* __restrict__ hq, const float* __restrict__ sh,
                                                    const int32_t* __restrict__ expert_offsets,
                                                    const uint8_t* __restrict__ w2, const void* __restrict__ w2s,
-                                                   float* __restrict__ y, int E, int L, int I) {
+                                                   float* __restrict__ y, int E, int L, int I, int skip_at) {
   __shared__ int s_tile[3];
   __shared__ float s_sh[kBM * kMaxKBlocks];
 
@@ -272,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void k_routed_l2(const uint8_t* __restrict_
   const int nb = blockIdx.y;
   if (wave == 0) {
     int e, row0, rows;
-    const bool ok = find_routed_tile(expert_offsets, E, blockIdx.x, e, row0, rows);
+    const bool ok = find_routed_tile(expert_offsets, E, blockIdx.x, skip_at, e, row0, rows);
     if (lane == 0) {
       s_tile[0] = ok ? e : -1;
       s_tile[1] = row0;

@@ -1,0 +1,382 @@
+// LDS-tiled MFMA GEMM for large row counts (prefill): the routed experts'
+// L1 / L2 (FP8 or FP8 x MXFP4, block-scaled) and the dense BF16 GEMMs of the
+// shared expert and the up-projection.
+//
+// Tile: kTM = 128 rows x kTN = 256 B rows, one 128-byte K step per stage (128
+// FP8 / FP4 elements or 64 BF16 elements), 4 waves as 2 (M) x 2 (N), each
+// wave 64 rows x 128 B rows = 4 x 8 MFMA tiles of 16 x 16.  Both operands are
+// staged in LDS, double-buffered, in "fragment order": a 16-row block of one
+// K step is stored as [half][lane][16 bytes], so that lane l's two 16-byte
+// halves of its MFMA operand sit at lane * 16 -- every LDS read is a
+// contiguous, conflict-free 1 KB per wave.  (8-bit operand: lane group g
+// holds K [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16) of the step; BF16 at
+// 64 elements per step: the same bytes are two 16x16x32 MFMAs; FP4: one
+// 16-byte chunk per lane, K [32g, 32g + 32).)
+//
+// FP8 / FP4 block scales are applied once per MFMA result in FP32 (one MFMA
+// covers one 128-wide scale block): acc += P * (s_act[row] * s_w[block]).
+//
+// Tiles are numbered m-slot major, n fastest, and the workgroup index is
+// remapped so that each of the 8 XCDs (workgroups are dealt round-robin to
+// them) runs a contiguous range of tiles: neighbouring n tiles share the A
+// rows and neighbouring m tiles of an expert share the weights in that XCD's
+// L2.
+#pragma once
+
+#include "common.hpp"
+#include "dense_gemm.hpp"
+#include "routed_gemm.hpp"
+
+namespace moe_tail {
+
+constexpr int kTM = 128;
+constexpr int kTN = 256;
+constexpr int kBigMinRows = 128;  // experts with at least this many rows use the tiled kernel
+
+enum { TK_L1 = 0, TK_L2 = 1, TK_DENSE = 2 };
+enum { TF_FP8 = 0, TF_FP4 = 1, TF_BF16 = 2 };
+
+struct TileArgs {
+  const uint8_t* a;               // L1: xq [Mr, L]; L2: hq [R, I]; dense: bf16 rows [M, K]
+  const float* a_scale;           // L1: sx [Mr, L/128]; L2: sh [R, I/128]
+  const int32_t* sorted_pair;     // L1: row -> token * k + slot
+  const int32_t* expert_offsets;  // routed
+  const uint8_t* b;               // weights (bytes)
+  const void* b_scale;            // FP8: [E, N/128, K/128] f32; FP4: [E, N, K/32] e8m0
+  uint8_t* hq;                    // L1 out
+  float* sh;                      // L1 out
+  float* y;                       // L2 out [R, L]
+  DenseEpi ep;                    // dense epilogue
+  int E, k;                       // routed
+  int M;                          // dense rows
+  int K;                          // reduction length (elements)
+  int N;                          // B rows per expert (routed) or output columns (dense)
+  int half;                       // L1: I (up rows start), dense SWIGLU: I_s
+  int ntn;                        // n tiles
+  int nslots;                     // m slots in the grid
+};
+
+// Row tiles of experts with >= kBigMinRows rows, kTM rows each (last one partial).
+__device__ __forceinline__ bool find_big_tile(const int32_t* __restrict__ off, int E, int mt, int& e_out,
+                                              int& row0_out, int& rows_out) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) / 64;
+  const int eb = min(lane * per, E), ee = min(eb + per, E);
+  auto ntile = [&](int e) {
+    const int c = off[e + 1] - off[e];
+    return c >= kBigMinRows ? (c + kTM - 1) / kTM : 0;
+  };
+  int local = 0;
+  for (int e = eb; e < ee; ++e) local += ntile(e);
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int n = __shfl_up(incl, d);
+    if (lane >= d) incl += n;
+  }
+  const int total = __shfl(incl, 63);
+  if (mt >= total) return false;
+  const int excl = incl - local;
+  int fe = -1, fr0 = 0, frows = 0;
+  if (mt >= excl && mt < incl) {
+    int acc = excl;
+    for (int e = eb; e < ee; ++e) {
+      const int n = ntile(e);
+      if (mt < acc + n) {
+        fe = e;
+        fr0 = off[e] + (mt - acc) * kTM;
+        frows = min(kTM, off[e + 1] - fr0);
+        break;
+      }
+      acc += n;
+    }
+  }
+  const unsigned long long who = __ballot(fe >= 0);
+  const int src = __ffsll(static_cast<long long>(who)) - 1;
+  e_out = __shfl(fe, src);
+  row0_out = __shfl(fr0, src);
+  rows_out = __shfl(frows, src);
+  return true;
+}
+
+template <int KIND, int FMT, int EPI>
+__global__ __launch_bounds__(256) void k_tile(TileArgs p) {
+  constexpr bool kFP4 = FMT == TF_FP4;
+  constexpr bool kBF16 = FMT == TF_BF16;
+  constexpr bool kScaled = !kBF16;
+  constexpr int kABytes = kTM * 128;                 // 16 KB
+  constexpr int kBBytes = kTN * (kFP4 ? 64 : 128);   // 16 or 32 KB
+  constexpr int kStage = kABytes + kBBytes + kTM * 4 + kTN * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  __shared__ int s_tile[3];
+  __shared__ int s_tok[kTM];
+  __shared__ float s_amax[2][kTM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  // workgroup -> tile, contiguous tile ranges per XCD
+  const int T = p.nslots * p.ntn;
+  const int b = blockIdx.x;
+  const int full = T - T % 8;
+  const int t = (b < full) ? (b % 8) * (full / 8) + b / 8 : b;
+  const int slot = t / p.ntn, nt = t % p.ntn;
+
+  int e = 0, row0 = 0, rows = 0;
+  if (KIND == TK_DENSE) {
+    row0 = slot * kTM;
+    rows = min(kTM, p.M - row0);
+  } else {
+    if (wave == 0) {
+      int fe, fr, fn;
+      const bool ok = find_big_tile(p.expert_offsets, p.E, slot, fe, fr, fn);
+      if (lane == 0) {
+        s_tile[0] = ok ? fe : -1;
+        s_tile[1] = fr;
+        s_tile[2] = fn;
+      }
+    }
+    __syncthreads();
+    e = s_tile[0];
+    if (e < 0) return;  // uniform
+    row0 = s_tile[1];
+    rows = s_tile[2];
+  }
+  if (KIND == TK_L1 && tid < kTM) s_tok[tid] = (tid < rows) ? p.sorted_pair[row0 + tid] / p.k : -1;
+  __syncthreads();
+
+  const int nk = kBF16 ? p.K / 64 : p.K / 128;    // K steps of 128 bytes
+  const int nkb = p.K / 128;                       // scale blocks along K (scaled formats)
+  const int elem = kBF16 ? 2 : 1;                  // bytes per A element
+
+  // ---- per-thread staging assignment ----
+  // A: 8 blocks x 128 chunks of 16 bytes; chunk q = tid + 256 i -> block q/128,
+  // row (q%128)/8, chunk c = q%8 (8 threads per row): the thread's rows are
+  // r0 + 32 i, its chunk c and LDS slot fixed, LDS offset + 4096 i.
+  const int a_c = tid & 7, a_r0 = 16 * (tid >> 7) + ((tid & 127) >> 3);
+  const int a_dst0 = (tid >> 7) * 2048 + (a_c >> 2) * 1024 + (16 * (a_c & 3) + ((tid & 127) >> 3)) * 16;
+  const uint8_t* a_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = a_r0 + 32 * i;
+    if (row < rows) {
+      const size_t arow = (KIND == TK_L1) ? static_cast<size_t>(s_tok[row]) : static_cast<size_t>(row0 + row);
+      a_src[i] = p.a + arow * p.K * elem + 16 * a_c;
+    } else {
+      a_src[i] = nullptr;
+    }
+  }
+  // B: the tile's 256 B rows map to weight rows wrow(j); the thread's rows are
+  // b_r0 + bstep * i (FP8 / BF16: 8 chunks of 16 bytes per row, bstep 32;
+  // FP4: 4 chunks, bstep 64).
+  constexpr bool kPaired = KIND == TK_L1 || (KIND == TK_DENSE && EPI == EPI_SWIGLU);
+  auto wrow = [&](int j) -> int {
+    if (kPaired) return (j < 128) ? 128 * nt + j : p.half + 128 * nt + (j - 128);
+    return kTN * nt + j;
+  };
+  constexpr int kBChunks = kFP4 ? 4 : 8;  // per thread
+  constexpr int kBStep = kFP4 ? 64 : 32;
+  const size_t brow_bytes = kFP4 ? static_cast<size_t>(p.K) / 2 : static_cast<size_t>(p.K) * elem;
+  const int b_c = kFP4 ? (tid & 3) : (tid & 7);
+  const int b_r0 = kFP4 ? 16 * (tid >> 6) + ((tid & 63) >> 2) : 16 * (tid >> 7) + ((tid & 127) >> 3);
+  const int b_dst0 = kFP4 ? kABytes + (tid >> 6) * 1024 + (16 * b_c + ((tid & 63) >> 2)) * 16
+                          : kABytes + (tid >> 7) * 2048 + (b_c >> 2) * 1024 + (16 * (b_c & 3) + ((tid & 127) >> 3)) * 16;
+  const uint8_t* b_base = p.b + static_cast<size_t>(e) * p.N * brow_bytes + 16 * b_c;
+  auto b_src = [&](int i) { return b_base + static_cast<size_t>(wrow(b_r0 + kBStep * i)) * brow_bytes; };
+  // activation scale of tile row tid (scaled formats), e8m0 scale word of B row tid (FP4)
+  const float* sa_src = nullptr;
+  if (kScaled && tid < kTM && tid < rows) {
+    const size_t arow = (KIND == TK_L1) ? static_cast<size_t>(s_tok[tid]) : static_cast<size_t>(row0 + tid);
+    sa_src = p.a_scale + arow * nkb;
+  }
+  const uint8_t* sb_src =
+      kFP4 ? static_cast<const uint8_t*>(p.b_scale) + (static_cast<size_t>(e) * p.N + wrow(tid)) * (p.K / 32) : nullptr;
+
+  uint4 ra[4], rb[kBChunks];
+  float rsa = 0.0f;
+  uint32_t rsb = 0;
+  auto stage_load = [&](int ks) {
+    const int boff = ks * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ra[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + boff) : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kBChunks; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src(i) + (kFP4 ? ks * 64 : boff));
+    if (kScaled) rsa = sa_src ? sa_src[ks] : 0.0f;
+    if (kFP4) rsb = *reinterpret_cast<const uint32_t*>(sb_src + 4 * ks);
+  };
+  auto stage_store = [&](int buf) {
+    uint8_t* st = smem + buf * kStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(st + a_dst0 + 4096 * i) = ra[i];
+#pragma unroll
+    for (int i = 0; i < kBChunks; ++i) *reinterpret_cast<uint4*>(st + b_dst0 + 4096 * i) = rb[i];
+    if (kScaled && tid < kTM) reinterpret_cast<float*>(st + kABytes + kBBytes)[tid] = rsa;
+    if (kFP4) reinterpret_cast<uint32_t*>(st + kABytes + kBBytes + kTM * 4)[tid] = rsb;
+  };
+
+  // weight scale pointer (FP8): [E, N/128, K/128]
+  const float* wsc = (FMT == TF_FP8) ? static_cast<const float*>(p.b_scale) + static_cast<size_t>(e) * (p.N / 128) * nkb
+                                     : nullptr;
+  // B blocks of this wave: j = 0..7
+  auto bblk = [&](int j) {
+    if (kPaired) return (j < 4) ? 4 * wn + j : 8 + 4 * wn + (j - 4);
+    return 8 * wn + j;
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
+    const bool more = ks + 1 < nk;
+    if (more) stage_load(ks + 1);
+    const uint8_t* st = smem + buf * kStage;
+    // weight scales of this step (FP8): one per 128-row block of B
+    float sw[8];
+    if (FMT == TF_FP8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sw[j] = wsc[static_cast<size_t>(wrow(16 * bblk(j)) / 128) * nkb + ks];
+    }
+    i32x8 af[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint8_t* ab = st + (4 * wm + mt) * 2048 + lane * 16;
+      const uint4 lo = *reinterpret_cast<const uint4*>(ab);
+      const uint4 hi = *reinterpret_cast<const uint4*>(ab + 1024);
+      af[mt] = i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                     static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+    }
+    float sa[4][4];
+    if (kScaled) {
+      const float* ss = reinterpret_cast<const float*>(st + kABytes + kBBytes);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[mt][i] = ss[64 * wm + 16 * mt + 4 * g + i];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int bb = bblk(j);
+      if (kBF16) {
+        const uint8_t* bp = st + kABytes + bb * 2048 + lane * 16;
+        const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(bp));
+        const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(bp + 1024));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const uint4 alo = uint4{static_cast<uint32_t>(af[mt][0]), static_cast<uint32_t>(af[mt][1]),
+                                  static_cast<uint32_t>(af[mt][2]), static_cast<uint32_t>(af[mt][3])};
+          const uint4 ahi = uint4{static_cast<uint32_t>(af[mt][4]), static_cast<uint32_t>(af[mt][5]),
+                                  static_cast<uint32_t>(af[mt][6]), static_cast<uint32_t>(af[mt][7])};
+          acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, alo), b0, acc[mt][j]);
+          acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, ahi), b1, acc[mt][j]);
+        }
+      } else {
+        i32x8 bf;
+        int sb = 127;
+        if (kFP4) {
+          const uint4 v = *reinterpret_cast<const uint4*>(st + kABytes + bb * 1024 + lane * 16);
+          bf = i32x8{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w),
+                     0, 0, 0, 0};
+          sb = st[kABytes + kBBytes + kTM * 4 + (16 * bb + l16) * 4 + g];
+        } else {
+          const uint8_t* bp = st + kABytes + bb * 2048 + lane * 16;
+          const uint4 lo = *reinterpret_cast<const uint4*>(bp);
+          const uint4 hi = *reinterpret_cast<const uint4*>(bp + 1024);
+          bf = i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
+                     static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+        }
+        const float swj = (FMT == TF_FP8) ? sw[j] : 1.0f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const f32x4 pr = kFP4 ? mfma_fp8_fp4(af[mt], bf, sb) : mfma_fp8(af[mt], bf);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][j][i] += pr[i] * (sa[mt][i] * swj);
+        }
+      }
+    }
+    if (more) stage_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- epilogues
+  if (KIND == TK_L1) {
+    // h = silu(gate) * up for this wave's 64 rows x 64 h columns; row amax over the tile's 128 h columns
+    float h[4][4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h[mt][j][i] = silu_mul(acc[mt][j][i], acc[mt][4 + j][i]);
+          m = fmaxf(m, fabsf(h[mt][j][i]));
+        }
+        m = group16_max(m);
+        if (l16 == 0) s_amax[wn][64 * wm + 16 * mt + 4 * g + i] = m;
+      }
+    __syncthreads();
+    uint8_t* sq = smem;  // [128 rows][128 codes], stage buffers are free now
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 64 * wm + 16 * mt + 4 * g + i;
+        const float amax = fmaxf(s_amax[0][r], s_amax[1][r]);
+        const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sq[r * 128 + 64 * wn + 16 * j + l16] = static_cast<uint8_t>(f32_to_e4m3(h[mt][j][i] / s));
+        if (wn == 0 && l16 == 0 && r < rows) p.sh[static_cast<size_t>(row0 + r) * (p.half / 128) + nt] = s;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i;
+      const int r = q >> 3, c16 = (q & 7) * 16;
+      if (r < rows)
+        *reinterpret_cast<uint4*>(p.hq + static_cast<size_t>(row0 + r) * p.half + 128 * nt + c16) =
+            *reinterpret_cast<const uint4*>(sq + r * 128 + c16);
+    }
+  } else if (KIND == TK_L2) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 64 * wm + 16 * mt + 4 * g + i;
+        if (r < rows) {
+          float* yr = p.y + static_cast<size_t>(row0 + r) * p.N + kTN * nt + 128 * wn + l16;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) yr[16 * j] = acc[mt][j][i];
+        }
+      }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 64 * wm + 16 * mt + 4 * g + i;
+        if (r < rows) {
+          if (EPI == EPI_SWIGLU) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              dense_epilogue<EPI>(p.ep, p.N, row0 + r, 128 * nt + 64 * wn + 16 * j + l16, acc[mt][j][i],
+                                  acc[mt][4 + j][i]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              dense_epilogue<EPI>(p.ep, p.N, row0 + r, kTN * nt + 128 * wn + 16 * j + l16, acc[mt][j][i], 0.0f);
+          }
+        }
+      }
+  }
+}
+
+}  // namespace moe_tail

@@ -168,6 +168,23 @@ def test_forward_ragged(wfmt):
     check_forward(dev, inp)
 
 
+@pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4])
+def test_forward_tiled_path(wfmt):
+    # Mr * k >= 2048 turns on the LDS-tiled routed kernel for experts with >= 128
+    # rows (here most experts, ~150 rows each: full and partial 128-row tiles),
+    # the others stay on the row-streaming kernel; M > 128 takes the tiled
+    # dense kernel for the shared expert and the up-projection.
+    wl = synth.Workload("tiled", Mr=300, Ms=333, E=18 if wfmt == 0 else 16, k=8, I=512, Is=512, wfmt=wfmt, seed=30,
+                        zipf_s=0.3 if wfmt else 0.0)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    loads = np.diff(to_np(dev.offsets))
+    assert loads.max() >= 128 and loads.min() < 128, loads
+    rng = np.random.default_rng(3)
+    sel = np.concatenate([np.sort(rng.choice(300, 24, replace=False)), [0, 299, 300, 332]]).astype(np.int32)
+    check_forward(dev, inp, sel=np.unique(sel))
+
+
 def test_forward_heavy_expert_many_row_tiles():
     # all-equal logits: every token goes to experts 0..k-1, 100 rows each (4 row tiles per expert)
     wl = synth.Workload("heavy", Mr=100, Ms=100, E=6, k=2, I=512, Is=128, wfmt=0, seed=22, zero_router=True)
