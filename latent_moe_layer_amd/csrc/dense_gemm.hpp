@@ -94,11 +94,15 @@ __global__ __launch_bounds__(256) void k_dense_small(const uint16_t* __restrict_
     }
   };
   auto stage_store = [&](int buf) {
+    // laundered buffer index: keeps these stores (and the waits on their
+    // global loads) after the current step's MFMAs
+    int b = buf;
+    asm volatile("" : "+v"(b));
 #pragma unroll
     for (int i = 0; i < kMaxStage; ++i) {
       const int idx = tid + 256 * i;
       const int r = idx >> 4, c = idx & 15;
-      if (r < rows_pad) *reinterpret_cast<uint4*>(&sA[buf][r * kAStride + 8 * c]) = st[i];
+      if (r < rows_pad) *reinterpret_cast<uint4*>(&sA[b][r * kAStride + 8 * c]) = st[i];
     }
   };
 
@@ -128,16 +132,21 @@ __global__ __launch_bounds__(256) void k_dense_small(const uint16_t* __restrict_
       }
     }
   };
+  // Pipeline: step kb's A rows are in LDS buffer (kb - kb0) & 1 and its B
+  // fragments in set (kb - kb0) & 1, while the registers hold step kb + 1's
+  // A rows and the other set its B fragments (loaded one step earlier).  After
+  // the MFMAs of step kb and a barrier, the A registers go to the other buffer
+  // and step kb + 2 is loaded into the registers and the freed B set.
   auto step = [&](int set, int kb) {
-    const int buf = (kb - kb0) & 1;
-    const bool more = kb + 1 < kb1;
-    if (more) {
-      stage_load(kb + 1);
+    mma_step(set, set);
+    __syncthreads();
+    if (kb + 1 < kb1) {
+      stage_store(set ^ 1);
+      const int k2 = (kb + 2 < kb1) ? kb + 2 : kb1 - 1;
+      stage_load(k2);
 #pragma unroll
-      for (int ns = 0; ns < NT; ++ns) load_bf16_frag(bptr[ns], (kb + 1) * 128, fb[set ^ 1][ns]);
+      for (int ns = 0; ns < NT; ++ns) load_bf16_frag(bptr[ns], k2 * 128, fb[set][ns]);
     }
-    mma_step(set, buf);
-    if (more) stage_store(buf ^ 1);
     __syncthreads();
   };
   if (kb0 < kb1) {
@@ -145,6 +154,10 @@ __global__ __launch_bounds__(256) void k_dense_small(const uint16_t* __restrict_
     stage_store(0);
 #pragma unroll
     for (int ns = 0; ns < NT; ++ns) load_bf16_frag(bptr[ns], kb0 * 128, fb[0][ns]);
+    const int k1 = (kb0 + 1 < kb1) ? kb0 + 1 : kb0;
+    stage_load(k1);
+#pragma unroll
+    for (int ns = 0; ns < NT; ++ns) load_bf16_frag(bptr[ns], k1 * 128, fb[1][ns]);
   }
   __syncthreads();
   for (int kb = kb0; kb < kb1; kb += 2) {

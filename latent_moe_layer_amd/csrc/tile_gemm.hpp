@@ -193,27 +193,37 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
   const uint8_t* sb_src =
       kFP4 ? static_cast<const uint8_t*>(p.b_scale) + (static_cast<size_t>(e) * p.N + wrow(tid)) * (p.K / 32) : nullptr;
 
-  uint4 ra[4], rb[kBChunks];
-  float rsa = 0.0f;
-  uint32_t rsb = 0;
-  auto stage_load = [&](int ks) {
+  struct StageRegs {
+    uint4 a[4];
+    uint4 b[kBChunks];
+    float sa;
+    uint32_t sb;
+  };
+  auto stage_load = [&](int ks) -> StageRegs {
+    StageRegs r;
     const int boff = ks * 128;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      ra[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + boff) : uint4{0u, 0u, 0u, 0u};
+      r.a[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + boff) : uint4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src(i) + (kFP4 ? ks * 64 : boff));
-    if (kScaled) rsa = sa_src ? sa_src[ks] : 0.0f;
-    if (kFP4) rsb = *reinterpret_cast<const uint32_t*>(sb_src + 4 * ks);
+    for (int i = 0; i < kBChunks; ++i) r.b[i] = *reinterpret_cast<const uint4*>(b_src(i) + (kFP4 ? ks * 64 : boff));
+    r.sa = (kScaled && sa_src) ? sa_src[ks] : 0.0f;
+    r.sb = kFP4 ? *reinterpret_cast<const uint32_t*>(sb_src + 4 * ks) : 0u;
+    return r;
   };
-  auto stage_store = [&](int buf) {
-    uint8_t* st = smem + buf * kStage;
+  auto stage_store = [&](int buf, const StageRegs& r) {
+    // the buffer offset is laundered so that the compiler cannot prove these
+    // stores disjoint from the current stage's LDS reads and hoist them (and
+    // the waits on their global loads) above the MFMAs
+    int off = buf * kStage;
+    asm volatile("" : "+v"(off));
+    uint8_t* st = smem + off;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(st + a_dst0 + 4096 * i) = ra[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(st + a_dst0 + 4096 * i) = r.a[i];
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i) *reinterpret_cast<uint4*>(st + b_dst0 + 4096 * i) = rb[i];
-    if (kScaled && tid < kTM) reinterpret_cast<float*>(st + kABytes + kBBytes)[tid] = rsa;
-    if (kFP4) reinterpret_cast<uint32_t*>(st + kABytes + kBBytes + kTM * 4)[tid] = rsb;
+    for (int i = 0; i < kBChunks; ++i) *reinterpret_cast<uint4*>(st + b_dst0 + 4096 * i) = r.b[i];
+    if (kScaled && tid < kTM) reinterpret_cast<float*>(st + kABytes + kBBytes)[tid] = r.sa;
+    if (kFP4) reinterpret_cast<uint32_t*>(st + kABytes + kBBytes + kTM * 4)[tid] = r.sb;
   };
 
   // weight scale pointer (FP8): [E, N/128, K/128]
@@ -231,19 +241,26 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  stage_load(0);
-  stage_store(0);
+  // Pipeline: stage ks is in LDS buffer ks & 1 while the registers hold stage
+  // ks + 1 (loaded one iteration earlier).  After the MFMAs of stage ks and a
+  // barrier, the registers go to the other buffer and stage ks + 2 is loaded.
+  // The global loads therefore have a whole iteration of MFMAs to land, however
+  // the compiler orders the MFMAs against the stores.
+  StageRegs nxt = stage_load(0);
+  stage_store(0, nxt);
+  nxt = stage_load(nk > 1 ? 1 : 0);
   __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
     const int buf = ks & 1;
-    const bool more = ks + 1 < nk;
-    if (more) stage_load(ks + 1);
     const uint8_t* st = smem + buf * kStage;
-    // weight scales of this step (FP8): one per 128-row block of B
-    float sw[8];
+    // weight scales of this step (FP8): the wave's B rows lie in two 128-row
+    // blocks (paired: gate, up) or one; wave-uniform, so scalar loads
+    float sw_lo = 1.0f, sw_hi = 1.0f;
     if (FMT == TF_FP8) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sw[j] = wsc[static_cast<size_t>(wrow(16 * bblk(j)) / 128) * nkb + ks];
+      const int blo = __builtin_amdgcn_readfirstlane(wrow(16 * bblk(0)) / 128);
+      const int bhi = __builtin_amdgcn_readfirstlane(wrow(16 * bblk(7)) / 128);
+      sw_lo = wsc[blo * nkb + ks];
+      sw_hi = wsc[bhi * nkb + ks];
     }
     i32x8 af[4];
 #pragma unroll
@@ -293,7 +310,7 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
           bf = i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
                      static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
         }
-        const float swj = (FMT == TF_FP8) ? sw[j] : 1.0f;
+        const float swj = (FMT == TF_FP8) ? (j < 4 ? sw_lo : sw_hi) : 1.0f;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const f32x4 pr = kFP4 ? mfma_fp8_fp4(af[mt], bf, sb) : mfma_fp8(af[mt], bf);
@@ -302,7 +319,11 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
         }
       }
     }
-    if (more) stage_store(buf ^ 1);
+    __syncthreads();
+    if (ks + 1 < nk) {
+      stage_store(buf ^ 1, nxt);
+      nxt = stage_load(ks + 2 < nk ? ks + 2 : nk - 1);
+    }
     __syncthreads();
   }
 
