@@ -38,6 +38,10 @@ int check_dims(const moe_tail_dims* d) {
   if (d->inter % 128 || d->shared_inter % 128 || d->inter > 128 * kMaxKBlocks) return MOE_TAIL_ERR_UNSUPPORTED;
   if (d->latent > 128 * kMaxKBlocks) return MOE_TAIL_ERR_UNSUPPORTED;
   if (d->num_experts > 1024 || d->top_k > 16) return MOE_TAIL_ERR_UNSUPPORTED;
+  // dense weights are addressed with 32-bit byte offsets
+  if (static_cast<int64_t>(d->hidden) * d->latent * 2 >= (1ll << 31) ||
+      static_cast<int64_t>(d->hidden) * d->shared_inter * 4 >= (1ll << 31))
+    return MOE_TAIL_ERR_UNSUPPORTED;
   return MOE_TAIL_OK;
 }
 
@@ -242,7 +246,8 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   // 1, 2: routed L1 and L2.  Experts with at least kBigMinRows rows go to the
   // LDS-tiled kernel when the batch is large enough for any to be likely; the
   // rest (and everything at decode sizes) to the row-streaming kernel.
-  const bool use_big = R >= static_cast<size_t>(kBigMinRows) * 16;
+  // (the tiled kernel addresses the gathered x rows with 32-bit offsets)
+  const bool use_big = R >= static_cast<size_t>(kBigMinRows) * 16 && static_cast<size_t>(Mr) * L < (1ull << 31);
   const int skip_at = use_big ? kBigMinRows : 0x7fffffff;
   const unsigned max_tiles = static_cast<unsigned>((R + kBM - 1) / kBM + E);
   const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
@@ -266,6 +271,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       TileArgs a1 = ta;
       a1.a = xq;
       a1.a_scale = sx;
+      a1.M = Mr;
       a1.b = w->w1;
       a1.b_scale = w->w1_scale;
       a1.hq = hq;

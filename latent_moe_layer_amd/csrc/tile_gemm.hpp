@@ -151,39 +151,57 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
   const int elem = kBF16 ? 2 : 1;                  // bytes per A element
 
   // ---- per-thread staging assignment ----
-  // A: 8 blocks x 128 chunks of 16 bytes; chunk q = tid + 256 i -> block q/128,
-  // row (q%128)/8, chunk c = q%8 (8 threads per row): the thread's rows are
-  // r0 + 32 i, its chunk c and LDS slot fixed, LDS offset + 4096 i.
-  const int a_c = tid & 7, a_r0 = 16 * (tid >> 7) + ((tid & 127) >> 3);
-  const int a_dst0 = (tid >> 7) * 2048 + (a_c >> 2) * 1024 + (16 * (a_c & 3) + ((tid & 127) >> 3)) * 16;
-  const uint8_t* a_src[4];
+  // Thread t fills the LDS slots t + 256 i (16 bytes each), so every wave
+  // writes one contiguous kilobyte (no bank conflicts).  Slot s of an operand
+  // is block s / 128 (FP4 B: s / 64), half h = (s / 64) % 2, lane' = s % 64 =
+  // 16 g + r: tile row 16 * block + r, 16-byte chunk c = 4 h + g (FP4: g).
+  const int t_r = tid & 15, t_g = (tid >> 4) & 3, t_h = (tid >> 6) & 1;
+  const int st_c = 4 * t_h + t_g;                       // chunk of an 8-bit / BF16 row step
+  const int st_r0 = 16 * (tid >> 7) + t_r;              // rows st_r0 + 32 i
+  // A operand: rows st_r0 + 32 i, i < 4; out-of-range rows read as zero
+  // (offset past the buffer's end).
+  constexpr uint32_t kNoRow = 0x80000000u;
+  const size_t a_row_bytes = static_cast<size_t>(p.K) * elem;
+  uint32_t a_off[4];
+  const uint8_t* a_base;
+  uint32_t a_records;
+  if (KIND == TK_L1) {
+    a_base = p.a;                                       // gathered token rows of x codes
+    a_records = static_cast<uint32_t>(static_cast<size_t>(p.M) * a_row_bytes);
+  } else {
+    a_base = p.a + static_cast<size_t>(row0) * a_row_bytes;
+    a_records = static_cast<uint32_t>(static_cast<size_t>(rows) * a_row_bytes);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = a_r0 + 32 * i;
+    const int row = st_r0 + 32 * i;
+    uint32_t o = kNoRow;
     if (row < rows) {
-      const size_t arow = (KIND == TK_L1) ? static_cast<size_t>(s_tok[row]) : static_cast<size_t>(row0 + row);
-      a_src[i] = p.a + arow * p.K * elem + 16 * a_c;
-    } else {
-      a_src[i] = nullptr;
+      const size_t rr = (KIND == TK_L1) ? static_cast<size_t>(s_tok[row]) : static_cast<size_t>(row);
+      o = static_cast<uint32_t>(rr * a_row_bytes) + 16u * st_c;
     }
+    a_off[i] = o;
   }
-  // B: the tile's 256 B rows map to weight rows wrow(j); the thread's rows are
-  // b_r0 + bstep * i (FP8 / BF16: 8 chunks of 16 bytes per row, bstep 32;
-  // FP4: 4 chunks, bstep 64).
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_base), static_cast<short>(0), a_records, 0x00020000);
+  // B operand: the tile's 256 B rows map to weight rows wrow(j)
   constexpr bool kPaired = KIND == TK_L1 || (KIND == TK_DENSE && EPI == EPI_SWIGLU);
   auto wrow = [&](int j) -> int {
     if (kPaired) return (j < 128) ? 128 * nt + j : p.half + 128 * nt + (j - 128);
     return kTN * nt + j;
   };
   constexpr int kBChunks = kFP4 ? 4 : 8;  // per thread
-  constexpr int kBStep = kFP4 ? 64 : 32;
   const size_t brow_bytes = kFP4 ? static_cast<size_t>(p.K) / 2 : static_cast<size_t>(p.K) * elem;
-  const int b_c = kFP4 ? (tid & 3) : (tid & 7);
-  const int b_r0 = kFP4 ? 16 * (tid >> 6) + ((tid & 63) >> 2) : 16 * (tid >> 7) + ((tid & 127) >> 3);
-  const int b_dst0 = kFP4 ? kABytes + (tid >> 6) * 1024 + (16 * b_c + ((tid & 63) >> 2)) * 16
-                          : kABytes + (tid >> 7) * 2048 + (b_c >> 2) * 1024 + (16 * (b_c & 3) + ((tid & 127) >> 3)) * 16;
-  const uint8_t* b_base = p.b + static_cast<size_t>(e) * p.N * brow_bytes + 16 * b_c;
-  auto b_src = [&](int i) { return b_base + static_cast<size_t>(wrow(b_r0 + kBStep * i)) * brow_bytes; };
+  uint32_t b_off[kBChunks];
+#pragma unroll
+  for (int i = 0; i < kBChunks; ++i) {
+    const int row = kFP4 ? 64 * i + 16 * (tid >> 6) + t_r : st_r0 + 32 * i;
+    const int c = kFP4 ? t_g : st_c;
+    b_off[i] = static_cast<uint32_t>(static_cast<size_t>(wrow(row)) * brow_bytes) + 16u * c;
+  }
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.b + static_cast<size_t>(e) * p.N * brow_bytes), static_cast<short>(0),
+      static_cast<uint32_t>(static_cast<size_t>(p.N) * brow_bytes), 0x00020000);
   // activation scale of tile row tid (scaled formats), e8m0 scale word of B row tid (FP4)
   const float* sa_src = nullptr;
   if (kScaled && tid < kTM && tid < rows) {
@@ -194,19 +212,19 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
       kFP4 ? static_cast<const uint8_t*>(p.b_scale) + (static_cast<size_t>(e) * p.N + wrow(tid)) * (p.K / 32) : nullptr;
 
   struct StageRegs {
-    uint4 a[4];
-    uint4 b[kBChunks];
+    i32x4 a[4];
+    i32x4 b[kBChunks];
     float sa;
     uint32_t sb;
   };
   auto stage_load = [&](int ks) -> StageRegs {
     StageRegs r;
-    const int boff = ks * 128;
+    const int soff = ks * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r.a[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + boff) : uint4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 4; ++i) r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[i], soff, 0);
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i) r.b[i] = *reinterpret_cast<const uint4*>(b_src(i) + (kFP4 ? ks * 64 : boff));
+    for (int i = 0; i < kBChunks; ++i)
+      r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[i], kFP4 ? ks * 64 : soff, 0);
     r.sa = (kScaled && sa_src) ? sa_src[ks] : 0.0f;
     r.sb = kFP4 ? *reinterpret_cast<const uint32_t*>(sb_src + 4 * ks) : 0u;
     return r;
@@ -217,13 +235,13 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
     // the waits on their global loads) above the MFMAs
     int off = buf * kStage;
     asm volatile("" : "+v"(off));
-    uint8_t* st = smem + off;
+    uint8_t* st = smem + off + 16 * tid;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(st + a_dst0 + 4096 * i) = r.a[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<i32x4*>(st + 4096 * i) = r.a[i];
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i) *reinterpret_cast<uint4*>(st + b_dst0 + 4096 * i) = r.b[i];
-    if (kScaled && tid < kTM) reinterpret_cast<float*>(st + kABytes + kBBytes)[tid] = r.sa;
-    if (kFP4) reinterpret_cast<uint32_t*>(st + kABytes + kBBytes + kTM * 4)[tid] = r.sb;
+    for (int i = 0; i < kBChunks; ++i) *reinterpret_cast<i32x4*>(st + kABytes + 4096 * i) = r.b[i];
+    if (kScaled && tid < kTM) reinterpret_cast<float*>(smem + off + kABytes + kBBytes)[tid] = r.sa;
+    if (kFP4) reinterpret_cast<uint32_t*>(smem + off + kABytes + kBBytes + kTM * 4)[tid] = r.sb;
   };
 
   // weight scale pointer (FP8): [E, N/128, K/128]
@@ -266,32 +284,35 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const uint8_t* ab = st + (4 * wm + mt) * 2048 + lane * 16;
-      const uint4 lo = *reinterpret_cast<const uint4*>(ab);
-      const uint4 hi = *reinterpret_cast<const uint4*>(ab + 1024);
-      af[mt] = i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                     static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(ab);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(ab + 1024);
+      af[mt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    float sa[4][4];
+    // per-row promotion factors of this step: activation scale x weight scale
+    float sc[2][4][4];
     if (kScaled) {
       const float* ss = reinterpret_cast<const float*>(st + kABytes + kBBytes);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ss + 64 * wm + 16 * mt + 4 * g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sa[mt][i] = ss[64 * wm + 16 * mt + 4 * g + i];
+        for (int i = 0; i < 4; ++i) {
+          sc[0][mt][i] = v[i] * sw_lo;
+          sc[1][mt][i] = v[i] * sw_hi;
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int bb = bblk(j);
       if (kBF16) {
         const uint8_t* bp = st + kABytes + bb * 2048 + lane * 16;
-        const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(bp));
-        const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(bp + 1024));
+        const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp));
+        const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + 1024));
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const uint4 alo = uint4{static_cast<uint32_t>(af[mt][0]), static_cast<uint32_t>(af[mt][1]),
-                                  static_cast<uint32_t>(af[mt][2]), static_cast<uint32_t>(af[mt][3])};
-          const uint4 ahi = uint4{static_cast<uint32_t>(af[mt][4]), static_cast<uint32_t>(af[mt][5]),
-                                  static_cast<uint32_t>(af[mt][6]), static_cast<uint32_t>(af[mt][7])};
+          const i32x4 alo = __builtin_shufflevector(af[mt], af[mt], 0, 1, 2, 3);
+          const i32x4 ahi = __builtin_shufflevector(af[mt], af[mt], 4, 5, 6, 7);
           acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, alo), b0, acc[mt][j]);
           acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, ahi), b1, acc[mt][j]);
         }
@@ -299,23 +320,22 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
         i32x8 bf;
         int sb = 127;
         if (kFP4) {
-          const uint4 v = *reinterpret_cast<const uint4*>(st + kABytes + bb * 1024 + lane * 16);
-          bf = i32x8{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w),
-                     0, 0, 0, 0};
+          const i32x4 v = *reinterpret_cast<const i32x4*>(st + kABytes + bb * 1024 + lane * 16);
+          const i32x4 z = {0, 0, 0, 0};
+          bf = __builtin_shufflevector(v, z, 0, 1, 2, 3, 4, 5, 6, 7);
           sb = st[kABytes + kBBytes + kTM * 4 + (16 * bb + l16) * 4 + g];
         } else {
           const uint8_t* bp = st + kABytes + bb * 2048 + lane * 16;
-          const uint4 lo = *reinterpret_cast<const uint4*>(bp);
-          const uint4 hi = *reinterpret_cast<const uint4*>(bp + 1024);
-          bf = i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z), static_cast<int>(lo.w),
-                     static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(bp);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(bp + 1024);
+          bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        const float swj = (FMT == TF_FP8) ? (j < 4 ? sw_lo : sw_hi) : 1.0f;
+        const int half_sel = (j < 4) ? 0 : 1;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const f32x4 pr = kFP4 ? mfma_fp8_fp4(af[mt], bf, sb) : mfma_fp8(af[mt], bf);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][j][i] += pr[i] * (sa[mt][i] * swj);
+          for (int i = 0; i < 4; ++i) acc[mt][j][i] += pr[i] * sc[half_sel][mt][i];
         }
       }
     }
