@@ -166,7 +166,7 @@ template <int KIND, int FMT, int EPI>
 void launch_tile(const TileArgs& a, hipStream_t st) {
   const unsigned T = static_cast<unsigned>(a.nslots) * static_cast<unsigned>(a.ntn);
   if (T == 0) return;
-  hipLaunchKernelGGL((k_tile<KIND, FMT, EPI>), dim3(T), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_tile<KIND, FMT, EPI>), dim3(T), dim3(512), 0, st, a);
 }
 
 template <int kEpi>

@@ -3,8 +3,9 @@
 // shared expert and the up-projection.
 //
 // Tile: kTM = 128 rows x kTN = 256 B rows, one 128-byte K step per stage (128
-// FP8 / FP4 elements or 64 BF16 elements), 4 waves as 2 (M) x 2 (N), each
-// wave 64 rows x 128 B rows = 4 x 8 MFMA tiles of 16 x 16.  Both operands are
+// FP8 / FP4 elements or 64 BF16 elements), 8 waves as 2 (M) x 4 (N), each
+// wave 64 rows x 64 B rows = 4 x 4 MFMA tiles of 16 x 16 (64 accumulator
+// registers, which leaves room for the FP32 promotion without spilling).  Both operands are
 // staged in LDS, double-buffered, in "fragment order": a 16-row block of one
 // K step is stored as [half][lane][16 bytes], so that lane l's two 16-byte
 // halves of its MFMA operand sit at lane * 16 -- every LDS read is a
@@ -100,7 +101,7 @@ __device__ __forceinline__ bool find_big_tile(const int32_t* __restrict__ off, i
 }
 
 template <int KIND, int FMT, int EPI>
-__global__ __launch_bounds__(256) void k_tile(TileArgs p) {
+__global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   constexpr bool kFP4 = FMT == TF_FP4;
   constexpr bool kBF16 = FMT == TF_BF16;
   constexpr bool kScaled = !kBF16;
@@ -110,10 +111,10 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
   __shared__ int s_tile[3];
   __shared__ int s_tok[kTM];
-  __shared__ float s_amax[2][kTM];
+  __shared__ float s_amax[4][kTM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int l16 = lane & 15, g = lane >> 4;
 
   // workgroup -> tile, contiguous tile ranges per XCD
@@ -151,18 +152,18 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
   const int elem = kBF16 ? 2 : 1;                  // bytes per A element
 
   // ---- per-thread staging assignment ----
-  // Thread t fills the LDS slots t + 256 i (16 bytes each), so every wave
+  // Thread t fills the LDS slots t + 512 i (16 bytes each), so every wave
   // writes one contiguous kilobyte (no bank conflicts).  Slot s of an operand
   // is block s / 128 (FP4 B: s / 64), half h = (s / 64) % 2, lane' = s % 64 =
   // 16 g + r: tile row 16 * block + r, 16-byte chunk c = 4 h + g (FP4: g).
   const int t_r = tid & 15, t_g = (tid >> 4) & 3, t_h = (tid >> 6) & 1;
   const int st_c = 4 * t_h + t_g;                       // chunk of an 8-bit / BF16 row step
-  const int st_r0 = 16 * (tid >> 7) + t_r;              // rows st_r0 + 32 i
-  // A operand: rows st_r0 + 32 i, i < 4; out-of-range rows read as zero
+  const int st_r0 = 16 * (tid >> 7) + t_r;              // rows st_r0 + 64 i
+  // A operand: rows st_r0 + 64 i, i < 2; out-of-range rows read as zero
   // (offset past the buffer's end).
   constexpr uint32_t kNoRow = 0x80000000u;
   const size_t a_row_bytes = static_cast<size_t>(p.K) * elem;
-  uint32_t a_off[4];
+  uint32_t a_off[2];
   const uint8_t* a_base;
   uint32_t a_records;
   if (KIND == TK_L1) {
@@ -173,8 +174,8 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
     a_records = static_cast<uint32_t>(static_cast<size_t>(rows) * a_row_bytes);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = st_r0 + 32 * i;
+  for (int i = 0; i < 2; ++i) {
+    const int row = st_r0 + 64 * i;
     uint32_t o = kNoRow;
     if (row < rows) {
       const size_t rr = (KIND == TK_L1) ? static_cast<size_t>(s_tok[row]) : static_cast<size_t>(row);
@@ -190,29 +191,31 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
     if (kPaired) return (j < 128) ? 128 * nt + j : p.half + 128 * nt + (j - 128);
     return kTN * nt + j;
   };
-  constexpr int kBChunks = kFP4 ? 4 : 8;  // per thread
+  const int nbrows = kPaired ? 2 * p.half : p.N;        // B rows of one expert / of the dense matrix
+  constexpr int kBChunks = kFP4 ? 2 : 4;  // per thread
   const size_t brow_bytes = kFP4 ? static_cast<size_t>(p.K) / 2 : static_cast<size_t>(p.K) * elem;
   uint32_t b_off[kBChunks];
 #pragma unroll
   for (int i = 0; i < kBChunks; ++i) {
-    const int row = kFP4 ? 64 * i + 16 * (tid >> 6) + t_r : st_r0 + 32 * i;
+    const int row = kFP4 ? 128 * i + 16 * (tid >> 6) + t_r : st_r0 + 64 * i;
     const int c = kFP4 ? t_g : st_c;
     b_off[i] = static_cast<uint32_t>(static_cast<size_t>(wrow(row)) * brow_bytes) + 16u * c;
   }
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.b + static_cast<size_t>(e) * p.N * brow_bytes), static_cast<short>(0),
-      static_cast<uint32_t>(static_cast<size_t>(p.N) * brow_bytes), 0x00020000);
+      const_cast<uint8_t*>(p.b + static_cast<size_t>(e) * nbrows * brow_bytes), static_cast<short>(0),
+      static_cast<uint32_t>(static_cast<size_t>(nbrows) * brow_bytes), 0x00020000);
   // activation scale of tile row tid (scaled formats), e8m0 scale word of B row tid (FP4)
   const float* sa_src = nullptr;
   if (kScaled && tid < kTM && tid < rows) {
     const size_t arow = (KIND == TK_L1) ? static_cast<size_t>(s_tok[tid]) : static_cast<size_t>(row0 + tid);
     sa_src = p.a_scale + arow * nkb;
   }
-  const uint8_t* sb_src =
-      kFP4 ? static_cast<const uint8_t*>(p.b_scale) + (static_cast<size_t>(e) * p.N + wrow(tid)) * (p.K / 32) : nullptr;
+  const uint8_t* sb_src = (kFP4 && tid < kTN)
+                              ? static_cast<const uint8_t*>(p.b_scale) + (static_cast<size_t>(e) * nbrows + wrow(tid)) * (p.K / 32)
+                              : nullptr;
 
   struct StageRegs {
-    i32x4 a[4];
+    i32x4 a[2];
     i32x4 b[kBChunks];
     float sa;
     uint32_t sb;
@@ -221,12 +224,12 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
     StageRegs r;
     const int soff = ks * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[i], soff, 0);
+    for (int i = 0; i < 2; ++i) r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[i], soff, 0);
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i)
       r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[i], kFP4 ? ks * 64 : soff, 0);
     r.sa = (kScaled && sa_src) ? sa_src[ks] : 0.0f;
-    r.sb = kFP4 ? *reinterpret_cast<const uint32_t*>(sb_src + 4 * ks) : 0u;
+    r.sb = (kFP4 && sb_src) ? *reinterpret_cast<const uint32_t*>(sb_src + 4 * ks) : 0u;
     return r;
   };
   auto stage_store = [&](int buf, const StageRegs& r) {
@@ -237,27 +240,28 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
     asm volatile("" : "+v"(off));
     uint8_t* st = smem + off + 16 * tid;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<i32x4*>(st + 4096 * i) = r.a[i];
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<i32x4*>(st + 8192 * i) = r.a[i];
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i) *reinterpret_cast<i32x4*>(st + kABytes + 4096 * i) = r.b[i];
+    for (int i = 0; i < kBChunks; ++i) *reinterpret_cast<i32x4*>(st + kABytes + 8192 * i) = r.b[i];
     if (kScaled && tid < kTM) reinterpret_cast<float*>(smem + off + kABytes + kBBytes)[tid] = r.sa;
-    if (kFP4) reinterpret_cast<uint32_t*>(smem + off + kABytes + kBBytes + kTM * 4)[tid] = r.sb;
+    if (kFP4 && tid < kTN) reinterpret_cast<uint32_t*>(smem + off + kABytes + kBBytes + kTM * 4)[tid] = r.sb;
   };
 
   // weight scale pointer (FP8): [E, N/128, K/128]
-  const float* wsc = (FMT == TF_FP8) ? static_cast<const float*>(p.b_scale) + static_cast<size_t>(e) * (p.N / 128) * nkb
+  const float* wsc = (FMT == TF_FP8) ? static_cast<const float*>(p.b_scale) + static_cast<size_t>(e) * (nbrows / 128) * nkb
                                      : nullptr;
-  // B blocks of this wave: j = 0..7
+  // B blocks of this wave, j = 0..3 (paired: two gate blocks, then the two
+  // matching up blocks)
   auto bblk = [&](int j) {
-    if (kPaired) return (j < 4) ? 4 * wn + j : 8 + 4 * wn + (j - 4);
-    return 8 * wn + j;
+    if (kPaired) return (j < 2) ? 2 * wn + j : 8 + 2 * wn + (j - 2);
+    return 4 * wn + j;
   };
 
-  f32x4 acc[4][8];
+  f32x4 acc[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Pipeline: stage ks is in LDS buffer ks & 1 while the registers hold stage
   // ks + 1 (loaded one iteration earlier).  After the MFMAs of stage ks and a
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
     float sw_lo = 1.0f, sw_hi = 1.0f;
     if (FMT == TF_FP8) {
       const int blo = __builtin_amdgcn_readfirstlane(wrow(16 * bblk(0)) / 128);
-      const int bhi = __builtin_amdgcn_readfirstlane(wrow(16 * bblk(7)) / 128);
+      const int bhi = __builtin_amdgcn_readfirstlane(wrow(16 * bblk(3)) / 128);
       sw_lo = wsc[blo * nkb + ks];
       sw_hi = wsc[bhi * nkb + ks];
     }
@@ -303,7 +307,7 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const int bb = bblk(j);
       if (kBF16) {
         const uint8_t* bp = st + kABytes + bb * 2048 + lane * 16;
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
           const i32x4 hi = *reinterpret_cast<const i32x4*>(bp + 1024);
           bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        const int half_sel = (j < 4) ? 0 : 1;
+        const int half_sel = (kPaired && j >= 2) ? 1 : 0;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const f32x4 pr = kFP4 ? mfma_fp8_fp4(af[mt], bf, sb) : mfma_fp8(af[mt], bf);
@@ -349,16 +353,16 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
 
   // ---------------------------------------------------------------- epilogues
   if (KIND == TK_L1) {
-    // h = silu(gate) * up for this wave's 64 rows x 64 h columns; row amax over the tile's 128 h columns
-    float h[4][4][4];
+    // h = silu(gate) * up for this wave's 64 rows x 32 h columns; row amax over the tile's 128 h columns
+    float h[4][2][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float m = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          h[mt][j][i] = silu_mul(acc[mt][j][i], acc[mt][4 + j][i]);
+        for (int j = 0; j < 2; ++j) {
+          h[mt][j][i] = silu_mul(acc[mt][j][i], acc[mt][2 + j][i]);
           m = fmaxf(m, fabsf(h[mt][j][i]));
         }
         m = group16_max(m);
@@ -371,16 +375,16 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 64 * wm + 16 * mt + 4 * g + i;
-        const float amax = fmaxf(s_amax[0][r], s_amax[1][r]);
+        const float amax = fmaxf(fmaxf(s_amax[0][r], s_amax[1][r]), fmaxf(s_amax[2][r], s_amax[3][r]));
         const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sq[r * 128 + 64 * wn + 16 * j + l16] = static_cast<uint8_t>(f32_to_e4m3(h[mt][j][i] / s));
+        for (int j = 0; j < 2; ++j) sq[r * 128 + 32 * wn + 16 * j + l16] = static_cast<uint8_t>(f32_to_e4m3(h[mt][j][i] / s));
         if (wn == 0 && l16 == 0 && r < rows) p.sh[static_cast<size_t>(row0 + r) * (p.half / 128) + nt] = s;
       }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i;
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + 512 * i;
       const int r = q >> 3, c16 = (q & 7) * 16;
       if (r < rows)
         *reinterpret_cast<uint4*>(p.hq + static_cast<size_t>(row0 + r) * p.half + 128 * nt + c16) =
@@ -393,9 +397,9 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
       for (int i = 0; i < 4; ++i) {
         const int r = 64 * wm + 16 * mt + 4 * g + i;
         if (r < rows) {
-          float* yr = p.y + static_cast<size_t>(row0 + r) * p.N + kTN * nt + 128 * wn + l16;
+          float* yr = p.y + static_cast<size_t>(row0 + r) * p.N + kTN * nt + 64 * wn + l16;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) yr[16 * j] = acc[mt][j][i];
+          for (int j = 0; j < 4; ++j) yr[16 * j] = acc[mt][j][i];
         }
       }
   } else {
@@ -407,13 +411,13 @@ __global__ __launch_bounds__(256) void k_tile(TileArgs p) {
         if (r < rows) {
           if (EPI == EPI_SWIGLU) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              dense_epilogue<EPI>(p.ep, p.N, row0 + r, 128 * nt + 64 * wn + 16 * j + l16, acc[mt][j][i],
-                                  acc[mt][4 + j][i]);
+            for (int j = 0; j < 2; ++j)
+              dense_epilogue<EPI>(p.ep, p.N, row0 + r, 128 * nt + 32 * wn + 16 * j + l16, acc[mt][j][i],
+                                  acc[mt][2 + j][i]);
           } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-              dense_epilogue<EPI>(p.ep, p.N, row0 + r, kTN * nt + 128 * wn + 16 * j + l16, acc[mt][j][i], 0.0f);
+            for (int j = 0; j < 4; ++j)
+              dense_epilogue<EPI>(p.ep, p.N, row0 + r, kTN * nt + 64 * wn + 16 * j + l16, acc[mt][j][i], 0.0f);
           }
         }
       }
