@@ -149,9 +149,11 @@ __global__ __launch_bounds__(256, 2) void k_routed_l1(const uint8_t* __restrict_
     }
   }
   __syncthreads();
-  const int e = s_tile[0];
+  // wave-uniform (scalar registers), so the per-step weight-scale loads are
+  // scalar loads that do not wait behind the vector prefetch
+  const int e = __builtin_amdgcn_readfirstlane(s_tile[0]);
   if (e < 0) return;  // uniform over the workgroup
-  const int row0 = s_tile[1], rows = s_tile[2];
+  const int row0 = __builtin_amdgcn_readfirstlane(s_tile[1]), rows = __builtin_amdgcn_readfirstlane(s_tile[2]);
   const int nkb = L / 128;
   if (tid < kBM) s_tok[tid] = (tid < rows) ? sorted_pair[row0 + tid] / k : -1;
   __syncthreads();
@@ -284,9 +286,9 @@ __global__ __launch_bounds__(256, 2) void k_routed_l2(const uint8_t* __restrict_
     }
   }
   __syncthreads();
-  const int e = s_tile[0];
+  const int e = __builtin_amdgcn_readfirstlane(s_tile[0]);
   if (e < 0) return;
-  const int row0 = s_tile[1], rows = s_tile[2];
+  const int row0 = __builtin_amdgcn_readfirstlane(s_tile[1]), rows = __builtin_amdgcn_readfirstlane(s_tile[2]);
   const int nkb = I / 128;
   for (int i = tid; i < kBM * nkb; i += 256) {
     const int r = i / nkb, kb = i % nkb;

@@ -112,6 +112,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   __shared__ int s_tile[3];
   __shared__ int s_tok[kTM];
   __shared__ float s_amax[4][kTM];
+  __shared__ float s_wsc[2][kMaxKBlocks];  // FP8 weight scales of the tile's two 128-row B blocks
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -139,17 +140,34 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
       }
     }
     __syncthreads();
-    e = s_tile[0];
+    e = __builtin_amdgcn_readfirstlane(s_tile[0]);
     if (e < 0) return;  // uniform
-    row0 = s_tile[1];
-    rows = s_tile[2];
+    row0 = __builtin_amdgcn_readfirstlane(s_tile[1]);
+    rows = __builtin_amdgcn_readfirstlane(s_tile[2]);
   }
-  if (KIND == TK_L1 && tid < kTM) s_tok[tid] = (tid < rows) ? p.sorted_pair[row0 + tid] / p.k : -1;
-  __syncthreads();
-
   const int nk = kBF16 ? p.K / 64 : p.K / 128;    // K steps of 128 bytes
   const int nkb = p.K / 128;                       // scale blocks along K (scaled formats)
   const int elem = kBF16 ? 2 : 1;                  // bytes per A element
+  constexpr bool kPaired = KIND == TK_L1 || (KIND == TK_DENSE && EPI == EPI_SWIGLU);
+  const int nbrows = kPaired ? 2 * p.half : p.N;  // B rows of one expert / of the dense matrix
+  // B row j of the tile (0..255) -> weight row: paired kinds take 128 gate
+  // rows and the matching 128 up rows, the others 256 consecutive rows
+  auto wrow = [&](int j) -> int {
+    if (kPaired) return (j < 128) ? 128 * nt + j : p.half + 128 * nt + (j - 128);
+    return kTN * nt + j;
+  };
+
+  if (KIND == TK_L1 && tid < kTM) s_tok[tid] = (tid < rows) ? p.sorted_pair[row0 + tid] / p.k : -1;
+  // FP8 weight scales [E, N/128, K/128] of tile rows [0, 128) and [128, 256)
+  // for every K step, read once here so that the main loop issues no global
+  // load besides the next stage's operands
+  if (FMT == TF_FP8 && tid < 2 * nkb) {
+    const int q = tid / nkb, kb = tid - q * nkb;
+    const int wr = wrow(128 * q);
+    s_wsc[q][kb] = (wr < nbrows) ? static_cast<const float*>(p.b_scale)[(static_cast<size_t>(e) * (nbrows / 128) + wr / 128) * nkb + kb]
+                                 : 0.0f;
+  }
+  __syncthreads();
 
   // ---- per-thread staging assignment ----
   // Thread t fills the LDS slots t + 512 i (16 bytes each), so every wave
@@ -186,12 +204,6 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_base), static_cast<short>(0), a_records, 0x00020000);
   // B operand: the tile's 256 B rows map to weight rows wrow(j)
-  constexpr bool kPaired = KIND == TK_L1 || (KIND == TK_DENSE && EPI == EPI_SWIGLU);
-  auto wrow = [&](int j) -> int {
-    if (kPaired) return (j < 128) ? 128 * nt + j : p.half + 128 * nt + (j - 128);
-    return kTN * nt + j;
-  };
-  const int nbrows = kPaired ? 2 * p.half : p.N;        // B rows of one expert / of the dense matrix
   constexpr int kBChunks = kFP4 ? 2 : 4;  // per thread
   const size_t brow_bytes = kFP4 ? static_cast<size_t>(p.K) / 2 : static_cast<size_t>(p.K) * elem;
   uint32_t b_off[kBChunks];
@@ -247,9 +259,6 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
     if (kFP4 && tid < kTN) reinterpret_cast<uint32_t*>(smem + off + kABytes + kBBytes + kTM * 4)[tid] = r.sb;
   };
 
-  // weight scale pointer (FP8): [E, N/128, K/128]
-  const float* wsc = (FMT == TF_FP8) ? static_cast<const float*>(p.b_scale) + static_cast<size_t>(e) * (nbrows / 128) * nkb
-                                     : nullptr;
   // B blocks of this wave, j = 0..3 (paired: two gate blocks, then the two
   // matching up blocks)
   auto bblk = [&](int j) {
@@ -275,14 +284,12 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   for (int ks = 0; ks < nk; ++ks) {
     const int buf = ks & 1;
     const uint8_t* st = smem + buf * kStage;
-    // weight scales of this step (FP8): the wave's B rows lie in two 128-row
-    // blocks (paired: gate, up) or one; wave-uniform, so scalar loads
+    // weight scales of this step (FP8): the wave's B rows lie in the tile's
+    // row half 16 * bblk(0) / 128 (paired: its gate rows) and 16 * bblk(3) / 128
     float sw_lo = 1.0f, sw_hi = 1.0f;
     if (FMT == TF_FP8) {
-      const int blo = __builtin_amdgcn_readfirstlane(wrow(16 * bblk(0)) / 128);
-      const int bhi = __builtin_amdgcn_readfirstlane(wrow(16 * bblk(3)) / 128);
-      sw_lo = wsc[blo * nkb + ks];
-      sw_hi = wsc[bhi * nkb + ks];
+      sw_lo = s_wsc[(16 * bblk(0)) / 128][ks];
+      sw_hi = s_wsc[(16 * bblk(3)) / 128][ks];
     }
     i32x8 af[4];
 #pragma unroll
