@@ -100,6 +100,37 @@ __device__ __forceinline__ bool find_big_tile(const int32_t* __restrict__ off, i
   return true;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct global -> LDS loads: lane l's 16 (or 4) bytes land at lds + 16 l
+// (4 l); an offset outside the resource's range writes zeros.  `lds` must be
+// the same for the whole wave.  Issued as inline assembly so that the
+// compiler does not track them: it cannot always tell which LDS reads they
+// may overlap and would then wait for every one in flight; ring_barrier
+// below does the waiting instead.  (No memory clobber: volatile asm keeps
+// its order against ring_barrier, and the compiler may move LDS reads of
+// other stages around these.)
+__device__ __forceinline__ uint32_t lds_offset(const uint8_t* lds) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds)));
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_offset(lds)), "v"(voff), "s"(r),
+               "s"(soff));
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(lds_offset(lds)), "v"(voff), "s"(r),
+               "s"(soff));
+}
+
+// Wait until at most N of this wave's direct loads are in flight and its LDS
+// reads are done, then meet the other waves: afterwards every load issued
+// before the newest N (by any wave) has landed.  (A fenced __syncthreads
+// would wait for all of them.)
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 template <int KIND, int FMT, int EPI>
 __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   constexpr bool kFP4 = FMT == TF_FP4;
@@ -107,8 +138,15 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   constexpr bool kScaled = !kBF16;
   constexpr int kABytes = kTM * 128;                 // 16 KB
   constexpr int kBBytes = kTN * (kFP4 ? 64 : 128);   // 16 or 32 KB
-  constexpr int kStage = kABytes + kBBytes + kTM * 4 + kTN * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+  constexpr int kSOff = kABytes + kBBytes;           // scale words: activation [0, 512), FP4 e8m0 [512, 1536)
+  constexpr int kStage = kSOff + (kScaled ? 2048 : 0);
+  constexpr int kBChunks = kFP4 ? 2 : 4;             // 16-byte B loads per thread and stage
+  constexpr int kLoads = 2 + kBChunks + (kScaled ? 1 : 0);  // direct loads per wave and stage
+  // three-stage ring, one array per stage so that the compiler can tell the
+  // stages apart (its own waits before LDS reads then cover just that stage)
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[kStage];
   __shared__ int s_tile[3];
   __shared__ int s_tok[kTM];
   __shared__ float s_amax[4][kTM];
@@ -117,6 +155,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int l16 = lane & 15, g = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   // workgroup -> tile, contiguous tile ranges per XCD
   const int T = p.nslots * p.ntn;
@@ -159,8 +198,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
 
   if (KIND == TK_L1 && tid < kTM) s_tok[tid] = (tid < rows) ? p.sorted_pair[row0 + tid] / p.k : -1;
   // FP8 weight scales [E, N/128, K/128] of tile rows [0, 128) and [128, 256)
-  // for every K step, read once here so that the main loop issues no global
-  // load besides the next stage's operands
+  // for every K step, read once here
   if (FMT == TF_FP8 && tid < 2 * nkb) {
     const int q = tid / nkb, kb = tid - q * nkb;
     const int wr = wrow(128 * q);
@@ -169,11 +207,13 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   }
   __syncthreads();
 
-  // ---- per-thread staging assignment ----
-  // Thread t fills the LDS slots t + 512 i (16 bytes each), so every wave
-  // writes one contiguous kilobyte (no bank conflicts).  Slot s of an operand
-  // is block s / 128 (FP4 B: s / 64), half h = (s / 64) % 2, lane' = s % 64 =
-  // 16 g + r: tile row 16 * block + r, 16-byte chunk c = 4 h + g (FP4: g).
+  // ---- per-thread load assignment ----
+  // Thread t fills the 16-byte LDS slots t + 512 i of an operand, so every
+  // wave's load writes one contiguous kilobyte.  Slot s is 16-row block
+  // s / 128 (FP4 B: s / 64), half h = (s / 64) % 2, lane' = s % 64 = 16 g + r:
+  // tile row 16 * block + r, 16-byte chunk c = 4 h + g (FP4: g).  This is the
+  // MFMA operand ("fragment") order, so each lane later reads its operand at
+  // lane * 16 of a block's half.
   const int t_r = tid & 15, t_g = (tid >> 4) & 3, t_h = (tid >> 6) & 1;
   const int st_c = 4 * t_h + t_g;                       // chunk of an 8-bit / BF16 row step
   const int st_r0 = 16 * (tid >> 7) + t_r;              // rows st_r0 + 64 i
@@ -204,7 +244,6 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_base), static_cast<short>(0), a_records, 0x00020000);
   // B operand: the tile's 256 B rows map to weight rows wrow(j)
-  constexpr int kBChunks = kFP4 ? 2 : 4;  // per thread
   const size_t brow_bytes = kFP4 ? static_cast<size_t>(p.K) / 2 : static_cast<size_t>(p.K) * elem;
   uint32_t b_off[kBChunks];
 #pragma unroll
@@ -216,47 +255,46 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(p.b + static_cast<size_t>(e) * nbrows * brow_bytes), static_cast<short>(0),
       static_cast<uint32_t>(static_cast<size_t>(nbrows) * brow_bytes), 0x00020000);
-  // activation scale of tile row tid (scaled formats), e8m0 scale word of B row tid (FP4)
-  const float* sa_src = nullptr;
-  if (kScaled && tid < kTM && tid < rows) {
-    const size_t arow = (KIND == TK_L1) ? static_cast<size_t>(s_tok[tid]) : static_cast<size_t>(row0 + tid);
-    sa_src = p.a_scale + arow * nkb;
+  // a resource with no valid bytes: loads through it write zeros
+  const __amdgpu_buffer_rsrc_t z_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.b), static_cast<short>(0), 0u, 0x00020000);
+  // scale words, one 4-byte load per lane and stage: waves 0-1 the
+  // activation scales of tile rows 64 w + lane, waves 2-5 (FP4) the e8m0
+  // words of B rows 64 (w - 2) + lane; the other waves load zeros
+  __amdgpu_buffer_rsrc_t s_rsrc = z_rsrc;
+  uint32_t s_off = kNoRow;
+  if (kScaled) {
+    if (wv < 2) {
+      const int row = 64 * wv + lane;
+      const float* sbase = (KIND == TK_L1) ? p.a_scale : p.a_scale + static_cast<size_t>(row0) * nkb;
+      const size_t srows = (KIND == TK_L1) ? static_cast<size_t>(p.M) : static_cast<size_t>(rows);
+      s_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sbase), static_cast<short>(0),
+                                                 static_cast<uint32_t>(srows * nkb * 4), 0x00020000);
+      if (row < rows) {
+        const size_t ar = (KIND == TK_L1) ? static_cast<size_t>(s_tok[row]) : static_cast<size_t>(row);
+        s_off = static_cast<uint32_t>(ar * nkb * 4);
+      }
+    } else if (kFP4 && wv < 6) {
+      const int j = 64 * (wv - 2) + lane;
+      const size_t wpr = static_cast<size_t>(p.K) / 32;  // e8m0 bytes per weight row
+      s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(static_cast<const uint8_t*>(p.b_scale) + static_cast<size_t>(e) * nbrows * wpr),
+          static_cast<short>(0), static_cast<uint32_t>(nbrows * wpr), 0x00020000);
+      s_off = static_cast<uint32_t>(wrow(j) * wpr);
+    }
   }
-  const uint8_t* sb_src = (kFP4 && tid < kTN)
-                              ? static_cast<const uint8_t*>(p.b_scale) + (static_cast<size_t>(e) * nbrows + wrow(tid)) * (p.K / 32)
-                              : nullptr;
 
-  struct StageRegs {
-    i32x4 a[2];
-    i32x4 b[kBChunks];
-    float sa;
-    uint32_t sb;
-  };
-  auto stage_load = [&](int ks) -> StageRegs {
-    StageRegs r;
-    const int soff = ks * 128;
+  // stage ks -> ring buffer; past the last stage the loads go through the
+  // empty resource (no memory traffic) so that every stage counts kLoads
+  auto issue = [&](uint8_t* ring, int ks) {
+    const bool live = ks < nk;
+    const __amdgpu_buffer_rsrc_t ra = live ? a_rsrc : z_rsrc;
+    const __amdgpu_buffer_rsrc_t rb = live ? b_rsrc : z_rsrc;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[i], soff, 0);
+    for (int i = 0; i < 2; ++i) dma16(ra, ring + 8192 * i + 1024 * wv, a_off[i], ks * 128);
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i)
-      r.b[i] = __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, b_off[i], kFP4 ? ks * 64 : soff, 0);
-    r.sa = (kScaled && sa_src) ? sa_src[ks] : 0.0f;
-    r.sb = (kFP4 && sb_src) ? *reinterpret_cast<const uint32_t*>(sb_src + 4 * ks) : 0u;
-    return r;
-  };
-  auto stage_store = [&](int buf, const StageRegs& r) {
-    // the buffer offset is laundered so that the compiler cannot prove these
-    // stores disjoint from the current stage's LDS reads and hoist them (and
-    // the waits on their global loads) above the MFMAs
-    int off = buf * kStage;
-    asm volatile("" : "+v"(off));
-    uint8_t* st = smem + off + 16 * tid;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<i32x4*>(st + 8192 * i) = r.a[i];
-#pragma unroll
-    for (int i = 0; i < kBChunks; ++i) *reinterpret_cast<i32x4*>(st + kABytes + 8192 * i) = r.b[i];
-    if (kScaled && tid < kTM) reinterpret_cast<float*>(smem + off + kABytes + kBBytes)[tid] = r.sa;
-    if (kFP4 && tid < kTN) reinterpret_cast<uint32_t*>(smem + off + kABytes + kBBytes + kTM * 4)[tid] = r.sb;
+    for (int i = 0; i < kBChunks; ++i) dma16(rb, ring + kABytes + 8192 * i + 1024 * wv, b_off[i], kFP4 ? ks * 64 : ks * 128);
+    if (kScaled) dma4(live ? s_rsrc : z_rsrc, ring + kSOff + 256 * wv, s_off, 4 * ks);
   };
 
   // B blocks of this wave, j = 0..3 (paired: two gate blocks, then the two
@@ -272,18 +310,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Pipeline: stage ks is in LDS buffer ks & 1 while the registers hold stage
-  // ks + 1 (loaded one iteration earlier).  After the MFMAs of stage ks and a
-  // barrier, the registers go to the other buffer and stage ks + 2 is loaded.
-  // The global loads therefore have a whole iteration of MFMAs to land, however
-  // the compiler orders the MFMAs against the stores.
-  StageRegs nxt = stage_load(0);
-  stage_store(0, nxt);
-  nxt = stage_load(nk > 1 ? 1 : 0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    const uint8_t* st = smem + buf * kStage;
+  auto compute = [&](const uint8_t* st, int ks) {
     // weight scales of this step (FP8): the wave's B rows lie in the tile's
     // row half 16 * bblk(0) / 128 (paired: its gate rows) and 16 * bblk(3) / 128
     float sw_lo = 1.0f, sw_hi = 1.0f;
@@ -302,7 +329,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
     // per-row promotion factors of this step: activation scale x weight scale
     float sc[2][4][4];
     if (kScaled) {
-      const float* ss = reinterpret_cast<const float*>(st + kABytes + kBBytes);
+      const float* ss = reinterpret_cast<const float*>(st + kSOff);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(ss + 64 * wm + 16 * mt + 4 * g);
@@ -334,7 +361,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
           const i32x4 v = *reinterpret_cast<const i32x4*>(st + kABytes + bb * 1024 + lane * 16);
           const i32x4 z = {0, 0, 0, 0};
           bf = __builtin_shufflevector(v, z, 0, 1, 2, 3, 4, 5, 6, 7);
-          sb = st[kABytes + kBBytes + kTM * 4 + (16 * bb + l16) * 4 + g];
+          sb = st[kSOff + 512 + (16 * bb + l16) * 4 + g];
         } else {
           const uint8_t* bp = st + kABytes + bb * 2048 + lane * 16;
           const i32x4 lo = *reinterpret_cast<const i32x4*>(bp);
@@ -350,13 +377,31 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
         }
       }
     }
-    __syncthreads();
+  };
+
+  // Pipeline: stage ks sits in ring ks % 3 while stages ks + 1 and ks + 2 are
+  // in flight.  Each step: wait for stage ks (all waves), start stage ks + 2
+  // into the buffer that stage ks - 1 (read by every wave before the
+  // barrier) leaves free, then compute stage ks.
+  issue(ring0, 0);
+  issue(ring1, 1);
+  for (int ks = 0; ks < nk; ks += 3) {
+    ring_barrier<kLoads>();
+    issue(ring2, ks + 2);
+    compute(ring0, ks);
     if (ks + 1 < nk) {
-      stage_store(buf ^ 1, nxt);
-      nxt = stage_load(ks + 2 < nk ? ks + 2 : nk - 1);
+      ring_barrier<kLoads>();
+      issue(ring0, ks + 3);
+      compute(ring1, ks + 1);
     }
-    __syncthreads();
+    if (ks + 2 < nk) {
+      ring_barrier<kLoads>();
+      issue(ring1, ks + 4);
+      compute(ring2, ks + 2);
+    }
   }
+  // drain the trailing (empty) loads before the epilogue reuses ring0
+  ring_barrier<0>();
 
   // ---------------------------------------------------------------- epilogues
   if (KIND == TK_L1) {
@@ -376,7 +421,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
         if (l16 == 0) s_amax[wn][64 * wm + 16 * mt + 4 * g + i] = m;
       }
     __syncthreads();
-    uint8_t* sq = smem;  // [128 rows][128 codes], stage buffers are free now
+    uint8_t* sq = ring0;  // [128 rows][128 codes], the ring is free now
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
