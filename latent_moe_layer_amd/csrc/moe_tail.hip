@@ -5,6 +5,7 @@
 // implementation"; DeepGEMM PR 416 mirror, Compatibility).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -162,11 +163,27 @@ int check_routing(const moe_tail_routing* r, int32_t Mr, int k, int E) {
   return MOE_TAIL_OK;
 }
 
+// Compute units of the current device (cached per device).
+unsigned num_cus() {
+  static unsigned cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = static_cast<unsigned>(n);
+  }
+  return cache[dev];
+}
+
 template <int KIND, int FMT, int EPI>
 void launch_tile(const TileArgs& a, hipStream_t st) {
   const unsigned T = static_cast<unsigned>(a.nslots) * static_cast<unsigned>(a.ntn);
   if (T == 0) return;
-  hipLaunchKernelGGL((k_tile<KIND, FMT, EPI>), dim3(T), dim3(512), 0, st, a);
+  // persistent: one workgroup per CU (the kernel's LDS allows no second),
+  // whole rounds of 8 so that every XCD gets the same number
+  const unsigned wg = std::min((T + 7) / 8 * 8, std::max(8u, num_cus() / 8 * 8));
+  hipLaunchKernelGGL((k_tile<KIND, FMT, EPI>), dim3(wg), dim3(512), 0, st, a);
 }
 
 template <int kEpi>
@@ -247,7 +264,9 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   // LDS-tiled kernel when the batch is large enough for any to be likely; the
   // rest (and everything at decode sizes) to the row-streaming kernel.
   // (the tiled kernel addresses the gathered x rows with 32-bit offsets)
-  const bool use_big = R >= static_cast<size_t>(kBigMinRows) * 16 && static_cast<size_t>(Mr) * L < (1ull << 31);
+  // (it keeps the expert tables in LDS and needs two K steps per tile)
+  const bool use_big = R >= static_cast<size_t>(kBigMinRows) * 16 && static_cast<size_t>(Mr) * L < (1ull << 31) &&
+                       E <= kTileMaxE && L >= 256 && I >= 256;
   const int skip_at = use_big ? kBigMinRows : 0x7fffffff;
   const unsigned max_tiles = static_cast<unsigned>((R + kBM - 1) / kBM + E);
   const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
@@ -256,7 +275,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   ta.expert_offsets = routing ? routing->expert_offsets : nullptr;
   ta.E = E;
   ta.k = k;
-  ta.nslots = static_cast<int>(R / (kTM / 2));  // an expert with c >= 128 rows has ceil(c/128) <= c/64 tiles
+  ta.nslots = static_cast<int>(R / (kTM / 2));  // bound on the row tiles (ceil(c/128) <= c/64 for c >= 128): sizes the grid
   mark(1);
   if (Mr > 0) {
     if (fp8)

@@ -5,23 +5,20 @@
 // Tile: kTM = 128 rows x kTN = 256 B rows, one 128-byte K step per stage (128
 // FP8 / FP4 elements or 64 BF16 elements), 8 waves as 2 (M) x 4 (N), each
 // wave 64 rows x 64 B rows = 4 x 4 MFMA tiles of 16 x 16 (64 accumulator
-// registers, which leaves room for the FP32 promotion without spilling).  Both operands are
-// staged in LDS, double-buffered, in "fragment order": a 16-row block of one
-// K step is stored as [half][lane][16 bytes], so that lane l's two 16-byte
-// halves of its MFMA operand sit at lane * 16 -- every LDS read is a
-// contiguous, conflict-free 1 KB per wave.  (8-bit operand: lane group g
-// holds K [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16) of the step; BF16 at
-// 64 elements per step: the same bytes are two 16x16x32 MFMAs; FP4: one
-// 16-byte chunk per lane, K [32g, 32g + 32).)
+// registers, which leaves room for the FP32 promotion without spilling).
+// Both operands go straight from memory to LDS (buffer loads with the LDS
+// flag) into a three-stage ring, two stages in flight.  Every load fetches
+// whole 128-byte lines; a row's 16-byte chunks are stored XOR-swizzled so
+// that the MFMA operand reads are free of bank conflicts.  (8-bit operand:
+// lane group g holds K [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16) of the
+// step; BF16 at 64 elements per step: the same bytes are two 16x16x32 MFMAs;
+// FP4: one 16-byte chunk per lane, K [32g, 32g + 32).)
 //
 // FP8 / FP4 block scales are applied once per MFMA result in FP32 (one MFMA
 // covers one 128-wide scale block): acc += P * (s_act[row] * s_w[block]).
 //
-// Tiles are numbered m-slot major, n fastest, and the workgroup index is
-// remapped so that each of the 8 XCDs (workgroups are dealt round-robin to
-// them) runs a contiguous range of tiles: neighbouring n tiles share the A
-// rows and neighbouring m tiles of an expert share the weights in that XCD's
-// L2.
+// Tiles are numbered m-slot major, n fastest; each of the 8 XCDs works
+// through a contiguous run of them (see xcd_tile).
 #pragma once
 
 #include "common.hpp"
@@ -33,6 +30,7 @@ namespace moe_tail {
 constexpr int kTM = 128;
 constexpr int kTN = 256;
 constexpr int kBigMinRows = 128;  // experts with at least this many rows use the tiled kernel
+constexpr int kTileMaxE = 512;    // expert tables of the routed kinds live in LDS
 
 enum { TK_L1 = 0, TK_L2 = 1, TK_DENSE = 2 };
 enum { TF_FP8 = 0, TF_FP4 = 1, TF_BF16 = 2 };
@@ -54,51 +52,8 @@ struct TileArgs {
   int N;                          // B rows per expert (routed) or output columns (dense)
   int half;                       // L1: I (up rows start), dense SWIGLU: I_s
   int ntn;                        // n tiles
-  int nslots;                     // m slots in the grid
+  int nslots;                     // dense: row tiles; routed: unused (the tile count comes from expert_offsets)
 };
-
-// Row tiles of experts with >= kBigMinRows rows, kTM rows each (last one partial).
-__device__ __forceinline__ bool find_big_tile(const int32_t* __restrict__ off, int E, int mt, int& e_out,
-                                              int& row0_out, int& rows_out) {
-  const int lane = threadIdx.x & 63;
-  const int per = (E + 63) / 64;
-  const int eb = min(lane * per, E), ee = min(eb + per, E);
-  auto ntile = [&](int e) {
-    const int c = off[e + 1] - off[e];
-    return c >= kBigMinRows ? (c + kTM - 1) / kTM : 0;
-  };
-  int local = 0;
-  for (int e = eb; e < ee; ++e) local += ntile(e);
-  int incl = local;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int n = __shfl_up(incl, d);
-    if (lane >= d) incl += n;
-  }
-  const int total = __shfl(incl, 63);
-  if (mt >= total) return false;
-  const int excl = incl - local;
-  int fe = -1, fr0 = 0, frows = 0;
-  if (mt >= excl && mt < incl) {
-    int acc = excl;
-    for (int e = eb; e < ee; ++e) {
-      const int n = ntile(e);
-      if (mt < acc + n) {
-        fe = e;
-        fr0 = off[e] + (mt - acc) * kTM;
-        frows = min(kTM, off[e + 1] - fr0);
-        break;
-      }
-      acc += n;
-    }
-  }
-  const unsigned long long who = __ballot(fe >= 0);
-  const int src = __ffsll(static_cast<long long>(who)) - 1;
-  e_out = __shfl(fe, src);
-  row0_out = __shfl(fr0, src);
-  rows_out = __shfl(frows, src);
-  return true;
-}
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -131,170 +86,226 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier for LDS traffic only (a fenced __syncthreads would also
+// wait for the direct loads in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+
+// Persistent: one workgroup per CU works through a list of tiles.  Tile t
+// of T: XCD x (workgroups are dealt to the 8 XCDs in turn, b % 8) owns tiles
+// [x * per, (x + 1) * per), per = ceil(T / 8), and its workgroups take them
+// in turn, so the XCD's CUs work on neighbouring tiles together
+// (neighbouring n tiles share the A rows, neighbouring slots of an expert its
+// weights, in that XCD's L2).  The K steps of all of a workgroup's tiles form
+// one stream through the three-stage ring: the first stages of the next tile
+// are loaded while the current one finishes and while its epilogue runs.
 template <int KIND, int FMT, int EPI>
 __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   constexpr bool kFP4 = FMT == TF_FP4;
   constexpr bool kBF16 = FMT == TF_BF16;
   constexpr bool kScaled = !kBF16;
+  constexpr bool kRouted = KIND != TK_DENSE;
+  constexpr bool kPaired = KIND == TK_L1 || (KIND == TK_DENSE && EPI == EPI_SWIGLU);
   constexpr int kABytes = kTM * 128;                 // 16 KB
   constexpr int kBBytes = kTN * (kFP4 ? 64 : 128);   // 16 or 32 KB
   constexpr int kSOff = kABytes + kBBytes;           // scale words: activation [0, 512), FP4 e8m0 [512, 1536)
   constexpr int kStage = kSOff + (kScaled ? 2048 : 0);
   constexpr int kBChunks = kFP4 ? 2 : 4;             // 16-byte B loads per thread and stage
   constexpr int kLoads = 2 + kBChunks + (kScaled ? 1 : 0);  // direct loads per wave and stage
-  // three-stage ring, one array per stage so that the compiler can tell the
-  // stages apart (its own waits before LDS reads then cover just that stage)
-  __shared__ __attribute__((aligned(16))) uint8_t ring0[kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t ring1[kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t ring2[kStage];
-  __shared__ int s_tile[3];
-  __shared__ int s_tok[kTM];
+  constexpr uint32_t kNoRow = 0x80000000u;           // offset past any buffer: reads zeros
+  __shared__ __attribute__((aligned(16))) uint8_t ring[3 * kStage];
+  __shared__ int s_eoff[kRouted ? kTileMaxE + 1 : 1];  // expert row offsets
+  __shared__ int s_pre[kRouted ? kTileMaxE + 1 : 1];   // row tiles of the experts before e
+  // per-tile data, buffer j % 3 for tile j: loaded while tile j - 2 still
+  // computes and read until tile j's last step
+  __shared__ int s_pair[3][kTM];                       // L1: sorted pair ids of a tile's rows
+  __shared__ float s_wsc[3][2][kMaxKBlocks];           // FP8: weight scales of a tile's two 128-row B halves
   __shared__ float s_amax[4][kTM];
-  __shared__ float s_wsc[2][kMaxKBlocks];  // FP8 weight scales of the tile's two 128-row B blocks
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int l16 = lane & 15, g = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-
-  // workgroup -> tile, contiguous tile ranges per XCD
-  const int T = p.nslots * p.ntn;
-  const int b = blockIdx.x;
-  const int full = T - T % 8;
-  const int t = (b < full) ? (b % 8) * (full / 8) + b / 8 : b;
-  const int slot = t / p.ntn, nt = t % p.ntn;
-
-  int e = 0, row0 = 0, rows = 0;
-  if (KIND == TK_DENSE) {
-    row0 = slot * kTM;
-    rows = min(kTM, p.M - row0);
-  } else {
-    if (wave == 0) {
-      int fe, fr, fn;
-      const bool ok = find_big_tile(p.expert_offsets, p.E, slot, fe, fr, fn);
-      if (lane == 0) {
-        s_tile[0] = ok ? fe : -1;
-        s_tile[1] = fr;
-        s_tile[2] = fn;
-      }
-    }
-    __syncthreads();
-    e = __builtin_amdgcn_readfirstlane(s_tile[0]);
-    if (e < 0) return;  // uniform
-    row0 = __builtin_amdgcn_readfirstlane(s_tile[1]);
-    rows = __builtin_amdgcn_readfirstlane(s_tile[2]);
-  }
-  const int nk = kBF16 ? p.K / 64 : p.K / 128;    // K steps of 128 bytes
+  const int nk = kBF16 ? p.K / 64 : p.K / 128;    // K steps of 128 bytes (at least 2)
   const int nkb = p.K / 128;                       // scale blocks along K (scaled formats)
   const int elem = kBF16 ? 2 : 1;                  // bytes per A element
-  constexpr bool kPaired = KIND == TK_L1 || (KIND == TK_DENSE && EPI == EPI_SWIGLU);
   const int nbrows = kPaired ? 2 * p.half : p.N;  // B rows of one expert / of the dense matrix
-  // B row j of the tile (0..255) -> weight row: paired kinds take 128 gate
+  const size_t a_row_bytes = static_cast<size_t>(p.K) * elem;
+  const size_t brow_bytes = kFP4 ? static_cast<size_t>(p.K) / 2 : static_cast<size_t>(p.K) * elem;
+  const size_t wpr = static_cast<size_t>(p.K) / 32;  // FP4: e8m0 bytes per weight row
+
+  // ---- this workgroup's tiles
+  int T;
+  if (kRouted) {
+    for (int i = tid; i <= p.E; i += 512) s_eoff[i] = p.expert_offsets[i];
+    __syncthreads();
+    if (wave == 0) {
+      // exclusive prefix over the experts of their row tiles (experts with
+      // fewer than kBigMinRows rows have none: the row-streaming kernel takes them)
+      const int per = (p.E + 63) / 64;
+      const int eb = min(lane * per, p.E), ee = min(eb + per, p.E);
+      auto ntile = [&](int e) {
+        const int c = s_eoff[e + 1] - s_eoff[e];
+        return c >= kBigMinRows ? (c + kTM - 1) / kTM : 0;
+      };
+      int local = 0;
+      for (int e = eb; e < ee; ++e) local += ntile(e);
+      int incl = local;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int n = __shfl_up(incl, d);
+        if (lane >= d) incl += n;
+      }
+      int run = incl - local;
+      for (int e = eb; e < ee; ++e) {
+        s_pre[e] = run;
+        run += ntile(e);
+      }
+      if (lane == 63) s_pre[p.E] = incl;
+    }
+    __syncthreads();
+    T = s_pre[p.E] * p.ntn;
+  } else {
+    T = p.nslots * p.ntn;
+  }
+  const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+  const int per = (T + 7) / 8, lo = xcd * per, hi = min(T, lo + per);
+  const int n_my = (lo + lb < hi) ? (hi - lo - lb + nbx - 1) / nbx : 0;
+  if (n_my == 0) return;  // uniform
+
+  struct Desc {
+    int e, row0, rows, nt;
+  };
+  // tile j of this workgroup
+  auto desc = [&](int j) -> Desc {
+    const int t = lo + lb + j * nbx;
+    const int slot = t / p.ntn;
+    Desc d;
+    d.nt = t - slot * p.ntn;
+    if (kRouted) {
+      int a = 0, b = p.E;  // s_pre[a] <= slot < s_pre[b]
+      while (b - a > 1) {
+        const int m = (a + b) >> 1;
+        if (s_pre[m] <= slot) a = m;
+        else b = m;
+      }
+      d.e = a;
+      d.row0 = s_eoff[a] + (slot - s_pre[a]) * kTM;
+      d.rows = min(kTM, s_eoff[a + 1] - d.row0);
+    } else {
+      d.e = 0;
+      d.row0 = slot * kTM;
+      d.rows = min(kTM, p.M - d.row0);
+    }
+    d.e = __builtin_amdgcn_readfirstlane(d.e);
+    d.row0 = __builtin_amdgcn_readfirstlane(d.row0);
+    d.rows = __builtin_amdgcn_readfirstlane(d.rows);
+    d.nt = __builtin_amdgcn_readfirstlane(d.nt);
+    return d;
+  };
+  // B row j of a tile (0..255) -> weight row: paired kinds take 128 gate
   // rows and the matching 128 up rows, the others 256 consecutive rows
-  auto wrow = [&](int j) -> int {
+  auto wrow = [&](int nt, int j) -> int {
     if (kPaired) return (j < 128) ? 128 * nt + j : p.half + 128 * nt + (j - 128);
     return kTN * nt + j;
   };
 
-  if (KIND == TK_L1 && tid < kTM) s_tok[tid] = (tid < rows) ? p.sorted_pair[row0 + tid] / p.k : -1;
-  // FP8 weight scales [E, N/128, K/128] of tile rows [0, 128) and [128, 256)
-  // for every K step, read once here
-  if (FMT == TF_FP8 && tid < 2 * nkb) {
-    const int q = tid / nkb, kb = tid - q * nkb;
-    const int wr = wrow(128 * q);
-    s_wsc[q][kb] = (wr < nbrows) ? static_cast<const float*>(p.b_scale)[(static_cast<size_t>(e) * (nbrows / 128) + wr / 128) * nkb + kb]
-                                 : 0.0f;
-  }
-  __syncthreads();
-
   // ---- per-thread load assignment ----
-  // Thread t fills the 16-byte LDS slots t + 512 i of an operand, so every
-  // wave's load writes one contiguous kilobyte.  Slot s is 16-row block
-  // s / 128 (FP4 B: s / 64), half h = (s / 64) % 2, lane' = s % 64 = 16 g + r:
-  // tile row 16 * block + r, 16-byte chunk c = 4 h + g (FP4: g).  This is the
-  // MFMA operand ("fragment") order, so each lane later reads its operand at
-  // lane * 16 of a block's half.
-  const int t_r = tid & 15, t_g = (tid >> 4) & 3, t_h = (tid >> 6) & 1;
-  const int st_c = 4 * t_h + t_g;                       // chunk of an 8-bit / BF16 row step
-  const int st_r0 = 16 * (tid >> 7) + t_r;              // rows st_r0 + 64 i
-  // A operand: rows st_r0 + 64 i, i < 2; out-of-range rows read as zero
-  // (offset past the buffer's end).
-  constexpr uint32_t kNoRow = 0x80000000u;
-  const size_t a_row_bytes = static_cast<size_t>(p.K) * elem;
-  uint32_t a_off[2];
-  const uint8_t* a_base;
-  uint32_t a_records;
-  if (KIND == TK_L1) {
-    a_base = p.a;                                       // gathered token rows of x codes
-    a_records = static_cast<uint32_t>(static_cast<size_t>(p.M) * a_row_bytes);
-  } else {
-    a_base = p.a + static_cast<size_t>(row0) * a_row_bytes;
-    a_records = static_cast<uint32_t>(static_cast<size_t>(rows) * a_row_bytes);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = st_r0 + 64 * i;
-    uint32_t o = kNoRow;
-    if (row < rows) {
-      const size_t rr = (KIND == TK_L1) ? static_cast<size_t>(s_tok[row]) : static_cast<size_t>(row);
-      o = static_cast<uint32_t>(rr * a_row_bytes) + 16u * st_c;
-    }
-    a_off[i] = o;
-  }
-  const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_base), static_cast<short>(0), a_records, 0x00020000);
-  // B operand: the tile's 256 B rows map to weight rows wrow(j)
-  const size_t brow_bytes = kFP4 ? static_cast<size_t>(p.K) / 2 : static_cast<size_t>(p.K) * elem;
-  uint32_t b_off[kBChunks];
-#pragma unroll
-  for (int i = 0; i < kBChunks; ++i) {
-    const int row = kFP4 ? 128 * i + 16 * (tid >> 6) + t_r : st_r0 + 64 * i;
-    const int c = kFP4 ? t_g : st_c;
-    b_off[i] = static_cast<uint32_t>(static_cast<size_t>(wrow(row)) * brow_bytes) + 16u * c;
-  }
-  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.b + static_cast<size_t>(e) * nbrows * brow_bytes), static_cast<short>(0),
-      static_cast<uint32_t>(static_cast<size_t>(nbrows) * brow_bytes), 0x00020000);
+  // A stage holds the operands' K step as 128-byte row pieces in 1 KB blocks
+  // of 8 rows.  Wave w loads blocks w + 8 i, so each of its loads fetches 8
+  // whole 128-byte lines (loads of half lines run at a third of the rate).
+  // Lane l lands at block + 16 l and carries row 8 * block + (l >> 3), chunk
+  // (l & 7) ^ (l >> 3): chunk c of row r sits in 16-byte slot c ^ (r & 7) of
+  // the row's 128 bytes, so the 8 lanes that read one chunk of 8
+  // consecutive rows hit 8 different slots (no bank conflicts).  FP4 B rows
+  // (64 bytes a step) keep one 16-row block per kilobyte, lane l holding row
+  // l % 16, chunk l / 16.
+  const int q8 = lane >> 3;                             // row within a block
+  const int st_c = (lane & 7) ^ q8;                     // chunk this lane fetches
+  const int st_r0 = 8 * wave + q8;                      // rows st_r0 + 64 i
+  const int t_r = tid & 15, t_g = (tid >> 4) & 3;       // FP4 B
   // a resource with no valid bytes: loads through it write zeros
-  const __amdgpu_buffer_rsrc_t z_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.b), static_cast<short>(0), 0u, 0x00020000);
-  // scale words, one 4-byte load per lane and stage: waves 0-1 the
-  // activation scales of tile rows 64 w + lane, waves 2-5 (FP4) the e8m0
-  // words of B rows 64 (w - 2) + lane; the other waves load zeros
-  __amdgpu_buffer_rsrc_t s_rsrc = z_rsrc;
-  uint32_t s_off = kNoRow;
-  if (kScaled) {
-    if (wv < 2) {
-      const int row = 64 * wv + lane;
-      const float* sbase = (KIND == TK_L1) ? p.a_scale : p.a_scale + static_cast<size_t>(row0) * nkb;
-      const size_t srows = (KIND == TK_L1) ? static_cast<size_t>(p.M) : static_cast<size_t>(rows);
-      s_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sbase), static_cast<short>(0),
-                                                 static_cast<uint32_t>(srows * nkb * 4), 0x00020000);
-      if (row < rows) {
-        const size_t ar = (KIND == TK_L1) ? static_cast<size_t>(s_tok[row]) : static_cast<size_t>(row);
-        s_off = static_cast<uint32_t>(ar * nkb * 4);
-      }
-    } else if (kFP4 && wv < 6) {
-      const int j = 64 * (wv - 2) + lane;
-      const size_t wpr = static_cast<size_t>(p.K) / 32;  // e8m0 bytes per weight row
-      s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(static_cast<const uint8_t*>(p.b_scale) + static_cast<size_t>(e) * nbrows * wpr),
-          static_cast<short>(0), static_cast<uint32_t>(nbrows * wpr), 0x00020000);
-      s_off = static_cast<uint32_t>(wrow(j) * wpr);
-    }
-  }
+  const __amdgpu_buffer_rsrc_t z_rsrc = make_rsrc(p.b, 0u);
 
-  // stage ks -> ring buffer; past the last stage the loads go through the
-  // empty resource (no memory traffic) so that every stage counts kLoads
-  auto issue = [&](uint8_t* ring, int ks) {
-    const bool live = ks < nk;
-    const __amdgpu_buffer_rsrc_t ra = live ? a_rsrc : z_rsrc;
-    const __amdgpu_buffer_rsrc_t rb = live ? b_rsrc : z_rsrc;
+  // load offsets of one tile
+  struct Iss {
+    __amdgpu_buffer_rsrc_t ra, rb, rs;
+    uint32_t a_off[2], b_off[kBChunks], s_off;
+  };
+  auto make_iss = [&](const Desc& d, int buf) -> Iss {
+    Iss r;
+    if (KIND == TK_L1)  // gathered token rows of x codes
+      r.ra = make_rsrc(p.a, static_cast<uint32_t>(static_cast<size_t>(p.M) * a_row_bytes));
+    else
+      r.ra = make_rsrc(p.a + static_cast<size_t>(d.row0) * a_row_bytes, static_cast<uint32_t>(static_cast<size_t>(d.rows) * a_row_bytes));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(ra, ring + 8192 * i + 1024 * wv, a_off[i], ks * 128);
+    for (int i = 0; i < 2; ++i) {
+      const int row = st_r0 + 64 * i;
+      uint32_t o = kNoRow;
+      if (row < d.rows) {
+        const size_t rr = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
+        o = static_cast<uint32_t>(rr * a_row_bytes) + 16u * st_c;
+      }
+      r.a_off[i] = o;
+    }
+    r.rb = make_rsrc(p.b + static_cast<size_t>(d.e) * nbrows * brow_bytes, static_cast<uint32_t>(static_cast<size_t>(nbrows) * brow_bytes));
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i) dma16(rb, ring + kABytes + 8192 * i + 1024 * wv, b_off[i], kFP4 ? ks * 64 : ks * 128);
-    if (kScaled) dma4(live ? s_rsrc : z_rsrc, ring + kSOff + 256 * wv, s_off, 4 * ks);
+    for (int i = 0; i < kBChunks; ++i) {
+      const int row = kFP4 ? 128 * i + 16 * wave + t_r : st_r0 + 64 * i;
+      const int c = kFP4 ? t_g : st_c;
+      r.b_off[i] = static_cast<uint32_t>(static_cast<size_t>(wrow(d.nt, row)) * brow_bytes) + 16u * c;
+    }
+    // scale words, one 4-byte load per lane and stage: waves 0-1 the
+    // activation scales of tile rows 64 w + lane, waves 2-5 (FP4) the e8m0
+    // words of B rows 64 (w - 2) + lane; the other waves load zeros
+    r.rs = z_rsrc;
+    r.s_off = kNoRow;
+    if (kScaled) {
+      if (wv < 2) {
+        const int row = 64 * wv + lane;
+        const float* sbase = (KIND == TK_L1) ? p.a_scale : p.a_scale + static_cast<size_t>(d.row0) * nkb;
+        const size_t srows = (KIND == TK_L1) ? static_cast<size_t>(p.M) : static_cast<size_t>(d.rows);
+        r.rs = make_rsrc(sbase, static_cast<uint32_t>(srows * nkb * 4));
+        if (row < d.rows) {
+          const size_t ar = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
+          r.s_off = static_cast<uint32_t>(ar * nkb * 4);
+        }
+      } else if (kFP4 && wv < 6) {
+        const int j = 64 * (wv - 2) + lane;
+        r.rs = make_rsrc(static_cast<const uint8_t*>(p.b_scale) + static_cast<size_t>(d.e) * nbrows * wpr,
+                         static_cast<uint32_t>(nbrows * wpr));
+        r.s_off = static_cast<uint32_t>(wrow(d.nt, j) * wpr);
+      }
+    }
+    return r;
+  };
+  // stage k of a tile -> ring slot; live == false loads zeros (no memory traffic)
+  auto issue = [&](uint8_t* st, const Iss& r, int k, bool live) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(live ? r.ra : z_rsrc, st + 8192 * i + 1024 * wv, r.a_off[i], k * 128);
+#pragma unroll
+    for (int i = 0; i < kBChunks; ++i)
+      dma16(live ? r.rb : z_rsrc, st + kABytes + 8192 * i + 1024 * wv, r.b_off[i], kFP4 ? k * 64 : k * 128);
+    if (kScaled) dma4(live ? r.rs : z_rsrc, st + kSOff + 256 * wv, r.s_off, 4 * k);
+  };
+  // per-tile data loaded ahead (issued first in a stage's batch, only by the
+  // waves that carry it): L1 sorted pair ids (waves 0-1), FP8 weight-scale
+  // rows (waves 2-3)
+  auto aux = [&](const Desc& d, int buf) {
+    if (KIND == TK_L1 && wv < 2) {
+      dma4(make_rsrc(p.sorted_pair + d.row0, static_cast<uint32_t>(d.rows) * 4u), reinterpret_cast<uint8_t*>(&s_pair[buf][64 * wv]),
+           4u * (64 * wv + lane), 0);
+    } else if (FMT == TF_FP8 && (wv == 2 || wv == 3)) {
+      const int q = wv - 2;
+      const int wr = wrow(d.nt, 128 * q);
+      const float* src = static_cast<const float*>(p.b_scale) +
+                         (static_cast<size_t>(d.e) * (nbrows / 128) + wr / 128) * nkb;
+      dma4(make_rsrc(src, (wr < nbrows) ? static_cast<uint32_t>(nkb) * 4u : 0u), reinterpret_cast<uint8_t*>(&s_wsc[buf][q][0]),
+           4u * lane, 0);
+    }
   };
 
   // B blocks of this wave, j = 0..3 (paired: two gate blocks, then the two
@@ -303,28 +314,28 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
     if (kPaired) return (j < 2) ? 2 * wn + j : 8 + 2 * wn + (j - 2);
     return 4 * wn + j;
   };
+  // this lane's MFMA operand pieces within a 16-row block (2 KB): row l16,
+  // chunk g (registers 0-3) and chunk 4 + g (registers 4-7)
+  const int fr = 1024 * (l16 >> 3) + 128 * (l16 & 7);
+  const int f_lo = fr + 16 * (g ^ (l16 & 7));
+  const int f_hi = fr + 16 * ((4 | g) ^ (l16 & 7));
 
   f32x4 acc[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](const uint8_t* st, int ks) {
+  auto compute = [&](const uint8_t* st, int ks, int buf) {
     // weight scales of this step (FP8): the wave's B rows lie in the tile's
     // row half 16 * bblk(0) / 128 (paired: its gate rows) and 16 * bblk(3) / 128
     float sw_lo = 1.0f, sw_hi = 1.0f;
     if (FMT == TF_FP8) {
-      sw_lo = s_wsc[(16 * bblk(0)) / 128][ks];
-      sw_hi = s_wsc[(16 * bblk(3)) / 128][ks];
+      sw_lo = s_wsc[buf][(16 * bblk(0)) / 128][ks];
+      sw_hi = s_wsc[buf][(16 * bblk(3)) / 128][ks];
     }
     i32x8 af[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const uint8_t* ab = st + (4 * wm + mt) * 2048 + lane * 16;
-      const i32x4 lo = *reinterpret_cast<const i32x4*>(ab);
-      const i32x4 hi = *reinterpret_cast<const i32x4*>(ab + 1024);
-      af[mt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const uint8_t* ab = st + (4 * wm + mt) * 2048;
+      const i32x4 lo4 = *reinterpret_cast<const i32x4*>(ab + f_lo);
+      const i32x4 hi4 = *reinterpret_cast<const i32x4*>(ab + f_hi);
+      af[mt] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     }
     // per-row promotion factors of this step: activation scale x weight scale
     float sc[2][4][4];
@@ -344,9 +355,9 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
     for (int j = 0; j < 4; ++j) {
       const int bb = bblk(j);
       if (kBF16) {
-        const uint8_t* bp = st + kABytes + bb * 2048 + lane * 16;
-        const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp));
-        const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + 1024));
+        const uint8_t* bp = st + kABytes + bb * 2048;
+        const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_lo));
+        const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_hi));
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const i32x4 alo = __builtin_shufflevector(af[mt], af[mt], 0, 1, 2, 3);
@@ -363,10 +374,10 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
           bf = __builtin_shufflevector(v, z, 0, 1, 2, 3, 4, 5, 6, 7);
           sb = st[kSOff + 512 + (16 * bb + l16) * 4 + g];
         } else {
-          const uint8_t* bp = st + kABytes + bb * 2048 + lane * 16;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(bp);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(bp + 1024);
-          bf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const uint8_t* bp = st + kABytes + bb * 2048;
+          const i32x4 lo4 = *reinterpret_cast<const i32x4*>(bp + f_lo);
+          const i32x4 hi4 = *reinterpret_cast<const i32x4*>(bp + f_hi);
+          bf = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         }
         const int half_sel = (kPaired && j >= 2) ? 1 : 0;
 #pragma unroll
@@ -379,101 +390,135 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
     }
   };
 
-  // Pipeline: stage ks sits in ring ks % 3 while stages ks + 1 and ks + 2 are
-  // in flight.  Each step: wait for stage ks (all waves), start stage ks + 2
-  // into the buffer that stage ks - 1 (read by every wave before the
-  // barrier) leaves free, then compute stage ks.
-  issue(ring0, 0);
-  issue(ring1, 1);
-  for (int ks = 0; ks < nk; ks += 3) {
-    ring_barrier<kLoads>();
-    issue(ring2, ks + 2);
-    compute(ring0, ks);
-    if (ks + 1 < nk) {
-      ring_barrier<kLoads>();
-      issue(ring0, ks + 3);
-      compute(ring1, ks + 1);
-    }
-    if (ks + 2 < nk) {
-      ring_barrier<kLoads>();
-      issue(ring1, ks + 4);
-      compute(ring2, ks + 2);
-    }
-  }
-  // drain the trailing (empty) loads before the epilogue reuses ring0
-  ring_barrier<0>();
-
   // ---------------------------------------------------------------- epilogues
-  if (KIND == TK_L1) {
-    // h = silu(gate) * up for this wave's 64 rows x 32 h columns; row amax over the tile's 128 h columns
-    float h[4][2][4];
+  auto epilogue = [&](const Desc& d, uint8_t* sq) {
+    if (KIND == TK_L1) {
+      // h = silu(gate) * up for this wave's 64 rows x 32 h columns; row amax
+      // over the tile's 128 h columns
+      float h[4][2][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float m = 0.0f;
+        for (int i = 0; i < 4; ++i) {
+          float m = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          h[mt][j][i] = silu_mul(acc[mt][j][i], acc[mt][2 + j][i]);
-          m = fmaxf(m, fabsf(h[mt][j][i]));
+          for (int j = 0; j < 2; ++j) {
+            h[mt][j][i] = silu_mul(acc[mt][j][i], acc[mt][2 + j][i]);
+            m = fmaxf(m, fabsf(h[mt][j][i]));
+          }
+          m = group16_max(m);
+          if (l16 == 0) s_amax[wn][64 * wm + 16 * mt + 4 * g + i] = m;
         }
-        m = group16_max(m);
-        if (l16 == 0) s_amax[wn][64 * wm + 16 * mt + 4 * g + i] = m;
-      }
-    __syncthreads();
-    uint8_t* sq = ring0;  // [128 rows][128 codes], the ring is free now
+      lds_barrier();  // s_amax complete; every wave is done with the stage in sq
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 64 * wm + 16 * mt + 4 * g + i;
-        const float amax = fmaxf(fmaxf(s_amax[0][r], s_amax[1][r]), fmaxf(s_amax[2][r], s_amax[3][r]));
-        const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+        for (int i = 0; i < 4; ++i) {
+          const int r = 64 * wm + 16 * mt + 4 * g + i;
+          const float amax = fmaxf(fmaxf(s_amax[0][r], s_amax[1][r]), fmaxf(s_amax[2][r], s_amax[3][r]));
+          const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) sq[r * 128 + 32 * wn + 16 * j + l16] = static_cast<uint8_t>(f32_to_e4m3(h[mt][j][i] / s));
-        if (wn == 0 && l16 == 0 && r < rows) p.sh[static_cast<size_t>(row0 + r) * (p.half / 128) + nt] = s;
-      }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = tid + 512 * i;
-      const int r = q >> 3, c16 = (q & 7) * 16;
-      if (r < rows)
-        *reinterpret_cast<uint4*>(p.hq + static_cast<size_t>(row0 + r) * p.half + 128 * nt + c16) =
-            *reinterpret_cast<const uint4*>(sq + r * 128 + c16);
-    }
-  } else if (KIND == TK_L2) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 64 * wm + 16 * mt + 4 * g + i;
-        if (r < rows) {
-          float* yr = p.y + static_cast<size_t>(row0 + r) * p.N + kTN * nt + 64 * wn + l16;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) yr[16 * j] = acc[mt][j][i];
+          for (int j = 0; j < 2; ++j) sq[r * 128 + 32 * wn + 16 * j + l16] = static_cast<uint8_t>(f32_to_e4m3(h[mt][j][i] / s));
+          if (wn == 0 && l16 == 0 && r < d.rows) p.sh[static_cast<size_t>(d.row0 + r) * (p.half / 128) + d.nt] = s;
         }
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int q = tid + 512 * i;
+        const int r = q >> 3, c16 = (q & 7) * 16;
+        if (r < d.rows)
+          *reinterpret_cast<uint4*>(p.hq + static_cast<size_t>(d.row0 + r) * p.half + 128 * d.nt + c16) =
+              *reinterpret_cast<const uint4*>(sq + r * 128 + c16);
       }
-  } else {
+    } else if (KIND == TK_L2) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 64 * wm + 16 * mt + 4 * g + i;
-        if (r < rows) {
-          if (EPI == EPI_SWIGLU) {
+        for (int i = 0; i < 4; ++i) {
+          const int r = 64 * wm + 16 * mt + 4 * g + i;
+          if (r < d.rows) {
+            float* yr = p.y + static_cast<size_t>(d.row0 + r) * p.N + kTN * d.nt + 64 * wn + l16;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-              dense_epilogue<EPI>(p.ep, p.N, row0 + r, 128 * nt + 32 * wn + 16 * j + l16, acc[mt][j][i],
-                                  acc[mt][2 + j][i]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              dense_epilogue<EPI>(p.ep, p.N, row0 + r, kTN * nt + 64 * wn + 16 * j + l16, acc[mt][j][i], 0.0f);
+            for (int j = 0; j < 4; ++j) yr[16 * j] = acc[mt][j][i];
           }
         }
-      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 64 * wm + 16 * mt + 4 * g + i;
+          if (r < d.rows) {
+            if (EPI == EPI_SWIGLU) {
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+                dense_epilogue<EPI>(p.ep, p.N, d.row0 + r, 128 * d.nt + 32 * wn + 16 * j + l16, acc[mt][j][i],
+                                    acc[mt][2 + j][i]);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                dense_epilogue<EPI>(p.ep, p.N, d.row0 + r, kTN * d.nt + 64 * wn + 16 * j + l16, acc[mt][j][i], 0.0f);
+            }
+          }
+        }
+    }
+  };
+
+  // ---- prologue: tile 0's pair ids and weight scales with ordinary loads
+  Desc dc = desc(0);
+  if (KIND == TK_L1 && tid < kTM) s_pair[0][tid] = (tid < dc.rows) ? p.sorted_pair[dc.row0 + tid] : 0;
+  if (FMT == TF_FP8 && tid < 2 * nkb) {
+    const int q = tid / nkb, kb = tid - q * nkb;
+    const int wr = wrow(dc.nt, 128 * q);
+    s_wsc[0][q][kb] = (wr < nbrows) ? static_cast<const float*>(p.b_scale)[(static_cast<size_t>(dc.e) * (nbrows / 128) + wr / 128) * nkb + kb]
+                                    : 0.0f;
   }
+  __syncthreads();
+
+  // Stage G of the stream is K step G % nk of tile G / nk and sits in ring
+  // slot G % 3.  Step G: wait for stage G (every wave's loads), start stage
+  // G + 2 into the slot that stage G - 1 (read by every wave before the
+  // barrier) leaves free, compute stage G; after a tile's last step its
+  // epilogue stages the h codes through that step's slot, which the next
+  // step's loads only reuse after their barrier.  A tile's pair ids and
+  // weight scales are loaded with the first stage of the tile before it,
+  // nk >= 2 steps ahead of their first use.
+  Iss is = make_iss(dc, 0);
+  int ji = 0;  // tile of `is`
+  const int G = n_my * nk;
+  auto issue_stage = [&](int g2) {
+    const int j2 = g2 / nk, k2 = g2 - j2 * nk;
+    uint8_t* st = ring + (g2 % 3) * kStage;
+    if (j2 >= n_my) {
+      issue(st, is, 0, false);
+      return;
+    }
+    if (k2 == 0 && j2 != ji) {
+      is = make_iss(desc(j2), j2 % 3);
+      ji = j2;
+    }
+    if (k2 == 0 && j2 + 1 < n_my) aux(desc(j2 + 1), (j2 + 1) % 3);
+    issue(st, is, k2, true);
+  };
+  issue_stage(0);
+  issue_stage(1);
+  for (int gg = 0; gg < G; ++gg) {
+    const int j = gg / nk, ks = gg - j * nk;
+    ring_barrier<kLoads>();
+    issue_stage(gg + 2);
+    if (ks == 0) {
+      if (j > 0) dc = desc(j);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[mt][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    uint8_t* st = ring + (gg % 3) * kStage;
+    compute(st, ks, j % 3);
+    if (ks == nk - 1) epilogue(dc, st);
+  }
+  // drain the trailing (empty) loads
+  ring_barrier<0>();
 }
 
 }  // namespace moe_tail

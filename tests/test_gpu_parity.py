@@ -185,6 +185,23 @@ def test_forward_tiled_path(wfmt):
     check_forward(dev, inp, sel=np.unique(sel))
 
 
+@pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4])
+def test_forward_tiled_several_tiles_per_workgroup(wfmt):
+    # ~36 row tiles x 16 n tiles (L1) and x 8 (L2): more tiles than workgroups,
+    # so each persistent workgroup runs two or three tiles back to back and
+    # loads the next tile's rows, pair ids and weight scales while the
+    # current one finishes.  Outputs are checked on a sample of tokens.
+    wl = synth.Workload("multi", Mr=1024, Ms=1184, E=8, k=4, I=2048, Is=256, wfmt=wfmt, seed=31, H=2048, L=2048,
+                        zipf_s=0.4 if wfmt else 0.0)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    loads = np.diff(to_np(dev.offsets))
+    assert loads.min() >= 128, loads
+    rng = np.random.default_rng(5)
+    sel = np.concatenate([np.sort(rng.choice(1024, 40, replace=False)), [0, 1023, 1024, 1183]]).astype(np.int32)
+    check_forward(dev, inp, sel=np.unique(sel))
+
+
 def test_forward_heavy_expert_many_row_tiles():
     # all-equal logits: every token goes to experts 0..k-1, 100 rows each (4 row tiles per expert)
     wl = synth.Workload("heavy", Mr=100, Ms=100, E=6, k=2, I=512, Is=128, wfmt=0, seed=22, zero_router=True)
