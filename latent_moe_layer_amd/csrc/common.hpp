@@ -22,20 +22,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
-// fp32 -> e4m3 ("fn": bias 7, max 448, no infinities) code, round to nearest
-// even, saturating to +-448; the sign bit of the input is kept.
+// fp32 -> e4m3 ("fn": bias 7, max 448, no infinities) code: the gfx950
+// conversion instruction, which rounds to nearest even, saturates to +-448
+// and keeps the sign bit of the input (including -0).
 __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  if (a >= 448.0f) return sign | 0x7eu;
-  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of 2^-9
-    return sign | static_cast<uint32_t>(rintf(a * 512.0f));
-  }
-  const int ex = static_cast<int>((__float_as_uint(a) >> 23) & 0xff) - 127;  // -6..8
-  // a * 2^(3 - ex) lies in [8, 16): its integer part carries the implicit bit
-  const float scaled = a * __uint_as_float(static_cast<uint32_t>(127 + 3 - ex) << 23);
-  const uint32_t q = static_cast<uint32_t>(rintf(scaled));                 // 8..16
-  return sign | ((static_cast<uint32_t>(ex + 7) << 3) + (q - 8u));
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false)) & 0xffu;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -58,6 +49,13 @@ __device__ __forceinline__ float group16_max(float v) {
 }
 
 __device__ __forceinline__ float silu_mul(float gate, float up) { return (gate / (1.0f + expf(-gate))) * up; }
+
+// silu(gate) * up with the hardware exp2 and reciprocal (about one ulp each),
+// for values that are re-quantized to FP8 right after
+__device__ __forceinline__ float silu_mul_fast(float gate, float up) {
+  const float e = __builtin_amdgcn_exp2f(gate * -1.44269504088896341f);
+  return gate * __builtin_amdgcn_rcpf(1.0f + e) * up;
+}
 
 // 16x16x128 FP8 x FP8 block product (e4m3 both sides, unit scales).
 __device__ __forceinline__ f32x4 mfma_fp8(const i32x8& a, const i32x8& b) {

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void k_routed_l1(const uint8_t* __restrict_
       float m = 0.0f;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        h[ms][c][i] = silu_mul(acc[ms][c][i], acc[ms][2 + c][i]);
+        h[ms][c][i] = silu_mul_fast(acc[ms][c][i], acc[ms][2 + c][i]);
         m = fmaxf(m, fabsf(h[ms][c][i]));
       }
       m = group16_max(m);
@@ -250,8 +250,9 @@ __global__ __launch_bounds__(256, 2) void k_routed_l1(const uint8_t* __restrict_
       const int r = 16 * ms + 4 * g + i;
       const float amax = fmaxf(fmaxf(s_amax[0][r], s_amax[1][r]), fmaxf(s_amax[2][r], s_amax[3][r]));
       const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+      const float inv = 1.0f / s;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) s_q[r][32 * wave + 16 * c + l16] = static_cast<uint8_t>(f32_to_e4m3(h[ms][c][i] / s));
+      for (int c = 0; c < 2; ++c) s_q[r][32 * wave + 16 * c + l16] = static_cast<uint8_t>(f32_to_e4m3(h[ms][c][i] * inv));
       if (wave == 0 && l16 == 0 && r < rows) sh[static_cast<size_t>(row0 + r) * (I / 128) + nb] = s;
     }
   __syncthreads();

@@ -403,7 +403,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
           float m = 0.0f;
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            h[mt][j][i] = silu_mul(acc[mt][j][i], acc[mt][2 + j][i]);
+            h[mt][j][i] = silu_mul_fast(acc[mt][j][i], acc[mt][2 + j][i]);
             m = fmaxf(m, fabsf(h[mt][j][i]));
           }
           m = group16_max(m);
@@ -417,8 +417,9 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
           const int r = 64 * wm + 16 * mt + 4 * g + i;
           const float amax = fmaxf(fmaxf(s_amax[0][r], s_amax[1][r]), fmaxf(s_amax[2][r], s_amax[3][r]));
           const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+          const float inv = 1.0f / s;
 #pragma unroll
-          for (int j = 0; j < 2; ++j) sq[r * 128 + 32 * wn + 16 * j + l16] = static_cast<uint8_t>(f32_to_e4m3(h[mt][j][i] / s));
+          for (int j = 0; j < 2; ++j) sq[r * 128 + 32 * wn + 16 * j + l16] = static_cast<uint8_t>(f32_to_e4m3(h[mt][j][i] * inv));
           if (wn == 0 && l16 == 0 && r < d.rows) p.sh[static_cast<size_t>(d.row0 + r) * (p.half / 128) + d.nt] = s;
         }
       lds_barrier();
