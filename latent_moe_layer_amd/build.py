@@ -13,6 +13,10 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     # no packed-FP32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: with the accumulation-register form
+    # the compiler copies the accumulators between the two register files on
+    # every K step of the small-M dense loop
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

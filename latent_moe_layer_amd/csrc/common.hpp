@@ -73,4 +73,45 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, con
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// ------------------------------------------------ direct global -> LDS loads
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct global -> LDS loads: lane l's 16 (or 4) bytes land at lds + 16 l
+// (4 l); an offset outside the resource's range writes zeros.  `lds` must be
+// the same for the whole wave.  Issued as inline assembly so that the
+// compiler does not track them: it cannot always tell which LDS reads they
+// may overlap and would then wait for every one in flight; ring_barrier
+// below does the waiting instead.  (No memory clobber: volatile asm keeps
+// its order against ring_barrier, and the compiler may move LDS reads of
+// other stages around these.)
+__device__ __forceinline__ uint32_t lds_offset(const uint8_t* lds) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds)));
+}
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_offset(lds)), "v"(voff), "s"(r),
+               "s"(soff));
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(lds_offset(lds)), "v"(voff), "s"(r),
+               "s"(soff));
+}
+
+// Wait until at most N of this wave's direct loads are in flight and its LDS
+// reads are done, then meet the other waves: afterwards every load issued
+// before the newest N (by any wave) has landed.  (A fenced __syncthreads
+// would wait for all of them.)
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS traffic only (a fenced __syncthreads would also
+// wait for the direct loads in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+
 }  // namespace moe_tail

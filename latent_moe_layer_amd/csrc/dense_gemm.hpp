@@ -7,13 +7,12 @@
 // ("[Kimi K3][Kernel] Fuse BF16 shared experts into latent MegaMoE tail",
 // Summary; DeepGEMM PR 416 mirror, Summary).
 //
-// C[M, N] = A[M, K] . B[N, K]^T, both operands K-contiguous.  Operand layout
-// of the 16x16x32 MFMA: lane l holds row l % 16 and 8 consecutive K elements
-// of group l / 16; one 128-wide K step is four MFMAs, lane group g covering
-// elements [32 g, 32 g + 32) of the step in both operands.  Decode-sized M
-// uses k_dense_small below (K split over the grid, FP32 partials reduced in
-// split order by k_dense_reduce, which applies the epilogue); larger M the
-// LDS-tiled kernel of tile_gemm.hpp with the epilogue fused.
+// C[M, N] = A[M, K] . B[N, K]^T, both operands K-contiguous; one 64-wide K
+// step of the 16x16x32 MFMA is two MFMAs, lane group g holding 8 consecutive K
+// elements of each.  Decode-sized M uses k_dense_small below (K split over
+// the grid, FP32 partials reduced in split order by k_dense_reduce, which
+// applies the epilogue); larger M the LDS-tiled kernel of tile_gemm.hpp with
+// the epilogue fused.
 #pragma once
 
 #include "common.hpp"
@@ -46,137 +45,101 @@ __device__ __forceinline__ void dense_epilogue(const DenseEpi& ep, int N, int ro
   }
 }
 
-__device__ __forceinline__ void load_bf16_frag(const uint16_t* __restrict__ row_ptr, int k0, bf16x8 (&f)[4]) {
-  const int g = (threadIdx.x & 63) >> 4;
-  const uint4* p = reinterpret_cast<const uint4*>(row_ptr + k0 + 32 * g);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint4 v = p[j];
-    f[j] = __builtin_bit_cast(bf16x8, v);
-  }
-}
-
 // ---------------------------------------------------------- small M --
-// Decode-sized M (<= 128 rows): one workgroup covers every row, so each
-// weight byte is read from HBM exactly once.  The A rows of one 128-wide K
-// step are staged in LDS (double-buffered, shared by the 4 waves); each wave
-// streams its own 16 * NT B rows with the next K step's fragments in flight.
-// K is split over gridDim.y; FP32 partial sums partial[z][row][brow] are
-// reduced (in split order) by k_dense_reduce, which applies the epilogue.
+// Decode-sized M (<= 128 rows): a workgroup covers every row and kSkinnyN
+// weight rows over a range of K steps (K is split over gridDim.y), so each
+// weight byte is read from HBM once.  Both operands go straight from memory
+// into a kSkinnyStages-deep LDS ring (buffer loads with the LDS flag, whole
+// 128-byte lines per load, rows XOR-swizzled as in the tiled kernel), so that
+// five steps of weights are in flight per CU.  Each of the 8 waves (two per
+// SIMD, so one can issue while the other waits) multiplies rows
+// [16 w, 16 w + 16) by the kSkinnyN weight rows; FP32 partial sums
+// partial[z][row][brow] are reduced in split order by k_dense_reduce, which
+// applies the epilogue.
 constexpr int kSmallMaxM = 128;
-constexpr int kAStride = 136;  // LDS row stride in bf16 (272 B: rows start 4 banks apart)
+constexpr int kSkinnyN = 64;      // weight rows per workgroup
+constexpr int kSkinnyStages = 6;  // LDS ring depth
 
-template <int NT>
-__global__ __launch_bounds__(256) void k_dense_small(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+__global__ __launch_bounds__(512) void k_dense_small(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                      int M, int nbrows, int K, int kps, float* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kSmallMaxM * kAStride];
+  constexpr int kABytes = kSmallMaxM * 128;  // one K step of 64 BF16: 128 rows x 128 bytes
+  constexpr int kBBytes = kSkinnyN * 128;
+  constexpr int kStage = kABytes + kBBytes;
+  constexpr int kLoads = 3;  // per wave and stage: A blocks w + 8 i (i < 2), B block w
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kSkinnyStages * kStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int l16 = lane & 15, g = lane >> 4;
-  const int mt = (M + 15) / 16;
-  const int rows_pad = 16 * mt;
-  const int brow0 = blockIdx.x * 64 * NT + wave * 16 * NT;
-  const uint16_t* bptr[NT];
-#pragma unroll
-  for (int ns = 0; ns < NT; ++ns) bptr[ns] = B + static_cast<size_t>(brow0 + 16 * ns + l16) * K;
-  const int nk = K / 128;
-  const int kb0 = blockIdx.y * kps, kb1 = min(kb0 + kps, nk);
+  const int brow0 = blockIdx.x * kSkinnyN;
+  const int nk = K / 64;
+  const int kb0 = blockIdx.y * kps, n = min(kb0 + kps, nk) - kb0;  // this workgroup's steps (>= 1)
+  const size_t rowb = static_cast<size_t>(K) * 2;
 
-  // A staging: rows_pad rows x 16 uint4 per K step; thread t moves uint4s t, t + 256, ...
-  constexpr int kMaxStage = kSmallMaxM * 16 / 256;  // 8
-  uint4 st[kMaxStage];
-  auto stage_load = [&](int kb) {
+  // 1 KB block b of a stage = rows 8 b .. 8 b + 7, 128 bytes each; lane l
+  // carries row 8 b + (l >> 3), chunk (l & 7) ^ (l >> 3) (rows past M read zeros)
+  const int q8 = lane >> 3, st_c = (lane & 7) ^ q8;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, static_cast<uint32_t>(static_cast<size_t>(M) * rowb));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + static_cast<size_t>(brow0) * K, static_cast<uint32_t>(kSkinnyN * rowb));
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(B, 0u);
+  uint32_t a_off[2];
 #pragma unroll
-    for (int i = 0; i < kMaxStage; ++i) {
-      const int idx = tid + 256 * i;
-      const int r = idx >> 4, c = idx & 15;
-      st[i] = (r < M) ? *reinterpret_cast<const uint4*>(A + static_cast<size_t>(r) * K + kb * 128 + 8 * c)
-                      : uint4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto stage_store = [&](int buf) {
-    // laundered buffer index: keeps these stores (and the waits on their
-    // global loads) after the current step's MFMAs
-    int b = buf;
-    asm volatile("" : "+v"(b));
+  for (int i = 0; i < 2; ++i) a_off[i] = static_cast<uint32_t>((8 * (wave + 8 * i) + q8) * rowb) + 16u * st_c;
+  const uint32_t b_off = static_cast<uint32_t>((8 * wave + q8) * rowb) + 16u * st_c;
+  // The workgroups of one K range all read the same activation rows; each
+  // starts at its own step (rotation by its weight tile) so that they do not
+  // request the same lines at the same time.  The summation order then
+  // depends on the tile only.
+  const int rot = blockIdx.x % n;
+  auto issue = [&](int s) {
+    uint8_t* st = ring + (s % kSkinnyStages) * kStage;
+    const bool live = s < n;
+    const int sr = s + rot < n ? s + rot : s + rot - n;
+    const int soff = (kb0 + sr) * 128;
 #pragma unroll
-    for (int i = 0; i < kMaxStage; ++i) {
-      const int idx = tid + 256 * i;
-      const int r = idx >> 4, c = idx & 15;
-      if (r < rows_pad) *reinterpret_cast<uint4*>(&sA[b][r * kAStride + 8 * c]) = st[i];
-    }
+    for (int i = 0; i < 2; ++i) dma16(live ? ra : rz, st + 1024 * (wv + 8 * i), a_off[i], soff);
+    dma16(live ? rb : rz, st + kABytes + 1024 * wv, b_off, soff);
   };
 
-  f32x4 acc[8][NT];
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-#pragma unroll
-    for (int ns = 0; ns < NT; ++ns) acc[m][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // this lane's operand pieces within a 16-row block (2 KB): row l16, chunk
+  // g (first MFMA of the step) and chunk 4 + g (second)
+  const int fr = 1024 * (l16 >> 3) + 128 * (l16 & 7);
+  const int f_lo = fr + 16 * (g ^ (l16 & 7));
+  const int f_hi = fr + 16 * ((4 | g) ^ (l16 & 7));
 
-  // B fragments in two sets used in turn; the A rows of the next step are
-  // loaded before the next B fragments so that storing them to LDS waits for
-  // the A loads only.
-  bf16x8 fb[2][NT][4];
-  auto mma_step = [&](int set, int buf) {
-    const uint16_t* sa = &sA[buf][0];
+  f32x4 acc[4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      if (m < mt) {
-        bf16x8 a[4];
-        const uint16_t* ar = sa + (16 * m + l16) * kAStride + 32 * g;
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Step s: wait for stage s (every wave's loads), start stage s + 5 into the
+  // buffer of stage s - 1, compute stage s.
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const bf16x8*>(ar + 8 * j);
+  for (int s = 0; s < kSkinnyStages - 1; ++s) issue(s);
+  for (int s = 0; s < n; ++s) {
+    ring_barrier<kLoads * (kSkinnyStages - 2)>();
+    issue(s + kSkinnyStages - 1);
+    // unconditional (a wave past M multiplies zero rows): a branch here makes
+    // the compiler copy the accumulators between register files every step
+    const uint8_t* st = ring + (s % kSkinnyStages) * kStage;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+    for (int h = 0; h < 2; ++h) {
+      const int fo = h ? f_hi : f_lo;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + 2048 * wave + fo);
+      bf16x8 b[4];
 #pragma unroll
-          for (int ns = 0; ns < NT; ++ns) acc[m][ns] = mfma_bf16(a[j], fb[set][ns][j], acc[m][ns]);
-      }
+      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(st + kABytes + 2048 * j + fo);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = mfma_bf16(a, b[j], acc[j]);
     }
-  };
-  // Pipeline: step kb's A rows are in LDS buffer (kb - kb0) & 1 and its B
-  // fragments in set (kb - kb0) & 1, while the registers hold step kb + 1's
-  // A rows and the other set its B fragments (loaded one step earlier).  After
-  // the MFMAs of step kb and a barrier, the A registers go to the other buffer
-  // and step kb + 2 is loaded into the registers and the freed B set.
-  auto step = [&](int set, int kb) {
-    mma_step(set, set);
-    __syncthreads();
-    if (kb + 1 < kb1) {
-      stage_store(set ^ 1);
-      const int k2 = (kb + 2 < kb1) ? kb + 2 : kb1 - 1;
-      stage_load(k2);
-#pragma unroll
-      for (int ns = 0; ns < NT; ++ns) load_bf16_frag(bptr[ns], k2 * 128, fb[set][ns]);
-    }
-    __syncthreads();
-  };
-  if (kb0 < kb1) {
-    stage_load(kb0);
-    stage_store(0);
-#pragma unroll
-    for (int ns = 0; ns < NT; ++ns) load_bf16_frag(bptr[ns], kb0 * 128, fb[0][ns]);
-    const int k1 = (kb0 + 1 < kb1) ? kb0 + 1 : kb0;
-    stage_load(k1);
-#pragma unroll
-    for (int ns = 0; ns < NT; ++ns) load_bf16_frag(bptr[ns], k1 * 128, fb[1][ns]);
   }
-  __syncthreads();
-  for (int kb = kb0; kb < kb1; kb += 2) {
-    step(0, kb);
-    if (kb + 1 < kb1) step(1, kb + 1);
-  }
+  ring_barrier<0>();  // the trailing (empty) loads
 
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    if (m < mt) {
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * wave + 4 * g + i;
+    if (row < M) {
+      float* pr = partial + (static_cast<size_t>(blockIdx.y) * M + row) * nbrows + brow0 + l16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * m + 4 * g + i;
-        if (row < M) {
-          float* pr = partial + (static_cast<size_t>(blockIdx.y) * M + row) * nbrows + brow0 + l16;
-#pragma unroll
-          for (int ns = 0; ns < NT; ++ns) pr[16 * ns] = acc[m][ns][i];
-        }
-      }
+      for (int j = 0; j < 4; ++j) pr[16 * j] = acc[j][i];
     }
   }
 }

@@ -60,15 +60,19 @@ struct DensePlan {
   int mt, nt, splits, kps;
 };
 
+constexpr int kPlanCUs = 256;
+
 DensePlan plan_dense(int M, int nbrows, int ntiles, int K) {
   DensePlan p;
-  const int nk = K / 128;
   p.small = M <= kSmallMaxM;
+  const int nk = p.small ? K / 64 : K / 128;  // K steps of the kernel
   int s = 1;
   if (p.small) {
+    // about one workgroup per CU of an MI355X (the kernel's LDS ring allows
+    // one); a fixed count keeps the workspace size independent of the device
     p.mt = 1;
-    p.nt = nbrows / 128;
-    if (p.nt > 0) s = std::min(nk, std::max(1, (256 + p.nt - 1) / p.nt));
+    p.nt = nbrows / kSkinnyN;
+    if (p.nt > 0) s = std::min(nk, std::max(1, kPlanCUs / p.nt));
   } else {
     p.mt = (M + kTM - 1) / kTM;
     p.nt = ntiles;
@@ -192,7 +196,7 @@ void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int 
   if (M == 0) return;
   const int nbrows = (kEpi == EPI_SWIGLU) ? 2 * ep.half : N;
   if (p.small) {
-    hipLaunchKernelGGL(k_dense_small<2>, dim3(p.nt, p.splits), dim3(256), 0, st, A, B, M, nbrows, K, p.kps, partial);
+    hipLaunchKernelGGL(k_dense_small, dim3(p.nt, p.splits), dim3(512), 0, st, A, B, M, nbrows, K, p.kps, partial);
     const int ncols = (kEpi == EPI_SWIGLU) ? ep.half : N;
     const long n = static_cast<long>(M) * (ncols / 4);
     hipLaunchKernelGGL(k_dense_reduce<kEpi>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
