@@ -110,8 +110,16 @@ __device__ __forceinline__ void ring_barrier() {
 // wait for the direct loads in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Buffer resource for `bytes` bytes at `base` (wave-uniform; read through
+// readfirstlane so that it lives in scalar registers, as the loads need).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+  // (readfirstlane returns int: convert through uint32_t, never sign-extend)
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a))));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32))));
+  const uint32_t n = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bytes)));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo),
+                                           static_cast<short>(0), n, 0x00020000);
 }
 
 }  // namespace moe_tail

@@ -419,12 +419,24 @@ int moe_tail_route(const moe_tail_dims* dims, const moe_tail_weights* w, const u
   int32_t* hist = at<int32_t>(ws, lay.hist);
   if (Mr > 0) {
     const int egroups = (E + 4 * kLogitExpPerWave - 1) / (4 * kLogitExpPerWave);
-    hipLaunchKernelGGL(k_router_logits, dim3((Mr + kLogitTok - 1) / kLogitTok, egroups), dim3(256), 0, st, x_lat,
+    const size_t xtile = static_cast<size_t>(kLogitTok) * L * 2;  // dynamic LDS of the logits kernel
+    static bool lds_raised = false;
+    if (!lds_raised) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_router_logits),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLogitTok * 8192 * 2);
+      lds_raised = true;
+    }
+    hipLaunchKernelGGL(k_router_logits, dim3((Mr + kLogitTok - 1) / kLogitTok, egroups), dim3(256), xtile, st, x_lat,
                        w->gate, w->gate_bias, logits, Mr, L, E);
     hipLaunchKernelGGL(k_router_topk, dim3((Mr + 3) / 4), dim3(256), 0, st, logits, out->topk_ids,
                        out->topk_weights, Mr, E, k);
-    hipLaunchKernelGGL(k_router_hist, dim3(ng), dim3(64), 0, st, out->topk_ids, hist, Mr, E, k, ng);
   }
+  if (static_cast<int64_t>(ng) * E <= kSortSmall) {
+    hipLaunchKernelGGL(k_router_sort, dim3(1), dim3(1024), 0, st, out->topk_ids, out->expert_offsets,
+                       out->sorted_pair, out->pair_to_row, Mr, E, k, ng);
+    return launched();
+  }
+  if (Mr > 0) hipLaunchKernelGGL(k_router_hist, dim3(ng), dim3(64), 0, st, out->topk_ids, hist, Mr, E, k, ng);
   hipLaunchKernelGGL(k_router_scan, dim3(1), dim3(1024), 0, st, hist, out->expert_offsets, E, ng);
   if (Mr > 0)
     hipLaunchKernelGGL(k_router_scatter, dim3(ng), dim3(64), 0, st, out->topk_ids, hist, out->sorted_pair,

@@ -17,23 +17,49 @@ namespace moe_tail {
 // experts.  Lane l of a wave accumulates p[l] = fma-chain over i of
 // x[64 i + l] * W[e, 64 i + l]; the 64 partials are then combined by an xor
 // butterfly (32, 16, 8, 4, 2, 1), which leaves the same value in every lane.
-// The x rows of the tile are staged in LDS (as fp32) one column chunk at a
-// time; the chain order over i is unchanged by the chunking.
+// The tile's x rows (bf16) are copied to LDS at once with direct loads; the
+// gate columns of the next kLogitChunk-column chunk are loaded while the
+// current one is used, so the loop waits for memory about once.
 constexpr int kLogitTok = 8;
 constexpr int kLogitExpPerWave = 2;
-constexpr int kLogitChunk = 1024;  // columns staged per pass
+constexpr int kLogitChunk = 1024;  // gate columns per prefetch
+// dynamic LDS: the x tile, kLogitTok x L bf16
 
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x_lat,
                                                        const float* __restrict__ gate,
                                                        const float* __restrict__ bias, float* __restrict__ logits,
                                                        int Mr, int L, int E) {
-  __shared__ float sx[kLogitTok][kLogitChunk];
+  extern __shared__ __attribute__((aligned(16))) uint16_t sx[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int t0 = blockIdx.x * kLogitTok;
   const int e0 = (blockIdx.y * 4 + wave) * kLogitExpPerWave;
+
+  // x rows t0 .. t0 + 7 as one linear byte array: 1 KB block j is loaded by
+  // wave j % 4, lane l copying bytes [16 (64 j + l), +16) (rows past Mr read
+  // as zeros)
+  {
+    const uint32_t row_bytes = static_cast<uint32_t>(L) * 2;
+    const int nrows = max(0, min(kLogitTok, Mr - t0));
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(x_lat + static_cast<size_t>(t0) * L, static_cast<uint32_t>(nrows) * row_bytes);
+    const int nblocks = (kLogitTok * L * 2) / 1024;  // L is a multiple of 256
+    for (int j = wv; j < nblocks; j += 4) dma16(r, reinterpret_cast<uint8_t*>(sx) + 1024 * j, 16u * (64 * j + lane), 0);
+  }
+
   const float* wp[kLogitExpPerWave];
 #pragma unroll
   for (int e = 0; e < kLogitExpPerWave; ++e) wp[e] = gate + static_cast<size_t>(min(e0 + e, E - 1)) * L + lane;
+  constexpr int kPer = kLogitChunk / 64;  // gate values per lane, expert and chunk
+  float wcur[kLogitExpPerWave][kPer], wnxt[kLogitExpPerWave][kPer];
+  auto load_w = [&](float (&w)[kLogitExpPerWave][kPer], int c0) {
+#pragma unroll
+    for (int e = 0; e < kLogitExpPerWave; ++e)
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) w[e][u] = (c0 + 64 * u < L) ? wp[e][c0 + 64 * u] : 0.0f;
+  };
+  load_w(wcur, 0);
+  ring_barrier<0>();  // the x tile is in LDS
 
   float acc[kLogitTok][kLogitExpPerWave];
 #pragma unroll
@@ -42,46 +68,22 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
     for (int e = 0; e < kLogitExpPerWave; ++e) acc[t][e] = 0.0f;
 
   for (int c0 = 0; c0 < L; c0 += kLogitChunk) {
-    const int cw = min(kLogitChunk, L - c0);  // multiple of 256
-    __syncthreads();
-    // kLogitTok rows x cw columns as 8-element groups: 4 per thread
+    if (c0 + kLogitChunk < L) load_w(wnxt, c0 + kLogitChunk);
 #pragma unroll
-    for (int q = 0; q < kLogitTok * kLogitChunk / 8 / 256; ++q) {
-      const int idx = tid + 256 * q;
-      const int t = idx / (kLogitChunk / 8), c = 8 * (idx % (kLogitChunk / 8));
-      const int tr = min(t0 + t, Mr - 1);
-      const int cc = min(c, cw - 8);
-      const uint4 v = *reinterpret_cast<const uint4*>(x_lat + static_cast<size_t>(tr) * L + c0 + cc);
-      if (c < cw) {
-        float* d = &sx[t][c];
-        d[0] = bf16_bits_to_f32(v.x & 0xffffu);
-        d[1] = bf16_bits_to_f32(v.x >> 16);
-        d[2] = bf16_bits_to_f32(v.y & 0xffffu);
-        d[3] = bf16_bits_to_f32(v.y >> 16);
-        d[4] = bf16_bits_to_f32(v.z & 0xffffu);
-        d[5] = bf16_bits_to_f32(v.z >> 16);
-        d[6] = bf16_bits_to_f32(v.w & 0xffffu);
-        d[7] = bf16_bits_to_f32(v.w >> 16);
-      }
-    }
-    __syncthreads();
-    // cw / 64 is a multiple of 4
-    for (int i0 = 0; i0 < cw / 64; i0 += 4) {
-      float wv[4][kLogitExpPerWave];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < kLogitExpPerWave; ++e) wv[u][e] = wp[e][c0 + 64 * (i0 + u)];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kPer; ++u) {
+      if (c0 + 64 * u < L) {
 #pragma unroll
         for (int t = 0; t < kLogitTok; ++t) {
-          const float xv = sx[t][64 * (i0 + u) + lane];
+          const float xv = bf16_bits_to_f32(sx[t * L + c0 + 64 * u + lane]);
 #pragma unroll
-          for (int e = 0; e < kLogitExpPerWave; ++e) acc[t][e] = __builtin_fmaf(xv, wv[u][e], acc[t][e]);
+          for (int e = 0; e < kLogitExpPerWave; ++e) acc[t][e] = __builtin_fmaf(xv, wcur[e][u], acc[t][e]);
         }
       }
     }
+#pragma unroll
+    for (int e = 0; e < kLogitExpPerWave; ++e)
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) wcur[e][u] = wnxt[e][u];
   }
 #pragma unroll
   for (int t = 0; t < kLogitTok; ++t)
@@ -106,12 +108,47 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 // One wave per token: k rounds of a wave-wide argmax with key (logit desc,
 // expert asc), then softmax over the k winners (sum in slot order).  Expert e
 // lives in lane e % 64, slot e / 64; a lane rescans its slots only after its
-// own best was taken.
+// own best was taken.  The argmax reduces within each 16-lane row with DPP
+// lane moves (xor 1, xor 2, mirror within 8, mirror within 16: ALU ops,
+// not LDS round trips) and then across the 4 rows through readlane.
 constexpr int kGroup = 64;              // tokens per permutation group (one mask bit each)
 constexpr int kMaxExpertsPerLane = 16;  // E <= 1024
+constexpr int kNoExpert = 0x7fffffff;
 
 __device__ __forceinline__ bool key_better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
+}
+
+// (value, index) of the better key of this lane and the lane kCtrl names
+template <int kCtrl>
+__device__ __forceinline__ void argmax_dpp(float& bv, int& bi) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(bv), __float_as_int(bv), kCtrl, 0xf, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(bi, bi, kCtrl, 0xf, 0xf, false);
+  if (oi != kNoExpert && (bi == kNoExpert || key_better(ov, oi, bv, bi))) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+// wave-wide best key; the result is the same in every lane
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  argmax_dpp<0xB1>(bv, bi);   // quad_perm(1, 0, 3, 2): lane ^ 1
+  argmax_dpp<0x4E>(bv, bi);   // quad_perm(2, 3, 0, 1): lane ^ 2
+  argmax_dpp<0x141>(bv, bi);  // row_half_mirror: quads 0 <-> 1 of each 8
+  argmax_dpp<0x140>(bv, bi);  // row_mirror: halves of each 16-lane row
+  float cv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+  int ci = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const float ov = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r));
+    const int oi = __builtin_amdgcn_readlane(bi, 16 * r);
+    if (oi != kNoExpert && (ci == kNoExpert || key_better(ov, oi, cv, ci))) {
+      cv = ov;
+      ci = oi;
+    }
+  }
+  bv = cv;
+  bi = ci;
 }
 
 __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int32_t* __restrict__ topk_ids,
@@ -130,11 +167,11 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
   uint32_t taken = 0;
   auto lane_best = [&](float& bv, int& bi) {
     bv = 0.0f;
-    bi = 0x7fffffff;
+    bi = kNoExpert;
 #pragma unroll
     for (int m = 0; m < kMaxExpertsPerLane; ++m) {
       const int e = lane + 64 * m;
-      if (m < per && e < E && !((taken >> m) & 1u) && (bi == 0x7fffffff || key_better(v[m], e, bv, bi))) {
+      if (m < per && e < E && !((taken >> m) & 1u) && (bi == kNoExpert || key_better(v[m], e, bv, bi))) {
         bv = v[m];
         bi = e;
       }
@@ -148,15 +185,7 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
   for (int j = 0; j < k; ++j) {
     float bv = lv;
     int bi = li;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (oi != 0x7fffffff && (bi == 0x7fffffff || key_better(ov, oi, bv, bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_argmax(bv, bi);
     if (j == 0) top_v = bv;
     if (lane == j) {
       my_v = bv;
@@ -252,6 +281,63 @@ __global__ __launch_bounds__(64) void k_router_scatter(const int32_t* __restrict
     const int p = t * k + j;
     const int e = topk_ids[p];
     const int row = base[static_cast<size_t>(e) * ngroups + g] + __popcll(s_mask[e] & below);
+    sorted_pair[row] = p;
+    pair_to_row[p] = row;
+  }
+}
+
+// ------------------------------------------------------- fused (small) --
+// The three steps above (group masks, exclusive scan over [expert][group],
+// scatter) in one workgroup of 1024 threads, for up to kSortSmall (group,
+// expert) cells; the same rows result.
+constexpr int kSortSmall = 4096;
+
+__global__ __launch_bounds__(1024) void k_router_sort(const int32_t* __restrict__ topk_ids,
+                                                      int32_t* __restrict__ expert_offsets,
+                                                      int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_to_row,
+                                                      int Mr, int E, int k, int ngroups) {
+  __shared__ unsigned long long s_mask[kSortSmall];  // [group][expert]
+  __shared__ int s_base[kSortSmall];                 // [expert][group]: first row
+  __shared__ int s_tot[1024];
+  const int tid = threadIdx.x;
+  const int n = E * ngroups;
+  for (int i = tid; i < n; i += 1024) s_mask[i] = 0ull;
+  __syncthreads();
+  const int npairs = Mr * k;
+  for (int p = tid; p < npairs; p += 1024) {
+    const int t = p / k;
+    atomicOr(&s_mask[(t / kGroup) * E + topk_ids[p]], 1ull << (t % kGroup));
+  }
+  __syncthreads();
+  // exclusive scan of the counts in [expert][group] order
+  const int chunk = (n + 1023) / 1024;
+  const int b = tid * chunk, end = min(b + chunk, n);
+  int sum = 0;
+  for (int i = b; i < end; ++i) {
+    const int e = i / ngroups, g = i - e * ngroups;
+    sum += __popcll(s_mask[g * E + e]);
+  }
+  s_tot[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int a = (tid >= off) ? s_tot[tid - off] : 0;
+    __syncthreads();
+    s_tot[tid] += a;
+    __syncthreads();
+  }
+  int run = (tid == 0) ? 0 : s_tot[tid - 1];
+  for (int i = b; i < end; ++i) {
+    const int e = i / ngroups, g = i - e * ngroups;
+    s_base[i] = run;
+    run += __popcll(s_mask[g * E + e]);
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += 1024) expert_offsets[e] = (e < E) ? (ngroups > 0 ? s_base[e * ngroups] : 0) : s_tot[1023];
+  for (int p = tid; p < npairs; p += 1024) {
+    const int t = p / k, g = t / kGroup, bit = t % kGroup;
+    const int e = topk_ids[p];
+    const unsigned long long below = (bit == 0) ? 0ull : (~0ull >> (64 - bit));
+    const int row = s_base[e * ngroups + g] + __popcll(s_mask[g * E + e] & below);
     sorted_pair[row] = p;
     pair_to_row[p] = row;
   }
