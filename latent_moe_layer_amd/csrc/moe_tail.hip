@@ -428,8 +428,9 @@ int moe_tail_route(const moe_tail_dims* dims, const moe_tail_weights* w, const u
     }
     hipLaunchKernelGGL(k_router_logits, dim3((Mr + kLogitTok - 1) / kLogitTok, egroups), dim3(256), xtile, st, x_lat,
                        w->gate, w->gate_bias, logits, Mr, L, E);
-    hipLaunchKernelGGL(k_router_topk, dim3((Mr + 3) / 4), dim3(256), 0, st, logits, out->topk_ids,
-                       out->topk_weights, Mr, E, k);
+    auto topk = (E <= 64) ? k_router_topk<1> : (E <= 128) ? k_router_topk<2> : (E <= 384) ? k_router_topk<6>
+                                                                                 : k_router_topk<kMaxExpertsPerLane>;
+    hipLaunchKernelGGL(topk, dim3((Mr + 3) / 4), dim3(256), 0, st, logits, out->topk_ids, out->topk_weights, Mr, E, k);
   }
   if (static_cast<int64_t>(ng) * E <= kSortSmall) {
     hipLaunchKernelGGL(k_router_sort, dim3(1), dim3(1024), 0, st, out->topk_ids, out->expert_offsets,

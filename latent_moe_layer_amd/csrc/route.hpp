@@ -20,7 +20,7 @@ namespace moe_tail {
 // The tile's x rows (bf16) are copied to LDS at once with direct loads; the
 // gate columns of the next kLogitChunk-column chunk are loaded while the
 // current one is used, so the loop waits for memory about once.
-constexpr int kLogitTok = 8;
+constexpr int kLogitTok = 4;
 constexpr int kLogitExpPerWave = 2;
 constexpr int kLogitChunk = 1024;  // gate columns per prefetch
 // dynamic LDS: the x tile, kLogitTok x L bf16
@@ -151,27 +151,27 @@ __device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
   bi = ci;
 }
 
+template <int kPer>  // experts per lane: ceil(E / 64) <= kPer
 __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int32_t* __restrict__ topk_ids,
                                                      float* __restrict__ topk_w, int Mr, int E, int k) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Mr) return;  // wave-uniform
-  const int per = (E + 63) / 64;
   const float* lr = logits + static_cast<size_t>(t) * E;
-  float v[kMaxExpertsPerLane];
+  float v[kPer];
 #pragma unroll
-  for (int m = 0; m < kMaxExpertsPerLane; ++m) {
+  for (int m = 0; m < kPer; ++m) {
     const int e = lane + 64 * m;
-    v[m] = (m < per && e < E) ? lr[e] : 0.0f;
+    v[m] = (e < E) ? lr[e] : 0.0f;
   }
   uint32_t taken = 0;
   auto lane_best = [&](float& bv, int& bi) {
     bv = 0.0f;
     bi = kNoExpert;
 #pragma unroll
-    for (int m = 0; m < kMaxExpertsPerLane; ++m) {
+    for (int m = 0; m < kPer; ++m) {
       const int e = lane + 64 * m;
-      if (m < per && e < E && !((taken >> m) & 1u) && (bi == kNoExpert || key_better(v[m], e, bv, bi))) {
+      if (e < E && !((taken >> m) & 1u) && (bi == kNoExpert || key_better(v[m], e, bv, bi))) {
         bv = v[m];
         bi = e;
       }
