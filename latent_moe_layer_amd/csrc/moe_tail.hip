@@ -180,14 +180,14 @@ unsigned num_cus() {
   return cache[dev];
 }
 
-template <int KIND, int FMT, int EPI>
+template <int KIND, int FMT, int EPI, int TM = kTM>
 void launch_tile(const TileArgs& a, hipStream_t st) {
   const unsigned T = static_cast<unsigned>(a.nslots) * static_cast<unsigned>(a.ntn);
   if (T == 0) return;
   // persistent: one workgroup per CU (the kernel's LDS allows no second),
   // whole rounds of 8 so that every XCD gets the same number
   const unsigned wg = std::min((T + 7) / 8 * 8, std::max(8u, num_cus() / 8 * 8));
-  hipLaunchKernelGGL((k_tile<KIND, FMT, EPI>), dim3(wg), dim3(512), 0, st, a);
+  hipLaunchKernelGGL((k_tile<KIND, FMT, EPI, TM>), dim3(wg), dim3(512), 0, st, a);
 }
 
 template <int kEpi>
@@ -264,14 +264,14 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
     hipLaunchKernelGGL(k_quant_1x128<true>, dim3(static_cast<unsigned>((blocks + 3) / 4)), dim3(256), 0, st, x_lat,
                        xq, sx, Mr, L);
   }
-  // 1, 2: routed L1 and L2.  Experts with at least kBigMinRows rows go to the
-  // LDS-tiled kernel when the batch is large enough for any to be likely; the
-  // rest (and everything at decode sizes) to the row-streaming kernel.
-  // (the tiled kernel addresses the gathered x rows with 32-bit offsets)
-  // (it keeps the expert tables in LDS and needs two K steps per tile)
-  const bool use_big = R >= static_cast<size_t>(kBigMinRows) * 16 && static_cast<size_t>(Mr) * L < (1ull << 31) &&
-                       E <= kTileMaxE && L >= 256 && I >= 256;
-  const int skip_at = use_big ? kBigMinRows : 0x7fffffff;
+  // 1, 2: routed L1 and L2 on the persistent LDS-tiled kernel: 128-row tiles
+  // for experts with at least kBigMinRows rows (only possible once Mr >=
+  // kBigMinRows), 32-row tiles for the others.  It keeps the expert tables in
+  // LDS (E <= kTileMaxE), addresses the gathered x rows with 32-bit offsets
+  // and loads a tile's side data kStages - 1 >= 3 steps ahead (K >= 384).
+  // Shapes outside that take the row-streaming kernel for every expert.
+  const bool tiled = E <= kTileMaxE && static_cast<size_t>(Mr) * L < (1ull << 31) && L >= 384 && I >= 384;
+  const bool big = tiled && Mr >= kBigMinRows;
   const unsigned max_tiles = static_cast<unsigned>((R + kBM - 1) / kBM + E);
   const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
   TileArgs ta{};
@@ -279,18 +279,22 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   ta.expert_offsets = routing ? routing->expert_offsets : nullptr;
   ta.E = E;
   ta.k = k;
-  ta.nslots = static_cast<int>(R / (kTM / 2));  // bound on the row tiles (ceil(c/128) <= c/64 for c >= 128): sizes the grid
+  // bounds on the row tiles, which size the grids: ceil(c / 128) <= c / 64
+  // for c >= 128, and ceil(c / 32) <= c / 32 + 1
+  const int slots_big = static_cast<int>(R / (kTM / 2));
+  const int slots_small = static_cast<int>(R / 32 + E);
   mark(1);
   if (Mr > 0) {
-    if (fp8)
-      hipLaunchKernelGGL(k_routed_l1<FMT_FP8>, dim3(max_tiles, I / 128), dim3(256), 0, st, xq, sx,
-                         routing->sorted_pair, routing->expert_offsets, w->w1, w->w1_scale, hq, sh, E, k, L, I,
-                         skip_at);
-    else
-      hipLaunchKernelGGL(k_routed_l1<FMT_MXFP4>, dim3(max_tiles, I / 128), dim3(256), 0, st, xq, sx,
-                         routing->sorted_pair, routing->expert_offsets, w->w1, w->w1_scale, hq, sh, E, k, L, I,
-                         skip_at);
-    if (use_big) {
+    if (!tiled) {
+      if (fp8)
+        hipLaunchKernelGGL(k_routed_l1<FMT_FP8>, dim3(max_tiles, I / 128), dim3(256), 0, st, xq, sx,
+                           routing->sorted_pair, routing->expert_offsets, w->w1, w->w1_scale, hq, sh, E, k, L, I,
+                           0x7fffffff);
+      else
+        hipLaunchKernelGGL(k_routed_l1<FMT_MXFP4>, dim3(max_tiles, I / 128), dim3(256), 0, st, xq, sx,
+                           routing->sorted_pair, routing->expert_offsets, w->w1, w->w1_scale, hq, sh, E, k, L, I,
+                           0x7fffffff);
+    } else {
       TileArgs a1 = ta;
       a1.a = xq;
       a1.a_scale = sx;
@@ -303,19 +307,26 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       a1.N = 2 * I;
       a1.half = I;
       a1.ntn = I / 128;
-      if (fp8) launch_tile<TK_L1, TF_FP8, 0>(a1, st);
-      else launch_tile<TK_L1, TF_FP4, 0>(a1, st);
+      a1.nslots = slots_small;
+      if (fp8) launch_tile<TK_L1, TF_FP8, 0, 32>(a1, st);
+      else launch_tile<TK_L1, TF_FP4, 0, 32>(a1, st);
+      if (big) {
+        a1.nslots = slots_big;
+        if (fp8) launch_tile<TK_L1, TF_FP8, 0>(a1, st);
+        else launch_tile<TK_L1, TF_FP4, 0>(a1, st);
+      }
     }
   }
   mark(2);
   if (Mr > 0) {
-    if (fp8)
-      hipLaunchKernelGGL(k_routed_l2<FMT_FP8>, dim3(max_tiles, L / 128), dim3(256), 0, st, hq, sh,
-                         routing->expert_offsets, w->w2, w->w2_scale, y, E, L, I, skip_at);
-    else
-      hipLaunchKernelGGL(k_routed_l2<FMT_MXFP4>, dim3(max_tiles, L / 128), dim3(256), 0, st, hq, sh,
-                         routing->expert_offsets, w->w2, w->w2_scale, y, E, L, I, skip_at);
-    if (use_big) {
+    if (!tiled) {
+      if (fp8)
+        hipLaunchKernelGGL(k_routed_l2<FMT_FP8>, dim3(max_tiles, L / 128), dim3(256), 0, st, hq, sh,
+                           routing->expert_offsets, w->w2, w->w2_scale, y, E, L, I, 0x7fffffff);
+      else
+        hipLaunchKernelGGL(k_routed_l2<FMT_MXFP4>, dim3(max_tiles, L / 128), dim3(256), 0, st, hq, sh,
+                           routing->expert_offsets, w->w2, w->w2_scale, y, E, L, I, 0x7fffffff);
+    } else {
       TileArgs a2 = ta;
       a2.a = hq;
       a2.a_scale = sh;
@@ -326,8 +337,14 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       a2.N = L;
       a2.half = 0;
       a2.ntn = L / kTN;
-      if (fp8) launch_tile<TK_L2, TF_FP8, 0>(a2, st);
-      else launch_tile<TK_L2, TF_FP4, 0>(a2, st);
+      a2.nslots = slots_small;
+      if (fp8) launch_tile<TK_L2, TF_FP8, 0, 32>(a2, st);
+      else launch_tile<TK_L2, TF_FP4, 0, 32>(a2, st);
+      if (big) {
+        a2.nslots = slots_big;
+        if (fp8) launch_tile<TK_L2, TF_FP8, 0>(a2, st);
+        else launch_tile<TK_L2, TF_FP4, 0>(a2, st);
+      }
     }
   }
   // 3: combine + RMSNorm

@@ -63,31 +63,44 @@ struct TileArgs {
 // weights, in that XCD's L2).  The K steps of all of a workgroup's tiles form
 // one stream through the three-stage ring: the first stages of the next tile
 // are loaded while the current one finishes and while its epilogue runs.
-template <int KIND, int FMT, int EPI>
+// TM = 128: tiles of 128 rows (experts with at least kBigMinRows rows, and
+// the dense GEMMs), 8 waves as 2 (M) x 4 (N) of 64 x 64.  TM = 32: tiles of
+// 32 rows for the experts with fewer rows (decode sizes), 8 waves of 32 x 32,
+// a deeper ring.  Either way 256 B rows (weight rows) per tile.
+template <int KIND, int FMT, int EPI, int TM = kTM>
 __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   constexpr bool kFP4 = FMT == TF_FP4;
   constexpr bool kBF16 = FMT == TF_BF16;
   constexpr bool kScaled = !kBF16;
   constexpr bool kRouted = KIND != TK_DENSE;
   constexpr bool kPaired = KIND == TK_L1 || (KIND == TK_DENSE && EPI == EPI_SWIGLU);
-  constexpr int kABytes = kTM * 128;                 // 16 KB
+  static_assert(TM == 128 || (TM == 32 && KIND != TK_DENSE), "tile rows");
+  constexpr int kWavesM = (TM == 128) ? 2 : 1;       // wave grid over the tile
+  constexpr int kWavesN = 8 / kWavesM;
+  constexpr int kMT = TM / (16 * kWavesM);           // 16-row MFMA tiles per wave
+  constexpr int kNJ = kTN / (16 * kWavesN);          // 16-column MFMA tiles per wave
+  constexpr int kStages = (TM == 128) ? 3 : 4;       // ring depth (kStages - 1 steps in flight)
+  constexpr int kABlk = TM / 8;                      // 1 KB blocks of A per stage
+  constexpr int kAL = (kABlk + 7) / 8;               // A blocks loaded per wave
+  constexpr int kABytes = TM * 128;                  // 16 or 4 KB
   constexpr int kBBytes = kTN * (kFP4 ? 64 : 128);   // 16 or 32 KB
   constexpr int kSOff = kABytes + kBBytes;           // scale words: activation [0, 512), FP4 e8m0 [512, 1536)
   constexpr int kStage = kSOff + (kScaled ? 2048 : 0);
   constexpr int kBChunks = kFP4 ? 2 : 4;             // 16-byte B loads per thread and stage
-  constexpr int kLoads = 2 + kBChunks + (kScaled ? 1 : 0);  // direct loads per wave and stage
+  constexpr int kLoads = kAL + kBChunks + (kScaled ? 1 : 0);  // direct loads per wave and stage
   constexpr uint32_t kNoRow = 0x80000000u;           // offset past any buffer: reads zeros
-  __shared__ __attribute__((aligned(16))) uint8_t ring[3 * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStage];
   __shared__ int s_eoff[kRouted ? kTileMaxE + 1 : 1];  // expert row offsets
   __shared__ int s_pre[kRouted ? kTileMaxE + 1 : 1];   // row tiles of the experts before e
   // per-tile data, buffer j % 3 for tile j: loaded while tile j - 2 still
   // computes and read until tile j's last step
-  __shared__ int s_pair[3][kTM];                       // L1: sorted pair ids of a tile's rows
+  constexpr int kPairRows = (TM < 64) ? 64 : TM;       // one 64-lane load per 64 rows
+  __shared__ int s_pair[3][kPairRows];                 // L1: sorted pair ids of a tile's rows
   __shared__ float s_wsc[3][2][kMaxKBlocks];           // FP8: weight scales of a tile's two 128-row B halves
-  __shared__ float s_amax[4][kTM];
+  __shared__ float s_amax[kWavesN][TM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int l16 = lane & 15, g = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int nk = kBF16 ? p.K / 64 : p.K / 128;    // K steps of 128 bytes (at least 2)
@@ -104,13 +117,14 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
     for (int i = tid; i <= p.E; i += 512) s_eoff[i] = p.expert_offsets[i];
     __syncthreads();
     if (wave == 0) {
-      // exclusive prefix over the experts of their row tiles (experts with
-      // fewer than kBigMinRows rows have none: the row-streaming kernel takes them)
+      // exclusive prefix over the experts of their row tiles (TM = 128: the
+      // experts with at least kBigMinRows rows; TM = 32: the others)
       const int per = (p.E + 63) / 64;
       const int eb = min(lane * per, p.E), ee = min(eb + per, p.E);
       auto ntile = [&](int e) {
         const int c = s_eoff[e + 1] - s_eoff[e];
-        return c >= kBigMinRows ? (c + kTM - 1) / kTM : 0;
+        if (TM == 128) return c >= kBigMinRows ? (c + TM - 1) / TM : 0;
+        return c < kBigMinRows ? (c + TM - 1) / TM : 0;
       };
       int local = 0;
       for (int e = eb; e < ee; ++e) local += ntile(e);
@@ -154,12 +168,12 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
         else b = m;
       }
       d.e = a;
-      d.row0 = s_eoff[a] + (slot - s_pre[a]) * kTM;
-      d.rows = min(kTM, s_eoff[a + 1] - d.row0);
+      d.row0 = s_eoff[a] + (slot - s_pre[a]) * TM;
+      d.rows = min(TM, s_eoff[a + 1] - d.row0);
     } else {
       d.e = 0;
-      d.row0 = slot * kTM;
-      d.rows = min(kTM, p.M - d.row0);
+      d.row0 = slot * TM;
+      d.rows = min(TM, p.M - d.row0);
     }
     d.e = __builtin_amdgcn_readfirstlane(d.e);
     d.row0 = __builtin_amdgcn_readfirstlane(d.row0);
@@ -186,7 +200,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   // l % 16, chunk l / 16.
   const int q8 = lane >> 3;                             // row within a block
   const int st_c = (lane & 7) ^ q8;                     // chunk this lane fetches
-  const int st_r0 = 8 * wave + q8;                      // rows st_r0 + 64 i
+  const int st_r0 = 8 * wave + q8;                      // B rows st_r0 + 64 i
   const int t_r = tid & 15, t_g = (tid >> 4) & 3;       // FP4 B
   // a resource with no valid bytes: loads through it write zeros
   const __amdgpu_buffer_rsrc_t z_rsrc = make_rsrc(p.b, 0u);
@@ -194,7 +208,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   // load offsets of one tile
   struct Iss {
     __amdgpu_buffer_rsrc_t ra, rb, rs;
-    uint32_t a_off[2], b_off[kBChunks], s_off;
+    uint32_t a_off[kAL], b_off[kBChunks], s_off;
   };
   auto make_iss = [&](const Desc& d, int buf) -> Iss {
     Iss r;
@@ -202,9 +216,11 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
       r.ra = make_rsrc(p.a, static_cast<uint32_t>(static_cast<size_t>(p.M) * a_row_bytes));
     else
       r.ra = make_rsrc(p.a + static_cast<size_t>(d.row0) * a_row_bytes, static_cast<uint32_t>(static_cast<size_t>(d.rows) * a_row_bytes));
+    // A block (wave + 8 i) % kABlk (TM = 32: waves 4-7 load the same blocks as
+    // waves 0-3, the same bytes to the same place)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = st_r0 + 64 * i;
+    for (int i = 0; i < kAL; ++i) {
+      const int row = 8 * ((wave + 8 * i) % kABlk) + q8;
       uint32_t o = kNoRow;
       if (row < d.rows) {
         const size_t rr = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
@@ -225,7 +241,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
     r.rs = z_rsrc;
     r.s_off = kNoRow;
     if (kScaled) {
-      if (wv < 2) {
+      if (wv < (TM + 63) / 64) {
         const int row = 64 * wv + lane;
         const float* sbase = (KIND == TK_L1) ? p.a_scale : p.a_scale + static_cast<size_t>(d.row0) * nkb;
         const size_t srows = (KIND == TK_L1) ? static_cast<size_t>(p.M) : static_cast<size_t>(d.rows);
@@ -234,7 +250,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
           const size_t ar = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
           r.s_off = static_cast<uint32_t>(ar * nkb * 4);
         }
-      } else if (kFP4 && wv < 6) {
+      } else if (kFP4 && wv >= 2 && wv < 6) {
         const int j = 64 * (wv - 2) + lane;
         r.rs = make_rsrc(static_cast<const uint8_t*>(p.b_scale) + static_cast<size_t>(d.e) * nbrows * wpr,
                          static_cast<uint32_t>(nbrows * wpr));
@@ -246,17 +262,17 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   // stage k of a tile -> ring slot; live == false loads zeros (no memory traffic)
   auto issue = [&](uint8_t* st, const Iss& r, int k, bool live) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(live ? r.ra : z_rsrc, st + 8192 * i + 1024 * wv, r.a_off[i], k * 128);
+    for (int i = 0; i < kAL; ++i) dma16(live ? r.ra : z_rsrc, st + 1024 * ((wv + 8 * i) % kABlk), r.a_off[i], k * 128);
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i)
       dma16(live ? r.rb : z_rsrc, st + kABytes + 8192 * i + 1024 * wv, r.b_off[i], kFP4 ? k * 64 : k * 128);
     if (kScaled) dma4(live ? r.rs : z_rsrc, st + kSOff + 256 * wv, r.s_off, 4 * k);
   };
   // per-tile data loaded ahead (issued first in a stage's batch, only by the
-  // waves that carry it): L1 sorted pair ids (waves 0-1), FP8 weight-scale
+  // waves that carry it): L1 sorted pair ids (one wave per 64 rows), FP8 weight-scale
   // rows (waves 2-3)
   auto aux = [&](const Desc& d, int buf) {
-    if (KIND == TK_L1 && wv < 2) {
+    if (KIND == TK_L1 && wv < kPairRows / 64) {
       dma4(make_rsrc(p.sorted_pair + d.row0, static_cast<uint32_t>(d.rows) * 4u), reinterpret_cast<uint8_t*>(&s_pair[buf][64 * wv]),
            4u * (64 * wv + lane), 0);
     } else if (FMT == TF_FP8 && (wv == 2 || wv == 3)) {
@@ -272,8 +288,8 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   // B blocks of this wave, j = 0..3 (paired: two gate blocks, then the two
   // matching up blocks)
   auto bblk = [&](int j) {
-    if (kPaired) return (j < 2) ? 2 * wn + j : 8 + 2 * wn + (j - 2);
-    return 4 * wn + j;
+    if (kPaired) return (j < kNJ / 2) ? (kNJ / 2) * wn + j : 8 + (kNJ / 2) * wn + (j - kNJ / 2);
+    return kNJ * wn + j;
   };
   // this lane's MFMA operand pieces within a 16-row block (2 KB): row l16,
   // chunk g (registers 0-3) and chunk 4 + g (registers 4-7)
@@ -281,30 +297,30 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   const int f_lo = fr + 16 * (g ^ (l16 & 7));
   const int f_hi = fr + 16 * ((4 | g) ^ (l16 & 7));
 
-  f32x4 acc[4][4];
+  f32x4 acc[kMT][kNJ];
   auto compute = [&](const uint8_t* st, int ks, int buf) {
     // weight scales of this step (FP8): the wave's B rows lie in the tile's
     // row half 16 * bblk(0) / 128 (paired: its gate rows) and 16 * bblk(3) / 128
     float sw_lo = 1.0f, sw_hi = 1.0f;
     if (FMT == TF_FP8) {
       sw_lo = s_wsc[buf][(16 * bblk(0)) / 128][ks];
-      sw_hi = s_wsc[buf][(16 * bblk(3)) / 128][ks];
+      sw_hi = s_wsc[buf][(16 * bblk(kNJ - 1)) / 128][ks];
     }
-    i32x8 af[4];
+    i32x8 af[kMT];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const uint8_t* ab = st + (4 * wm + mt) * 2048;
+    for (int mt = 0; mt < kMT; ++mt) {
+      const uint8_t* ab = st + (kMT * wm + mt) * 2048;
       const i32x4 lo4 = *reinterpret_cast<const i32x4*>(ab + f_lo);
       const i32x4 hi4 = *reinterpret_cast<const i32x4*>(ab + f_hi);
       af[mt] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     }
     // per-row promotion factors of this step: activation scale x weight scale
-    float sc[2][4][4];
+    float sc[2][kMT][4];
     if (kScaled) {
       const float* ss = reinterpret_cast<const float*>(st + kSOff);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(ss + 64 * wm + 16 * mt + 4 * g);
+      for (int mt = 0; mt < kMT; ++mt) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ss + 16 * kMT * wm + 16 * mt + 4 * g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sc[0][mt][i] = v[i] * sw_lo;
@@ -313,14 +329,14 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kNJ; ++j) {
       const int bb = bblk(j);
       if (kBF16) {
         const uint8_t* bp = st + kABytes + bb * 2048;
         const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_lo));
         const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_hi));
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < kMT; ++mt) {
           const i32x4 alo = __builtin_shufflevector(af[mt], af[mt], 0, 1, 2, 3);
           const i32x4 ahi = __builtin_shufflevector(af[mt], af[mt], 4, 5, 6, 7);
           acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, alo), b0, acc[mt][j]);
@@ -340,9 +356,9 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
           const i32x4 hi4 = *reinterpret_cast<const i32x4*>(bp + f_hi);
           bf = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        const int half_sel = (kPaired && j >= 2) ? 1 : 0;
+        const int half_sel = (kPaired && j >= kNJ / 2) ? 1 : 0;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mt = 0; mt < kMT; ++mt) {
           const f32x4 pr = kFP4 ? mfma_fp8_fp4(af[mt], bf, sb) : mfma_fp8(af[mt], bf);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mt][j][i] += pr[i] * sc[half_sel][mt][i];
@@ -352,40 +368,46 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   };
 
   // ---------------------------------------------------------------- epilogues
+  // Wave (wm, wn) holds rows 16 kMT wm + 16 mt + 4 g + i and, of the tile's
+  // 256 B rows, its kNJ 16-row blocks bblk(j).
   auto epilogue = [&](const Desc& d, uint8_t* sq) {
     if (KIND == TK_L1) {
-      // h = silu(gate) * up for this wave's 64 rows x 32 h columns; row amax
-      // over the tile's 128 h columns
-      float h[4][2][4];
+      // h = silu(gate) * up: the wave's kH 16-column blocks of h; row amax
+      // over the tile's 128 h columns (all kWavesN waves of the row)
+      constexpr int kH = kNJ / 2;
+      float h[kMT][kH][4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float m = 0.0f;
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            h[mt][j][i] = silu_mul_fast(acc[mt][j][i], acc[mt][2 + j][i]);
+          for (int j = 0; j < kH; ++j) {
+            h[mt][j][i] = silu_mul_fast(acc[mt][j][i], acc[mt][kH + j][i]);
             m = fmaxf(m, fabsf(h[mt][j][i]));
           }
           m = group16_max(m);
-          if (l16 == 0) s_amax[wn][64 * wm + 16 * mt + 4 * g + i] = m;
+          if (l16 == 0) s_amax[wn][16 * kMT * wm + 16 * mt + 4 * g + i] = m;
         }
       lds_barrier();  // s_amax complete; every wave is done with the stage in sq
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 64 * wm + 16 * mt + 4 * g + i;
-          const float amax = fmaxf(fmaxf(s_amax[0][r], s_amax[1][r]), fmaxf(s_amax[2][r], s_amax[3][r]));
+          const int r = 16 * kMT * wm + 16 * mt + 4 * g + i;
+          float amax = s_amax[0][r];
+#pragma unroll
+          for (int w = 1; w < kWavesN; ++w) amax = fmaxf(amax, s_amax[w][r]);
           const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
           const float inv = 1.0f / s;
 #pragma unroll
-          for (int j = 0; j < 2; ++j) sq[r * 128 + 32 * wn + 16 * j + l16] = static_cast<uint8_t>(f32_to_e4m3(h[mt][j][i] * inv));
+          for (int j = 0; j < kH; ++j)
+            sq[r * 128 + 16 * (kH * wn + j) + l16] = static_cast<uint8_t>(f32_to_e4m3(h[mt][j][i] * inv));
           if (wn == 0 && l16 == 0 && r < d.rows) p.sh[static_cast<size_t>(d.row0 + r) * (p.half / 128) + d.nt] = s;
         }
       lds_barrier();
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < (TM * 8 + 511) / 512; ++i) {
         const int q = tid + 512 * i;
         const int r = q >> 3, c16 = (q & 7) * 16;
         if (r < d.rows)
@@ -394,32 +416,32 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
       }
     } else if (KIND == TK_L2) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 64 * wm + 16 * mt + 4 * g + i;
+          const int r = 16 * kMT * wm + 16 * mt + 4 * g + i;
           if (r < d.rows) {
-            float* yr = p.y + static_cast<size_t>(d.row0 + r) * p.N + kTN * d.nt + 64 * wn + l16;
+            float* yr = p.y + static_cast<size_t>(d.row0 + r) * p.N + kTN * d.nt + 16 * kNJ * wn + l16;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) yr[16 * j] = acc[mt][j][i];
+            for (int j = 0; j < kNJ; ++j) yr[16 * j] = acc[mt][j][i];
           }
         }
     } else {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 64 * wm + 16 * mt + 4 * g + i;
+          const int r = 16 * kMT * wm + 16 * mt + 4 * g + i;
           if (r < d.rows) {
             if (EPI == EPI_SWIGLU) {
 #pragma unroll
-              for (int j = 0; j < 2; ++j)
-                dense_epilogue<EPI>(p.ep, p.N, d.row0 + r, 128 * d.nt + 32 * wn + 16 * j + l16, acc[mt][j][i],
-                                    acc[mt][2 + j][i]);
+              for (int j = 0; j < kNJ / 2; ++j)
+                dense_epilogue<EPI>(p.ep, p.N, d.row0 + r, 128 * d.nt + 16 * ((kNJ / 2) * wn + j) + l16, acc[mt][j][i],
+                                    acc[mt][kNJ / 2 + j][i]);
             } else {
 #pragma unroll
-              for (int j = 0; j < 4; ++j)
-                dense_epilogue<EPI>(p.ep, p.N, d.row0 + r, kTN * d.nt + 64 * wn + 16 * j + l16, acc[mt][j][i], 0.0f);
+              for (int j = 0; j < kNJ; ++j)
+                dense_epilogue<EPI>(p.ep, p.N, d.row0 + r, kTN * d.nt + 16 * kNJ * wn + 16 * j + l16, acc[mt][j][i], 0.0f);
             }
           }
         }
@@ -428,7 +450,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
 
   // ---- prologue: tile 0's pair ids and weight scales with ordinary loads
   Desc dc = desc(0);
-  if (KIND == TK_L1 && tid < kTM) s_pair[0][tid] = (tid < dc.rows) ? p.sorted_pair[dc.row0 + tid] : 0;
+  if (KIND == TK_L1 && tid < TM) s_pair[0][tid] = (tid < dc.rows) ? p.sorted_pair[dc.row0 + tid] : 0;
   if (FMT == TF_FP8 && tid < 2 * nkb) {
     const int q = tid / nkb, kb = tid - q * nkb;
     const int wr = wrow(dc.nt, 128 * q);
@@ -438,19 +460,20 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   __syncthreads();
 
   // Stage G of the stream is K step G % nk of tile G / nk and sits in ring
-  // slot G % 3.  Step G: wait for stage G (every wave's loads), start stage
-  // G + 2 into the slot that stage G - 1 (read by every wave before the
-  // barrier) leaves free, compute stage G; after a tile's last step its
-  // epilogue stages the h codes through that step's slot, which the next
-  // step's loads only reuse after their barrier.  A tile's pair ids and
-  // weight scales are loaded with the first stage of the tile before it,
-  // nk >= 2 steps ahead of their first use.
+  // slot G % kStages.  Step G: wait for stage G (every wave's loads), start
+  // stage G + kStages - 1 into the slot that stage G - 1 (read by every wave
+  // before the barrier) leaves free, compute stage G; after a tile's last
+  // step its epilogue stages the h codes through that step's slot, which
+  // the next step's loads only reuse after their barrier.  A tile's pair ids
+  // and weight scales are loaded with the first stage of the tile before it;
+  // with nk >= kStages - 1 (the launcher's condition) they have landed before
+  // their first use and the buffer j % 3 they go to is no longer read.
   Iss is = make_iss(dc, 0);
   int ji = 0;  // tile of `is`
   const int G = n_my * nk;
   auto issue_stage = [&](int g2) {
     const int j2 = g2 / nk, k2 = g2 - j2 * nk;
-    uint8_t* st = ring + (g2 % 3) * kStage;
+    uint8_t* st = ring + (g2 % kStages) * kStage;
     if (j2 >= n_my) {
       issue(st, is, 0, false);
       return;
@@ -462,20 +485,20 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
     if (k2 == 0 && j2 + 1 < n_my) aux(desc(j2 + 1), (j2 + 1) % 3);
     issue(st, is, k2, true);
   };
-  issue_stage(0);
-  issue_stage(1);
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) issue_stage(s);
   for (int gg = 0; gg < G; ++gg) {
     const int j = gg / nk, ks = gg - j * nk;
-    ring_barrier<kLoads>();
-    issue_stage(gg + 2);
+    ring_barrier<kLoads * (kStages - 2)>();
+    issue_stage(gg + kStages - 1);
     if (ks == 0) {
       if (j > 0) dc = desc(j);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[mt][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int jj = 0; jj < kNJ; ++jj) acc[mt][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    uint8_t* st = ring + (gg % 3) * kStage;
+    uint8_t* st = ring + (gg % kStages) * kStage;
     compute(st, ks, j % 3);
     if (ks == nk - 1) epilogue(dc, st);
   }
