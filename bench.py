@@ -7,7 +7,7 @@ add) over one batch of seeded synthetic input already resident in HBM.
 
 Prints ONE JSON line.  `value` is the whole tail's achieved HBM throughput
 (algorithmic bytes / time per layer); `us_per_layer` is the step time.  The
-`roofline` object covers the dominant kernel (routed L1), timed with HIP events
+`roofline` object covers the dominant kernel (the routed L1 launch), timed with HIP events
 recorded on the stream it runs on.  `cpu_baseline` times the CPU oracle on the
 same inputs (rank 0, N = 1 only).
 """
@@ -25,6 +25,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "latent-MoE tail µs/layer + achieved HBM GB/s (M<=128) / MFMA TFLOP/s (M>=1024)"
 HBM_PEAK_GBS = 8000.0
+# HBM bytes per launch of the routed L1 kernel from FETCH_SIZE and WRITE_SIZE
+# counter runs, scaled by the same counters' reading of a copy kernel of known
+# size (profiles/decode_routed_traffic.md); taken on the current kernels.
+MEASURED_L1_TRAFFIC = {"decode": 945.8e6}
 FP8_PEAK_TFLOPS = 5000.0
 MXFP4_PEAK_TFLOPS = 10100.0
 STAGES = ["quant_x", "routed_l1", "routed_l2", "combine_rmsnorm", "shared_l1", "shared_l2", "up_proj_add"]
@@ -153,8 +157,11 @@ def main() -> int:
         peak = FP8_PEAK_TFLOPS if wl.wfmt == 0 else MXFP4_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": l1_flops / (l1_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = "k_routed_l1"
+    roof["traffic"] = MEASURED_L1_TRAFFIC.get(wl.name)
+    # the routed L1 stage: the persistent tiled kernel with 32-row tiles
+    # (experts under 128 rows) and, once Mr >= 128, with 128-row tiles
+    roof["kernel"] = ("k_tile<TK_L1, %s, 0, 32>" % ("TF_FP8" if wl.wfmt == 0 else "TF_FP4")) + \
+        ("" if wl.Mr < 128 else " + k_tile<TK_L1, %s, 0, 128>" % ("TF_FP8" if wl.wfmt == 0 else "TF_FP4"))
     roof["algorithmic_bytes_per_launch"] = l1_bytes
     roof["avg_launch_us"] = l1_ms * 1e3
 
