@@ -265,13 +265,16 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
                        xq, sx, Mr, L);
   }
   // 1, 2: routed L1 and L2 on the persistent LDS-tiled kernel: 128-row tiles
-  // for experts with at least kBigMinRows rows (only possible once Mr >=
-  // kBigMinRows), 32-row tiles for the others.  It keeps the expert tables in
-  // LDS (E <= kTileMaxE), addresses the gathered x rows with 32-bit offsets
-  // and loads a tile's side data kStages - 1 >= 3 steps ahead (K >= 384).
-  // Shapes outside that take the row-streaming kernel for every expert.
+  // for experts with at least kBigMinRows rows, 32-row tiles for the others;
+  // up to kSmallOnlyMr tokens every expert takes 32-row tiles (an expert
+  // reaching 128 rows is then rare, and it saves the second launch).  The
+  // kernel keeps the expert tables in LDS (E <= kTileMaxE), addresses the
+  // gathered x rows with 32-bit offsets and loads a tile's side data
+  // kStages - 1 >= 3 steps ahead (K >= 384).  Shapes outside that take the
+  // row-streaming kernel for every expert.
   const bool tiled = E <= kTileMaxE && static_cast<size_t>(Mr) * L < (1ull << 31) && L >= 384 && I >= 384;
-  const bool big = tiled && Mr >= kBigMinRows;
+  constexpr int kSmallOnlyMr = 256;
+  const bool big = tiled && Mr > kSmallOnlyMr;
   const unsigned max_tiles = static_cast<unsigned>((R + kBM - 1) / kBM + E);
   const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
   TileArgs ta{};
@@ -279,6 +282,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   ta.expert_offsets = routing ? routing->expert_offsets : nullptr;
   ta.E = E;
   ta.k = k;
+  ta.big_rows = big ? kBigMinRows : 0x7fffffff;
   // bounds on the row tiles, which size the grids: ceil(c / 128) <= c / 64
   // for c >= 128, and ceil(c / 32) <= c / 32 + 1
   const int slots_big = static_cast<int>(R / (kTM / 2));
@@ -350,8 +354,8 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   // 3: combine + RMSNorm
   mark(3);
   if (Mr > 0) {
-    const int nc = L / 256;
-    auto kern = (nc == 14) ? k_combine_rmsnorm<14> : (nc <= 16) ? k_combine_rmsnorm<16> : k_combine_rmsnorm<32>;
+    const int nc4 = (L / 4 + 255) / 256;  // 4-column groups per thread
+    auto kern = (nc4 <= 2) ? k_combine_rmsnorm<2> : (nc4 <= 4) ? k_combine_rmsnorm<4> : k_combine_rmsnorm<8>;
     hipLaunchKernelGGL(kern, dim3(Mr), dim3(256), 0, st, y, routing->topk_weights, routing->pair_to_row,
                        w->rms_gamma, rn, L, k, d.rms_eps);
   }

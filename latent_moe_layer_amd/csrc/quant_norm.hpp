@@ -44,9 +44,11 @@ __global__ __launch_bounds__(256) void k_quant_1x128(const void* __restrict__ x,
 // the bias study in tokenspeed PR 1062.
 constexpr int kNormMaxCols = 32;  // L <= 256 * 32
 
-// NC = columns per thread (L / 256, or an upper bound of it: extra columns are
-// clamped and unused).
-template <int NC>
+// One workgroup per token; thread tid owns the 4-column groups tid + 256 c
+// (NC4 = an upper bound of L / 1024: groups past L are clamped, loaded and
+// unused).  The rows' 16-byte loads are issued in batches before any is
+// used; each column still sums its k slots in slot order.
+template <int NC4>
 __global__ __launch_bounds__(256) void k_combine_rmsnorm(const float* __restrict__ y, const float* __restrict__ topk_w,
                                                          const int32_t* __restrict__ pair_to_row,
                                                          const uint16_t* __restrict__ gamma,
@@ -54,49 +56,63 @@ __global__ __launch_bounds__(256) void k_combine_rmsnorm(const float* __restrict
   __shared__ float s_part[4];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  float z[NC];
-  const int nc = L / 256;
+  const int ng = L / 4;  // 4-column groups
+  int grp[NC4];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) z[c] = 0.0f;
-  // row pointers and weights of the k slots first, so the y loads issue
-  // together (columns past L are clamped, loaded and never used)
-  const float* yr[16];
-  float w[16];
+  for (int c = 0; c < NC4; ++c) grp[c] = min(tid + 256 * c, ng - 1);
+  float4 z[NC4];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int jj = min(j, k - 1);
-    w[j] = topk_w[static_cast<size_t>(t) * k + jj];
-    yr[j] = y + static_cast<size_t>(pair_to_row[static_cast<size_t>(t) * k + jj]) * L;
-  }
-  int colc[NC];
+  for (int c = 0; c < NC4; ++c) z[c] = float4{0.f, 0.f, 0.f, 0.f};
+  // rows in batches of kB (k <= 16): each batch's loads are issued before
+  // any is used; rows past k are clamped to the last slot, loaded and unused
+  constexpr int kB = (NC4 <= 4) ? 8 : 4;
+  for (int j0 = 0; j0 < k; j0 += kB) {
+    float4 v[kB][NC4];
+    float w[kB];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) colc[c] = min(tid + 256 * c, L - 1);
+    for (int j = 0; j < kB; ++j) {
+      const int jj = min(j0 + j, k - 1);
+      w[j] = topk_w[static_cast<size_t>(t) * k + jj];
+      const float4* yr =
+          reinterpret_cast<const float4*>(y + static_cast<size_t>(pair_to_row[static_cast<size_t>(t) * k + jj]) * L);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (j < k) {
-      float v[NC];
+      for (int c = 0; c < NC4; ++c) v[j][c] = yr[grp[c]];
+    }
 #pragma unroll
-      for (int c = 0; c < NC; ++c) v[c] = yr[j][colc[c]];
+    for (int j = 0; j < kB; ++j) {
+      if (j0 + j < k) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) z[c] = z[c] + w[j] * v[c];
+        for (int c = 0; c < NC4; ++c) {
+          z[c].x = z[c].x + w[j] * v[j][c].x;
+          z[c].y = z[c].y + w[j] * v[j][c].y;
+          z[c].z = z[c].z + w[j] * v[j][c].z;
+          z[c].w = z[c].w + w[j] * v[j][c].w;
+        }
+      }
     }
   }
   float ss = 0.0f;
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-    if (c < nc) ss += z[c] * z[c];
+  for (int c = 0; c < NC4; ++c)
+    if (tid + 256 * c < ng) ss += ((z[c].x * z[c].x + z[c].y * z[c].y) + z[c].z * z[c].z) + z[c].w * z[c].w;
   ss = wave_sum(ss);
   if ((tid & 63) == 0) s_part[tid >> 6] = ss;
   __syncthreads();
   const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
   const float r = 1.0f / sqrtf(tot / static_cast<float>(L) + eps);
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-    if (c < nc) {
-      const int col = tid + 256 * c;
-      rn[static_cast<size_t>(t) * L + col] =
-          static_cast<uint16_t>(f32_to_bf16_bits((z[c] * r) * bf16_bits_to_f32(gamma[col])));
+  for (int c = 0; c < NC4; ++c) {
+    const int gi = tid + 256 * c;
+    if (gi < ng) {
+      const uint2 gm = *reinterpret_cast<const uint2*>(gamma + 4 * gi);
+      uint2 o;
+      o.x = f32_to_bf16_bits((z[c].x * r) * bf16_bits_to_f32(gm.x & 0xffffu)) |
+            (f32_to_bf16_bits((z[c].y * r) * bf16_bits_to_f32(gm.x >> 16)) << 16);
+      o.y = f32_to_bf16_bits((z[c].z * r) * bf16_bits_to_f32(gm.y & 0xffffu)) |
+            (f32_to_bf16_bits((z[c].w * r) * bf16_bits_to_f32(gm.y >> 16)) << 16);
+      *reinterpret_cast<uint2*>(rn + static_cast<size_t>(t) * L + 4 * gi) = o;
     }
+  }
 }
 
 }  // namespace moe_tail

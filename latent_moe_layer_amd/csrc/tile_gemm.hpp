@@ -29,7 +29,7 @@ namespace moe_tail {
 
 constexpr int kTM = 128;
 constexpr int kTN = 256;
-constexpr int kBigMinRows = 128;  // experts with at least this many rows use the tiled kernel
+constexpr int kBigMinRows = 128;  // experts with at least this many rows use 128-row tiles (by default)
 constexpr int kTileMaxE = 512;    // expert tables of the routed kinds live in LDS
 
 enum { TK_L1 = 0, TK_L2 = 1, TK_DENSE = 2 };
@@ -53,6 +53,7 @@ struct TileArgs {
   int half;                       // L1: I (up rows start), dense SWIGLU: I_s
   int ntn;                        // n tiles
   int nslots;                     // dense: row tiles; routed: unused (the tile count comes from expert_offsets)
+  int big_rows;                   // routed: experts with >= big_rows rows take 128-row tiles, the others 32-row tiles
 };
 
 // Persistent: one workgroup per CU works through a list of tiles.  Tile t
@@ -63,7 +64,7 @@ struct TileArgs {
 // weights, in that XCD's L2).  The K steps of all of a workgroup's tiles form
 // one stream through the three-stage ring: the first stages of the next tile
 // are loaded while the current one finishes and while its epilogue runs.
-// TM = 128: tiles of 128 rows (experts with at least kBigMinRows rows, and
+// TM = 128: tiles of 128 rows (experts with at least big_rows rows, and
 // the dense GEMMs), 8 waves as 2 (M) x 4 (N) of 64 x 64.  TM = 32: tiles of
 // 32 rows for the experts with fewer rows (decode sizes), 8 waves of 32 x 32,
 // a deeper ring.  Either way 256 B rows (weight rows) per tile.
@@ -118,13 +119,13 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
     __syncthreads();
     if (wave == 0) {
       // exclusive prefix over the experts of their row tiles (TM = 128: the
-      // experts with at least kBigMinRows rows; TM = 32: the others)
+      // experts with at least big_rows rows; TM = 32: the others)
       const int per = (p.E + 63) / 64;
       const int eb = min(lane * per, p.E), ee = min(eb + per, p.E);
       auto ntile = [&](int e) {
         const int c = s_eoff[e + 1] - s_eoff[e];
-        if (TM == 128) return c >= kBigMinRows ? (c + TM - 1) / TM : 0;
-        return c < kBigMinRows ? (c + TM - 1) / TM : 0;
+        if (TM == 128) return c >= p.big_rows ? (c + TM - 1) / TM : 0;
+        return c < p.big_rows ? (c + TM - 1) / TM : 0;
       };
       int local = 0;
       for (int e = eb; e < ee; ++e) local += ntile(e);
