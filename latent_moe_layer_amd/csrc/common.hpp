@@ -106,6 +106,12 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Workgroup barrier for LDS traffic only (a fenced __syncthreads would also
 // wait for the direct loads in flight).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

@@ -49,56 +49,71 @@ __device__ __forceinline__ void dense_epilogue(const DenseEpi& ep, int N, int ro
 // Decode-sized M (<= 128 rows): a workgroup covers every row and kSkinnyN
 // weight rows over a range of K steps (K is split over gridDim.y), so each
 // weight byte is read from HBM once.  Both operands go straight from memory
-// into a kSkinnyStages-deep LDS ring (buffer loads with the LDS flag, whole
-// 128-byte lines per load, rows XOR-swizzled as in the tiled kernel), so that
-// five steps of weights are in flight per CU.  Each of the 8 waves (two per
-// SIMD, so one can issue while the other waits) multiplies rows
-// [16 w, 16 w + 16) by the kSkinnyN weight rows; FP32 partial sums
-// partial[z][row][brow] are reduced in split order by k_dense_reduce, which
-// applies the epilogue.
+// into LDS (buffer loads with the LDS flag, whole 128-byte lines per load,
+// rows XOR-swizzled as in the tiled kernel).  A CU's vector-memory path moves
+// about 54 bytes per clock whether a load hits L2 or not, and every
+// workgroup loads all activation rows of its K range, so the weight tile is
+// as wide as the activation tile (128 rows): half of what a CU loads is
+// weights.  Two rings: the weights, which come from HBM, through a deeper
+// one (kBSt - 1 steps in flight), the activation rows, which the workgroups
+// of a K range share and so mostly hit in L2, through a shallower one
+// (kASt - 1 steps ahead).  A wave's load counter retires in issue order, so
+// a wave waiting for activations would also wait for every weight load it
+// issued before them: waves 0-3 load only weights and waves 4-7 only
+// activations, each waiting for its own ring.  All 8 waves compute: wave w
+// multiplies rows [32 (w & 3), +32) by weight rows [64 (w >> 2), +64).  FP32
+// partial sums partial[z][row][brow] are reduced in split order by
+// k_dense_reduce, which applies the epilogue.
 constexpr int kSmallMaxM = 128;
-constexpr int kSkinnyN = 64;      // weight rows per workgroup
-constexpr int kSkinnyStages = 6;  // LDS ring depth
+constexpr int kSkinnyN = 128;        // weight rows per workgroup
+constexpr int kSkinnyBStages = 4;    // weight ring depth
+constexpr int kSkinnyAStages = 3;    // activation ring depth
 
+template <int kBSt = kSkinnyBStages, int kASt = kSkinnyAStages>
 __global__ __launch_bounds__(512) void k_dense_small(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                      int M, int nbrows, int K, int kps, float* __restrict__ partial) {
+  static_assert(kASt >= 2 && kBSt >= kASt, "the weight ring runs ahead of the activation ring");
   constexpr int kABytes = kSmallMaxM * 128;  // one K step of 64 BF16: 128 rows x 128 bytes
   constexpr int kBBytes = kSkinnyN * 128;
-  constexpr int kStage = kABytes + kBBytes;
-  constexpr int kLoads = 3;  // per wave and stage: A blocks w + 8 i (i < 2), B block w
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kSkinnyStages * kStage];
+  constexpr int kBLoads = kBBytes / 4096;  // per weight wave and step (1 KB each)
+  constexpr int kALoads = kABytes / 4096;  // per activation wave and step
+  __shared__ __attribute__((aligned(16))) uint8_t ring_b[kBSt * kBBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring_a[kASt * kABytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const bool loads_b = wv < 4;
+  const int lw = wv & 3;  // index among the waves of its role
   const int l16 = lane & 15, g = lane >> 4;
+  const int wr = wave & 3, wc = wave >> 2;  // this wave's 32 rows and 64 weight rows
   const int brow0 = blockIdx.x * kSkinnyN;
   const int nk = K / 64;
   const int kb0 = blockIdx.y * kps, n = min(kb0 + kps, nk) - kb0;  // this workgroup's steps (>= 1)
   const size_t rowb = static_cast<size_t>(K) * 2;
 
   // 1 KB block b of a stage = rows 8 b .. 8 b + 7, 128 bytes each; lane l
-  // carries row 8 b + (l >> 3), chunk (l & 7) ^ (l >> 3) (rows past M read zeros)
+  // carries row 8 b + (l >> 3), chunk (l & 7) ^ (l >> 3) (rows past M read
+  // zeros).  A wave of a role loads blocks lw, lw + 4, lw + 8, lw + 12.
   const int q8 = lane >> 3, st_c = (lane & 7) ^ q8;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, static_cast<uint32_t>(static_cast<size_t>(M) * rowb));
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + static_cast<size_t>(brow0) * K, static_cast<uint32_t>(kSkinnyN * rowb));
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(B, 0u);
-  uint32_t a_off[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) a_off[i] = static_cast<uint32_t>((8 * (wave + 8 * i) + q8) * rowb) + 16u * st_c;
-  const uint32_t b_off = static_cast<uint32_t>((8 * wave + q8) * rowb) + 16u * st_c;
+  const __amdgpu_buffer_rsrc_t rl = loads_b ? rb : ra;
   // The workgroups of one K range all read the same activation rows; each
   // starts at its own step (rotation by its weight tile) so that they do not
   // request the same lines at the same time.  The summation order then
   // depends on the tile only.
   const int rot = blockIdx.x % n;
-  auto issue = [&](int s) {
-    uint8_t* st = ring + (s % kSkinnyStages) * kStage;
-    const bool live = s < n;
+  // stage s of this wave's ring into `slot`: blocks lw + 4 i
+  auto issue = [&](int s, uint8_t* slot, int nl) {
     const int sr = s + rot < n ? s + rot : s + rot - n;
     const int soff = (kb0 + sr) * 128;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(live ? ra : rz, st + 1024 * (wv + 8 * i), a_off[i], soff);
-    dma16(live ? rb : rz, st + kABytes + 1024 * wv, b_off, soff);
+    for (int i = 0; i < nl; ++i) {
+      const int blk = lw + 4 * i;
+      dma16(s < n ? rl : rz, slot + 1024 * blk, static_cast<uint32_t>((8 * blk + q8) * rowb) + 16u * st_c, soff);
+    }
   };
+  auto issue_b = [&](int s) { issue(s, ring_b + (s % kBSt) * kBBytes, kBLoads); };
+  auto issue_a = [&](int s) { issue(s, ring_a + (s % kASt) * kABytes, kALoads); };
 
   // this lane's operand pieces within a 16-row block (2 KB): row l16, chunk
   // g (first MFMA of the step) and chunk 4 + g (second)
@@ -106,42 +121,59 @@ __global__ __launch_bounds__(512) void k_dense_small(const uint16_t* __restrict_
   const int f_lo = fr + 16 * (g ^ (l16 & 7));
   const int f_hi = fr + 16 * ((4 | g) ^ (l16 & 7));
 
-  f32x4 acc[4];
+  f32x4 acc[2][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Step s: wait for stage s (every wave's loads), start stage s + 5 into the
-  // buffer of stage s - 1, compute stage s.
+  // Step s: wait for this wave's part of stage s, barrier (stage s complete,
+  // every wave done with step s - 1), start stage s + kBSt - 1 (weights) or
+  // s + kASt - 1 (activations) into the slot of step s - 1, compute step s.
+  if (loads_b) {
 #pragma unroll
-  for (int s = 0; s < kSkinnyStages - 1; ++s) issue(s);
+    for (int s = 0; s < kBSt - 1; ++s) issue_b(s);
+  } else {
+#pragma unroll
+    for (int s = 0; s < kASt - 1; ++s) issue_a(s);
+  }
   for (int s = 0; s < n; ++s) {
-    ring_barrier<kLoads * (kSkinnyStages - 2)>();
-    issue(s + kSkinnyStages - 1);
+    if (loads_b) vm_wait<kBLoads * (kBSt - 2)>();
+    else vm_wait<kALoads * (kASt - 2)>();
+    lds_barrier();
+    if (loads_b) issue_b(s + kBSt - 1);
+    else issue_a(s + kASt - 1);
     // unconditional (a wave past M multiplies zero rows): a branch here makes
     // the compiler copy the accumulators between register files every step
-    const uint8_t* st = ring + (s % kSkinnyStages) * kStage;
+    const uint8_t* sa = ring_a + (s % kASt) * kABytes + 4096 * wr;
+    const uint8_t* sb = ring_b + (s % kBSt) * kBBytes + 8192 * wc;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int fo = h ? f_hi : f_lo;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + 2048 * wave + fo);
-      bf16x8 b[4];
+      bf16x8 a[2], b[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(st + kABytes + 2048 * j + fo);
+      for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8*>(sa + 2048 * i + fo);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = mfma_bf16(a, b[j], acc[j]);
+      for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(sb + 2048 * j + fo);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
     }
   }
-  ring_barrier<0>();  // the trailing (empty) loads
+  vm_wait<0>();  // the trailing (empty) loads
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * wave + 4 * g + i;
-    if (row < M) {
-      float* pr = partial + (static_cast<size_t>(blockIdx.y) * M + row) * nbrows + brow0 + l16;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pr[16 * j] = acc[j][i];
+    for (int e = 0; e < 4; ++e) {
+      const int row = 32 * wr + 16 * i + 4 * g + e;
+      if (row < M) {
+        float* pr = partial + (static_cast<size_t>(blockIdx.y) * M + row) * nbrows + brow0 + 64 * wc + l16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pr[16 * j] = acc[i][j][e];
+      }
     }
-  }
 }
 
 // Sums the split-K partials in split order and applies the epilogue.

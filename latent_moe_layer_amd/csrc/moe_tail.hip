@@ -52,7 +52,7 @@ int check_counts(int32_t Mr, int32_t Ms) {
 }
 
 // Plan of one dense BF16 GEMM.  Up to kSmallMaxM rows: k_dense_small (all
-// rows per workgroup, 128 B rows per workgroup) with K split until the grid
+// rows per workgroup, kSkinnyN B rows per workgroup) with K split until the grid
 // holds about 256 workgroups, always through FP32 partials.  More rows: the
 // LDS-tiled kernel (128 x 256 tiles, epilogue fused, no split).
 struct DensePlan {
@@ -196,7 +196,7 @@ void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int 
   if (M == 0) return;
   const int nbrows = (kEpi == EPI_SWIGLU) ? 2 * ep.half : N;
   if (p.small) {
-    hipLaunchKernelGGL(k_dense_small, dim3(p.nt, p.splits), dim3(512), 0, st, A, B, M, nbrows, K, p.kps, partial);
+    hipLaunchKernelGGL(k_dense_small<>, dim3(p.nt, p.splits), dim3(512), 0, st, A, B, M, nbrows, K, p.kps, partial);
     const int ncols = (kEpi == EPI_SWIGLU) ? ep.half : N;
     const long n = static_cast<long>(M) * (ncols / 4);
     hipLaunchKernelGGL(k_dense_reduce<kEpi>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,

@@ -17,12 +17,13 @@ namespace moe_tail {
 // experts.  Lane l of a wave accumulates p[l] = fma-chain over i of
 // x[64 i + l] * W[e, 64 i + l]; the 64 partials are then combined by an xor
 // butterfly (32, 16, 8, 4, 2, 1), which leaves the same value in every lane.
-// The tile's x rows (bf16) are copied to LDS at once with direct loads; the
-// gate columns of the next kLogitChunk-column chunk are loaded while the
-// current one is used, so the loop waits for memory about once.
+// The kernel is latency-bound (a few hundred KB in all), so it waits for
+// memory once: the tile's x rows (bf16) go to LDS with direct loads while
+// every gate value a lane needs (up to kLogitChunk columns) is loaded into
+// registers, and only then does the arithmetic start.
 constexpr int kLogitTok = 4;
 constexpr int kLogitExpPerWave = 2;
-constexpr int kLogitChunk = 1024;  // gate columns per prefetch
+constexpr int kLogitChunk = 4096;  // gate columns in registers at once
 // dynamic LDS: the x tile, kLogitTok x L bf16
 
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x_lat,
@@ -35,9 +36,9 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
   const int t0 = blockIdx.x * kLogitTok;
   const int e0 = (blockIdx.y * 4 + wave) * kLogitExpPerWave;
 
-  // x rows t0 .. t0 + 7 as one linear byte array: 1 KB block j is loaded by
-  // wave j % 4, lane l copying bytes [16 (64 j + l), +16) (rows past Mr read
-  // as zeros)
+  // x rows t0 .. t0 + kLogitTok - 1 as one linear byte array: 1 KB block j is
+  // loaded by wave j % 4, lane l copying bytes [16 (64 j + l), +16) (rows
+  // past Mr read as zeros)
   {
     const uint32_t row_bytes = static_cast<uint32_t>(L) * 2;
     const int nrows = max(0, min(kLogitTok, Mr - t0));
@@ -47,28 +48,26 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
     for (int j = wv; j < nblocks; j += 4) dma16(r, reinterpret_cast<uint8_t*>(sx) + 1024 * j, 16u * (64 * j + lane), 0);
   }
 
-  const float* wp[kLogitExpPerWave];
+  // gate row of each expert as a buffer (columns past L read as zeros)
+  __amdgpu_buffer_rsrc_t wr[kLogitExpPerWave];
 #pragma unroll
-  for (int e = 0; e < kLogitExpPerWave; ++e) wp[e] = gate + static_cast<size_t>(min(e0 + e, E - 1)) * L + lane;
-  constexpr int kPer = kLogitChunk / 64;  // gate values per lane, expert and chunk
-  float wcur[kLogitExpPerWave][kPer], wnxt[kLogitExpPerWave][kPer];
-  auto load_w = [&](float (&w)[kLogitExpPerWave][kPer], int c0) {
-#pragma unroll
-    for (int e = 0; e < kLogitExpPerWave; ++e)
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) w[e][u] = (c0 + 64 * u < L) ? wp[e][c0 + 64 * u] : 0.0f;
-  };
-  load_w(wcur, 0);
-  ring_barrier<0>();  // the x tile is in LDS
-
+  for (int e = 0; e < kLogitExpPerWave; ++e)
+    wr[e] = make_rsrc(gate + static_cast<size_t>(min(e0 + e, E - 1)) * L, static_cast<uint32_t>(L) * 4);
+  constexpr int kPer = kLogitChunk / 64;  // gate values per lane and expert
   float acc[kLogitTok][kLogitExpPerWave];
 #pragma unroll
   for (int t = 0; t < kLogitTok; ++t)
 #pragma unroll
     for (int e = 0; e < kLogitExpPerWave; ++e) acc[t][e] = 0.0f;
 
-  for (int c0 = 0; c0 < L; c0 += kLogitChunk) {
-    if (c0 + kLogitChunk < L) load_w(wnxt, c0 + kLogitChunk);
+  for (int c0 = 0; c0 < L; c0 += kLogitChunk) {  // one pass for L <= kLogitChunk
+    float w[kLogitExpPerWave][kPer];
+#pragma unroll
+    for (int e = 0; e < kLogitExpPerWave; ++e)
+#pragma unroll
+      for (int u = 0; u < kPer; ++u)
+        w[e][u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr[e], 4 * lane, 4 * (c0 + 64 * u), 0));
+    ring_barrier<0>();  // the gate values and (first pass) the x tile are in
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       if (c0 + 64 * u < L) {
@@ -76,14 +75,10 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
         for (int t = 0; t < kLogitTok; ++t) {
           const float xv = bf16_bits_to_f32(sx[t * L + c0 + 64 * u + lane]);
 #pragma unroll
-          for (int e = 0; e < kLogitExpPerWave; ++e) acc[t][e] = __builtin_fmaf(xv, wcur[e][u], acc[t][e]);
+          for (int e = 0; e < kLogitExpPerWave; ++e) acc[t][e] = __builtin_fmaf(xv, w[e][u], acc[t][e]);
         }
       }
     }
-#pragma unroll
-    for (int e = 0; e < kLogitExpPerWave; ++e)
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) wcur[e][u] = wnxt[e][u];
   }
 #pragma unroll
   for (int t = 0; t < kLogitTok; ++t)
