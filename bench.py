@@ -76,6 +76,8 @@ def main() -> int:
     ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "mxfp4", "indep"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--add3", action="store_true",
+                    help="time moe_tail_forward_add3 (the residual joined in the up-projection epilogue)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs the tail on one GPU only; --gpus {args.gpus} is not supported "
@@ -93,6 +95,8 @@ def main() -> int:
     inp = synth.make_inputs(wl)
     gen_s = time.time() - t0
     dev = DeviceTail(inp, "cuda:0")
+    if args.add3:
+        dev.set_residual(synth.make_residual(wl))
     stream = torch.cuda.Stream()
     nst = len(STAGES)
     hev = HipEvents((args.steps + 1) * (nst + 1) + 2)
@@ -131,10 +135,13 @@ def main() -> int:
     ms_per_step = total_ms / args.steps
 
     # per-stage durations: K more eager steps, the library recording HIP events
-    # on the stream its kernels run on
+    # on the stream its kernels run on (the profiled entry point has no add3
+    # variant; the stages run the same kernels)
+    residual, dev.residual = getattr(dev, "residual", None), None
     for i in range(args.steps):
         step(stream, hev.ev[i * (nst + 1):(i + 1) * (nst + 1)])
     torch.cuda.synchronize()
+    dev.residual = residual
     stage_ms = np.zeros(nst)
     for i in range(args.steps):
         base = i * (nst + 1)
@@ -144,7 +151,7 @@ def main() -> int:
 
     offsets = to_np(dev.offsets)
     touched = int(np.count_nonzero(np.diff(offsets)))
-    nbytes = synth.algorithmic_bytes(wl, touched)["total"]
+    nbytes = synth.algorithmic_bytes(wl, touched)["total"] + (wl.Mr * wl.H * 2 if args.add3 else 0)
     flops = synth.algorithmic_flops(wl)
     us = ms_per_step * 1e3
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -188,7 +195,8 @@ def main() -> int:
         "data": "synthetic (seeded; random-init weights of the tail's shapes)",
         "config": {"workload": f"{wl.name}: Mr={wl.Mr} Ms={wl.Ms} E={wl.E} top{wl.k} I={wl.I} I_s={wl.Is} "
                                f"H={wl.H} L={wl.L} {'FP8 128x128' if wl.wfmt == 0 else 'MXFP4'} routed weights",
-                   "global_batch": wl.Mr, "parallelism": "single GPU"},
+                   "global_batch": wl.Mr, "parallelism": "single GPU",
+                   "epilogue": "add3: up + shared + residual, one rounding" if args.add3 else "up + shared"},
         "algorithmic_bytes": nbytes, "touched_experts": touched,
         "tflops_lowp": flops["lowp"] / (ms_per_step * 1e-3) / 1e12,
         "tflops_bf16": flops["bf16"] / (ms_per_step * 1e-3) / 1e12,

@@ -138,6 +138,22 @@ int moe_tail_forward(const moe_tail_dims *dims, const moe_tail_weights *weights,
                      const uint16_t *x_hid, int32_t Ms, const moe_tail_routing *routing, uint16_t *out,
                      uint16_t *shared_out, void *workspace, size_t ws_bytes, void *stream);
 
+/* moe_tail_forward with the residual stream joined in the same epilogue
+ * ("add3"): out[t, n] = bf16((up(RMSNorm(routed))[t, n] + f32(shared[t, n]))
+ * + f32(residual[t, n])) for t < Mr, the three terms added in FP32 in that
+ * order and rounded to bf16 once.  The pages' finalize tail joins
+ * projection, shared partial and residual in one step and finds that
+ * storing bf16 before the residual add rounds twice and biases the output
+ * (tokenspeed PR "MNNVL CuTe-DSL finalize tail + K3 comm layer extraction",
+ * commit log).
+ *   residual [Mr, H] bf16, read only; may be NULL only when Mr == 0.
+ * Every other argument, the workspace and the errors are those of
+ * moe_tail_forward; shared_out rows get no residual. */
+int moe_tail_forward_add3(const moe_tail_dims *dims, const moe_tail_weights *weights, const uint16_t *x_lat,
+                          int32_t Mr, const uint16_t *x_hid, int32_t Ms, const moe_tail_routing *routing,
+                          const uint16_t *residual, uint16_t *out, uint16_t *shared_out, void *workspace,
+                          size_t ws_bytes, void *stream);
+
 /* Number of stages moe_tail_forward_profiled brackets with events. */
 #define MOE_TAIL_NUM_STAGES 7
 /* Stage order: 0 quantize x_lat, 1 routed L1 (+SwiGLU + h quantization),

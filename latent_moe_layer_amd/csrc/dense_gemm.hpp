@@ -27,6 +27,7 @@ struct DenseEpi {
   uint16_t* out0;         // SWIGLU: hs [M, I_s]; SHARED: s [Mr, N]; UPADD: out [M, N]
   uint16_t* out1;         // SHARED: shared_out [M - Mr, N]
   const uint16_t* addsrc; // UPADD: s [M, N] bf16 added in FP32
+  const uint16_t* resid;  // UPADD: residual [M, N] bf16 added in FP32 after s, or null
 };
 
 // Column of output produced by B row `brow` (SWIGLU pairs gate row c with up
@@ -40,8 +41,10 @@ __device__ __forceinline__ void dense_epilogue(const DenseEpi& ep, int N, int ro
     if (row < ep.Mr) ep.out0[static_cast<size_t>(row) * N + col] = b;
     else ep.out1[static_cast<size_t>(row - ep.Mr) * N + col] = b;
   } else {
-    const float s = bf16_bits_to_f32(ep.addsrc[static_cast<size_t>(row) * N + col]);
-    ep.out0[static_cast<size_t>(row) * N + col] = static_cast<uint16_t>(f32_to_bf16_bits(v0 + s));
+    const size_t o = static_cast<size_t>(row) * N + col;
+    float v = v0 + bf16_bits_to_f32(ep.addsrc[o]);
+    if (ep.resid != nullptr) v += bf16_bits_to_f32(ep.resid[o]);  // residual, same single rounding
+    ep.out0[o] = static_cast<uint16_t>(f32_to_bf16_bits(v));
   }
 }
 

@@ -217,8 +217,8 @@ void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int 
 }
 
 int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
-                 const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, uint16_t* out,
-                 uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+                 const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, const uint16_t* residual,
+                 uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream, void* const* events) {
   int rc = check_dims(dims);
   if (rc) return rc;
   rc = check_counts(Mr, Ms);
@@ -231,6 +231,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   if (!ptr_ok(x_lat, static_cast<size_t>(Mr) * L * 2) || !ptr_ok(x_hid, static_cast<size_t>(Ms) * H * 2) ||
       !ptr_ok(out, static_cast<size_t>(Mr) * H * 2))
     return MOE_TAIL_ERR_INVALID;
+  if (residual != nullptr && !ptr_ok(residual, static_cast<size_t>(Mr) * H * 2)) return MOE_TAIL_ERR_INVALID;
   if ((Ms > Mr) != (shared_out != nullptr)) return MOE_TAIL_ERR_INVALID;
   if (shared_out != nullptr && !aligned16(shared_out)) return MOE_TAIL_ERR_INVALID;
   const Layout lay = layout_of(d, Mr, Ms);
@@ -362,19 +363,19 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   // 4: shared L1 + SwiGLU
   mark(4);
   {
-    DenseEpi ep{Mr, Is, hs, nullptr, nullptr};
+    DenseEpi ep{Mr, Is, hs, nullptr, nullptr, nullptr};
     launch_dense<EPI_SWIGLU>(plans.s1, x_hid, w->ws1, Ms, Is, H, partial, ep, st);
   }
   // 5: shared L2 -> s (rows < Mr) and shared_out (rows >= Mr)
   mark(5);
   {
-    DenseEpi ep{Mr, Is, s, shared_out, nullptr};
+    DenseEpi ep{Mr, Is, s, shared_out, nullptr, nullptr};
     launch_dense<EPI_SHARED>(plans.s2, hs, w->ws2, Ms, H, Is, partial, ep, st);
   }
-  // 6: up-projection + FP32 shared add
+  // 6: up-projection + FP32 shared add (+ FP32 residual add)
   mark(6);
   {
-    DenseEpi ep{Mr, Is, out, nullptr, s};
+    DenseEpi ep{Mr, Is, out, nullptr, s, residual};
     launch_dense<EPI_UPADD>(plans.up, rn, w->w_up, Mr, H, L, partial, ep, st);
   }
   mark(7);
@@ -469,7 +470,14 @@ int moe_tail_route(const moe_tail_dims* dims, const moe_tail_weights* w, const u
 int moe_tail_forward(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
                      const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, uint16_t* out,
                      uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream) {
-  return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, out, shared_out, ws, ws_bytes, stream, nullptr);
+  return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, nullptr, out, shared_out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_tail_forward_add3(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
+                          const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, const uint16_t* residual,
+                          uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream) {
+  if (Mr > 0 && residual == nullptr) return MOE_TAIL_ERR_INVALID;
+  return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, stream, nullptr);
 }
 
 int moe_tail_forward_profiled(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat,
@@ -477,7 +485,8 @@ int moe_tail_forward_profiled(const moe_tail_dims* dims, const moe_tail_weights*
                               uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream,
                               void* const* stage_events) {
   if (stage_events == nullptr) return MOE_TAIL_ERR_INVALID;
-  return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, out, shared_out, ws, ws_bytes, stream, stage_events);
+  return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, nullptr, out, shared_out, ws, ws_bytes, stream,
+                      stage_events);
 }
 
 int moe_tail_quant_fp8_1x128(const void* x, int32_t x_is_bf16, int32_t rows, int32_t cols, uint8_t* codes,

@@ -61,7 +61,18 @@ class DeviceTail:
         B.moe_tail_route(self.dims, self.weights, self.t["x_lat"], self.Mr, self.routing, self.ws, self.ws_bytes,
                          stream)
 
+    def set_residual(self, residual: np.ndarray | None) -> None:
+        """Upload the add3 residual ([Mr, H] bf16 bits); None goes back to the plain forward."""
+        self.residual = None if residual is None else _dev(residual, self.device)
+
     def forward(self, stream=None, events=None) -> None:
+        res = getattr(self, "residual", None)
+        if res is not None:
+            if events is not None:
+                raise ValueError("the profiled forward has no add3 variant")
+            B.moe_tail_forward_add3(self.dims, self.weights, self.t["x_lat"], self.Mr, self.t["x_hid"], self.Ms,
+                                    self.routing, res, self.out, self.shared_out, self.ws, self.ws_bytes, stream)
+            return
         args = (self.dims, self.weights, self.t["x_lat"], self.Mr, self.t["x_hid"], self.Ms, self.routing, self.out,
                 self.shared_out, self.ws, self.ws_bytes, stream)
         if events is None:

@@ -51,6 +51,7 @@ WFMT_MXFP4 = 1
 
 # tensor tags for the per-tensor seed streams
 _T_XLAT, _T_WG, _T_W1, _T_W2, _T_GAMMA, _T_WUP, _T_XHID, _T_WS1, _T_WS2 = range(1, 10)
+_T_RESID = 10  # the add3 residual stream
 
 
 @dataclass(frozen=True)
@@ -225,6 +226,15 @@ def make_inputs(wl: Workload | str, Mr: int | None = None, Ms: int | None = None
         ws1 = f32_to_bf16_bits(_normal(wl.seed, _T_WS1, 0, (2 * Is, H), 1.0 / np.sqrt(H)))
         ws2 = f32_to_bf16_bits(_normal(wl.seed, _T_WS2, 0, (H, Is), 1.0 / np.sqrt(Is)))
     return Inputs(wl, x_lat, x_hid, gate, gate_bias, w1, w1s, w2, w2s, gamma, w_up, ws1, ws2)
+
+
+def make_residual(wl: Workload | str, Mr: int | None = None) -> np.ndarray:
+    """The residual stream joined by the add3 epilogue: [Mr, H] bf16 bits,
+    N(0, 1), its own stream of the workload's seed."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    Mr = wl.Mr if Mr is None else Mr
+    return f32_to_bf16_bits(_normal(wl.seed, _T_RESID, 0, (Mr, wl.H), 1.0))
 
 
 def algorithmic_bytes(wl: Workload, touched_experts: int | None = None) -> dict:

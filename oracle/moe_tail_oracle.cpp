@@ -315,7 +315,8 @@ void oracle_permute(int E, int k, int Mr, const int32_t* ids, int32_t* offsets, 
 // Forward pass for the tokens listed in `sel` (indices into 0..Ms-1).
 // Token t < Mr produces the combined output row; t >= Mr only the shared row.
 // Per selected token s (outputs are [n_sel, ...], optional ones may be NULL):
-//   out_f32[s, H]  t < Mr: up(rn) + f32(s_bf) before rounding; t >= Mr: f32(s_bf)
+//   out_f32[s, H]  t < Mr: up(rn) + f32(s_bf) before rounding, then + f32(residual[t])
+//                  when a residual is given ("add3": tokenspeed PR, commit log); t >= Mr: f32(s_bf)
 //   out_bf16[s, H] t < Mr: bf16(out_f32); t >= Mr: s_bf (the shared_out row)
 //   xq[s, L], sx[s, L/128]                  x_lat codes and scales (t < Mr)
 //   hq[s, k, I], sh[s, k, I/128], h[s, k, I] h codes, scales, pre-quantization h
@@ -326,7 +327,7 @@ int oracle_forward(int H, int L, int E, int k, int I, int Is, int wfmt, float ep
                    const uint8_t* w1, const void* w1s, const uint8_t* w2, const void* w2s,
                    const uint16_t* gamma, const uint16_t* w_up, const uint16_t* ws1, const uint16_t* ws2,
                    const uint16_t* x_lat, int Mr, const uint16_t* x_hid, int Ms,
-                   const int32_t* topk_ids, const float* topk_w,
+                   const int32_t* topk_ids, const float* topk_w, const uint16_t* residual,
                    int n_sel, const int32_t* sel,
                    float* out_f32, uint16_t* out_bf16,
                    uint8_t* xq_out, float* sx_out, uint8_t* hq_out, float* sh_out, float* h_out,
@@ -460,7 +461,9 @@ int oracle_forward(int H, int L, int E, int k, int I, int Is, int wfmt, float ep
       for (int c = 0; c < L; ++c) rr[c] = bf16_to_f32(rn[static_cast<size_t>(a) * L + c]);
       for (int n = 0; n < H; ++n) {
         for (int c = 0; c < L; ++c) wr[c] = bf16_to_f32(w_up[static_cast<size_t>(n) * L + c]);
-        of[static_cast<size_t>(s) * H + n] = dot(rr.data(), wr.data(), L) + bf16_to_f32(sbf[static_cast<size_t>(s) * H + n]);
+        float v = dot(rr.data(), wr.data(), L) + bf16_to_f32(sbf[static_cast<size_t>(s) * H + n]);
+        if (residual) v = v + bf16_to_f32(residual[static_cast<size_t>(t) * H + n]);
+        of[static_cast<size_t>(s) * H + n] = v;
       }
     }
   }

@@ -156,8 +156,10 @@ class ForwardResult:
     sbf: np.ndarray         # [n, H] bf16 bits
 
 
-def forward(inp, topk_ids, topk_w, sel=None, Mr=None, Ms=None) -> ForwardResult:
-    """Run the oracle on ``synth.Inputs`` for the tokens in ``sel`` (default all)."""
+def forward(inp, topk_ids, topk_w, sel=None, Mr=None, Ms=None, residual=None) -> ForwardResult:
+    """Run the oracle on ``synth.Inputs`` for the tokens in ``sel`` (default all).
+    ``residual`` ([Mr, H] bf16 bits, row t for token t) is added to the routed
+    rows after the shared add, before the one rounding ("add3")."""
     wl = inp.wl
     Mr = inp.x_lat.shape[0] if Mr is None else Mr
     Ms = inp.x_hid.shape[0] if Ms is None else Ms
@@ -177,11 +179,14 @@ def forward(inp, topk_ids, topk_w, sel=None, Mr=None, Ms=None) -> ForwardResult:
             _c(inp.w2_scale, inp.w2_scale.dtype), _c(inp.gamma, np.uint16), _c(inp.w_up, np.uint16),
             _c(inp.ws1, np.uint16), _c(inp.ws2, np.uint16), _c(inp.x_lat, np.uint16), _c(inp.x_hid, np.uint16),
             _c(topk_ids, np.int32), _c(topk_w, np.float32)]
+    res = None if residual is None else _c(residual, np.uint16)
+    if res is not None and res.shape != (Mr, H):
+        raise ValueError("residual must be [Mr, H]")
     rc = lib().oracle_forward(
         C.c_int(H), C.c_int(L), C.c_int(wl.E), C.c_int(k), C.c_int(I), C.c_int(Is), C.c_int(wl.wfmt),
         C.c_float(wl.rms_eps),
         _p(arrs[0]), _p(arrs[1]), _p(arrs[2]), _p(arrs[3]), _p(arrs[4]), _p(arrs[5]), _p(arrs[6]), _p(arrs[7]),
-        _p(arrs[8]), C.c_int(Mr), _p(arrs[9]), C.c_int(Ms), _p(arrs[10]), _p(arrs[11]),
+        _p(arrs[8]), C.c_int(Mr), _p(arrs[9]), C.c_int(Ms), _p(arrs[10]), _p(arrs[11]), _p(res),
         C.c_int(n), _p(sel),
         _p(r.out_f32), _p(r.out_bf16), _p(r.xq), _p(r.sx), _p(r.hq), _p(r.sh), _p(r.h), _p(r.y), _p(r.rn),
         _p(r.hs), _p(r.sbf))

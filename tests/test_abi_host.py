@@ -144,6 +144,23 @@ def test_forward_rejections():
                                              None, None) == B.MOE_TAIL_ERR_INVALID
 
 
+def test_forward_add3_rejections():
+    d, w, r = dims(), _fake_weights(), _fake_routing()
+    need = B.moe_tail_workspace_bytes(d, 16, 16)
+    f = B.lib().moe_tail_forward_add3
+    RES = 1 << 46
+    # the residual is required when there are routed tokens, and 16-byte aligned
+    assert f(C.byref(d), C.byref(w), X, 16, X, 16, C.byref(r), None, OUT, None, WS, need, None) == \
+        B.MOE_TAIL_ERR_INVALID
+    assert f(C.byref(d), C.byref(w), X, 16, X, 16, C.byref(r), RES + 2, OUT, None, WS, need, None) == \
+        B.MOE_TAIL_ERR_INVALID
+    # every other check is the plain forward's
+    assert f(C.byref(d), C.byref(w), X, 16, X, 16, C.byref(r), RES, OUT, None, WS, need - 1, None) == \
+        B.MOE_TAIL_ERR_WORKSPACE
+    assert f(C.byref(d), C.byref(w), X, 17, X, 16, C.byref(r), RES, OUT, None, WS, need, None) == \
+        B.MOE_TAIL_ERR_INVALID
+
+
 def test_quant_rejections():
     q = B.lib().moe_tail_quant_fp8_1x128
     assert q(X, 1, 4, 100, OUT, SOUT, None) == B.MOE_TAIL_ERR_INVALID

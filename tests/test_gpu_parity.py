@@ -22,8 +22,9 @@ def _gpu():
     B.lib()  # a missing library fails loudly here
 
 
-def run(inp, Mr=None, Ms=None):
+def run(inp, Mr=None, Ms=None, residual=None):
     dev = DeviceTail(inp, "cuda:0", Mr=Mr, Ms=Ms)
+    dev.set_residual(residual)
     dev.route()
     dev.forward()
     torch.cuda.synchronize()
@@ -43,14 +44,15 @@ def check_routing(dev, inp):
     return oids, ow, p2r
 
 
-def check_forward(dev, inp, sel=None, report=None):
-    """Compare outputs and intermediates on the tokens in `sel` (default all)."""
+def check_forward(dev, inp, sel=None, report=None, residual=None):
+    """Compare outputs and intermediates on the tokens in `sel` (default all);
+    `residual` ([Mr, H] bf16 bits): the add3 output is expected."""
     wl, Mr, Ms = inp.wl, dev.Mr, dev.Ms
     oids, ow, p2r = check_routing(dev, inp)
     if sel is None:
         sel = np.arange(Ms, dtype=np.int32)
     sel = np.asarray(sel, np.int32)
-    ref = orc.forward(inp, oids, ow, sel=sel, Mr=Mr, Ms=Ms)
+    ref = orc.forward(inp, oids, ow, sel=sel, Mr=Mr, Ms=Ms, residual=residual)
     inter = {k: to_np(v) for k, v in dev.intermediates().items()}
     rsel = np.flatnonzero(sel < Mr)
     ssel = np.flatnonzero(sel >= Mr)
@@ -200,6 +202,45 @@ def test_forward_tiled_several_tiles_per_workgroup(wfmt):
     rng = np.random.default_rng(5)
     sel = np.concatenate([np.sort(rng.choice(1024, 40, replace=False)), [0, 1023, 1024, 1183]]).astype(np.int32)
     check_forward(dev, inp, sel=np.unique(sel))
+
+
+# ------------------------------------------------------------------- add3 --
+# The up-projection epilogue joining the residual stream: out = bf16((up +
+# shared) + residual), one rounding (tokenspeed PR "MNNVL CuTe-DSL finalize
+# tail + K3 comm layer extraction", commit log).
+
+@pytest.mark.parametrize("Mr,Ms", [(40, 56), (300, 320)])  # small-M dense path, tiled dense path
+def test_forward_add3(Mr, Ms):
+    wl = synth.Workload("add3", Mr=Mr, Ms=Ms, E=8, k=2, I=256, Is=256, wfmt=0, seed=41 + Mr, H=1024, L=512)
+    inp = synth.make_inputs(wl)
+    r = synth.make_residual(wl)
+    dev = run(inp, residual=r)
+    check_forward(dev, inp, residual=r)
+    # the same call without the residual: shared_out rows are untouched by it
+    plain = run(inp)
+    assert np.array_equal(to_np(dev.shared_out), to_np(plain.shared_out))
+
+
+def test_forward_add3_decode_sampled():
+    wl = synth.WORKLOADS["decode"]
+    inp = synth.make_inputs(wl)
+    r = synth.make_residual(wl)
+    dev = run(inp, residual=r)
+    sel = np.array([0, 1, 37, 64, 100, 127], np.int32)
+    check_forward(dev, inp, sel=sel, residual=r)
+
+
+def test_forward_add3_without_routed_tokens():
+    # Mr = 0: no up-projection, the residual may be NULL, the shared rows are the plain ones
+    wl = synth.Workload("a3mr0", Mr=0, Ms=20, E=4, k=2, I=128, Is=256, wfmt=0, seed=24)
+    inp = synth.make_inputs(wl)
+    dev = DeviceTail(inp, "cuda:0")
+    B.moe_tail_forward_add3(dev.dims, dev.weights, dev.t["x_lat"], 0, dev.t["x_hid"], dev.Ms, dev.routing, None,
+                            dev.out, dev.shared_out, dev.ws, dev.ws_bytes)
+    torch.cuda.synchronize()
+    got = to_np(dev.shared_out)
+    plain = run(inp)
+    assert np.array_equal(got, to_np(plain.shared_out))
 
 
 def test_forward_heavy_expert_many_row_tiles():
