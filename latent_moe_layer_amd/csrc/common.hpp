@@ -69,6 +69,12 @@ __device__ __forceinline__ f32x4 mfma_fp8_fp4(const i32x8& a, const i32x8& b, in
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 4, 0, 127, 0, scale_b);
 }
 
+// 16x16x128 FP4 e2m1 (A, one e8m0 scale per lane) x FP8 e4m3 (B).
+__device__ __forceinline__ f32x4 mfma_fp4_fp8(const i32x8& a, int scale_a, const i32x8& b) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 4, 0, 0, scale_a, 0, 127);
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -88,13 +94,15 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ uint32_t lds_offset(const uint8_t* lds) {
   return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)lds)));
 }
+// (soff is wave-uniform by construction; readfirstlane keeps it in a scalar
+// register where the compiler cannot prove that.)
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t voff, int soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds_offset(lds)), "v"(voff), "s"(r),
-               "s"(soff));
+               "s"(__builtin_amdgcn_readfirstlane(soff)));
 }
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const uint8_t* lds, uint32_t voff, int soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(lds_offset(lds)), "v"(voff), "s"(r),
-               "s"(soff));
+               "s"(__builtin_amdgcn_readfirstlane(soff)));
 }
 
 // Wait until at most N of this wave's direct loads are in flight and its LDS

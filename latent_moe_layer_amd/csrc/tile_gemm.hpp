@@ -298,6 +298,16 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   const int f_lo = fr + 16 * (g ^ (l16 & 7));
   const int f_hi = fr + 16 * ((4 | g) ^ (l16 & 7));
 
+  // Accumulators.  L1 (kTrans): the weight block is the MFMA's A operand
+  // and the activation block its B operand, so acc[mt][j][i] is weight
+  // column 16 bblk(j) + 4 g + i (of the tile's 256 B rows) for tile row
+  // 16 kMT wm + 16 mt + l16: a lane holds one token row per mt, and the FP8
+  // promotion factor (activation scale x weight scale) is one value per
+  // (mt, weight half); its epilogue goes through LDS anyway.  L2 and the
+  // dense kinds keep the activation block as A (acc[mt][j][i] is tile row
+  // 16 kMT wm + 16 mt + 4 g + i, column 16 bblk(j) + l16), whose direct
+  // stores put 16 lanes on one row.
+  constexpr bool kTrans = KIND == TK_L1;
   f32x4 acc[kMT][kNJ];
   auto compute = [&](const uint8_t* st, int ks, int buf) {
     // weight scales of this step (FP8): the wave's B rows lie in the tile's
@@ -315,25 +325,10 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
       const i32x4 hi4 = *reinterpret_cast<const i32x4*>(ab + f_hi);
       af[mt] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    // per-row promotion factors of this step: activation scale x weight scale
-    float sc[2][kMT][4];
-    if (kScaled) {
-      const float* ss = reinterpret_cast<const float*>(st + kSOff);
+    if (kBF16) {
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(ss + 16 * kMT * wm + 16 * mt + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sc[0][mt][i] = v[i] * sw_lo;
-          sc[1][mt][i] = v[i] * sw_hi;
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kNJ; ++j) {
-      const int bb = bblk(j);
-      if (kBF16) {
-        const uint8_t* bp = st + kABytes + bb * 2048;
+      for (int j = 0; j < kNJ; ++j) {
+        const uint8_t* bp = st + kABytes + bblk(j) * 2048;
         const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_lo));
         const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_hi));
 #pragma unroll
@@ -343,69 +338,135 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
           acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, alo), b0, acc[mt][j]);
           acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, ahi), b1, acc[mt][j]);
         }
-      } else {
-        i32x8 bf;
-        int sb = 127;
-        if (kFP4) {
-          const i32x4 v = *reinterpret_cast<const i32x4*>(st + kABytes + bb * 1024 + lane * 16);
-          const i32x4 z = {0, 0, 0, 0};
-          bf = __builtin_shufflevector(v, z, 0, 1, 2, 3, 4, 5, 6, 7);
-          sb = st[kSOff + 512 + (16 * bb + l16) * 4 + g];
+      }
+      return;
+    }
+    // promotion factors of this step: activation scale of the row times the
+    // weight scale of the half (kTrans: the lane's row in each 16-row block;
+    // else its 4 rows 4 g + i)
+    constexpr int kSR = kTrans ? 1 : 4;
+    float sc[2][kMT][kSR];
+    {
+      const float* ss = reinterpret_cast<const float*>(st + kSOff);
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        if (kTrans) {
+          const float v = ss[16 * kMT * wm + 16 * mt + l16];
+          sc[0][mt][0] = v * sw_lo;
+          sc[1][mt][0] = v * sw_hi;
         } else {
-          const uint8_t* bp = st + kABytes + bb * 2048;
-          const i32x4 lo4 = *reinterpret_cast<const i32x4*>(bp + f_lo);
-          const i32x4 hi4 = *reinterpret_cast<const i32x4*>(bp + f_hi);
-          bf = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+          const f32x4 v = *reinterpret_cast<const f32x4*>(ss + 16 * kMT * wm + 16 * mt + 4 * g);
+#pragma unroll
+          for (int i = 0; i < kSR; ++i) {
+            sc[0][mt][i] = v[i] * sw_lo;
+            sc[1][mt][i] = v[i] * sw_hi;
+          }
         }
-        const int half_sel = (kPaired && j >= kNJ / 2) ? 1 : 0;
+      }
+    }
+    // weight fragments of the step (FP4: with their e8m0 scales)
+    auto load_b = [&](int j, i32x8& bfj, int& sbj) {
+      const int bb = bblk(j);
+      if (kFP4) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(st + kABytes + bb * 1024 + lane * 16);
+        const i32x4 z = {0, 0, 0, 0};
+        bfj = __builtin_shufflevector(v, z, 0, 1, 2, 3, 4, 5, 6, 7);
+        sbj = st[kSOff + 512 + (16 * bb + l16) * 4 + g];
+      } else {
+        const uint8_t* bp = st + kABytes + bb * 2048;
+        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(bp + f_lo);
+        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(bp + f_hi);
+        bfj = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        sbj = 127;
+      }
+    };
+    if (kTrans) {
+      // kNJ groups of kMT block products; group j - 1 is promoted (FP32
+      // multiply-add of the block product into the accumulator) after group
+      // j has gone to the matrix cores, so the multiply-adds find their
+      // products done
+      i32x8 bf[kNJ];
+      int sb[kNJ];
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j) load_b(j, bf[j], sb[j]);
+      f32x4 pr[2][kMT];
+#pragma unroll
+      for (int j = 0; j <= kNJ; ++j) {
+        if (j < kNJ) {
+#pragma unroll
+          for (int mt = 0; mt < kMT; ++mt)
+            pr[j & 1][mt] = kFP4 ? mfma_fp4_fp8(bf[j], sb[j], af[mt]) : mfma_fp8(bf[j], af[mt]);
+        }
+        if (j > 0) {
+          const int jp = j - 1;
+          const int hsel = (kPaired && jp >= kNJ / 2) ? 1 : 0;
+#pragma unroll
+          for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][jp][i] += pr[jp & 1][mt][i] * sc[hsel][mt][0];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j) {
+        i32x8 bf;
+        int sb;
+        load_b(j, bf, sb);
+        const int hsel = (kPaired && j >= kNJ / 2) ? 1 : 0;
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
           const f32x4 pr = kFP4 ? mfma_fp8_fp4(af[mt], bf, sb) : mfma_fp8(af[mt], bf);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][j][i] += pr[i] * sc[half_sel][mt][i];
+          for (int i = 0; i < 4; ++i) acc[mt][j][i] += pr[i] * sc[hsel][mt][kTrans ? 0 : i];
         }
       }
     }
   };
 
   // ---------------------------------------------------------------- epilogues
-  // Wave (wm, wn) holds rows 16 kMT wm + 16 mt + 4 g + i and, of the tile's
-  // 256 B rows, its kNJ 16-row blocks bblk(j).
+  // Wave (wm, wn) holds, of the tile's 256 B rows, the kNJ 16-column blocks
+  // bblk(j); lane (l16, g) holds rows 16 kMT wm + 16 mt + l16, columns
+  // 4 g + i of each block (L1), or rows 16 kMT wm + 16 mt + 4 g + i, column
+  // l16 (the others).
   auto epilogue = [&](const Desc& d, uint8_t* sq) {
     if (KIND == TK_L1) {
       // h = silu(gate) * up: the wave's kH 16-column blocks of h; row amax
-      // over the tile's 128 h columns (all kWavesN waves of the row)
+      // over the tile's 128 h columns (the 4 lane groups of the row, then
+      // all kWavesN waves of the row)
       constexpr int kH = kNJ / 2;
       float h[kMT][kH][4];
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
+      for (int mt = 0; mt < kMT; ++mt) {
+        float m = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float m = 0.0f;
+        for (int j = 0; j < kH; ++j)
 #pragma unroll
-          for (int j = 0; j < kH; ++j) {
+          for (int i = 0; i < 4; ++i) {
             h[mt][j][i] = silu_mul_fast(acc[mt][j][i], acc[mt][kH + j][i]);
             m = fmaxf(m, fabsf(h[mt][j][i]));
           }
-          m = group16_max(m);
-          if (l16 == 0) s_amax[wn][16 * kMT * wm + 16 * mt + 4 * g + i] = m;
-        }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (g == 0) s_amax[wn][16 * kMT * wm + 16 * mt + l16] = m;
+      }
       lds_barrier();  // s_amax complete; every wave is done with the stage in sq
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
+      for (int mt = 0; mt < kMT; ++mt) {
+        const int r = 16 * kMT * wm + 16 * mt + l16;
+        float amax = s_amax[0][r];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * kMT * wm + 16 * mt + 4 * g + i;
-          float amax = s_amax[0][r];
+        for (int w = 1; w < kWavesN; ++w) amax = fmaxf(amax, s_amax[w][r]);
+        const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+        const float inv = 1.0f / s;
 #pragma unroll
-          for (int w = 1; w < kWavesN; ++w) amax = fmaxf(amax, s_amax[w][r]);
-          const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
-          const float inv = 1.0f / s;
+        for (int j = 0; j < kH; ++j) {
+          uint32_t q4 = 0;
 #pragma unroll
-          for (int j = 0; j < kH; ++j)
-            sq[r * 128 + 16 * (kH * wn + j) + l16] = static_cast<uint8_t>(f32_to_e4m3(h[mt][j][i] * inv));
-          if (wn == 0 && l16 == 0 && r < d.rows) p.sh[static_cast<size_t>(d.row0 + r) * (p.half / 128) + d.nt] = s;
+          for (int i = 0; i < 4; ++i) q4 |= static_cast<uint32_t>(f32_to_e4m3(h[mt][j][i] * inv)) << (8 * i);
+          *reinterpret_cast<uint32_t*>(sq + r * 128 + 16 * (kH * wn + j) + 4 * g) = q4;
         }
+        if (wn == 0 && g == 0 && r < d.rows) p.sh[static_cast<size_t>(d.row0 + r) * (p.half / 128) + d.nt] = s;
+      }
       lds_barrier();
 #pragma unroll
       for (int i = 0; i < (TM * 8 + 511) / 512; ++i) {
@@ -472,26 +533,33 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   Iss is = make_iss(dc, 0);
   int ji = 0;  // tile of `is`
   const int G = n_my * nk;
-  auto issue_stage = [&](int g2) {
-    const int j2 = g2 / nk, k2 = g2 - j2 * nk;
-    uint8_t* st = ring + (g2 % kStages) * kStage;
-    if (j2 >= n_my) {
+  // the stream position the next issue loads: tile ij, K step ik, ring slot
+  // islot (counters instead of divisions by nk: they run every step)
+  int ij = 0, ik = 0, islot = 0;
+  auto issue_next = [&]() {
+    uint8_t* st = ring + islot * kStage;
+    if (ij >= n_my) {
       issue(st, is, 0, false);
-      return;
+    } else {
+      if (ik == 0 && ij != ji) {
+        is = make_iss(desc(ij), ij % 3);
+        ji = ij;
+      }
+      if (ik == 0 && ij + 1 < n_my) aux(desc(ij + 1), (ij + 1) % 3);
+      issue(st, is, ik, true);
     }
-    if (k2 == 0 && j2 != ji) {
-      is = make_iss(desc(j2), j2 % 3);
-      ji = j2;
+    if (++ik == nk) {
+      ik = 0;
+      ++ij;
     }
-    if (k2 == 0 && j2 + 1 < n_my) aux(desc(j2 + 1), (j2 + 1) % 3);
-    issue(st, is, k2, true);
+    if (++islot == kStages) islot = 0;
   };
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue_stage(s);
+  for (int s = 0; s < kStages - 1; ++s) issue_next();
+  int j = 0, ks = 0, jb = 0, cslot = 0;  // the computed stage: tile j (buffer jb = j % 3), K step ks, slot
   for (int gg = 0; gg < G; ++gg) {
-    const int j = gg / nk, ks = gg - j * nk;
     ring_barrier<kLoads * (kStages - 2)>();
-    issue_stage(gg + kStages - 1);
+    issue_next();
     if (ks == 0) {
       if (j > 0) dc = desc(j);
 #pragma unroll
@@ -499,9 +567,15 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
 #pragma unroll
         for (int jj = 0; jj < kNJ; ++jj) acc[mt][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    uint8_t* st = ring + (gg % kStages) * kStage;
-    compute(st, ks, j % 3);
+    uint8_t* st = ring + cslot * kStage;
+    compute(st, ks, jb);
     if (ks == nk - 1) epilogue(dc, st);
+    if (++ks == nk) {
+      ks = 0;
+      ++j;
+      if (++jb == 3) jb = 0;
+    }
+    if (++cslot == kStages) cslot = 0;
   }
   // drain the trailing (empty) loads
   ring_barrier<0>();
