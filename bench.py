@@ -28,7 +28,7 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per launch of the routed L1 kernel from FETCH_SIZE and WRITE_SIZE
 # counter runs, scaled by the same counters' reading of a copy kernel of known
 # size (profiles/decode_routed_traffic.md); taken on the current kernels.
-MEASURED_L1_TRAFFIC = {"decode": 945.8e6}
+MEASURED_L1_TRAFFIC = {"decode": 945.7e6}
 FP8_PEAK_TFLOPS = 5000.0
 MXFP4_PEAK_TFLOPS = 10100.0
 STAGES = ["quant_x", "routed_l1", "routed_l2", "combine_rmsnorm", "shared_l1", "shared_l2", "up_proj_add"]

@@ -454,7 +454,9 @@ int moe_tail_route(const moe_tail_dims* dims, const moe_tail_weights* w, const u
                                                                                  : k_router_topk<kMaxExpertsPerLane>;
     hipLaunchKernelGGL(topk, dim3((Mr + 3) / 4), dim3(256), 0, st, logits, out->topk_ids, out->topk_weights, Mr, E, k);
   }
-  if (static_cast<int64_t>(ng) * E <= kSortSmall) {
+  // one workgroup for the whole permutation while it is short (it walks the
+  // token groups one wave at a time); three grid-wide passes beyond that
+  if (static_cast<int64_t>(ng) * E <= kSortSmall && ng <= kSortSmallGroups) {
     hipLaunchKernelGGL(k_router_sort, dim3(1), dim3(1024), 0, st, out->topk_ids, out->expert_offsets,
                        out->sorted_pair, out->pair_to_row, Mr, E, k, ng);
     return launched();

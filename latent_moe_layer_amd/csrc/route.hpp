@@ -286,6 +286,7 @@ __global__ __launch_bounds__(64) void k_router_scatter(const int32_t* __restrict
 // scatter) in one workgroup of 1024 threads, for up to kSortSmall (group,
 // expert) cells; the same rows result.
 constexpr int kSortSmall = 4096;
+constexpr int kSortSmallGroups = 24;  // token groups of 64 (beyond: the grid-wide passes are faster)
 
 __global__ __launch_bounds__(1024) void k_router_sort(const int32_t* __restrict__ topk_ids,
                                                       int32_t* __restrict__ expert_offsets,

@@ -129,7 +129,7 @@ def test_quantizer_bit_exact():
 
 @pytest.mark.parametrize("E,k,Mr,zipf", [(8, 2, 16, 0.0), (64, 8, 128, 0.0), (64, 8, 4096, 0.0), (128, 8, 1024, 1.2),
                                          (384, 8, 2048, 0.0), (1024, 16, 200, 0.0), (5, 5, 70, 0.0), (9, 3, 1, 0.0),
-                                         (16, 4, 130, 0.0)])
+                                         (16, 4, 130, 0.0), (64, 8, 530, 0.0), (32, 4, 1600, 0.0)])
 def test_route_bit_exact(E, k, Mr, zipf):
     wl = synth.Workload("r", Mr=Mr, Ms=Mr, E=E, k=k, I=128, Is=128, wfmt=0, seed=100 + E, zipf_s=zipf)
     inp = synth.make_inputs(wl, routing_only=True)
