@@ -212,8 +212,14 @@ void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int 
   a.N = N;
   a.half = ep.half;
   a.ntn = (kEpi == EPI_SWIGLU) ? ep.half / 128 : N / kTN;
-  a.nslots = (M + kTM - 1) / kTM;
-  launch_tile<TK_DENSE, TF_BF16, kEpi>(a, st);
+  if (static_cast<unsigned>((M + kHugeTM - 1) / kHugeTM) * static_cast<unsigned>(a.ntn) >= num_cus()) {
+    // 256-row tiles once they alone fill the chip
+    a.nslots = (M + kHugeTM - 1) / kHugeTM;
+    launch_tile<TK_DENSE, TF_BF16, kEpi, kHugeTM>(a, st);
+  } else {
+    a.nslots = (M + kTM - 1) / kTM;
+    launch_tile<TK_DENSE, TF_BF16, kEpi>(a, st);
+  }
 }
 
 int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
@@ -284,9 +290,11 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   ta.E = E;
   ta.k = k;
   ta.big_rows = big ? kBigMinRows : 0x7fffffff;
+  ta.huge_rows = big ? kHugeTM : 0x7fffffff;
   // bounds on the row tiles, which size the grids: ceil(c / 128) <= c / 64
   // for c >= 128, and ceil(c / 32) <= c / 32 + 1
   const int slots_big = static_cast<int>(R / (kTM / 2));
+  const int slots_huge = static_cast<int>(R / (kHugeTM / 2));  // ceil(c / 256) <= c / 128 for c >= 256
   const int slots_small = static_cast<int>(R / 32 + E);
   mark(1);
   if (Mr > 0) {
@@ -319,6 +327,9 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
         a1.nslots = slots_big;
         if (fp8) launch_tile<TK_L1, TF_FP8, 0>(a1, st);
         else launch_tile<TK_L1, TF_FP4, 0>(a1, st);
+        a1.nslots = slots_huge;
+        if (fp8) launch_tile<TK_L1, TF_FP8, 0, kHugeTM>(a1, st);
+        else launch_tile<TK_L1, TF_FP4, 0, kHugeTM>(a1, st);
       }
     }
   }
@@ -349,6 +360,9 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
         a2.nslots = slots_big;
         if (fp8) launch_tile<TK_L2, TF_FP8, 0>(a2, st);
         else launch_tile<TK_L2, TF_FP4, 0>(a2, st);
+        a2.nslots = slots_huge;
+        if (fp8) launch_tile<TK_L2, TF_FP8, 0, kHugeTM>(a2, st);
+        else launch_tile<TK_L2, TF_FP4, 0, kHugeTM>(a2, st);
       }
     }
   }

@@ -2,12 +2,12 @@
 // L1 / L2 (FP8 or FP8 x MXFP4, block-scaled) and the dense BF16 GEMMs of the
 // shared expert and the up-projection.
 //
-// Tile: kTM = 128 rows x kTN = 256 B rows, one 128-byte K step per stage (128
-// FP8 / FP4 elements or 64 BF16 elements), 8 waves as 2 (M) x 4 (N), each
-// wave 64 rows x 64 B rows = 4 x 4 MFMA tiles of 16 x 16 (64 accumulator
-// registers, which leaves room for the FP32 promotion without spilling).
-// Both operands go straight from memory to LDS (buffer loads with the LDS
-// flag) into a three-stage ring, two stages in flight.  Every load fetches
+// Tile: TM = 256, 128 or 32 rows x kTN = 256 B rows, one 128-byte K step per
+// stage (128 FP8 / FP4 elements or 64 BF16 elements), 8 waves as 2 (M) x 4
+// (N), each wave 128 or 64 rows x 64 B rows (8 or 4 x 4 MFMA tiles of
+// 16 x 16), or for 32-row tiles 8 waves of 32 x 32.  Both operands go
+// straight from memory to LDS (buffer loads with the LDS flag) into a ring of
+// two (256 rows), three (128) or four (32) stages.  Every load fetches
 // whole 128-byte lines; a row's 16-byte chunks are stored XOR-swizzled so
 // that the MFMA operand reads are free of bank conflicts.  (8-bit operand:
 // lane group g holds K [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16) of the
@@ -30,6 +30,14 @@ namespace moe_tail {
 constexpr int kTM = 128;
 constexpr int kTN = 256;
 constexpr int kBigMinRows = 128;  // experts with at least this many rows use 128-row tiles (by default)
+constexpr int kHugeTM = 256;      // ... and from this many rows on, 256-row tiles where they pay
+
+// An expert with c >= huge rows takes 256-row tiles even when its last tile
+// is mostly padding: at the prefill loads (450-590 rows per expert) that
+// measured faster than switching such experts to 128-row tiles (routed L1
+// 699 against 752 us), the padded rows costing less than a second launch's
+// tail.
+__host__ __device__ __forceinline__ bool use256(int c, int huge) { return c >= huge; }
 constexpr int kTileMaxE = 512;    // expert tables of the routed kinds live in LDS
 
 enum { TK_L1 = 0, TK_L2 = 1, TK_DENSE = 2 };
@@ -54,6 +62,7 @@ struct TileArgs {
   int ntn;                        // n tiles
   int nslots;                     // dense: row tiles; routed: unused (the tile count comes from expert_offsets)
   int big_rows;                   // routed: experts with >= big_rows rows take 128-row tiles, the others 32-row tiles
+  int huge_rows;                  // routed: experts with >= huge_rows rows take 256-row tiles instead
 };
 
 // Persistent: one workgroup per CU works through a list of tiles.  Tile t
@@ -64,10 +73,13 @@ struct TileArgs {
 // weights, in that XCD's L2).  The K steps of all of a workgroup's tiles form
 // one stream through the three-stage ring: the first stages of the next tile
 // are loaded while the current one finishes and while its epilogue runs.
-// TM = 128: tiles of 128 rows (experts with at least big_rows rows, and
-// the dense GEMMs), 8 waves as 2 (M) x 4 (N) of 64 x 64.  TM = 32: tiles of
-// 32 rows for the experts with fewer rows (decode sizes), 8 waves of 32 x 32,
-// a deeper ring.  Either way 256 B rows (weight rows) per tile.
+// TM = 256: tiles of 256 rows (experts with at least huge_rows rows, the
+// dense GEMMs with many rows): a quarter less LDS and L2 traffic per FLOP
+// than 128 rows and half the barriers, one stage in flight.  TM = 128:
+// experts with big_rows .. huge_rows - 1 rows, 8 waves as 2 (M) x 4 (N) of
+// 64 x 64.  TM = 32: tiles of 32 rows for the experts with fewer rows (decode
+// sizes), 8 waves of 32 x 32, a deeper ring.  Either way 256 B rows (weight
+// rows) per tile.
 template <int KIND, int FMT, int EPI, int TM = kTM>
 __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   constexpr bool kFP4 = FMT == TF_FP4;
@@ -75,17 +87,23 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   constexpr bool kScaled = !kBF16;
   constexpr bool kRouted = KIND != TK_DENSE;
   constexpr bool kPaired = KIND == TK_L1 || (KIND == TK_DENSE && EPI == EPI_SWIGLU);
-  static_assert(TM == 128 || (TM == 32 && KIND != TK_DENSE), "tile rows");
-  constexpr int kWavesM = (TM == 128) ? 2 : 1;       // wave grid over the tile
+  static_assert(TM == 256 || TM == 128 || (TM == 32 && KIND != TK_DENSE), "tile rows");
+  constexpr int kWavesM = (TM == 32) ? 1 : 2;        // wave grid over the tile
   constexpr int kWavesN = 8 / kWavesM;
   constexpr int kMT = TM / (16 * kWavesM);           // 16-row MFMA tiles per wave
   constexpr int kNJ = kTN / (16 * kWavesN);          // 16-column MFMA tiles per wave
-  constexpr int kStages = (TM == 128) ? 3 : 4;       // ring depth (kStages - 1 steps in flight)
+  constexpr int kStages = (TM == 256) ? 2 : (TM == 128) ? 3 : 4;  // ring depth (kStages - 1 steps in flight)
   constexpr int kABlk = TM / 8;                      // 1 KB blocks of A per stage
   constexpr int kAL = (kABlk + 7) / 8;               // A blocks loaded per wave
-  constexpr int kABytes = TM * 128;                  // 16 or 4 KB
+  constexpr int kABytes = TM * 128;                  // 32, 16 or 4 KB
   constexpr int kBBytes = kTN * (kFP4 ? 64 : 128);   // 16 or 32 KB
-  constexpr int kSOff = kABytes + kBBytes;           // scale words: activation [0, 512), FP4 e8m0 [512, 1536)
+  // scale words of a stage (2 KB, 256 bytes per wave): activation scales
+  // (one word per row) loaded by waves 0 .. kActW - 1, FP4 e8m0 words (four
+  // per B row) by the next four; the other waves load zeros into their part
+  constexpr int kActW = (TM + 63) / 64 < 2 ? 2 : (TM + 63) / 64;
+  constexpr int kSOff = kABytes + kBBytes;           // activation [0, 4 TM), FP4 e8m0 [kE8Off, + 1024)
+  constexpr int kE8Off = 256 * kActW;
+  static_assert(kE8Off + 1024 <= 2048, "scale words");
   constexpr int kStage = kSOff + (kScaled ? 2048 : 0);
   constexpr int kBChunks = kFP4 ? 2 : 4;             // 16-byte B loads per thread and stage
   constexpr int kLoads = kAL + kBChunks + (kScaled ? 1 : 0);  // direct loads per wave and stage
@@ -97,6 +115,9 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   // computes and read until tile j's last step
   constexpr int kPairRows = (TM < 64) ? 64 : TM;       // one 64-lane load per 64 rows
   __shared__ int s_pair[3][kPairRows];                 // L1: sorted pair ids of a tile's rows
+  // aux loads of the next tile: pair ids by waves 0 .. kPairRows / 64 - 1 (L1),
+  // the two weight-scale rows (FP8) by waves kWscW and kWscW + 1
+  constexpr int kWscW = (kPairRows / 64 < 2) ? 2 : kPairRows / 64;
   __shared__ float s_wsc[3][2][kMaxKBlocks];           // FP8: weight scales of a tile's two 128-row B halves
   __shared__ float s_amax[kWavesN][TM];
 
@@ -118,13 +139,15 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
     for (int i = tid; i <= p.E; i += 512) s_eoff[i] = p.expert_offsets[i];
     __syncthreads();
     if (wave == 0) {
-      // exclusive prefix over the experts of their row tiles (TM = 128: the
-      // experts with at least big_rows rows; TM = 32: the others)
+      // exclusive prefix over the experts of their row tiles (TM = 256: the
+      // experts with at least huge_rows rows; TM = 128: big_rows ..
+      // huge_rows - 1; TM = 32: the others)
       const int per = (p.E + 63) / 64;
       const int eb = min(lane * per, p.E), ee = min(eb + per, p.E);
       auto ntile = [&](int e) {
         const int c = s_eoff[e + 1] - s_eoff[e];
-        if (TM == 128) return c >= p.big_rows ? (c + TM - 1) / TM : 0;
+        if (TM == 256) return use256(c, p.huge_rows) ? (c + TM - 1) / TM : 0;
+        if (TM == 128) return (c >= p.big_rows && !use256(c, p.huge_rows)) ? (c + TM - 1) / TM : 0;
         return c < p.big_rows ? (c + TM - 1) / TM : 0;
       };
       int local = 0;
@@ -237,8 +260,9 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
       r.b_off[i] = static_cast<uint32_t>(static_cast<size_t>(wrow(d.nt, row)) * brow_bytes) + 16u * c;
     }
     // scale words, one 4-byte load per lane and stage: waves 0-1 the
-    // activation scales of tile rows 64 w + lane, waves 2-5 (FP4) the e8m0
-    // words of B rows 64 (w - 2) + lane; the other waves load zeros
+    // activation scales of tile rows 64 w + lane (w < kActW), waves kActW ..
+    // kActW + 3 (FP4) the e8m0 words of B rows 64 (w - kActW) + lane; the
+    // other waves load zeros
     r.rs = z_rsrc;
     r.s_off = kNoRow;
     if (kScaled) {
@@ -251,8 +275,8 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
           const size_t ar = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
           r.s_off = static_cast<uint32_t>(ar * nkb * 4);
         }
-      } else if (kFP4 && wv >= 2 && wv < 6) {
-        const int j = 64 * (wv - 2) + lane;
+      } else if (kFP4 && wv >= kActW && wv < kActW + 4) {
+        const int j = 64 * (wv - kActW) + lane;
         r.rs = make_rsrc(static_cast<const uint8_t*>(p.b_scale) + static_cast<size_t>(d.e) * nbrows * wpr,
                          static_cast<uint32_t>(nbrows * wpr));
         r.s_off = static_cast<uint32_t>(wrow(d.nt, j) * wpr);
@@ -271,13 +295,13 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   };
   // per-tile data loaded ahead (issued first in a stage's batch, only by the
   // waves that carry it): L1 sorted pair ids (one wave per 64 rows), FP8 weight-scale
-  // rows (waves 2-3)
+  // rows (waves kWscW, kWscW + 1)
   auto aux = [&](const Desc& d, int buf) {
     if (KIND == TK_L1 && wv < kPairRows / 64) {
       dma4(make_rsrc(p.sorted_pair + d.row0, static_cast<uint32_t>(d.rows) * 4u), reinterpret_cast<uint8_t*>(&s_pair[buf][64 * wv]),
            4u * (64 * wv + lane), 0);
-    } else if (FMT == TF_FP8 && (wv == 2 || wv == 3)) {
-      const int q = wv - 2;
+    } else if (FMT == TF_FP8 && (wv == kWscW || wv == kWscW + 1)) {
+      const int q = wv - kWscW;
       const int wr = wrow(d.nt, 128 * q);
       const float* src = static_cast<const float*>(p.b_scale) +
                          (static_cast<size_t>(d.e) * (nbrows / 128) + wr / 128) * nkb;
@@ -317,53 +341,6 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
       sw_lo = s_wsc[buf][(16 * bblk(0)) / 128][ks];
       sw_hi = s_wsc[buf][(16 * bblk(kNJ - 1)) / 128][ks];
     }
-    i32x8 af[kMT];
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-      const uint8_t* ab = st + (kMT * wm + mt) * 2048;
-      const i32x4 lo4 = *reinterpret_cast<const i32x4*>(ab + f_lo);
-      const i32x4 hi4 = *reinterpret_cast<const i32x4*>(ab + f_hi);
-      af[mt] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-    if (kBF16) {
-#pragma unroll
-      for (int j = 0; j < kNJ; ++j) {
-        const uint8_t* bp = st + kABytes + bblk(j) * 2048;
-        const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_lo));
-        const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_hi));
-#pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) {
-          const i32x4 alo = __builtin_shufflevector(af[mt], af[mt], 0, 1, 2, 3);
-          const i32x4 ahi = __builtin_shufflevector(af[mt], af[mt], 4, 5, 6, 7);
-          acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, alo), b0, acc[mt][j]);
-          acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, ahi), b1, acc[mt][j]);
-        }
-      }
-      return;
-    }
-    // promotion factors of this step: activation scale of the row times the
-    // weight scale of the half (kTrans: the lane's row in each 16-row block;
-    // else its 4 rows 4 g + i)
-    constexpr int kSR = kTrans ? 1 : 4;
-    float sc[2][kMT][kSR];
-    {
-      const float* ss = reinterpret_cast<const float*>(st + kSOff);
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        if (kTrans) {
-          const float v = ss[16 * kMT * wm + 16 * mt + l16];
-          sc[0][mt][0] = v * sw_lo;
-          sc[1][mt][0] = v * sw_hi;
-        } else {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(ss + 16 * kMT * wm + 16 * mt + 4 * g);
-#pragma unroll
-          for (int i = 0; i < kSR; ++i) {
-            sc[0][mt][i] = v[i] * sw_lo;
-            sc[1][mt][i] = v[i] * sw_hi;
-          }
-        }
-      }
-    }
     // weight fragments of the step (FP4: with their e8m0 scales)
     auto load_b = [&](int j, i32x8& bfj, int& sbj) {
       const int bb = bblk(j);
@@ -371,7 +348,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
         const i32x4 v = *reinterpret_cast<const i32x4*>(st + kABytes + bb * 1024 + lane * 16);
         const i32x4 z = {0, 0, 0, 0};
         bfj = __builtin_shufflevector(v, z, 0, 1, 2, 3, 4, 5, 6, 7);
-        sbj = st[kSOff + 512 + (16 * bb + l16) * 4 + g];
+        sbj = st[kSOff + kE8Off + (16 * bb + l16) * 4 + g];
       } else {
         const uint8_t* bp = st + kABytes + bb * 2048;
         const i32x4 lo4 = *reinterpret_cast<const i32x4*>(bp + f_lo);
@@ -380,44 +357,169 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
         sbj = 127;
       }
     };
-    if (kTrans) {
-      // kNJ groups of kMT block products; group j - 1 is promoted (FP32
-      // multiply-add of the block product into the accumulator) after group
-      // j has gone to the matrix cores, so the multiply-adds find their
-      // products done
+    // this lane's activation fragment of row block mt
+    auto load_a = [&](int mt) -> i32x8 {
+      const uint8_t* ab = st + (kMT * wm + mt) * 2048;
+      const i32x4 lo4 = *reinterpret_cast<const i32x4*>(ab + f_lo);
+      const i32x4 hi4 = *reinterpret_cast<const i32x4*>(ab + f_hi);
+      return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    if constexpr (kMT > 4) {
+      // 256-row tiles: 8 row blocks per wave and 128 accumulator registers,
+      // so the weight fragments are loaded once per step and the activation
+      // fragments one row block at a time
+      if (kBF16) {
+        bf16x8 b0[kNJ], b1[kNJ];
+#pragma unroll
+        for (int j = 0; j < kNJ; ++j) {
+          const uint8_t* bp = st + kABytes + bblk(j) * 2048;
+          b0[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_lo));
+          b1[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_hi));
+        }
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+          const i32x8 a8 = load_a(mt);
+          const i32x4 alo = __builtin_shufflevector(a8, a8, 0, 1, 2, 3);
+          const i32x4 ahi = __builtin_shufflevector(a8, a8, 4, 5, 6, 7);
+#pragma unroll
+          for (int j = 0; j < kNJ; ++j) {
+            acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, alo), b0[j], acc[mt][j]);
+            acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, ahi), b1[j], acc[mt][j]);
+          }
+        }
+        return;
+      }
       i32x8 bf[kNJ];
       int sb[kNJ];
 #pragma unroll
       for (int j = 0; j < kNJ; ++j) load_b(j, bf[j], sb[j]);
-      f32x4 pr[2][kMT];
+      const float* ss = reinterpret_cast<const float*>(st + kSOff);
+      if (kTrans) {
+        // row block mt - 1 is promoted after row block mt's products are
+        // issued
+        f32x4 pr[2][kNJ];
 #pragma unroll
-      for (int j = 0; j <= kNJ; ++j) {
-        if (j < kNJ) {
+        for (int mt = 0; mt <= kMT; ++mt) {
+          if (mt < kMT) {
+            const i32x8 a8 = load_a(mt);
 #pragma unroll
-          for (int mt = 0; mt < kMT; ++mt)
-            pr[j & 1][mt] = kFP4 ? mfma_fp4_fp8(bf[j], sb[j], af[mt]) : mfma_fp8(bf[j], af[mt]);
+            for (int j = 0; j < kNJ; ++j)
+              pr[mt & 1][j] = kFP4 ? mfma_fp4_fp8(bf[j], sb[j], a8) : mfma_fp8(bf[j], a8);
+          }
+          if (mt > 0) {
+            const int mp = mt - 1;
+            const float v = ss[16 * kMT * wm + 16 * mp + l16];
+            const float s_lo = v * sw_lo, s_hi = v * sw_hi;
+#pragma unroll
+            for (int j = 0; j < kNJ; ++j) {
+              const float f = (kPaired && j >= kNJ / 2) ? s_hi : s_lo;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[mp][j][i] += pr[mp & 1][j][i] * f;
+            }
+          }
         }
-        if (j > 0) {
-          const int jp = j - 1;
-          const int hsel = (kPaired && jp >= kNJ / 2) ? 1 : 0;
-#pragma unroll
-          for (int mt = 0; mt < kMT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mt][jp][i] += pr[jp & 1][mt][i] * sc[hsel][mt][0];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kNJ; ++j) {
-        i32x8 bf;
-        int sb;
-        load_b(j, bf, sb);
-        const int hsel = (kPaired && j >= kNJ / 2) ? 1 : 0;
+      } else {
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
-          const f32x4 pr = kFP4 ? mfma_fp8_fp4(af[mt], bf, sb) : mfma_fp8(af[mt], bf);
+          const i32x8 a8 = load_a(mt);
+          const f32x4 v = *reinterpret_cast<const f32x4*>(ss + 16 * kMT * wm + 16 * mt + 4 * g);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][j][i] += pr[i] * sc[hsel][mt][kTrans ? 0 : i];
+          for (int j = 0; j < kNJ; ++j) {
+            const float sw = (kPaired && j >= kNJ / 2) ? sw_hi : sw_lo;
+            const f32x4 pr = kFP4 ? mfma_fp8_fp4(a8, bf[j], sb[j]) : mfma_fp8(a8, bf[j]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][j][i] += pr[i] * (v[i] * sw);
+          }
+        }
+      }
+      return;
+    } else {
+      i32x8 af[kMT];
+  #pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) {
+        const uint8_t* ab = st + (kMT * wm + mt) * 2048;
+        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(ab + f_lo);
+        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(ab + f_hi);
+        af[mt] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      if (kBF16) {
+  #pragma unroll
+        for (int j = 0; j < kNJ; ++j) {
+          const uint8_t* bp = st + kABytes + bblk(j) * 2048;
+          const bf16x8 b0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_lo));
+          const bf16x8 b1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_hi));
+  #pragma unroll
+          for (int mt = 0; mt < kMT; ++mt) {
+            const i32x4 alo = __builtin_shufflevector(af[mt], af[mt], 0, 1, 2, 3);
+            const i32x4 ahi = __builtin_shufflevector(af[mt], af[mt], 4, 5, 6, 7);
+            acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, alo), b0, acc[mt][j]);
+            acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, ahi), b1, acc[mt][j]);
+          }
+        }
+        return;
+      }
+      // promotion factors of this step: activation scale of the row times the
+      // weight scale of the half (kTrans: the lane's row in each 16-row block;
+      // else its 4 rows 4 g + i)
+      constexpr int kSR = kTrans ? 1 : 4;
+      float sc[2][kMT][kSR];
+      {
+        const float* ss = reinterpret_cast<const float*>(st + kSOff);
+  #pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+          if (kTrans) {
+            const float v = ss[16 * kMT * wm + 16 * mt + l16];
+            sc[0][mt][0] = v * sw_lo;
+            sc[1][mt][0] = v * sw_hi;
+          } else {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(ss + 16 * kMT * wm + 16 * mt + 4 * g);
+  #pragma unroll
+            for (int i = 0; i < kSR; ++i) {
+              sc[0][mt][i] = v[i] * sw_lo;
+              sc[1][mt][i] = v[i] * sw_hi;
+            }
+          }
+        }
+      }
+      if (kTrans) {
+        // kNJ groups of kMT block products; group j - 1 is promoted (FP32
+        // multiply-add of the block product into the accumulator) after group
+        // j has gone to the matrix cores, so the multiply-adds find their
+        // products done
+        i32x8 bf[kNJ];
+        int sb[kNJ];
+  #pragma unroll
+        for (int j = 0; j < kNJ; ++j) load_b(j, bf[j], sb[j]);
+        f32x4 pr[2][kMT];
+  #pragma unroll
+        for (int j = 0; j <= kNJ; ++j) {
+          if (j < kNJ) {
+  #pragma unroll
+            for (int mt = 0; mt < kMT; ++mt)
+              pr[j & 1][mt] = kFP4 ? mfma_fp4_fp8(bf[j], sb[j], af[mt]) : mfma_fp8(bf[j], af[mt]);
+          }
+          if (j > 0) {
+            const int jp = j - 1;
+            const int hsel = (kPaired && jp >= kNJ / 2) ? 1 : 0;
+  #pragma unroll
+            for (int mt = 0; mt < kMT; ++mt)
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) acc[mt][jp][i] += pr[jp & 1][mt][i] * sc[hsel][mt][0];
+          }
+        }
+      } else {
+  #pragma unroll
+        for (int j = 0; j < kNJ; ++j) {
+          i32x8 bf;
+          int sb;
+          load_b(j, bf, sb);
+          const int hsel = (kPaired && j >= kNJ / 2) ? 1 : 0;
+  #pragma unroll
+          for (int mt = 0; mt < kMT; ++mt) {
+            const f32x4 pr = kFP4 ? mfma_fp8_fp4(af[mt], bf, sb) : mfma_fp8(af[mt], bf);
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][j][i] += pr[i] * sc[hsel][mt][kTrans ? 0 : i];
+          }
         }
       }
     }
@@ -432,19 +534,17 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
     if (KIND == TK_L1) {
       // h = silu(gate) * up: the wave's kH 16-column blocks of h; row amax
       // over the tile's 128 h columns (the 4 lane groups of the row, then
-      // all kWavesN waves of the row)
+      // all kWavesN waves of the row).  h is computed twice, for the amax and
+      // then for the codes (the same arithmetic, so the same values), rather
+      // than held in registers beside the accumulators.
       constexpr int kH = kNJ / 2;
-      float h[kMT][kH][4];
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
         float m = 0.0f;
 #pragma unroll
         for (int j = 0; j < kH; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            h[mt][j][i] = silu_mul_fast(acc[mt][j][i], acc[mt][kH + j][i]);
-            m = fmaxf(m, fabsf(h[mt][j][i]));
-          }
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(silu_mul_fast(acc[mt][j][i], acc[mt][kH + j][i])));
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
         if (g == 0) s_amax[wn][16 * kMT * wm + 16 * mt + l16] = m;
@@ -462,7 +562,8 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
         for (int j = 0; j < kH; ++j) {
           uint32_t q4 = 0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) q4 |= static_cast<uint32_t>(f32_to_e4m3(h[mt][j][i] * inv)) << (8 * i);
+          for (int i = 0; i < 4; ++i)
+            q4 |= static_cast<uint32_t>(f32_to_e4m3(silu_mul_fast(acc[mt][j][i], acc[mt][kH + j][i]) * inv)) << (8 * i);
           *reinterpret_cast<uint32_t*>(sq + r * 128 + 16 * (kH * wn + j) + 4 * g) = q4;
         }
         if (wn == 0 && g == 0 && r < d.rows) p.sh[static_cast<size_t>(d.row0 + r) * (p.half / 128) + d.nt] = s;

@@ -243,6 +243,18 @@ def test_forward_add3_without_routed_tokens():
     assert np.array_equal(got, to_np(plain.shared_out))
 
 
+@pytest.mark.parametrize("wfmt", [0, 1])
+def test_forward_256_row_tiles(wfmt):
+    # about 490 rows per expert: a full 256-row tile and a ragged second one
+    # (experts between 385 and 512 rows take 256-row tiles)
+    wl = synth.Workload("huge", Mr=960, Ms=1100, E=4, k=2, I=512, Is=256, wfmt=wfmt, seed=51, H=1024, L=512)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    loads = np.diff(to_np(dev.offsets))
+    assert loads.min() > 384 and loads.max() <= 512 and np.all(loads % 256 != 0), loads
+    check_forward(dev, inp)
+
+
 def test_forward_heavy_expert_many_row_tiles():
     # all-equal logits: every token goes to experts 0..k-1, 100 rows each (4 row tiles per expert)
     wl = synth.Workload("heavy", Mr=100, Ms=100, E=6, k=2, I=512, Is=128, wfmt=0, seed=22, zero_router=True)
