@@ -28,7 +28,20 @@ struct DenseEpi {
   uint16_t* out1;         // SHARED: shared_out [M - Mr, N]
   const uint16_t* addsrc; // UPADD: s [M, N] bf16 added in FP32
   const uint16_t* resid;  // UPADD: residual [M, N] bf16 added in FP32 after s, or null
+  // UPADD, small M, Ms == Mr: s is formed here from the shared L2's split-K
+  // partials (summed in split order and rounded to bf16, as the shared L2's
+  // own reduction would) and stored to out1; addsrc is then unused
+  const float* s_partial = nullptr;
+  int s_splits = 0;
 };
+
+// The up-projection's output element: (acc + f32(s)) + f32(residual), one
+// rounding to bf16.
+__device__ __forceinline__ uint16_t up_join(float acc, uint16_t s_bits, const uint16_t* resid, size_t o) {
+  float v = acc + bf16_bits_to_f32(s_bits);
+  if (resid != nullptr) v += bf16_bits_to_f32(resid[o]);  // residual, same single rounding
+  return static_cast<uint16_t>(f32_to_bf16_bits(v));
+}
 
 // Column of output produced by B row `brow` (SWIGLU pairs gate row c with up
 // row half + c into output column c).
@@ -42,9 +55,7 @@ __device__ __forceinline__ void dense_epilogue(const DenseEpi& ep, int N, int ro
     else ep.out1[static_cast<size_t>(row - ep.Mr) * N + col] = b;
   } else {
     const size_t o = static_cast<size_t>(row) * N + col;
-    float v = v0 + bf16_bits_to_f32(ep.addsrc[o]);
-    if (ep.resid != nullptr) v += bf16_bits_to_f32(ep.resid[o]);  // residual, same single rounding
-    ep.out0[o] = static_cast<uint16_t>(f32_to_bf16_bits(v));
+    ep.out0[o] = up_join(v0, ep.addsrc[o], ep.resid, o);
   }
 }
 
@@ -206,6 +217,28 @@ __global__ __launch_bounds__(256) void k_dense_reduce(const float* __restrict__ 
       v1.z += b.z;
       v1.w += b.w;
     }
+  }
+  if (kEpi == EPI_UPADD && ep.s_partial != nullptr) {
+    float4 s4 = {0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < ep.s_splits; ++z) {
+      const float4 a = *reinterpret_cast<const float4*>(ep.s_partial + (static_cast<size_t>(z) * M + row) * N + col);
+      s4.x += a.x;
+      s4.y += a.y;
+      s4.z += a.z;
+      s4.w += a.w;
+    }
+    const size_t o = static_cast<size_t>(row) * N + col;
+    const uint16_t s0 = static_cast<uint16_t>(f32_to_bf16_bits(s4.x)), s1 = static_cast<uint16_t>(f32_to_bf16_bits(s4.y));
+    const uint16_t s2 = static_cast<uint16_t>(f32_to_bf16_bits(s4.z)), s3 = static_cast<uint16_t>(f32_to_bf16_bits(s4.w));
+    ep.out1[o + 0] = s0;
+    ep.out1[o + 1] = s1;
+    ep.out1[o + 2] = s2;
+    ep.out1[o + 3] = s3;
+    ep.out0[o + 0] = up_join(v0.x, s0, ep.resid, o + 0);
+    ep.out0[o + 1] = up_join(v0.y, s1, ep.resid, o + 1);
+    ep.out0[o + 2] = up_join(v0.z, s2, ep.resid, o + 2);
+    ep.out0[o + 3] = up_join(v0.w, s3, ep.resid, o + 3);
+    return;
   }
   dense_epilogue<kEpi>(ep, N, row, col + 0, v0.x, v1.x);
   dense_epilogue<kEpi>(ep, N, row, col + 1, v0.y, v1.y);

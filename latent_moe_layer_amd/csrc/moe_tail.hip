@@ -94,9 +94,15 @@ Plans plan_all(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   return p;
 }
 
+// Small M with as many shared as routed tokens: the shared L2's split-K
+// reduction is folded into the up-projection's (one launch less), which
+// then also stores s.
+bool fuse_shared_reduce(const Plans& p, int32_t Mr, int32_t Ms) { return Mr > 0 && Ms == Mr && p.s2.small && p.up.small; }
+
 struct Layout {
   size_t logits, hist;                              // routing scratch
   size_t xq, sx, hq, sh, y, rn, hs, s, partial;     // forward intermediates
+  size_t partial_s;                                 // the shared L2's partials when the up-projection reduces them
   size_t total;
 };
 
@@ -128,6 +134,7 @@ Layout layout_of(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   l.hs = take(static_cast<size_t>(Ms) * Is * 2);
   l.s = take(static_cast<size_t>(Mr) * H * 2);
   l.partial = take(partial);
+  l.partial_s = take(fuse_shared_reduce(p, Mr, Ms) ? static_cast<size_t>(p.s2.splits) * Ms * H * 4 : 0);
   l.total = o;
   return l;
 }
@@ -192,11 +199,12 @@ void launch_tile(const TileArgs& a, hipStream_t st) {
 
 template <int kEpi>
 void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int M, int N, int K, float* partial,
-                  const DenseEpi& ep, hipStream_t st) {
+                  const DenseEpi& ep, hipStream_t st, bool reduce = true) {
   if (M == 0) return;
   const int nbrows = (kEpi == EPI_SWIGLU) ? 2 * ep.half : N;
   if (p.small) {
     hipLaunchKernelGGL(k_dense_small<>, dim3(p.nt, p.splits), dim3(512), 0, st, A, B, M, nbrows, K, p.kps, partial);
+    if (!reduce) return;  // the partials are reduced by a later launch
     const int ncols = (kEpi == EPI_SWIGLU) ? ep.half : N;
     const long n = static_cast<long>(M) * (ncols / 4);
     hipLaunchKernelGGL(k_dense_reduce<kEpi>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
@@ -382,14 +390,22 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   }
   // 5: shared L2 -> s (rows < Mr) and shared_out (rows >= Mr)
   mark(5);
+  const bool fuse_s = fuse_shared_reduce(plans, Mr, Ms);
+  float* partial_s = at<float>(ws, lay.partial_s);
   {
     DenseEpi ep{Mr, Is, s, shared_out, nullptr, nullptr};
-    launch_dense<EPI_SHARED>(plans.s2, hs, w->ws2, Ms, H, Is, partial, ep, st);
+    if (fuse_s) launch_dense<EPI_SHARED>(plans.s2, hs, w->ws2, Ms, H, Is, partial_s, ep, st, false);
+    else launch_dense<EPI_SHARED>(plans.s2, hs, w->ws2, Ms, H, Is, partial, ep, st);
   }
   // 6: up-projection + FP32 shared add (+ FP32 residual add)
   mark(6);
   {
     DenseEpi ep{Mr, Is, out, nullptr, s, residual};
+    if (fuse_s) {
+      ep.out1 = s;
+      ep.s_partial = partial_s;
+      ep.s_splits = plans.s2.splits;
+    }
     launch_dense<EPI_UPADD>(plans.up, rn, w->w_up, Mr, H, L, partial, ep, st);
   }
   mark(7);
