@@ -166,9 +166,11 @@ def main() -> int:
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = MEASURED_L1_TRAFFIC.get(wl.name)
     # the routed L1 stage: the persistent tiled kernel with 32-row tiles
-    # (experts under 128 rows) and, once Mr >= 128, with 128-row tiles
-    roof["kernel"] = ("k_tile<TK_L1, %s, 0, 32>" % ("TF_FP8" if wl.wfmt == 0 else "TF_FP4")) + \
-        ("" if wl.Mr < 128 else " + k_tile<TK_L1, %s, 0, 128>" % ("TF_FP8" if wl.wfmt == 0 else "TF_FP4"))
+    # (experts under 128 rows) and, past 256 tokens, the 128-row (128 to 255
+    # rows) and 256-row (256 rows and more) launches
+    fmt = "TF_FP8" if wl.wfmt == 0 else "TF_FP4"
+    roof["kernel"] = f"k_tile<TK_L1, {fmt}, 0, 32>" + \
+        ("" if wl.Mr <= 256 else f" + k_tile<TK_L1, {fmt}, 0, 128> + k_tile<TK_L1, {fmt}, 0, 256>")
     roof["algorithmic_bytes_per_launch"] = l1_bytes
     roof["avg_launch_us"] = l1_ms * 1e3
 
