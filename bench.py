@@ -29,6 +29,8 @@ HBM_PEAK_GBS = 8000.0
 # counter runs, scaled by the same counters' reading of a copy kernel of known
 # size (profiles/decode_routed_traffic.md); taken on the current kernels.
 MEASURED_L1_TRAFFIC = {"decode": 945.7e6}
+# the same for the single-launch forward (quantizer + persistent tail)
+MEASURED_FUSED_TRAFFIC: dict = {}
 FP8_PEAK_TFLOPS = 5000.0
 MXFP4_PEAK_TFLOPS = 10100.0
 STAGES = ["quant_x", "routed_l1", "routed_l2", "combine_rmsnorm", "shared_l1", "shared_l2", "up_proj_add"]
@@ -43,11 +45,15 @@ class HipEvents:
         self.rt.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
         self.rt.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self.rt.hipEventSynchronize.argtypes = [C.c_void_p]
+        self.rt.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
         self.ev = []
         for _ in range(n):
             h = C.c_void_p()
             assert self.rt.hipEventCreate(C.byref(h)) == 0
             self.ev.append(h.value)
+
+    def record(self, i: int, stream) -> None:
+        assert self.rt.hipEventRecord(C.c_void_p(self.ev[i]), C.c_void_p(stream.cuda_stream)) == 0
 
     def elapsed_ms(self, a: int, b: int) -> float:
         ms = C.c_float()
@@ -78,6 +84,8 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--add3", action="store_true",
                     help="time moe_tail_forward_add3 (the residual joined in the up-projection epilogue)")
+    ap.add_argument("--fused", action="store_true",
+                    help="time moe_tail_forward_fused (the x quantizer, then one persistent launch for the rest)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs the tail on one GPU only; --gpus {args.gpus} is not supported "
@@ -103,7 +111,7 @@ def main() -> int:
 
     def step(st, events=None):
         dev.route(st)
-        dev.forward(st, events)
+        dev.forward(st, events, fused=args.fused and events is None)
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -149,6 +157,20 @@ def main() -> int:
             stage_ms[s] += hev.elapsed_ms(base + s, base + s + 1)
     stage_ms /= args.steps
 
+    fused_ms = None
+    if args.fused:
+        # the single-launch forward (x quantizer + persistent tail) bracketed
+        # by HIP events on its stream, route outside the brackets
+        base = args.steps * (nst + 1)
+        tot = 0.0
+        for i in range(args.steps):
+            dev.route(stream)
+            hev.record(base, stream)
+            dev.forward(stream, fused=True)
+            hev.record(base + 1, stream)
+            tot += hev.elapsed_ms(base, base + 1)
+        fused_ms = tot / args.steps
+
     offsets = to_np(dev.offsets)
     touched = int(np.count_nonzero(np.diff(offsets)))
     nbytes = synth.algorithmic_bytes(wl, touched)["total"] + (wl.Mr * wl.H * 2 if args.add3 else 0)
@@ -173,6 +195,17 @@ def main() -> int:
         ("" if wl.Mr <= 256 else f" + k_tile<TK_L1, {fmt}, 0, 128> + k_tile<TK_L1, {fmt}, 0, 256>")
     roof["algorithmic_bytes_per_launch"] = l1_bytes
     roof["avg_launch_us"] = l1_ms * 1e3
+    if fused_ms is not None:
+        # the dominant launch is then the persistent tail itself: every byte of
+        # the forward (all but the router's weights), timed with the quantizer
+        # launch that precedes it
+        fw_bytes = nbytes - 4 * wl.E * wl.L
+        roof = {"bound": "hbm", "achieved": fw_bytes / (fused_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = MEASURED_FUSED_TRAFFIC.get(wl.name)
+        roof["kernel"] = f"k_quant_clear + k_tail_small<{fmt}>"
+        roof["algorithmic_bytes_per_launch"] = fw_bytes
+        roof["avg_launch_us"] = fused_ms * 1e3
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -203,7 +236,8 @@ def main() -> int:
         "tflops_lowp": flops["lowp"] / (ms_per_step * 1e-3) / 1e12,
         "tflops_bf16": flops["bf16"] / (ms_per_step * 1e-3) / 1e12,
         "hbm_frac": gbs / HBM_PEAK_GBS,
-        "timing": "eager launches" if args.eager else "HIP graph replay of route + forward",
+        "timing": ("eager launches" if args.eager else "HIP graph replay of route + forward") +
+                  (" (single-launch forward)" if args.fused else ""),
         "stage_us": {n: float(v * 1e3) for n, v in zip(STAGES, stage_ms)},
         "roofline": roof, "cpu_baseline": cpu, "input_gen_s": gen_s,
     }

@@ -154,6 +154,31 @@ int moe_tail_forward_add3(const moe_tail_dims *dims, const moe_tail_weights *wei
                           const uint16_t *residual, uint16_t *out, uint16_t *shared_out, void *workspace,
                           size_t ws_bytes, void *stream);
 
+/* moe_tail_forward (residual NULL) or moe_tail_forward_add3 (residual
+ * non-NULL) as two launches: the x quantizer, then ONE persistent launch
+ * that runs the routed experts, the shared expert, combine + RMSNorm and the
+ * up-projection as a fixed sequence of stages, one workgroup per CU, the
+ * stages joined by completion counters in the workspace instead of kernel
+ * boundaries.  The pages' producer schedules routed and shared work together
+ * in one kernel (DeepGEMM PR 416 mirror, Summary); here the tail's
+ * up-projection and final join run in the same launch as well.
+ *   Sizes: decode-sized token counts, Ms <= 128 (hence Mr <= 128), with
+ *   num_experts <= 512, L >= 384 and I >= 384; Mr = 0 runs the shared expert
+ *   alone exactly as moe_tail_forward does.  Other sizes return
+ *   MOE_TAIL_ERR_UNSUPPORTED with nothing enqueued (use moe_tail_forward).
+ *   Results: bit for bit those of moe_tail_forward / _add3 (the same tiles
+ *   and summation orders).  Workspace: moe_tail_workspace_bytes.
+ *   The persistent launch needs all of its workgroups resident together (its
+ *   stages wait on each other): do not run it concurrently with other work
+ *   that occupies CUs for long, including another call of this entry point
+ *   on another stream.  A stage that waits for more than about a second
+ *   gives up and lets the launch finish (with wrong results) instead of
+ *   hanging the device. */
+int moe_tail_forward_fused(const moe_tail_dims *dims, const moe_tail_weights *weights, const uint16_t *x_lat,
+                           int32_t Mr, const uint16_t *x_hid, int32_t Ms, const moe_tail_routing *routing,
+                           const uint16_t *residual, uint16_t *out, uint16_t *shared_out, void *workspace,
+                           size_t ws_bytes, void *stream);
+
 /* Number of stages moe_tail_forward_profiled brackets with events. */
 #define MOE_TAIL_NUM_STAGES 7
 /* Stage order: 0 quantize x_lat, 1 routed L1 (+SwiGLU + h quantization),

@@ -28,7 +28,8 @@ MOE_TAIL_WS_NUM = 8
 MOE_TAIL_NUM_STAGES = 7
 
 EXPORTED = ("moe_tail_workspace_bytes", "moe_tail_workspace_layout", "moe_tail_route", "moe_tail_forward",
-            "moe_tail_forward_add3", "moe_tail_forward_profiled", "moe_tail_quant_fp8_1x128", "moe_tail_strerror")
+            "moe_tail_forward_add3", "moe_tail_forward_fused", "moe_tail_forward_profiled", "moe_tail_quant_fp8_1x128",
+            "moe_tail_strerror")
 
 
 class MoeTailError(RuntimeError):
@@ -75,6 +76,8 @@ def lib() -> C.CDLL:
         L.moe_tail_forward.argtypes = fwd
         L.moe_tail_forward_add3.restype = C.c_int
         L.moe_tail_forward_add3.argtypes = fwd[:7] + [C.c_void_p] + fwd[7:]
+        L.moe_tail_forward_fused.restype = C.c_int
+        L.moe_tail_forward_fused.argtypes = fwd[:7] + [C.c_void_p] + fwd[7:]
         L.moe_tail_forward_profiled.restype = C.c_int
         L.moe_tail_forward_profiled.argtypes = fwd + [C.POINTER(C.c_void_p)]
         L.moe_tail_quant_fp8_1x128.restype = C.c_int
@@ -152,6 +155,14 @@ def moe_tail_forward_add3(dims: Dims, weights: Weights, x_lat, Mr: int, x_hid, M
     _check(lib().moe_tail_forward_add3(C.byref(dims), C.byref(weights), ptr(x_lat), Mr, ptr(x_hid), Ms,
                                        C.byref(routing), ptr(residual), ptr(out), ptr(shared_out), ptr(workspace),
                                        ws_bytes, stream_handle(stream)), "moe_tail_forward_add3")
+
+
+def moe_tail_forward_fused(dims: Dims, weights: Weights, x_lat, Mr: int, x_hid, Ms: int, routing: Routing, residual,
+                           out, shared_out, workspace, ws_bytes: int, stream=None) -> None:
+    """``residual`` None: moe_tail_forward's result; else moe_tail_forward_add3's."""
+    _check(lib().moe_tail_forward_fused(C.byref(dims), C.byref(weights), ptr(x_lat), Mr, ptr(x_hid), Ms,
+                                        C.byref(routing), ptr(residual), ptr(out), ptr(shared_out), ptr(workspace),
+                                        ws_bytes, stream_handle(stream)), "moe_tail_forward_fused")
 
 
 def moe_tail_forward_profiled(dims: Dims, weights: Weights, x_lat, Mr: int, x_hid, Ms: int, routing: Routing, out,

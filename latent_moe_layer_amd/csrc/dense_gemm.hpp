@@ -84,24 +84,35 @@ constexpr int kSkinnyBStages = 4;    // weight ring depth
 constexpr int kSkinnyAStages = 3;    // activation ring depth
 
 template <int kBSt = kSkinnyBStages, int kASt = kSkinnyAStages>
-__global__ __launch_bounds__(512) void k_dense_small(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                                                     int M, int nbrows, int K, int kps, float* __restrict__ partial) {
+constexpr int dense_small_lds() {
+  return kBSt * kSkinnyN * 128 + kASt * kSmallMaxM * 128;
+}
+
+// One workgroup's item (weight rows [bx kSkinnyN, +kSkinnyN), K range by)
+// with its LDS at smem.  kPart 1 issues only the weight ring's first stages
+// and returns (the weights do not depend on earlier work, so a persistent
+// kernel starts them before it waits for the activations); kPart 2 is the
+// rest of such an item, kPart 0 a whole item.
+template <int kBSt = kSkinnyBStages, int kASt = kSkinnyAStages, int kPart = 0>
+__device__ __forceinline__ void dense_small_run(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int M,
+                                                int nbrows, int K, int kps, float* __restrict__ partial, uint8_t* smem,
+                                                int bx, int by) {
   static_assert(kASt >= 2 && kBSt >= kASt, "the weight ring runs ahead of the activation ring");
   constexpr int kABytes = kSmallMaxM * 128;  // one K step of 64 BF16: 128 rows x 128 bytes
   constexpr int kBBytes = kSkinnyN * 128;
   constexpr int kBLoads = kBBytes / 4096;  // per weight wave and step (1 KB each)
   constexpr int kALoads = kABytes / 4096;  // per activation wave and step
-  __shared__ __attribute__((aligned(16))) uint8_t ring_b[kBSt * kBBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t ring_a[kASt * kABytes];
+  uint8_t* ring_b = smem;
+  uint8_t* ring_a = smem + kBSt * kBBytes;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const bool loads_b = wv < 4;
   const int lw = wv & 3;  // index among the waves of its role
   const int l16 = lane & 15, g = lane >> 4;
   const int wr = wave & 3, wc = wave >> 2;  // this wave's 32 rows and 64 weight rows
-  const int brow0 = blockIdx.x * kSkinnyN;
+  const int brow0 = bx * kSkinnyN;
   const int nk = K / 64;
-  const int kb0 = blockIdx.y * kps, n = min(kb0 + kps, nk) - kb0;  // this workgroup's steps (>= 1)
+  const int kb0 = by * kps, n = min(kb0 + kps, nk) - kb0;  // this item's steps (>= 1)
   const size_t rowb = static_cast<size_t>(K) * 2;
 
   // 1 KB block b of a stage = rows 8 b .. 8 b + 7, 128 bytes each; lane l
@@ -116,7 +127,7 @@ __global__ __launch_bounds__(512) void k_dense_small(const uint16_t* __restrict_
   // starts at its own step (rotation by its weight tile) so that they do not
   // request the same lines at the same time.  The summation order then
   // depends on the tile only.
-  const int rot = blockIdx.x % n;
+  const int rot = bx % n;
   // stage s of this wave's ring into `slot`: blocks lw + 4 i
   auto issue = [&](int s, uint8_t* slot, int nl) {
     const int sr = s + rot < n ? s + rot : s + rot - n;
@@ -145,12 +156,15 @@ __global__ __launch_bounds__(512) void k_dense_small(const uint16_t* __restrict_
   // every wave done with step s - 1), start stage s + kBSt - 1 (weights) or
   // s + kASt - 1 (activations) into the slot of step s - 1, compute step s.
   if (loads_b) {
+    if (kPart != 2) {
 #pragma unroll
-    for (int s = 0; s < kBSt - 1; ++s) issue_b(s);
-  } else {
+      for (int s = 0; s < kBSt - 1; ++s) issue_b(s);
+    }
+  } else if (kPart != 1) {
 #pragma unroll
     for (int s = 0; s < kASt - 1; ++s) issue_a(s);
   }
+  if (kPart == 1) return;
   for (int s = 0; s < n; ++s) {
     if (loads_b) vm_wait<kBLoads * (kBSt - 2)>();
     else vm_wait<kALoads * (kASt - 2)>();
@@ -183,50 +197,60 @@ __global__ __launch_bounds__(512) void k_dense_small(const uint16_t* __restrict_
     for (int e = 0; e < 4; ++e) {
       const int row = 32 * wr + 16 * i + 4 * g + e;
       if (row < M) {
-        float* pr = partial + (static_cast<size_t>(blockIdx.y) * M + row) * nbrows + brow0 + 64 * wc + l16;
+        float* pr = partial + (static_cast<size_t>(by) * M + row) * nbrows + brow0 + 64 * wc + l16;
 #pragma unroll
         for (int j = 0; j < 4; ++j) pr[16 * j] = acc[i][j][e];
       }
     }
 }
 
-// Sums the split-K partials in split order and applies the epilogue.
-// One thread per output element; grid covers M * ncols (ncols = I_s for
-// SWIGLU, N otherwise).
+template <int kBSt = kSkinnyBStages, int kASt = kSkinnyAStages>
+__global__ __launch_bounds__(512) void k_dense_small(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+                                                     int M, int nbrows, int K, int kps, float* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[dense_small_lds<kBSt, kASt>()];
+  dense_small_run<kBSt, kASt>(A, B, M, nbrows, K, kps, partial, smem, blockIdx.x, blockIdx.y);
+}
+
+// Sum over z < splits of the float4 at base + z * stride, added in z order;
+// the loads of kChunk splits are issued before any is added (one memory
+// latency per chunk instead of one per split).
+template <int kChunk = 8>
+__device__ __forceinline__ float4 sum_splits(const float* base, size_t stride, int splits) {
+  float4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < splits; z0 += kChunk) {
+    float4 a[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+      if (z0 + i < splits) a[i] = *reinterpret_cast<const float4*>(base + (z0 + i) * stride);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+      if (z0 + i < splits) {
+        v.x += a[i].x;
+        v.y += a[i].y;
+        v.z += a[i].z;
+        v.w += a[i].w;
+      }
+  }
+  return v;
+}
+
+// Sums the split-K partials in split order and applies the epilogue to
+// output group idx (four neighbouring columns) of M * ncols / 4 (ncols = I_s
+// for SWIGLU, N otherwise).
 template <int kEpi>
-__global__ __launch_bounds__(256) void k_dense_reduce(const float* __restrict__ partial, int M, int N, int splits,
-                                                      DenseEpi ep) {
-  // four neighbouring output columns per thread
+__device__ __forceinline__ void dense_reduce_group(const float* __restrict__ partial, int M, int N, int splits,
+                                                   const DenseEpi& ep, long idx) {
   const int nraw = (kEpi == EPI_SWIGLU) ? 2 * ep.half : N;
   const int ncols = (kEpi == EPI_SWIGLU) ? ep.half : N;
-  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<long>(M) * (ncols / 4)) return;
   const int row = static_cast<int>(idx / (ncols / 4)), col = 4 * static_cast<int>(idx % (ncols / 4));
-  float4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
-  for (int z = 0; z < splits; ++z) {
-    const float* pr = partial + (static_cast<size_t>(z) * M + row) * nraw;
-    const float4 a = *reinterpret_cast<const float4*>(pr + col);
-    v0.x += a.x;
-    v0.y += a.y;
-    v0.z += a.z;
-    v0.w += a.w;
-    if (kEpi == EPI_SWIGLU) {
-      const float4 b = *reinterpret_cast<const float4*>(pr + ep.half + col);
-      v1.x += b.x;
-      v1.y += b.y;
-      v1.z += b.z;
-      v1.w += b.w;
-    }
-  }
+  const size_t zs = static_cast<size_t>(M) * nraw;  // split stride
+  const float* pr = partial + static_cast<size_t>(row) * nraw + col;
+  const float4 v0 = sum_splits(pr, zs, splits);
+  float4 v1 = {0.f, 0.f, 0.f, 0.f};
+  if (kEpi == EPI_SWIGLU) v1 = sum_splits(pr + ep.half, zs, splits);
   if (kEpi == EPI_UPADD && ep.s_partial != nullptr) {
-    float4 s4 = {0.f, 0.f, 0.f, 0.f};
-    for (int z = 0; z < ep.s_splits; ++z) {
-      const float4 a = *reinterpret_cast<const float4*>(ep.s_partial + (static_cast<size_t>(z) * M + row) * N + col);
-      s4.x += a.x;
-      s4.y += a.y;
-      s4.z += a.z;
-      s4.w += a.w;
-    }
+    const float4 s4 = sum_splits(ep.s_partial + static_cast<size_t>(row) * N + col, static_cast<size_t>(M) * N,
+                                 ep.s_splits);
     const size_t o = static_cast<size_t>(row) * N + col;
     const uint16_t s0 = static_cast<uint16_t>(f32_to_bf16_bits(s4.x)), s1 = static_cast<uint16_t>(f32_to_bf16_bits(s4.y));
     const uint16_t s2 = static_cast<uint16_t>(f32_to_bf16_bits(s4.z)), s3 = static_cast<uint16_t>(f32_to_bf16_bits(s4.w));
@@ -244,6 +268,15 @@ __global__ __launch_bounds__(256) void k_dense_reduce(const float* __restrict__ 
   dense_epilogue<kEpi>(ep, N, row, col + 1, v0.y, v1.y);
   dense_epilogue<kEpi>(ep, N, row, col + 2, v0.z, v1.z);
   dense_epilogue<kEpi>(ep, N, row, col + 3, v0.w, v1.w);
+}
+
+template <int kEpi>
+__global__ __launch_bounds__(256) void k_dense_reduce(const float* __restrict__ partial, int M, int N, int splits,
+                                                      DenseEpi ep) {
+  const int ncols = (kEpi == EPI_SWIGLU) ? ep.half : N;
+  const long idx = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<long>(M) * (ncols / 4)) return;
+  dense_reduce_group<kEpi>(partial, M, N, splits, ep, idx);
 }
 
 }  // namespace moe_tail

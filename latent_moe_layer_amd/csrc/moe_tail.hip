@@ -14,6 +14,7 @@
 #include "quant_norm.hpp"
 #include "route.hpp"
 #include "routed_gemm.hpp"
+#include "tail_fused.hpp"
 #include "tile_gemm.hpp"
 
 using namespace moe_tail;
@@ -99,10 +100,25 @@ Plans plan_all(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
 // then also stores s.
 bool fuse_shared_reduce(const Plans& p, int32_t Mr, int32_t Ms) { return Mr > 0 && Ms == Mr && p.s2.small && p.up.small; }
 
+// Shapes of the routed tiled kernel: expert tables in LDS (E <= kTileMaxE),
+// gathered x rows addressed with 32-bit offsets, a tile's side data loaded
+// kStages - 1 >= 3 steps ahead (K >= 384 for L1 and L2).
+bool tiled_ok(const moe_tail_dims& d, int32_t Mr) {
+  return d.num_experts <= kTileMaxE && static_cast<size_t>(Mr) * d.latent < (1ull << 31) && d.latent >= 384 &&
+         d.inter >= 384;
+}
+
+// The single-launch tail covers decode sizes: every dense GEMM on the
+// small-M kernel (Ms <= 128) and every expert on 32-row tiles.
+bool fused_ok(const moe_tail_dims& d, const Plans& p, int32_t Mr, int32_t Ms) {
+  return Mr > 0 && Ms <= kSmallMaxM && p.s1.small && p.s2.small && p.up.small && tiled_ok(d, Mr);
+}
+
 struct Layout {
   size_t logits, hist;                              // routing scratch
   size_t xq, sx, hq, sh, y, rn, hs, s, partial;     // forward intermediates
-  size_t partial_s;                                 // the shared L2's partials when the up-projection reduces them
+  size_t partial_s;                                 // the shared L2's partials when a later step reduces them
+  size_t sync;                                      // completion counters of the single-launch tail
   size_t total;
 };
 
@@ -134,7 +150,9 @@ Layout layout_of(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   l.hs = take(static_cast<size_t>(Ms) * Is * 2);
   l.s = take(static_cast<size_t>(Mr) * H * 2);
   l.partial = take(partial);
-  l.partial_s = take(fuse_shared_reduce(p, Mr, Ms) ? static_cast<size_t>(p.s2.splits) * Ms * H * 4 : 0);
+  const bool keep_s2 = fuse_shared_reduce(p, Mr, Ms) || fused_ok(d, p, Mr, Ms);
+  l.partial_s = take(keep_s2 ? static_cast<size_t>(p.s2.splits) * Ms * H * 4 : 0);
+  l.sync = take(fused_ok(d, p, Mr, Ms) ? kSyncWords * 4 : 0);
   l.total = o;
   return l;
 }
@@ -230,15 +248,85 @@ void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int 
   }
 }
 
-int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
-                 const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, const uint16_t* residual,
-                 uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+// Arguments of the decode-sized kernels (the single-launch tail and the
+// co-scheduled launches share them).
+FusedArgs fused_args(const moe_tail_dims& d, const moe_tail_weights* w, int32_t Mr, const uint16_t* x_hid, int32_t Ms,
+                     const moe_tail_routing* routing, const uint16_t* residual, uint16_t* out, uint16_t* shared_out,
+                     void* ws, const Layout& lay, const Plans& plans) {
+  const int L = d.latent, H = d.hidden, I = d.inter, Is = d.shared_inter, E = d.num_experts, k = d.top_k;
+  FusedArgs f{};
+  TileArgs ta{};
+  ta.sorted_pair = routing->sorted_pair;
+  ta.expert_offsets = routing->expert_offsets;
+  ta.E = E;
+  ta.k = k;
+  ta.big_rows = 0x7fffffff;
+  ta.huge_rows = 0x7fffffff;
+  f.l1 = ta;
+  f.l1.a = at<uint8_t>(ws, lay.xq);
+  f.l1.a_scale = at<float>(ws, lay.sx);
+  f.l1.M = Mr;
+  f.l1.b = w->w1;
+  f.l1.b_scale = w->w1_scale;
+  f.l1.hq = at<uint8_t>(ws, lay.hq);
+  f.l1.sh = at<float>(ws, lay.sh);
+  f.l1.K = L;
+  f.l1.N = 2 * I;
+  f.l1.half = I;
+  f.l1.ntn = I / 128;
+  f.l1.nslots = static_cast<int>(static_cast<size_t>(Mr) * k / 32 + E);  // bound on the row tiles (grid size)
+  f.l2 = ta;
+  f.l2.a = at<uint8_t>(ws, lay.hq);
+  f.l2.a_scale = at<float>(ws, lay.sh);
+  f.l2.b = w->w2;
+  f.l2.b_scale = w->w2_scale;
+  f.l2.y = at<float>(ws, lay.y);
+  f.l2.K = I;
+  f.l2.N = L;
+  f.l2.half = 0;
+  f.l2.ntn = L / kTN;
+  f.x_hid = x_hid;
+  f.ws1 = w->ws1;
+  f.ws2 = w->ws2;
+  f.w_up = w->w_up;
+  f.Mr = Mr;
+  f.Ms = Ms;
+  f.H = H;
+  f.Is = Is;
+  f.L = L;
+  f.k = k;
+  f.s1 = DenseItems{plans.s1.nt, plans.s1.splits, plans.s1.kps};
+  f.s2 = DenseItems{plans.s2.nt, plans.s2.splits, plans.s2.kps};
+  f.up = DenseItems{plans.up.nt, plans.up.splits, plans.up.kps};
+  f.part_s1 = at<float>(ws, lay.partial);
+  f.part_s2 = at<float>(ws, lay.partial_s);
+  f.part_up = at<float>(ws, lay.partial);
+  f.hs = at<uint16_t>(ws, lay.hs);
+  f.y = at<float>(ws, lay.y);
+  f.topk_w = routing->topk_weights;
+  f.pair_to_row = routing->pair_to_row;
+  f.gamma = w->rms_gamma;
+  f.rn = at<uint16_t>(ws, lay.rn);
+  f.eps = d.rms_eps;
+  f.out = out;
+  f.s = at<uint16_t>(ws, lay.s);
+  f.shared_out = shared_out;
+  f.resid = residual;
+  f.sync = at<int>(ws, lay.sync);
+  return f;
+}
+
+// The host checks every forward entry point makes (before anything is
+// enqueued); fills *lay on success.
+int check_forward(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
+                  const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, const uint16_t* residual,
+                  uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, Layout* lay) {
   int rc = check_dims(dims);
   if (rc) return rc;
   rc = check_counts(Mr, Ms);
   if (rc) return rc;
   const moe_tail_dims& d = *dims;
-  const int L = d.latent, H = d.hidden, I = d.inter, Is = d.shared_inter, E = d.num_experts, k = d.top_k;
+  const int L = d.latent, H = d.hidden, E = d.num_experts, k = d.top_k;
   rc = check_weights(d, w, false, Mr > 0, Ms > 0, Mr > 0);
   if (rc) return rc;
   if (Mr > 0 && (rc = check_routing(routing, Mr, k, E))) return rc;
@@ -248,9 +336,20 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   if (residual != nullptr && !ptr_ok(residual, static_cast<size_t>(Mr) * H * 2)) return MOE_TAIL_ERR_INVALID;
   if ((Ms > Mr) != (shared_out != nullptr)) return MOE_TAIL_ERR_INVALID;
   if (shared_out != nullptr && !aligned16(shared_out)) return MOE_TAIL_ERR_INVALID;
-  const Layout lay = layout_of(d, Mr, Ms);
-  if (ws_bytes < lay.total) return MOE_TAIL_ERR_WORKSPACE;
-  if (lay.total > 0 && !ptr_ok(ws, 1)) return MOE_TAIL_ERR_INVALID;
+  *lay = layout_of(d, Mr, Ms);
+  if (ws_bytes < lay->total) return MOE_TAIL_ERR_WORKSPACE;
+  if (lay->total > 0 && !ptr_ok(ws, 1)) return MOE_TAIL_ERR_INVALID;
+  return MOE_TAIL_OK;
+}
+
+int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
+                 const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, const uint16_t* residual,
+                 uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+  Layout lay;
+  int rc = check_forward(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, &lay);
+  if (rc) return rc;
+  const moe_tail_dims& d = *dims;
+  const int L = d.latent, H = d.hidden, I = d.inter, Is = d.shared_inter, E = d.num_experts, k = d.top_k;
   if (events != nullptr)
     for (int i = 0; i <= MOE_TAIL_NUM_STAGES; ++i)
       if (events[i] == nullptr) return MOE_TAIL_ERR_INVALID;
@@ -272,6 +371,32 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   uint16_t* s = at<uint16_t>(ws, lay.s);
   float* partial = at<float>(ws, lay.partial);
 
+  // Decode sizes (every dense GEMM small-M, every expert on 32-row tiles):
+  // six launches, independent work sharing a launch (the profiled variant
+  // keeps one launch per stage so that each stage can be timed)
+  if (events == nullptr && fused_ok(d, plans, Mr, Ms)) {
+    const FusedArgs f = fused_args(d, w, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, lay, plans);
+    const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
+    const long qblocks = static_cast<long>(Mr) * (L / 128);
+    hipLaunchKernelGGL(k_quant_clear, dim3(static_cast<unsigned>((qblocks + 3) / 4)), dim3(256), 0, st, x_lat, xq, sx,
+                       Mr, L, f.sync, kSyncWords);
+    if (fp8) launch_tile<TK_L1, TF_FP8, 0, 32>(f.l1, st);
+    else launch_tile<TK_L1, TF_FP4, 0, 32>(f.l1, st);
+    const unsigned pgrid = std::max(8u, num_cus() / 8 * 8);  // persistent: one workgroup per CU
+    if (fp8) hipLaunchKernelGGL(k_l2_shared1<TF_FP8>, dim3(pgrid), dim3(512), 0, st, f);
+    else hipLaunchKernelGGL(k_l2_shared1<TF_FP4>, dim3(pgrid), dim3(512), 0, st, f);
+    const long r_groups = static_cast<long>(Ms) * (Is / 4);
+    const unsigned cgrid = static_cast<unsigned>(Mr + (r_groups + 255) / 256);
+    const int nc4 = (L / 4 + 255) / 256;
+    auto kc = (nc4 <= 2) ? k_combine_shared1r<2> : (nc4 <= 4) ? k_combine_shared1r<4> : k_combine_shared1r<8>;
+    hipLaunchKernelGGL(kc, dim3(cgrid), dim3(256), 0, st, f);
+    const unsigned dgrid = static_cast<unsigned>(plans.s2.nt * plans.s2.splits + plans.up.nt * plans.up.splits);
+    hipLaunchKernelGGL(k_shared2_up, dim3(dgrid), dim3(512), 0, st, f);
+    const long f_groups = static_cast<long>(Ms) * (H / 4);
+    hipLaunchKernelGGL(k_final_join, dim3(static_cast<unsigned>((f_groups + 255) / 256)), dim3(256), 0, st, f);
+    return launched();
+  }
+
   // 0: quantize x_lat
   mark(0);
   if (Mr > 0) {
@@ -287,7 +412,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   // gathered x rows with 32-bit offsets and loads a tile's side data
   // kStages - 1 >= 3 steps ahead (K >= 384).  Shapes outside that take the
   // row-streaming kernel for every expert.
-  const bool tiled = E <= kTileMaxE && static_cast<size_t>(Mr) * L < (1ull << 31) && L >= 384 && I >= 384;
+  const bool tiled = tiled_ok(d, Mr);
   constexpr int kSmallOnlyMr = 256;
   const bool big = tiled && Mr > kSmallOnlyMr;
   const unsigned max_tiles = static_cast<unsigned>((R + kBM - 1) / kBM + E);
@@ -412,6 +537,51 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   return launched();
 }
 
+// Workgroups of the single-launch tail: one per CU, whole rounds of 8 (one
+// per XCD), provided the kernel fits one workgroup per CU at all.
+template <int FMT>
+unsigned fused_grid() {
+  static int fits[64] = {};  // per device: 0 unknown, 1 yes, 2 no
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (fits[dev] == 0) {
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k_tail_small<FMT>), 512, 0);
+    fits[dev] = (e == hipSuccess && n >= 1) ? 1 : 2;
+  }
+  return fits[dev] == 1 ? num_cus() / 8 * 8 : 0;
+}
+
+int fused_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
+               const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, const uint16_t* residual,
+               uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream) {
+  Layout lay;
+  int rc = check_forward(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, &lay);
+  if (rc) return rc;
+  const moe_tail_dims& d = *dims;
+  const int L = d.latent;
+  const Plans plans = plan_all(d, Mr, Ms);
+  if (Mr == 0 && Ms <= kSmallMaxM)  // no routed work: the shared expert alone, as moe_tail_forward runs it
+    return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, stream,
+                        nullptr);
+  if (!fused_ok(d, plans, Mr, Ms)) return MOE_TAIL_ERR_UNSUPPORTED;
+  const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
+  const unsigned grid = fp8 ? fused_grid<TF_FP8>() : fused_grid<TF_FP4>();
+  if (grid < 8) return MOE_TAIL_ERR_UNSUPPORTED;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // launch errors below are ours, not an earlier call's
+  const FusedArgs f = fused_args(d, w, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, lay, plans);
+  {
+    const long blocks = static_cast<long>(Mr) * (L / 128);
+    hipLaunchKernelGGL(k_quant_clear, dim3(static_cast<unsigned>((blocks + 3) / 4)), dim3(256), 0, st, x_lat,
+                       at<uint8_t>(ws, lay.xq), at<float>(ws, lay.sx), Mr, L, f.sync, kSyncWords);
+  }
+  if (fp8) hipLaunchKernelGGL(k_tail_small<TF_FP8>, dim3(grid), dim3(512), 0, st, f);
+  else hipLaunchKernelGGL(k_tail_small<TF_FP4>, dim3(grid), dim3(512), 0, st, f);
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -510,6 +680,12 @@ int moe_tail_forward_add3(const moe_tail_dims* dims, const moe_tail_weights* w, 
                           uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream) {
   if (Mr > 0 && residual == nullptr) return MOE_TAIL_ERR_INVALID;
   return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_tail_forward_fused(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
+                           const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, const uint16_t* residual,
+                           uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream) {
+  return fused_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, stream);
 }
 
 int moe_tail_forward_profiled(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat,

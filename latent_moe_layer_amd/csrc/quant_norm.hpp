@@ -10,10 +10,8 @@ namespace moe_tail {
 // code = e4m3(x / s).  Activations are quantized per 1x128 block with fp32
 // scales, matching the 128-wide K blocks of the weights.
 template <bool kBf16In>
-__global__ __launch_bounds__(256) void k_quant_1x128(const void* __restrict__ x, uint8_t* __restrict__ codes,
-                                                     float* __restrict__ scales, int rows, int cols) {
-  const int lane = threadIdx.x & 63;
-  const long blk = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+__device__ __forceinline__ void quant_block(const void* __restrict__ x, uint8_t* __restrict__ codes,
+                                            float* __restrict__ scales, int rows, int cols, long blk, int lane) {
   const int nb = cols / 128;
   if (blk >= static_cast<long>(rows) * nb) return;
   const long r = blk / nb;
@@ -36,6 +34,24 @@ __global__ __launch_bounds__(256) void k_quant_1x128(const void* __restrict__ x,
   if (lane == 0) scales[static_cast<size_t>(r) * nb + b] = s;
 }
 
+template <bool kBf16In>
+__global__ __launch_bounds__(256) void k_quant_1x128(const void* __restrict__ x, uint8_t* __restrict__ codes,
+                                                     float* __restrict__ scales, int rows, int cols) {
+  quant_block<kBf16In>(x, codes, scales, rows, cols, static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6),
+                       threadIdx.x & 63);
+}
+
+// The same quantizer of x, whose first workgroup also clears n words at
+// `zero` (the completion counters of the single-launch tail that follows).
+__global__ __launch_bounds__(256) void k_quant_clear(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
+                                                     float* __restrict__ scales, int rows, int cols,
+                                                     int* __restrict__ zero, int n) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n; i += 256) zero[i] = 0;
+  quant_block<true>(x, codes, scales, rows, cols, static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6),
+                    threadIdx.x & 63);
+}
+
 // One workgroup (256 threads) per routed token: z = sum_j w_j * y[row(t, j)]
 // in FP32 (slot order), then RMSNorm with FP32 statistics:
 // rn = bf16((z / sqrt(mean(z^2) + eps)) * gamma).  The routed latent is
@@ -48,14 +64,17 @@ constexpr int kNormMaxCols = 32;  // L <= 256 * 32
 // (NC4 = an upper bound of L / 1024: groups past L are clamped, loaded and
 // unused).  The rows' 16-byte loads are issued in batches before any is
 // used; each column still sums its k slots in slot order.
+//
+// combine_token: token t by the 256 threads tid = 0..255 of one half of a
+// workgroup (s_part: 4 words of that half); t < 0 only takes part in the
+// workgroup barrier.
 template <int NC4>
-__global__ __launch_bounds__(256) void k_combine_rmsnorm(const float* __restrict__ y, const float* __restrict__ topk_w,
-                                                         const int32_t* __restrict__ pair_to_row,
-                                                         const uint16_t* __restrict__ gamma,
-                                                         uint16_t* __restrict__ rn, int L, int k, float eps) {
-  __shared__ float s_part[4];
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void combine_token(const float* __restrict__ y, const float* __restrict__ topk_w,
+                                              const int32_t* __restrict__ pair_to_row,
+                                              const uint16_t* __restrict__ gamma, uint16_t* __restrict__ rn, int L,
+                                              int k, float eps, int t, int tid, float* s_part) {
+  const bool live = t >= 0;
+  if (!live) t = 0;
   const int ng = L / 4;  // 4-column groups
   int grp[NC4];
 #pragma unroll
@@ -66,7 +85,7 @@ __global__ __launch_bounds__(256) void k_combine_rmsnorm(const float* __restrict
   // rows in batches of kB (k <= 16): each batch's loads are issued before
   // any is used; rows past k are clamped to the last slot, loaded and unused
   constexpr int kB = (NC4 <= 4) ? 8 : 4;
-  for (int j0 = 0; j0 < k; j0 += kB) {
+  for (int j0 = 0; j0 < (live ? k : 0); j0 += kB) {
     float4 v[kB][NC4];
     float w[kB];
 #pragma unroll
@@ -103,7 +122,7 @@ __global__ __launch_bounds__(256) void k_combine_rmsnorm(const float* __restrict
 #pragma unroll
   for (int c = 0; c < NC4; ++c) {
     const int gi = tid + 256 * c;
-    if (gi < ng) {
+    if (live && gi < ng) {
       const uint2 gm = *reinterpret_cast<const uint2*>(gamma + 4 * gi);
       uint2 o;
       o.x = f32_to_bf16_bits((z[c].x * r) * bf16_bits_to_f32(gm.x & 0xffffu)) |
@@ -113,6 +132,15 @@ __global__ __launch_bounds__(256) void k_combine_rmsnorm(const float* __restrict
       *reinterpret_cast<uint2*>(rn + static_cast<size_t>(t) * L + 4 * gi) = o;
     }
   }
+}
+
+template <int NC4>
+__global__ __launch_bounds__(256) void k_combine_rmsnorm(const float* __restrict__ y, const float* __restrict__ topk_w,
+                                                         const int32_t* __restrict__ pair_to_row,
+                                                         const uint16_t* __restrict__ gamma,
+                                                         uint16_t* __restrict__ rn, int L, int k, float eps) {
+  __shared__ float s_part[4];
+  combine_token<NC4>(y, topk_w, pair_to_row, gamma, rn, L, k, eps, blockIdx.x, threadIdx.x, s_part);
 }
 
 }  // namespace moe_tail

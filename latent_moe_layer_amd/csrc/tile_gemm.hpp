@@ -80,8 +80,50 @@ struct TileArgs {
 // 64 x 64.  TM = 32: tiles of 32 rows for the experts with fewer rows (decode
 // sizes), 8 waves of 32 x 32, a deeper ring.  Either way 256 B rows (weight
 // rows) per tile.
+// LDS of one workgroup of the tiled kernel (ring + expert tables + per-tile
+// side data), carved from one buffer so that a persistent kernel running
+// several stages of the tail can reuse it.
+template <int KIND, int FMT, int TM>
+struct TileLds {
+  static constexpr bool kFP4 = FMT == TF_FP4;
+  static constexpr bool kScaled = FMT != TF_BF16;
+  static constexpr bool kRouted = KIND != TK_DENSE;
+  static constexpr int kStages = (TM == 256) ? 2 : (TM == 128) ? 3 : 4;
+  static constexpr int kStage = TM * 128 + kTN * (kFP4 ? 64 : 128) + (kScaled ? 2048 : 0);
+  static constexpr int kPairRows = (TM < 64) ? 64 : TM;
+  static constexpr int kWavesN = (TM == 32) ? 8 : 4;
+  static constexpr int kRing = 0;
+  static constexpr int kEoff = kRing + kStages * kStage;
+  static constexpr int kPre = kEoff + 4 * (kRouted ? kTileMaxE + 1 : 1);
+  static constexpr int kPair = kPre + 4 * (kRouted ? kTileMaxE + 1 : 1);
+  static constexpr int kWsc = kPair + 4 * 3 * kPairRows;
+  static constexpr int kAmax = kWsc + 4 * 3 * 2 * kMaxKBlocks;
+  static constexpr int kBytes = kAmax + 4 * kWavesN * TM;
+};
+
+// The LDS pieces of one workgroup of the tiled kernel.  The standalone
+// kernel passes separate arrays (so the compiler knows they do not overlap);
+// a kernel that runs several stages carves them from one buffer
+// (tile_smem_in).
+struct TileSmem {
+  uint8_t* ring;
+  int* eoff;
+  int* pre;
+  int* pair;
+  float* wsc;
+  float* amax;
+};
+
+template <int KIND, int FMT, int TM>
+__device__ __forceinline__ TileSmem tile_smem_in(uint8_t* base) {
+  using Lds = TileLds<KIND, FMT, TM>;
+  return TileSmem{base + Lds::kRing, reinterpret_cast<int*>(base + Lds::kEoff), reinterpret_cast<int*>(base + Lds::kPre),
+                  reinterpret_cast<int*>(base + Lds::kPair), reinterpret_cast<float*>(base + Lds::kWsc),
+                  reinterpret_cast<float*>(base + Lds::kAmax)};
+}
+
 template <int KIND, int FMT, int EPI, int TM = kTM>
-__global__ __launch_bounds__(512) void k_tile(TileArgs p) {
+__device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, int wg, int nwg) {
   constexpr bool kFP4 = FMT == TF_FP4;
   constexpr bool kBF16 = FMT == TF_BF16;
   constexpr bool kScaled = !kBF16;
@@ -108,18 +150,20 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   constexpr int kBChunks = kFP4 ? 2 : 4;             // 16-byte B loads per thread and stage
   constexpr int kLoads = kAL + kBChunks + (kScaled ? 1 : 0);  // direct loads per wave and stage
   constexpr uint32_t kNoRow = 0x80000000u;           // offset past any buffer: reads zeros
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStage];
-  __shared__ int s_eoff[kRouted ? kTileMaxE + 1 : 1];  // expert row offsets
-  __shared__ int s_pre[kRouted ? kTileMaxE + 1 : 1];   // row tiles of the experts before e
+  using Lds = TileLds<KIND, FMT, TM>;
+  static_assert(Lds::kStage == kStage && Lds::kStages == kStages && Lds::kWavesN == kWavesN, "LDS plan");
+  uint8_t* ring = sm.ring;
+  int* s_eoff = sm.eoff;  // expert row offsets
+  int* s_pre = sm.pre;    // row tiles of the experts before e
   // per-tile data, buffer j % 3 for tile j: loaded while tile j - 2 still
   // computes and read until tile j's last step
-  constexpr int kPairRows = (TM < 64) ? 64 : TM;       // one 64-lane load per 64 rows
-  __shared__ int s_pair[3][kPairRows];                 // L1: sorted pair ids of a tile's rows
+  constexpr int kPairRows = Lds::kPairRows;  // one 64-lane load per 64 rows
+  auto s_pair = reinterpret_cast<int(*)[kPairRows]>(sm.pair);  // L1: sorted pair ids of a tile's rows
   // aux loads of the next tile: pair ids by waves 0 .. kPairRows / 64 - 1 (L1),
   // the two weight-scale rows (FP8) by waves kWscW and kWscW + 1
   constexpr int kWscW = (kPairRows / 64 < 2) ? 2 : kPairRows / 64;
-  __shared__ float s_wsc[3][2][kMaxKBlocks];           // FP8: weight scales of a tile's two 128-row B halves
-  __shared__ float s_amax[kWavesN][TM];
+  auto s_wsc = reinterpret_cast<float(*)[2][kMaxKBlocks]>(sm.wsc);  // FP8: weight scales of a tile's two 128-row B halves
+  auto s_amax = reinterpret_cast<float(*)[TM]>(sm.amax);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
@@ -170,7 +214,7 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   } else {
     T = p.nslots * p.ntn;
   }
-  const int xcd = blockIdx.x & 7, lb = blockIdx.x >> 3, nbx = gridDim.x >> 3;
+  const int xcd = wg & 7, lb = wg >> 3, nbx = nwg >> 3;
   const int per = (T + 7) / 8, lo = xcd * per, hi = min(T, lo + per);
   const int n_my = (lo + lb < hi) ? (hi - lo - lb + nbx - 1) / nbx : 0;
   if (n_my == 0) return;  // uniform
@@ -680,6 +724,18 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   }
   // drain the trailing (empty) loads
   ring_barrier<0>();
+}
+
+template <int KIND, int FMT, int EPI, int TM = kTM>
+__global__ __launch_bounds__(512) void k_tile(TileArgs p) {
+  using Lds = TileLds<KIND, FMT, TM>;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[Lds::kStages * Lds::kStage];
+  __shared__ int s_eoff[Lds::kRouted ? kTileMaxE + 1 : 1];
+  __shared__ int s_pre[Lds::kRouted ? kTileMaxE + 1 : 1];
+  __shared__ int s_pair[3 * Lds::kPairRows];
+  __shared__ float s_wsc[3 * 2 * kMaxKBlocks];
+  __shared__ float s_amax[Lds::kWavesN * TM];
+  tile_run<KIND, FMT, EPI, TM>(p, TileSmem{ring, s_eoff, s_pre, s_pair, s_wsc, s_amax}, blockIdx.x, gridDim.x);
 }
 
 }  // namespace moe_tail

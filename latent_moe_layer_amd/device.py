@@ -65,8 +65,16 @@ class DeviceTail:
         """Upload the add3 residual ([Mr, H] bf16 bits); None goes back to the plain forward."""
         self.residual = None if residual is None else _dev(residual, self.device)
 
-    def forward(self, stream=None, events=None) -> None:
+    def forward(self, stream=None, events=None, fused: bool = False) -> None:
+        """The multi-launch forward (with stage events if given), or with
+        ``fused`` the single-launch one (moe_tail_forward_fused)."""
         res = getattr(self, "residual", None)
+        if fused:
+            if events is not None:
+                raise ValueError("the single-launch forward has no stage events")
+            B.moe_tail_forward_fused(self.dims, self.weights, self.t["x_lat"], self.Mr, self.t["x_hid"], self.Ms,
+                                     self.routing, res, self.out, self.shared_out, self.ws, self.ws_bytes, stream)
+            return
         if res is not None:
             if events is not None:
                 raise ValueError("the profiled forward has no add3 variant")

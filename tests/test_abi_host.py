@@ -161,6 +161,30 @@ def test_forward_add3_rejections():
         B.MOE_TAIL_ERR_INVALID
 
 
+def test_forward_fused_rejections():
+    d, w, r = dims(), _fake_weights(), _fake_routing()
+    f = B.lib().moe_tail_forward_fused
+    need = B.moe_tail_workspace_bytes(d, 16, 16)
+    RES = 1 << 46
+    # the plain forward's checks come first
+    assert f(C.byref(d), C.byref(w), X, 17, X, 16, C.byref(r), None, OUT, None, WS, need, None) == \
+        B.MOE_TAIL_ERR_INVALID
+    assert f(C.byref(d), C.byref(w), X, 16, X, 16, C.byref(r), None, OUT, None, WS, need - 1, None) == \
+        B.MOE_TAIL_ERR_WORKSPACE
+    assert f(C.byref(d), C.byref(w), X, 16, X, 16, C.byref(r), RES + 2, OUT, None, WS, need, None) == \
+        B.MOE_TAIL_ERR_INVALID
+    assert f(C.byref(d), C.byref(w), X, 16, X, 16, C.byref(r), None, OUT, SOUT, WS, need, None) == \
+        B.MOE_TAIL_ERR_INVALID
+    # sizes outside the single launch's range are declined (nothing enqueued)
+    need129 = B.moe_tail_workspace_bytes(d, 16, 129)
+    assert f(C.byref(d), C.byref(w), X, 16, X, 129, C.byref(r), None, OUT, SOUT, WS, need129, None) == \
+        B.MOE_TAIL_ERR_UNSUPPORTED
+    dn = dims(inter=256)
+    needn = B.moe_tail_workspace_bytes(dn, 16, 16)
+    assert f(C.byref(dn), C.byref(w), X, 16, X, 16, C.byref(r), None, OUT, None, WS, needn, None) == \
+        B.MOE_TAIL_ERR_UNSUPPORTED
+
+
 def test_quant_rejections():
     q = B.lib().moe_tail_quant_fp8_1x128
     assert q(X, 1, 4, 100, OUT, SOUT, None) == B.MOE_TAIL_ERR_INVALID
