@@ -63,7 +63,7 @@ struct DensePlan {
 
 constexpr int kPlanCUs = 256;
 
-DensePlan plan_dense(int M, int nbrows, int ntiles, int K) {
+DensePlan plan_dense(int M, int nbrows, int ntiles, int K, int cus = kPlanCUs) {
   DensePlan p;
   p.small = M <= kSmallMaxM;
   const int nk = p.small ? K / 64 : K / 128;  // K steps of the kernel
@@ -73,7 +73,7 @@ DensePlan plan_dense(int M, int nbrows, int ntiles, int K) {
     // one); a fixed count keeps the workspace size independent of the device
     p.mt = 1;
     p.nt = nbrows / kSkinnyN;
-    if (p.nt > 0) s = std::min(nk, std::max(1, kPlanCUs / p.nt));
+    if (p.nt > 0) s = std::min(nk, std::max(1, cus / p.nt));
   } else {
     p.mt = (M + kTM - 1) / kTM;
     p.nt = ntiles;
@@ -89,9 +89,14 @@ struct Plans {
 
 Plans plan_all(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   Plans p;
+  // at decode sizes the shared L2 and the up-projection share one launch:
+  // each gets half of the workgroups (fewer, longer items, and half the
+  // partial sums to write and reduce).  The shared expert's plan depends on
+  // Ms only, so its rows come out the same whatever Mr is.
+  const int pair = Ms <= kSmallMaxM ? 2 : 1;
   p.s1 = plan_dense(Ms, 2 * d.shared_inter, d.shared_inter / 64, d.hidden);
-  p.s2 = plan_dense(Ms, d.hidden, d.hidden / 128, d.shared_inter);
-  p.up = plan_dense(Mr, d.hidden, d.hidden / 128, d.latent);
+  p.s2 = plan_dense(Ms, d.hidden, d.hidden / 128, d.shared_inter, kPlanCUs / pair);
+  p.up = plan_dense(Mr, d.hidden, d.hidden / 128, d.latent, kPlanCUs / pair);
   return p;
 }
 
