@@ -3,7 +3,10 @@
 One step = one pass of the whole tail (route + forward: router top-k and
 permutation, x quantization, routed L1 + SwiGLU + h quantization, routed L2,
 combine + RMSNorm, shared L1 + SwiGLU, shared L2, up-projection + FP32 shared
-add) over one batch of seeded synthetic input already resident in HBM.
+add) over one batch of seeded synthetic input already resident in HBM.  At
+decode sizes moe_tail_forward runs independent stages in shared launches;
+the per-stage breakdown (`stage_us`) comes from moe_tail_forward_profiled,
+which keeps one launch per stage (the same kernels' bodies and bits).
 
 Prints ONE JSON line.  `value` is the whole tail's achieved HBM throughput
 (algorithmic bytes / time per layer); `us_per_layer` is the step time.  The
@@ -239,6 +242,7 @@ def main() -> int:
         "timing": ("eager launches" if args.eager else "HIP graph replay of route + forward") +
                   (" (single-launch forward)" if args.fused else ""),
         "stage_us": {n: float(v * 1e3) for n, v in zip(STAGES, stage_ms)},
+        "stage_timing": "one launch per stage (moe_tail_forward_profiled), HIP events on its stream",
         "roofline": roof, "cpu_baseline": cpu, "input_gen_s": gen_s,
     }
     print(json.dumps(out))
