@@ -32,12 +32,19 @@ constexpr int kTN = 256;
 constexpr int kBigMinRows = 128;  // experts with at least this many rows use 128-row tiles (by default)
 constexpr int kHugeTM = 256;      // ... and from this many rows on, 256-row tiles where they pay
 
-// An expert with c >= huge rows takes 256-row tiles even when its last tile
-// is mostly padding: at the prefill loads (450-590 rows per expert) that
-// measured faster than switching such experts to 128-row tiles (routed L1
-// 699 against 752 us), the padded rows costing less than a second launch's
-// tail.
+// An expert with c >= huge rows takes 256-row tiles for its first c / 256 *
+// 256 rows; a tail of more than 128 rows takes one more (partly padded)
+// 256-row tile, a shorter tail one 128-row tile.  Switching whole experts
+// to 128-row tiles measured slower at the prefill loads (routed L1 752
+// against 699 us: a 128-row tile does half a 256-row tile's work per byte it
+// moves), while moving only the short tails took routed L1 from 699 to 678
+// us.
 __host__ __device__ __forceinline__ bool use256(int c, int huge) { return c >= huge; }
+// Such an expert's rows past its last full 256-row tile: up to 128 of them
+// go to one 128-row tile (a 256-row tile would be more than half padding),
+// more stay in a last, partly padded 256-row tile.
+__host__ __device__ __forceinline__ int tiles256(int c) { return c / 256 + ((c % 256) > 128 ? 1 : 0); }
+__host__ __device__ __forceinline__ bool tail128(int c) { return (c % 256) > 0 && (c % 256) <= 128; }
 constexpr int kTileMaxE = 512;    // expert tables of the routed kinds live in LDS
 
 enum { TK_L1 = 0, TK_L2 = 1, TK_DENSE = 2 };
@@ -190,8 +197,11 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       const int eb = min(lane * per, p.E), ee = min(eb + per, p.E);
       auto ntile = [&](int e) {
         const int c = s_eoff[e + 1] - s_eoff[e];
-        if (TM == 256) return use256(c, p.huge_rows) ? (c + TM - 1) / TM : 0;
-        if (TM == 128) return (c >= p.big_rows && !use256(c, p.huge_rows)) ? (c + TM - 1) / TM : 0;
+        if (TM == 256) return use256(c, p.huge_rows) ? tiles256(c) : 0;
+        if (TM == 128) {
+          if (use256(c, p.huge_rows)) return tail128(c) ? 1 : 0;
+          return c >= p.big_rows ? (c + TM - 1) / TM : 0;
+        }
         return c < p.big_rows ? (c + TM - 1) / TM : 0;
       };
       int local = 0;
@@ -236,7 +246,11 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
         else b = m;
       }
       d.e = a;
-      d.row0 = s_eoff[a] + (slot - s_pre[a]) * TM;
+      // 128-row tiles of an expert with 256-row tiles cover only the rows
+      // past its full 256-row tiles
+      const int c = s_eoff[a + 1] - s_eoff[a];
+      const int base = (TM == 128 && use256(c, p.huge_rows)) ? c / 256 * 256 : 0;
+      d.row0 = s_eoff[a] + base + (slot - s_pre[a]) * TM;
       d.rows = min(TM, s_eoff[a + 1] - d.row0);
     } else {
       d.e = 0;

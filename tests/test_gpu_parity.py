@@ -255,6 +255,18 @@ def test_forward_256_row_tiles(wfmt):
     check_forward(dev, inp)
 
 
+@pytest.mark.parametrize("wfmt", [0, 1])
+def test_forward_256_row_tiles_short_tail(wfmt):
+    # about 300 rows per expert: one full 256-row tile and a tail of at most
+    # 128 rows, which goes to a 128-row tile past the expert's 256-row tiles
+    wl = synth.Workload("tail", Mr=600, Ms=640, E=4, k=2, I=512, Is=256, wfmt=wfmt, seed=52, H=1024, L=512)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    loads = np.diff(to_np(dev.offsets))
+    assert loads.min() > 256 and loads.max() <= 384, loads
+    check_forward(dev, inp)
+
+
 def test_forward_heavy_expert_many_row_tiles():
     # all-equal logits: every token goes to experts 0..k-1, 100 rows each (4 row tiles per expert)
     wl = synth.Workload("heavy", Mr=100, Ms=100, E=6, k=2, I=512, Is=128, wfmt=0, seed=22, zero_router=True)
