@@ -653,8 +653,13 @@ int moe_tail_route(const moe_tail_dims* dims, const moe_tail_weights* w, const u
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLogitTok * 8192 * 2);
       lds_raised = true;
     }
-    hipLaunchKernelGGL(k_router_logits, dim3((Mr + kLogitTok - 1) / kLogitTok, egroups), dim3(256), xtile, st, x_lat,
-                       w->gate, w->gate_bias, logits, Mr, L, E);
+    if (Mr >= kWideMinTokens)
+      hipLaunchKernelGGL((k_router_logits_wide<kWideTok, kWideEW>),
+                         dim3((Mr + kWideTok - 1) / kWideTok, (E + 4 * kWideEW - 1) / (4 * kWideEW)), dim3(256), 0, st,
+                         x_lat, w->gate, w->gate_bias, logits, Mr, L, E);
+    else
+      hipLaunchKernelGGL(k_router_logits, dim3((Mr + kLogitTok - 1) / kLogitTok, egroups), dim3(256), xtile, st, x_lat,
+                         w->gate, w->gate_bias, logits, Mr, L, E);
     auto topk = (E <= 64) ? k_router_topk<1> : (E <= 128) ? k_router_topk<2> : (E <= 384) ? k_router_topk<6>
                                                                                  : k_router_topk<kMaxExpertsPerLane>;
     hipLaunchKernelGGL(topk, dim3((Mr + 3) / 4), dim3(256), 0, st, logits, out->topk_ids, out->topk_weights, Mr, E, k);
