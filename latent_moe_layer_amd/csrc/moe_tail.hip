@@ -267,6 +267,7 @@ FusedArgs fused_args(const moe_tail_dims& d, const moe_tail_weights* w, int32_t 
   ta.k = k;
   ta.big_rows = 0x7fffffff;
   ta.huge_rows = 0x7fffffff;
+  ta.mid_rows = 0x7fffffff;
   f.l1 = ta;
   f.l1.a = at<uint8_t>(ws, lay.xq);
   f.l1.a_scale = at<float>(ws, lay.sx);
@@ -412,7 +413,10 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   // 1, 2: routed L1 and L2 on the persistent LDS-tiled kernel: 128-row tiles
   // for experts with at least kBigMinRows rows, 32-row tiles for the others;
   // up to kSmallOnlyMr tokens every expert takes 32-row tiles (an expert
-  // reaching 128 rows is then rare, and it saves the second launch).  The
+  // reaching 128 rows is then rare, and it saves the second launch).  When
+  // the experts average more than 32 rows, those with 33 .. 127 take 64-row
+  // tiles instead (two 32-row tiles of one expert stream the same weights
+  // side by side, which halves the distinct weight streams in flight).  The
   // kernel keeps the expert tables in LDS (E <= kTileMaxE), addresses the
   // gathered x rows with 32-bit offsets and loads a tile's side data
   // kStages - 1 >= 3 steps ahead (K >= 384).  Shapes outside that take the
@@ -429,11 +433,15 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   ta.k = k;
   ta.big_rows = big ? kBigMinRows : 0x7fffffff;
   ta.huge_rows = big ? kHugeTM : 0x7fffffff;
+  const bool mid = tiled && R > static_cast<size_t>(32) * E;
+  ta.mid_rows = mid ? 33 : 0x7fffffff;
   // bounds on the row tiles, which size the grids: ceil(c / 128) <= c / 64
-  // for c >= 128, and ceil(c / 32) <= c / 32 + 1
+  // for c >= 128, ceil(c / 64) <= c / 32 for c >= 33, and ceil(c / 32) <=
+  // c / 32 + 1
   const int slots_big = static_cast<int>(R / (kTM / 2));
   const int slots_huge = static_cast<int>(R / (kHugeTM / 2));  // ceil(c / 256) <= c / 128 for c >= 256
   const int slots_small = static_cast<int>(R / 32 + E);
+  const int slots_mid = static_cast<int>(R / 32);
   mark(1);
   if (Mr > 0) {
     if (!tiled) {
@@ -461,6 +469,11 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       a1.nslots = slots_small;
       if (fp8) launch_tile<TK_L1, TF_FP8, 0, 32>(a1, st);
       else launch_tile<TK_L1, TF_FP4, 0, 32>(a1, st);
+      if (mid) {
+        a1.nslots = slots_mid;
+        if (fp8) launch_tile<TK_L1, TF_FP8, 0, kMidTM>(a1, st);
+        else launch_tile<TK_L1, TF_FP4, 0, kMidTM>(a1, st);
+      }
       if (big) {
         a1.nslots = slots_big;
         if (fp8) launch_tile<TK_L1, TF_FP8, 0>(a1, st);
@@ -494,6 +507,11 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       a2.nslots = slots_small;
       if (fp8) launch_tile<TK_L2, TF_FP8, 0, 32>(a2, st);
       else launch_tile<TK_L2, TF_FP4, 0, 32>(a2, st);
+      if (mid) {
+        a2.nslots = slots_mid;
+        if (fp8) launch_tile<TK_L2, TF_FP8, 0, kMidTM>(a2, st);
+        else launch_tile<TK_L2, TF_FP4, 0, kMidTM>(a2, st);
+      }
       if (big) {
         a2.nslots = slots_big;
         if (fp8) launch_tile<TK_L2, TF_FP8, 0>(a2, st);

@@ -31,6 +31,7 @@ constexpr int kTM = 128;
 constexpr int kTN = 256;
 constexpr int kBigMinRows = 128;  // experts with at least this many rows use 128-row tiles (by default)
 constexpr int kHugeTM = 256;      // ... and from this many rows on, 256-row tiles where they pay
+constexpr int kMidTM = 64;        // experts between 32 and kBigMinRows rows, when the experts average over 32
 
 // An expert with c >= huge rows takes 256-row tiles for its first c / 256 *
 // 256 rows; a tail of more than 128 rows takes one more (partly padded)
@@ -70,6 +71,7 @@ struct TileArgs {
   int nslots;                     // dense: row tiles; routed: unused (the tile count comes from expert_offsets)
   int big_rows;                   // routed: experts with >= big_rows rows take 128-row tiles, the others 32-row tiles
   int huge_rows;                  // routed: experts with >= huge_rows rows take 256-row tiles instead
+  int mid_rows;                   // routed: experts with mid_rows .. big_rows - 1 rows take 64-row tiles
 };
 
 // Persistent: one workgroup per CU works through a list of tiles.  Tile t
@@ -84,9 +86,10 @@ struct TileArgs {
 // dense GEMMs with many rows): a quarter less LDS and L2 traffic per FLOP
 // than 128 rows and half the barriers, one stage in flight.  TM = 128:
 // experts with big_rows .. huge_rows - 1 rows, 8 waves as 2 (M) x 4 (N) of
-// 64 x 64.  TM = 32: tiles of 32 rows for the experts with fewer rows (decode
-// sizes), 8 waves of 32 x 32, a deeper ring.  Either way 256 B rows (weight
-// rows) per tile.
+// 64 x 64.  TM = 64: experts with mid_rows .. big_rows - 1 rows, 8 waves of
+// 64 x 32, three stages.  TM = 32: tiles of 32 rows for the experts with
+// fewer rows (decode sizes), 8 waves of 32 x 32, a deeper ring.  Either way
+// 256 B rows (weight rows) per tile.
 // LDS of one workgroup of the tiled kernel (ring + expert tables + per-tile
 // side data), carved from one buffer so that a persistent kernel running
 // several stages of the tail can reuse it.
@@ -95,10 +98,10 @@ struct TileLds {
   static constexpr bool kFP4 = FMT == TF_FP4;
   static constexpr bool kScaled = FMT != TF_BF16;
   static constexpr bool kRouted = KIND != TK_DENSE;
-  static constexpr int kStages = (TM == 256) ? 2 : (TM == 128) ? 3 : 4;
+  static constexpr int kStages = (TM == 256) ? 2 : (TM == 32) ? 4 : 3;
   static constexpr int kStage = TM * 128 + kTN * (kFP4 ? 64 : 128) + (kScaled ? 2048 : 0);
   static constexpr int kPairRows = (TM < 64) ? 64 : TM;
-  static constexpr int kWavesN = (TM == 32) ? 8 : 4;
+  static constexpr int kWavesN = (TM <= 64) ? 8 : 4;
   static constexpr int kRing = 0;
   static constexpr int kEoff = kRing + kStages * kStage;
   static constexpr int kPre = kEoff + 4 * (kRouted ? kTileMaxE + 1 : 1);
@@ -136,12 +139,12 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   constexpr bool kScaled = !kBF16;
   constexpr bool kRouted = KIND != TK_DENSE;
   constexpr bool kPaired = KIND == TK_L1 || (KIND == TK_DENSE && EPI == EPI_SWIGLU);
-  static_assert(TM == 256 || TM == 128 || (TM == 32 && KIND != TK_DENSE), "tile rows");
-  constexpr int kWavesM = (TM == 32) ? 1 : 2;        // wave grid over the tile
+  static_assert(TM == 256 || TM == 128 || ((TM == 64 || TM == 32) && KIND != TK_DENSE), "tile rows");
+  constexpr int kWavesM = (TM <= 64) ? 1 : 2;        // wave grid over the tile
   constexpr int kWavesN = 8 / kWavesM;
   constexpr int kMT = TM / (16 * kWavesM);           // 16-row MFMA tiles per wave
   constexpr int kNJ = kTN / (16 * kWavesN);          // 16-column MFMA tiles per wave
-  constexpr int kStages = (TM == 256) ? 2 : (TM == 128) ? 3 : 4;  // ring depth (kStages - 1 steps in flight)
+  constexpr int kStages = (TM == 256) ? 2 : (TM == 32) ? 4 : 3;  // ring depth (kStages - 1 steps in flight)
   constexpr int kABlk = TM / 8;                      // 1 KB blocks of A per stage
   constexpr int kAL = (kABlk + 7) / 8;               // A blocks loaded per wave
   constexpr int kABytes = TM * 128;                  // 32, 16 or 4 KB
@@ -202,7 +205,8 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
           if (use256(c, p.huge_rows)) return tail128(c) ? 1 : 0;
           return c >= p.big_rows ? (c + TM - 1) / TM : 0;
         }
-        return c < p.big_rows ? (c + TM - 1) / TM : 0;
+        if (TM == 64) return (c >= p.mid_rows && c < p.big_rows) ? (c + TM - 1) / TM : 0;
+        return (c < p.big_rows && c < p.mid_rows) ? (c + TM - 1) / TM : 0;
       };
       int local = 0;
       for (int e = eb; e < ee; ++e) local += ntile(e);

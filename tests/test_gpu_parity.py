@@ -267,6 +267,21 @@ def test_forward_256_row_tiles_short_tail(wfmt):
     check_forward(dev, inp)
 
 
+@pytest.mark.parametrize("wfmt", [0, 1])
+@pytest.mark.parametrize("Mr,E", [(200, 8), (600, 16)])
+def test_forward_64_row_tiles(Mr, E, wfmt):
+    # experts averaging more than 32 rows: those with 33 .. 127 rows take
+    # 64-row tiles (ragged), the others 32-row tiles, and from 257 tokens on
+    # experts with 128 rows or more take the 128- and 256-row tiles
+    wl = synth.Workload("mid", Mr=Mr, Ms=Mr + 20, E=E, k=2, I=512, Is=256, wfmt=wfmt, seed=53 + E, H=1024, L=512,
+                        zipf_s=0.6)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    loads = np.diff(to_np(dev.offsets))
+    assert np.any((loads > 32) & (loads < 128)) and np.any(loads % 64 != 0), loads
+    check_forward(dev, inp)
+
+
 def test_forward_heavy_expert_many_row_tiles():
     # all-equal logits: every token goes to experts 0..k-1, 100 rows each (4 row tiles per expert)
     wl = synth.Workload("heavy", Mr=100, Ms=100, E=6, k=2, I=512, Is=128, wfmt=0, seed=22, zero_router=True)
