@@ -220,6 +220,13 @@ void launch_tile(const TileArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((k_tile<KIND, FMT, EPI, TM>), dim3(wg), dim3(512), 0, st, a);
 }
 
+// The 32-row and 64-row tiles in one persistent launch (one workgroup per CU)
+template <int KIND, int FMT>
+void launch_small_mid(const TileArgs& a, hipStream_t st) {
+  const unsigned wg = std::max(8u, num_cus() / 8 * 8);
+  hipLaunchKernelGGL((k_tile_small_mid<KIND, FMT>), dim3(wg), dim3(512), 0, st, a);
+}
+
 template <int kEpi>
 void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int M, int N, int K, float* partial,
                   const DenseEpi& ep, hipStream_t st, bool reduce = true) {
@@ -436,12 +443,11 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   const bool mid = tiled && R > static_cast<size_t>(32) * E;
   ta.mid_rows = mid ? 33 : 0x7fffffff;
   // bounds on the row tiles, which size the grids: ceil(c / 128) <= c / 64
-  // for c >= 128, ceil(c / 64) <= c / 32 for c >= 33, and ceil(c / 32) <=
-  // c / 32 + 1
+  // for c >= 128, and ceil(c / 32) <= c / 32 + 1 (the launch of the 32- and
+  // 64-row tiles together takes one workgroup per CU)
   const int slots_big = static_cast<int>(R / (kTM / 2));
   const int slots_huge = static_cast<int>(R / (kHugeTM / 2));  // ceil(c / 256) <= c / 128 for c >= 256
   const int slots_small = static_cast<int>(R / 32 + E);
-  const int slots_mid = static_cast<int>(R / 32);
   mark(1);
   if (Mr > 0) {
     if (!tiled) {
@@ -467,12 +473,12 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       a1.half = I;
       a1.ntn = I / 128;
       a1.nslots = slots_small;
-      if (fp8) launch_tile<TK_L1, TF_FP8, 0, 32>(a1, st);
-      else launch_tile<TK_L1, TF_FP4, 0, 32>(a1, st);
       if (mid) {
-        a1.nslots = slots_mid;
-        if (fp8) launch_tile<TK_L1, TF_FP8, 0, kMidTM>(a1, st);
-        else launch_tile<TK_L1, TF_FP4, 0, kMidTM>(a1, st);
+        if (fp8) launch_small_mid<TK_L1, TF_FP8>(a1, st);
+        else launch_small_mid<TK_L1, TF_FP4>(a1, st);
+      } else {
+        if (fp8) launch_tile<TK_L1, TF_FP8, 0, 32>(a1, st);
+        else launch_tile<TK_L1, TF_FP4, 0, 32>(a1, st);
       }
       if (big) {
         a1.nslots = slots_big;
@@ -505,12 +511,12 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       a2.half = 0;
       a2.ntn = L / kTN;
       a2.nslots = slots_small;
-      if (fp8) launch_tile<TK_L2, TF_FP8, 0, 32>(a2, st);
-      else launch_tile<TK_L2, TF_FP4, 0, 32>(a2, st);
       if (mid) {
-        a2.nslots = slots_mid;
-        if (fp8) launch_tile<TK_L2, TF_FP8, 0, kMidTM>(a2, st);
-        else launch_tile<TK_L2, TF_FP4, 0, kMidTM>(a2, st);
+        if (fp8) launch_small_mid<TK_L2, TF_FP8>(a2, st);
+        else launch_small_mid<TK_L2, TF_FP4>(a2, st);
+      } else {
+        if (fp8) launch_tile<TK_L2, TF_FP8, 0, 32>(a2, st);
+        else launch_tile<TK_L2, TF_FP4, 0, 32>(a2, st);
       }
       if (big) {
         a2.nslots = slots_big;

@@ -756,4 +756,22 @@ __global__ __launch_bounds__(512) void k_tile(TileArgs p) {
   tile_run<KIND, FMT, EPI, TM>(p, TileSmem{ring, s_eoff, s_pre, s_pair, s_wsc, s_amax}, blockIdx.x, gridDim.x);
 }
 
+// The 32-row and 64-row tiles of one routed GEMM in one persistent launch:
+// each workgroup takes its share of the 32-row tiles, then of the 64-row
+// ones (a separate launch for a few hundred 64-row tiles paid its own ramp
+// and tail).
+template <int KIND, int FMT>
+constexpr int small_mid_lds() {
+  constexpr int a = TileLds<KIND, FMT, 32>::kBytes, b = TileLds<KIND, FMT, kMidTM>::kBytes;
+  return a > b ? a : b;
+}
+
+template <int KIND, int FMT>
+__global__ __launch_bounds__(512) void k_tile_small_mid(TileArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[small_mid_lds<KIND, FMT>()];
+  tile_run<KIND, FMT, 0, 32>(p, tile_smem_in<KIND, FMT, 32>(smem), blockIdx.x, gridDim.x);
+  __syncthreads();
+  tile_run<KIND, FMT, 0, kMidTM>(p, tile_smem_in<KIND, FMT, kMidTM>(smem), blockIdx.x, gridDim.x);
+}
+
 }  // namespace moe_tail
