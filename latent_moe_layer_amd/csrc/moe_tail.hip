@@ -391,8 +391,8 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
     const FusedArgs f = fused_args(d, w, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, lay, plans);
     const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
     const long qblocks = static_cast<long>(Mr) * (L / 128);
-    hipLaunchKernelGGL(k_quant_clear, dim3(static_cast<unsigned>((qblocks + 3) / 4)), dim3(256), 0, st, x_lat, xq, sx,
-                       Mr, L, f.sync, kSyncWords);
+    hipLaunchKernelGGL(k_quant_clear, dim3(quant_grid(qblocks)), dim3(256), 0, st, x_lat, xq, sx, qblocks, f.sync,
+                       kSyncWords);
     if (fp8) launch_tile<TK_L1, TF_FP8, 0, 32>(f.l1, st);
     else launch_tile<TK_L1, TF_FP4, 0, 32>(f.l1, st);
     const unsigned pgrid = std::max(8u, num_cus() / 8 * 8);  // persistent: one workgroup per CU
@@ -414,8 +414,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   mark(0);
   if (Mr > 0) {
     const long blocks = static_cast<long>(Mr) * (L / 128);
-    hipLaunchKernelGGL(k_quant_1x128<true>, dim3(static_cast<unsigned>((blocks + 3) / 4)), dim3(256), 0, st, x_lat,
-                       xq, sx, Mr, L);
+    hipLaunchKernelGGL(k_quant_1x128<true>, dim3(quant_grid(blocks)), dim3(256), 0, st, x_lat, xq, sx, blocks);
   }
   // 1, 2: routed L1 and L2 on the persistent LDS-tiled kernel: 128-row tiles
   // for experts with at least kBigMinRows rows, 32-row tiles for the others;
@@ -603,8 +602,8 @@ int fused_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint1
   const FusedArgs f = fused_args(d, w, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, lay, plans);
   {
     const long blocks = static_cast<long>(Mr) * (L / 128);
-    hipLaunchKernelGGL(k_quant_clear, dim3(static_cast<unsigned>((blocks + 3) / 4)), dim3(256), 0, st, x_lat,
-                       at<uint8_t>(ws, lay.xq), at<float>(ws, lay.sx), Mr, L, f.sync, kSyncWords);
+    hipLaunchKernelGGL(k_quant_clear, dim3(quant_grid(blocks)), dim3(256), 0, st, x_lat, at<uint8_t>(ws, lay.xq),
+                       at<float>(ws, lay.sx), blocks, f.sync, kSyncWords);
   }
   if (fp8) hipLaunchKernelGGL(k_tail_small<TF_FP8>, dim3(grid), dim3(512), 0, st, f);
   else hipLaunchKernelGGL(k_tail_small<TF_FP4>, dim3(grid), dim3(512), 0, st, f);
@@ -740,11 +739,11 @@ int moe_tail_quant_fp8_1x128(const void* x, int32_t x_is_bf16, int32_t rows, int
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const long blocks = static_cast<long>(rows) * (cols / 128);
-  const dim3 grid(static_cast<unsigned>((blocks + 3) / 4));
+  const dim3 grid(quant_grid(blocks));
   if (x_is_bf16)
-    hipLaunchKernelGGL(k_quant_1x128<true>, grid, dim3(256), 0, st, x, codes, scales, rows, cols);
+    hipLaunchKernelGGL(k_quant_1x128<true>, grid, dim3(256), 0, st, x, codes, scales, blocks);
   else
-    hipLaunchKernelGGL(k_quant_1x128<false>, grid, dim3(256), 0, st, x, codes, scales, rows, cols);
+    hipLaunchKernelGGL(k_quant_1x128<false>, grid, dim3(256), 0, st, x, codes, scales, blocks);
   return launched();
 }
 

@@ -5,51 +5,76 @@
 
 namespace moe_tail {
 
-// One wave per (row, 128-wide block); each lane owns two neighbouring
-// elements.  s = amax / 448 (IEEE division), 1.0 for an all-zero block;
-// code = e4m3(x / s).  Activations are quantized per 1x128 block with fp32
-// scales, matching the 128-wide K blocks of the weights.
+// Per 1x128 block: s = amax / 448 (IEEE division), 1.0 for an all-zero
+// block; code = e4m3(x / s).  Activations are quantized per 1x128 block with
+// fp32 scales, matching the 128-wide K blocks of the weights.  A row-major
+// [rows, cols] matrix is a sequence of blocks (cols % 128 == 0), block i
+// covering elements [128 i, 128 i + 128) and owning scale i.  Wave w takes
+// blocks 4 w .. 4 w + 3: lanes 16 j .. 16 j + 15 block 4 w + j, eight
+// neighbouring elements each (16-byte loads).
+constexpr int kQuantBlocksPerWave = 4;
+
 template <bool kBf16In>
-__device__ __forceinline__ void quant_block(const void* __restrict__ x, uint8_t* __restrict__ codes,
-                                            float* __restrict__ scales, int rows, int cols, long blk, int lane) {
-  const int nb = cols / 128;
-  if (blk >= static_cast<long>(rows) * nb) return;
-  const long r = blk / nb;
-  const int b = static_cast<int>(blk % nb);
-  const size_t base = static_cast<size_t>(r) * cols + 128 * b + 2 * lane;
-  float v0, v1;
+__device__ __forceinline__ void quant_wave(const void* __restrict__ x, uint8_t* __restrict__ codes,
+                                           float* __restrict__ scales, long nblocks, long w, int lane) {
+  const long blk = w * kQuantBlocksPerWave + (lane >> 4);
+  if (w * kQuantBlocksPerWave >= nblocks) return;  // wave-uniform
+  const bool live = blk < nblocks;                 // uniform within a block's 16 lanes
+  const size_t e0 = static_cast<size_t>(live ? blk : 0) * 128 + 8 * (lane & 15);
+  float v[8];
   if (kBf16In) {
-    const uint32_t pair = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(x) + base);
-    v0 = bf16_bits_to_f32(pair & 0xffffu);
-    v1 = bf16_bits_to_f32(pair >> 16);
+    const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e0);
+    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_bits_to_f32(u[i] & 0xffffu);
+      v[2 * i + 1] = bf16_bits_to_f32(u[i] >> 16);
+    }
   } else {
-    const float2 p = *reinterpret_cast<const float2*>(static_cast<const float*>(x) + base);
-    v0 = p.x;
-    v1 = p.y;
+    const float4 p0 = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + e0);
+    const float4 p1 = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + e0 + 4);
+    v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+    v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
   }
-  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  const float amax = group16_max(m);
   const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
-  const uint32_t q = f32_to_e4m3(v0 / s) | (f32_to_e4m3(v1 / s) << 8);
-  *reinterpret_cast<uint16_t*>(codes + base) = static_cast<uint16_t>(q);
-  if (lane == 0) scales[static_cast<size_t>(r) * nb + b] = s;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= f32_to_e4m3(v[i] / s) << (8 * i);
+    hi |= f32_to_e4m3(v[4 + i] / s) << (8 * i);
+  }
+  if (live) {
+    *reinterpret_cast<uint2*>(codes + e0) = make_uint2(lo, hi);
+    if ((lane & 15) == 0) scales[blk] = s;
+  }
 }
 
 template <bool kBf16In>
 __global__ __launch_bounds__(256) void k_quant_1x128(const void* __restrict__ x, uint8_t* __restrict__ codes,
-                                                     float* __restrict__ scales, int rows, int cols) {
-  quant_block<kBf16In>(x, codes, scales, rows, cols, static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6),
-                       threadIdx.x & 63);
+                                                     float* __restrict__ scales, long nblocks) {
+  quant_wave<kBf16In>(x, codes, scales, nblocks, static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6),
+                      threadIdx.x & 63);
+}
+
+// Workgroups of 256 threads for nblocks 1x128 blocks.
+inline unsigned quant_grid(long nblocks) {
+  const long per = 4L * kQuantBlocksPerWave;
+  return static_cast<unsigned>((nblocks + per - 1) / per);
 }
 
 // The same quantizer of x, whose first workgroup also clears n words at
 // `zero` (the completion counters of the single-launch tail that follows).
 __global__ __launch_bounds__(256) void k_quant_clear(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
-                                                     float* __restrict__ scales, int rows, int cols,
+                                                     float* __restrict__ scales, long nblocks,
                                                      int* __restrict__ zero, int n) {
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < n; i += 256) zero[i] = 0;
-  quant_block<true>(x, codes, scales, rows, cols, static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6),
-                    threadIdx.x & 63);
+  quant_wave<true>(x, codes, scales, nblocks, static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6),
+                   threadIdx.x & 63);
 }
 
 // One workgroup (256 threads) per routed token: z = sum_j w_j * y[row(t, j)]
