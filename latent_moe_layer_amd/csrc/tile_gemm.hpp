@@ -38,8 +38,8 @@ constexpr int kMidTM = 64;        // experts between 32 and kBigMinRows rows, wh
 // 256-row tile, a shorter tail one 128-row tile.  Switching whole experts
 // to 128-row tiles measured slower at the prefill loads (routed L1 752
 // against 699 us: a 128-row tile does half a 256-row tile's work per byte it
-// moves), while moving only the short tails took routed L1 from 699 to 678
-// us.
+// moves); moving only the short tails measured about neutral in kernel time
+// (621 us of 256-row tiles + 102 us of tails against 722 us).
 __host__ __device__ __forceinline__ bool use256(int c, int huge) { return c >= huge; }
 // Such an expert's rows past its last full 256-row tile: up to 128 of them
 // go to one 128-row tile (a 256-row tile would be more than half padding),
