@@ -107,10 +107,13 @@ bool fuse_shared_reduce(const Plans& p, int32_t Mr, int32_t Ms) { return Mr > 0 
 
 // Shapes of the routed tiled kernel: expert tables in LDS (E <= kTileMaxE),
 // gathered x rows addressed with 32-bit offsets, a tile's side data loaded
-// kStages - 1 >= 3 steps ahead (K >= 384 for L1 and L2).
+// kStages - 1 steps ahead (K >= 384 for L1 and L2; MXFP4, whose small tiles
+// take two 128-wide K blocks per step: K a multiple of 256, at least 512).
 bool tiled_ok(const moe_tail_dims& d, int32_t Mr) {
+  const bool fp4_ok = d.wfmt != MOE_TAIL_W_MXFP4 ||
+                      (d.latent % 256 == 0 && d.inter % 256 == 0 && d.latent >= 512 && d.inter >= 512);
   return d.num_experts <= kTileMaxE && static_cast<size_t>(Mr) * d.latent < (1ull << 31) && d.latent >= 384 &&
-         d.inter >= 384;
+         d.inter >= 384 && fp4_ok;
 }
 
 // The single-launch tail covers decode sizes: every dense GEMM on the

@@ -51,6 +51,20 @@ constexpr int kTileMaxE = 512;    // expert tables of the routed kinds live in L
 enum { TK_L1 = 0, TK_L2 = 1, TK_DENSE = 2 };
 enum { TF_FP8 = 0, TF_FP4 = 1, TF_BF16 = 2 };
 
+// K halves (128-wide blocks) per stage.  An MXFP4 weight row holds 64 bytes
+// per 128 K, and loads of half lines run at a fraction of the rate of whole
+// ones (the 1024-token MXFP4 workload's routed L1 + L2: 460 + 238 us with
+// half-line weight loads, 387 + 199 us in a timing-only variant that moved
+// the same bytes as whole lines), so the 32- and 64-row MXFP4 tiles, which
+// stream weights, take two K blocks (one 128-byte line of every weight row)
+// per stage.  Larger tiles keep one: a 256-K stage of their activation rows
+// would not leave room for two stages.
+constexpr int tile_khalves(int FMT, int TM) { return (FMT == TF_FP4 && TM <= 128) ? 2 : 1; }
+// Ring depth: kStages - 1 stages in flight.
+constexpr int tile_stages(int FMT, int TM) {
+  return (TM == 256 || (TM == 128 && tile_khalves(FMT, TM) == 2)) ? 2 : (TM == 32 && tile_khalves(FMT, TM) == 1) ? 4 : 3;
+}
+
 struct TileArgs {
   const uint8_t* a;               // L1: xq [Mr, L]; L2: hq [R, I]; dense: bf16 rows [M, K]
   const float* a_scale;           // L1: sx [Mr, L/128]; L2: sh [R, I/128]
@@ -98,8 +112,10 @@ struct TileLds {
   static constexpr bool kFP4 = FMT == TF_FP4;
   static constexpr bool kScaled = FMT != TF_BF16;
   static constexpr bool kRouted = KIND != TK_DENSE;
-  static constexpr int kStages = (TM == 256) ? 2 : (TM == 32) ? 4 : 3;
-  static constexpr int kStage = TM * 128 + kTN * (kFP4 ? 64 : 128) + (kScaled ? 2048 : 0);
+  static constexpr int kKH = tile_khalves(FMT, TM);
+  static constexpr int kStages = tile_stages(FMT, TM);
+  static constexpr int kStage = TM * 128 * kKH + kTN * ((kFP4 && kKH == 1) ? 64 : 128) +
+                                (kScaled ? (kKH == 2 ? 8 * TM + 2048 : 2048) : 0);
   static constexpr int kPairRows = (TM < 64) ? 64 : TM;
   static constexpr int kWavesN = (TM <= 64) ? 8 : 4;
   static constexpr int kRing = 0;
@@ -144,21 +160,32 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   constexpr int kWavesN = 8 / kWavesM;
   constexpr int kMT = TM / (16 * kWavesM);           // 16-row MFMA tiles per wave
   constexpr int kNJ = kTN / (16 * kWavesN);          // 16-column MFMA tiles per wave
-  constexpr int kStages = (TM == 256) ? 2 : (TM == 32) ? 4 : 3;  // ring depth (kStages - 1 steps in flight)
-  constexpr int kABlk = TM / 8;                      // 1 KB blocks of A per stage
-  constexpr int kAL = (kABlk + 7) / 8;               // A blocks loaded per wave
-  constexpr int kABytes = TM * 128;                  // 32, 16 or 4 KB
-  constexpr int kBBytes = kTN * (kFP4 ? 64 : 128);   // 16 or 32 KB
-  // scale words of a stage (2 KB, 256 bytes per wave): activation scales
-  // (one word per row) loaded by waves 0 .. kActW - 1, FP4 e8m0 words (four
-  // per B row) by the next four; the other waves load zeros into their part
+  constexpr int kStages = tile_stages(FMT, TM);     // ring depth (kStages - 1 steps in flight)
+  constexpr int kKH = tile_khalves(FMT, TM);         // 128-wide K blocks per stage
+  constexpr bool kB64 = kFP4 && kKH == 1;            // B rows of 64 bytes a stage (else 128)
+  constexpr int kABlk = TM / 8;                      // 1 KB blocks of A per stage and K block
+  constexpr int kAL = (kABlk + 7) / 8;               // A blocks loaded per wave and K block
+  constexpr int kABytes1 = TM * 128;                 // A bytes of one K block: 32, 16, 8 or 4 KB
+  constexpr int kABytes = kABytes1 * kKH;
+  constexpr int kBBytes = kTN * (kB64 ? 64 : 128);   // 16 or 32 KB
+  // scale words of a stage.  One K block (2 KB, 256 bytes per wave):
+  // activation scales (one word per row) loaded by waves 0 .. kActW - 1, FP4
+  // e8m0 words (four per B row) by the next four; the other waves load zeros
+  // into their part.  Two K blocks (MXFP4 small tiles): activation words
+  // [half][row] (8 TM bytes: every wave loads its share of them, waves
+  // past the 2 TM words repeating the first ones, the same bytes to the same
+  // place), then the e8m0 words [half][B row] (2 KB, wave w: half w / 4,
+  // B rows 64 (w % 4) + lane).
   constexpr int kActW = (TM + 63) / 64 < 2 ? 2 : (TM + 63) / 64;
-  constexpr int kSOff = kABytes + kBBytes;           // activation [0, 4 TM), FP4 e8m0 [kE8Off, + 1024)
-  constexpr int kE8Off = 256 * kActW;
-  static_assert(kE8Off + 1024 <= 2048, "scale words");
-  constexpr int kStage = kSOff + (kScaled ? 2048 : 0);
-  constexpr int kBChunks = kFP4 ? 2 : 4;             // 16-byte B loads per thread and stage
-  constexpr int kLoads = kAL + kBChunks + (kScaled ? 1 : 0);  // direct loads per wave and stage
+  constexpr int kActW2 = (2 * TM) / 64;              // two K blocks: waves with distinct activation words
+  constexpr int kSOff = kABytes + kBBytes;
+  constexpr int kE8Off = (kKH == 2) ? 8 * TM : 256 * kActW;
+  static_assert(kKH == 2 || kE8Off + 1024 <= 2048, "scale words");
+  constexpr int kSBytes = !kScaled ? 0 : (kKH == 2) ? 8 * TM + 2048 : 2048;
+  constexpr int kStage = kSOff + kSBytes;
+  constexpr int kBChunks = kB64 ? 2 : 4;             // 16-byte B loads per thread and stage
+  constexpr int kSLoads = kScaled ? kKH : 0;         // 4-byte scale loads per thread and stage
+  constexpr int kLoads = kAL * kKH + kBChunks + kSLoads;  // direct loads per wave and stage
   constexpr uint32_t kNoRow = 0x80000000u;           // offset past any buffer: reads zeros
   using Lds = TileLds<KIND, FMT, TM>;
   static_assert(Lds::kStage == kStage && Lds::kStages == kStages && Lds::kWavesN == kWavesN, "LDS plan");
@@ -179,7 +206,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int l16 = lane & 15, g = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int nk = kBF16 ? p.K / 64 : p.K / 128;    // K steps of 128 bytes (at least 2)
+  const int nk = kBF16 ? p.K / 64 : p.K / (128 * kKH);  // K steps (stages of the stream) of a tile
   const int nkb = p.K / 128;                       // scale blocks along K (scaled formats)
   const int elem = kBF16 ? 2 : 1;                  // bytes per A element
   const int nbrows = kPaired ? 2 * p.half : p.N;  // B rows of one expert / of the dense matrix
@@ -293,8 +320,8 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
 
   // load offsets of one tile
   struct Iss {
-    __amdgpu_buffer_rsrc_t ra, rb, rs;
-    uint32_t a_off[kAL], b_off[kBChunks], s_off;
+    __amdgpu_buffer_rsrc_t ra, rb, rs, rs2;
+    uint32_t a_off[kAL], b_off[kBChunks], s_off, s_off2;
   };
   auto make_iss = [&](const Desc& d, int buf) -> Iss {
     Iss r;
@@ -317,8 +344,8 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     r.rb = make_rsrc(p.b + static_cast<size_t>(d.e) * nbrows * brow_bytes, static_cast<uint32_t>(static_cast<size_t>(nbrows) * brow_bytes));
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i) {
-      const int row = kFP4 ? 128 * i + 16 * wave + t_r : st_r0 + 64 * i;
-      const int c = kFP4 ? t_g : st_c;
+      const int row = kB64 ? 128 * i + 16 * wave + t_r : st_r0 + 64 * i;
+      const int c = kB64 ? t_g : st_c;
       r.b_off[i] = static_cast<uint32_t>(static_cast<size_t>(wrow(d.nt, row)) * brow_bytes) + 16u * c;
     }
     // scale words, one 4-byte load per lane and stage: waves 0-1 the
@@ -327,7 +354,24 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     // other waves load zeros
     r.rs = z_rsrc;
     r.s_off = kNoRow;
-    if (kScaled) {
+    r.rs2 = z_rsrc;
+    r.s_off2 = kNoRow;
+    if (kScaled && kKH == 2) {
+      // e8m0 words of half wv / 4, B row 64 (wv % 4) + lane (8 bytes a row and stage)
+      const int j = 64 * (wv & 3) + lane;
+      r.rs = make_rsrc(static_cast<const uint8_t*>(p.b_scale) + static_cast<size_t>(d.e) * nbrows * wpr,
+                       static_cast<uint32_t>(nbrows * wpr));
+      r.s_off = static_cast<uint32_t>(wrow(d.nt, j) * wpr) + 4u * static_cast<uint32_t>(wv >> 2);
+      // activation word q: half q / TM, row q % TM
+      const int q = 64 * (wv % kActW2) + lane, hh = q / TM, row = q - hh * TM;
+      const float* sbase = (KIND == TK_L1) ? p.a_scale : p.a_scale + static_cast<size_t>(d.row0) * nkb;
+      const size_t srows = (KIND == TK_L1) ? static_cast<size_t>(p.M) : static_cast<size_t>(d.rows);
+      r.rs2 = make_rsrc(sbase, static_cast<uint32_t>(srows * nkb * 4));
+      if (row < d.rows) {
+        const size_t ar = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
+        r.s_off2 = static_cast<uint32_t>(ar * nkb * 4) + 4u * static_cast<uint32_t>(hh);
+      }
+    } else if (kScaled) {
       if (wv < (TM + 63) / 64) {
         const int row = 64 * wv + lane;
         const float* sbase = (KIND == TK_L1) ? p.a_scale : p.a_scale + static_cast<size_t>(d.row0) * nkb;
@@ -349,11 +393,19 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   // stage k of a tile -> ring slot; live == false loads zeros (no memory traffic)
   auto issue = [&](uint8_t* st, const Iss& r, int k, bool live) {
 #pragma unroll
-    for (int i = 0; i < kAL; ++i) dma16(live ? r.ra : z_rsrc, st + 1024 * ((wv + 8 * i) % kABlk), r.a_off[i], k * 128);
+    for (int h = 0; h < kKH; ++h)
+#pragma unroll
+      for (int i = 0; i < kAL; ++i)
+        dma16(live ? r.ra : z_rsrc, st + kABytes1 * h + 1024 * ((wv + 8 * i) % kABlk), r.a_off[i], (k * kKH + h) * 128);
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i)
-      dma16(live ? r.rb : z_rsrc, st + kABytes + 8192 * i + 1024 * wv, r.b_off[i], kFP4 ? k * 64 : k * 128);
-    if (kScaled) dma4(live ? r.rs : z_rsrc, st + kSOff + 256 * wv, r.s_off, 4 * k);
+      dma16(live ? r.rb : z_rsrc, st + kABytes + 8192 * i + 1024 * wv, r.b_off[i], kB64 ? k * 64 : k * 128);
+    if (kScaled && kKH == 2) {
+      dma4(live ? r.rs : z_rsrc, st + kSOff + kE8Off + 256 * wv, r.s_off, 8 * k);
+      dma4(live ? r.rs2 : z_rsrc, st + kSOff + 256 * (wv % kActW2), r.s_off2, 8 * k);
+    } else if (kScaled) {
+      dma4(live ? r.rs : z_rsrc, st + kSOff + 256 * wv, r.s_off, 4 * k);
+    }
   };
   // per-tile data loaded ahead (issued first in a stage's batch, only by the
   // waves that carry it): L1 sorted pair ids (one wave per 64 rows), FP8 weight-scale
@@ -403,14 +455,18 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       sw_lo = s_wsc[buf][(16 * bblk(0)) / 128][ks];
       sw_hi = s_wsc[buf][(16 * bblk(kNJ - 1)) / 128][ks];
     }
-    // weight fragments of the step (FP4: with their e8m0 scales)
-    auto load_b = [&](int j, i32x8& bfj, int& sbj) {
+    // weight fragments of K block h of the step (FP4: with their e8m0 scales)
+    auto load_b = [&](int j, i32x8& bfj, int& sbj, int h = 0) {
       const int bb = bblk(j);
       if (kFP4) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(st + kABytes + bb * 1024 + lane * 16);
+        // 64-byte rows: 16 rows x 16 bytes per chunk, lane l at 16 l; 128-byte
+        // rows (two K blocks): the swizzled layout of the 8-bit operands, K
+        // block h in chunks 4 h .. 4 h + 3
+        const i32x4 v = kB64 ? *reinterpret_cast<const i32x4*>(st + kABytes + bb * 1024 + lane * 16)
+                             : *reinterpret_cast<const i32x4*>(st + kABytes + bb * 2048 + (h ? f_hi : f_lo));
         const i32x4 z = {0, 0, 0, 0};
         bfj = __builtin_shufflevector(v, z, 0, 1, 2, 3, 4, 5, 6, 7);
-        sbj = st[kSOff + kE8Off + (16 * bb + l16) * 4 + g];
+        sbj = st[kSOff + kE8Off + 1024 * h + (16 * bb + l16) * 4 + g];
       } else {
         const uint8_t* bp = st + kABytes + bb * 2048;
         const i32x4 lo4 = *reinterpret_cast<const i32x4*>(bp + f_lo);
@@ -496,10 +552,12 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       }
       return;
     } else {
+  #pragma unroll
+     for (int h = 0; h < kKH; ++h) {
       i32x8 af[kMT];
   #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
-        const uint8_t* ab = st + (kMT * wm + mt) * 2048;
+        const uint8_t* ab = st + kABytes1 * h + (kMT * wm + mt) * 2048;
         const i32x4 lo4 = *reinterpret_cast<const i32x4*>(ab + f_lo);
         const i32x4 hi4 = *reinterpret_cast<const i32x4*>(ab + f_hi);
         af[mt] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -526,7 +584,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       constexpr int kSR = kTrans ? 1 : 4;
       float sc[2][kMT][kSR];
       {
-        const float* ss = reinterpret_cast<const float*>(st + kSOff);
+        const float* ss = reinterpret_cast<const float*>(st + kSOff) + TM * h;
   #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
           if (kTrans) {
@@ -551,7 +609,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
         i32x8 bf[kNJ];
         int sb[kNJ];
   #pragma unroll
-        for (int j = 0; j < kNJ; ++j) load_b(j, bf[j], sb[j]);
+        for (int j = 0; j < kNJ; ++j) load_b(j, bf[j], sb[j], h);
         f32x4 pr[2][kMT];
   #pragma unroll
         for (int j = 0; j <= kNJ; ++j) {
@@ -574,7 +632,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
         for (int j = 0; j < kNJ; ++j) {
           i32x8 bf;
           int sb;
-          load_b(j, bf, sb);
+          load_b(j, bf, sb, h);
           const int hsel = (kPaired && j >= kNJ / 2) ? 1 : 0;
   #pragma unroll
           for (int mt = 0; mt < kMT; ++mt) {
@@ -584,6 +642,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
           }
         }
       }
+     }
     }
   };
 

@@ -230,10 +230,11 @@ def test_fused_declines_large_token_counts():
     with pytest.raises(B.MoeTailError) as e:
         dev.forward(fused=True)
     assert e.value.status == B.MOE_TAIL_ERR_UNSUPPORTED
-    # narrow experts (I < 384) are declined too
-    wl2 = replace(wl, Ms=16, I=128)
-    dev2 = DeviceTail(synth.make_inputs(wl2), "cuda:0")
-    dev2.route()
-    with pytest.raises(B.MoeTailError) as e:
-        dev2.forward(fused=True)
-    assert e.value.status == B.MOE_TAIL_ERR_UNSUPPORTED
+    # narrow experts (I < 384) are declined too, and MXFP4 experts whose width
+    # is not a multiple of 256
+    for wl2 in (replace(wl, Ms=16, I=128), replace(wl, Ms=16, I=640, wfmt=synth.WFMT_MXFP4)):
+        dev2 = DeviceTail(synth.make_inputs(wl2), "cuda:0")
+        dev2.route()
+        with pytest.raises(B.MoeTailError) as e:
+            dev2.forward(fused=True)
+        assert e.value.status == B.MOE_TAIL_ERR_UNSUPPORTED

@@ -170,6 +170,16 @@ def test_forward_ragged(wfmt):
     check_forward(dev, inp)
 
 
+def test_forward_mxfp4_width_not_a_multiple_of_256():
+    # MXFP4 experts 640 wide: the tiled kernel's small MXFP4 tiles step 256 K
+    # at a time, so every routed GEMM runs on the row-streaming kernel here
+    wl = synth.Workload("fp4w640", Mr=37, Ms=53, E=8, k=3, I=640, Is=384, wfmt=synth.WFMT_MXFP4, seed=26,
+                        zipf_s=1.2, H=1024, L=512)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    check_forward(dev, inp)
+
+
 @pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4])
 def test_forward_tiled_path(wfmt):
     # Mr * k >= 2048 turns on the LDS-tiled routed kernel for experts with >= 128
