@@ -390,16 +390,22 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     }
     return r;
   };
-  // stage k of a tile -> ring slot; live == false loads zeros (no memory traffic)
-  auto issue = [&](uint8_t* st, const Iss& r, int k, bool live) {
+  // stage k of a tile -> ring slot; live == false loads zeros (no memory
+  // traffic).  part: 1 = the B rows, 2 = the A rows and the scale words, 3 = all
+  auto issue = [&](uint8_t* st, const Iss& r, int k, bool live, int part = 3) {
+    if (part & 2) {
 #pragma unroll
-    for (int h = 0; h < kKH; ++h)
+      for (int h = 0; h < kKH; ++h)
 #pragma unroll
-      for (int i = 0; i < kAL; ++i)
-        dma16(live ? r.ra : z_rsrc, st + kABytes1 * h + 1024 * ((wv + 8 * i) % kABlk), r.a_off[i], (k * kKH + h) * 128);
+        for (int i = 0; i < kAL; ++i)
+          dma16(live ? r.ra : z_rsrc, st + kABytes1 * h + 1024 * ((wv + 8 * i) % kABlk), r.a_off[i], (k * kKH + h) * 128);
+    }
+    if (part & 1) {
 #pragma unroll
-    for (int i = 0; i < kBChunks; ++i)
-      dma16(live ? r.rb : z_rsrc, st + kABytes + 8192 * i + 1024 * wv, r.b_off[i], kB64 ? k * 64 : k * 128);
+      for (int i = 0; i < kBChunks; ++i)
+        dma16(live ? r.rb : z_rsrc, st + kABytes + 8192 * i + 1024 * wv, r.b_off[i], kB64 ? k * 64 : k * 128);
+    }
+    if (!(part & 2)) return;
     if (kScaled && kKH == 2) {
       dma4(live ? r.rs : z_rsrc, st + kSOff + kE8Off + 256 * wv, r.s_off, 8 * k);
       dma4(live ? r.rs2 : z_rsrc, st + kSOff + 256 * (wv % kActW2), r.s_off2, 8 * k);
@@ -732,16 +738,18 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     }
   };
 
-  // ---- prologue: tile 0's pair ids and weight scales with ordinary loads
+  // ---- prologue.  The weight rows of tile 0's first kStages - 1 stages
+  // depend only on its expert and n tile, so they are loaded first; then,
+  // once tile 0's pair ids and weight scales (direct loads issued before
+  // them) have landed, the gathered A rows and the scale words of those
+  // stages.  Loads in flight after the A part of stage s: the A parts of the
+  // stages after it, then the full stages issued by the loop (ring_barrier
+  // counts below).
+  constexpr int kS = kStages - 1;        // stages in flight
+  constexpr int kA = kLoads - kBChunks;  // A and scale loads per wave and stage
+  static_assert(kStages >= 2 && kStages <= 4, "prologue barrier counts");
   Desc dc = desc(0);
-  if (KIND == TK_L1 && tid < TM) s_pair[0][tid] = (tid < dc.rows) ? p.sorted_pair[dc.row0 + tid] : 0;
-  if (FMT == TF_FP8 && tid < 2 * nkb) {
-    const int q = tid / nkb, kb = tid - q * nkb;
-    const int wr = wrow(dc.nt, 128 * q);
-    s_wsc[0][q][kb] = (wr < nbrows) ? static_cast<const float*>(p.b_scale)[(static_cast<size_t>(dc.e) * (nbrows / 128) + wr / 128) * nkb + kb]
-                                    : 0.0f;
-  }
-  __syncthreads();
+  aux(dc, 0);
 
   // Stage G of the stream is K step G % nk of tile G / nk and sits in ring
   // slot G % kStages.  Step G: wait for stage G (every wave's loads), start
@@ -752,12 +760,24 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   // and weight scales are loaded with the first stage of the tile before it;
   // with nk >= kStages - 1 (the launcher's condition) they have landed before
   // their first use and the buffer j % 3 they go to is no longer read.
-  Iss is = make_iss(dc, 0);
+  Iss is = make_iss(dc, 0);  // (its A offsets are not valid yet)
+#pragma unroll
+  for (int s = 0; s < kS; ++s) issue(ring + s * kStage, is, s, true, 1);
+  vm_wait<kBChunks * kS>();  // this wave's pair-id / weight-scale loads
+  lds_barrier();             // every wave's
+  is = make_iss(dc, 0);
+  if (n_my > 1) aux(desc(1), 1);
+#pragma unroll
+  for (int s = 0; s < kS; ++s) issue(ring + s * kStage, is, s, true, 2);
   int ji = 0;  // tile of `is`
   const int G = n_my * nk;
   // the stream position the next issue loads: tile ij, K step ik, ring slot
   // islot (counters instead of divisions by nk: they run every step)
-  int ij = 0, ik = 0, islot = 0;
+  int ij = 0, ik = kS, islot = kS;
+  if (ik == nk) {
+    ik = 0;
+    ij = 1;
+  }
   auto issue_next = [&]() {
     uint8_t* st = ring + islot * kStage;
     if (ij >= n_my) {
@@ -776,11 +796,11 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     }
     if (++islot == kStages) islot = 0;
   };
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue_next();
   int j = 0, ks = 0, jb = 0, cslot = 0;  // the computed stage: tile j (buffer jb = j % 3), K step ks, slot
   for (int gg = 0; gg < G; ++gg) {
-    ring_barrier<kLoads * (kStages - 2)>();
+    if (kStages >= 3 && gg == 0) ring_barrier<kA * (kStages - 2)>();
+    else if (kStages >= 4 && gg == 1) ring_barrier<kA * (kStages - 3) + kLoads>();
+    else ring_barrier<kLoads * (kStages - 2)>();
     issue_next();
     if (ks == 0) {
       if (j > 0) dc = desc(j);
