@@ -324,6 +324,14 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     uint32_t a_off[kAL], b_off[kBChunks], s_off, s_off2;
   };
   auto make_iss = [&](const Desc& d, int buf) -> Iss {
+    // the lane's coordinates, recomputed from an opaque copy of the thread
+    // index rather than held live across the K loop (the 256-row L1 tile has
+    // no registers to spare, and a spilled value's reload would wait for
+    // every load in flight)
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int lane = tid_o & 63, wave = tid_o >> 6, q8 = lane >> 3, st_c = (lane & 7) ^ q8, st_r0 = 8 * wave + q8;
+    const int t_r = tid_o & 15, t_g = (tid_o >> 4) & 3;
     Iss r;
     if (KIND == TK_L1)  // gathered token rows of x codes
       r.ra = make_rsrc(p.a, static_cast<uint32_t>(static_cast<size_t>(p.M) * a_row_bytes));
@@ -417,6 +425,9 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   // waves that carry it): L1 sorted pair ids (one wave per 64 rows), FP8 weight-scale
   // rows (waves kWscW, kWscW + 1)
   auto aux = [&](const Desc& d, int buf) {
+    int tid_o = threadIdx.x;  // (recomputed, as in make_iss)
+    asm volatile("" : "+v"(tid_o));
+    const int lane = tid_o & 63;
     if (KIND == TK_L1 && wv < kPairRows / 64) {
       dma4(make_rsrc(p.sorted_pair + d.row0, static_cast<uint32_t>(d.rows) * 4u), reinterpret_cast<uint8_t*>(&s_pair[buf][64 * wv]),
            4u * (64 * wv + lane), 0);
@@ -659,11 +670,9 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   // l16 (the others).
   auto epilogue = [&](const Desc& d, uint8_t* sq) {
     if (KIND == TK_L1) {
-      // h = silu(gate) * up: the wave's kH 16-column blocks of h; row amax
-      // over the tile's 128 h columns (the 4 lane groups of the row, then
-      // all kWavesN waves of the row).  h is computed twice, for the amax and
-      // then for the codes (the same arithmetic, so the same values), rather
-      // than held in registers beside the accumulators.
+      // h = silu(gate) * up: the wave's kH 16-column blocks of h, written
+      // over the gate accumulators; row amax over the tile's 128 h columns
+      // (the 4 lane groups of the row, then all kWavesN waves of the row)
       constexpr int kH = kNJ / 2;
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
@@ -671,7 +680,10 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
 #pragma unroll
         for (int j = 0; j < kH; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(silu_mul_fast(acc[mt][j][i], acc[mt][kH + j][i])));
+          for (int i = 0; i < 4; ++i) {
+            acc[mt][j][i] = silu_mul_fast(acc[mt][j][i], acc[mt][kH + j][i]);
+            m = fmaxf(m, fabsf(acc[mt][j][i]));
+          }
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
         if (g == 0) s_amax[wn][16 * kMT * wm + 16 * mt + l16] = m;
@@ -690,7 +702,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
           uint32_t q4 = 0;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            q4 |= static_cast<uint32_t>(f32_to_e4m3(silu_mul_fast(acc[mt][j][i], acc[mt][kH + j][i]) * inv)) << (8 * i);
+            q4 |= static_cast<uint32_t>(f32_to_e4m3(acc[mt][j][i] * inv)) << (8 * i);
           *reinterpret_cast<uint32_t*>(sq + r * 128 + 16 * (kH * wn + j) + 4 * g) = q4;
         }
         if (wn == 0 && g == 0 && r < d.rows) p.sh[static_cast<size_t>(d.row0 + r) * (p.half / 128) + d.nt] = s;
