@@ -511,16 +511,18 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
           b0[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_lo));
           b1[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const i32x4*>(bp + f_hi));
         }
+        // (the next row block's fragment is read while this one's products run)
+        i32x8 a_cur = load_a(0);
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
-          const i32x8 a8 = load_a(mt);
-          const i32x4 alo = __builtin_shufflevector(a8, a8, 0, 1, 2, 3);
-          const i32x4 ahi = __builtin_shufflevector(a8, a8, 4, 5, 6, 7);
+          const i32x4 alo = __builtin_shufflevector(a_cur, a_cur, 0, 1, 2, 3);
+          const i32x4 ahi = __builtin_shufflevector(a_cur, a_cur, 4, 5, 6, 7);
 #pragma unroll
           for (int j = 0; j < kNJ; ++j) {
             acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, alo), b0[j], acc[mt][j]);
             acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, ahi), b1[j], acc[mt][j]);
           }
+          if (mt + 1 < kMT) a_cur = load_a(mt + 1);
         }
         return;
       }
@@ -530,8 +532,9 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       for (int j = 0; j < kNJ; ++j) load_b(j, bf[j], sb[j]);
       const float* ss = reinterpret_cast<const float*>(st + kSOff);
       if (kTrans) {
-        // row block mt - 1 is promoted after row block mt's products are
-        // issued
+        // L1: row block mt - 1 is promoted after row block mt's products are
+        // issued, so the multiply-adds find their products done (reading the
+        // next block's operands ahead instead measured no faster here)
         f32x4 pr[2][kNJ];
 #pragma unroll
         for (int mt = 0; mt <= kMT; ++mt) {
@@ -554,17 +557,33 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
           }
         }
       } else {
+        // L2: software-pipelined by one row block: the activation fragment
+        // and scales of block mt + 1 are read from LDS while block mt's
+        // products run, and block mt is promoted after that (reading them
+        // just before their use left two LDS round trips per block exposed,
+        // which the stage loads landing in LDS lengthen: prefill routed L2
+        // 400 -> 368 us)
+        i32x8 a_cur = load_a(0);
+        f32x4 v_cur = *reinterpret_cast<const f32x4*>(ss + 16 * kMT * wm + 4 * g);
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) {
-          const i32x8 a8 = load_a(mt);
-          const f32x4 v = *reinterpret_cast<const f32x4*>(ss + 16 * kMT * wm + 16 * mt + 4 * g);
+          f32x4 pr[kNJ];
+#pragma unroll
+          for (int j = 0; j < kNJ; ++j) pr[j] = kFP4 ? mfma_fp8_fp4(a_cur, bf[j], sb[j]) : mfma_fp8(a_cur, bf[j]);
+          i32x8 a_nxt = a_cur;
+          f32x4 v_nxt = v_cur;
+          if (mt + 1 < kMT) {
+            a_nxt = load_a(mt + 1);
+            v_nxt = *reinterpret_cast<const f32x4*>(ss + 16 * kMT * wm + 16 * (mt + 1) + 4 * g);
+          }
 #pragma unroll
           for (int j = 0; j < kNJ; ++j) {
             const float sw = (kPaired && j >= kNJ / 2) ? sw_hi : sw_lo;
-            const f32x4 pr = kFP4 ? mfma_fp8_fp4(a8, bf[j], sb[j]) : mfma_fp8(a8, bf[j]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mt][j][i] += pr[i] * (v[i] * sw);
+            for (int i = 0; i < 4; ++i) acc[mt][j][i] += pr[j][i] * (v_cur[i] * sw);
           }
+          a_cur = a_nxt;
+          v_cur = v_nxt;
         }
       }
       return;
