@@ -292,6 +292,21 @@ def test_forward_64_row_tiles(Mr, E, wfmt):
     check_forward(dev, inp)
 
 
+@pytest.mark.parametrize("Mr", [40, 300])
+def test_forward_mxfp4_skewed_loads(Mr):
+    # strongly skewed MXFP4 loads (at 300 tokens: 0 .. 15, 20, 49, 100, 152,
+    # 251, 296, 300 rows): every tile size at once, experts with a handful of
+    # rows on the 32-row tiles, with MXFP4's two K blocks per step; more
+    # shared than routed tokens keeps the forward on one launch per stage
+    wl = synth.Workload("tiny16", Mr=Mr, Ms=320, E=16, k=4, I=512, Is=256, wfmt=synth.WFMT_MXFP4, seed=87,
+                        H=1024, L=512, zipf_s=1.2)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    loads = np.diff(to_np(dev.offsets))
+    assert np.any((loads > 0) & (loads <= 16)) and np.any(loads > 16), loads
+    check_forward(dev, inp)
+
+
 def test_forward_heavy_expert_many_row_tiles():
     # all-equal logits: every token goes to experts 0..k-1, 100 rows each (4 row tiles per expert)
     wl = synth.Workload("heavy", Mr=100, Ms=100, E=6, k=2, I=512, Is=128, wfmt=0, seed=22, zero_router=True)
