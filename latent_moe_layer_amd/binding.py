@@ -21,6 +21,7 @@ MOE_TAIL_ERR_DEVICE = 4
 
 MOE_TAIL_W_FP8_BLOCK128 = 0
 MOE_TAIL_W_MXFP4 = 1
+MOE_TAIL_W_MXFP4_PACKED = 2
 
 MOE_TAIL_WS_XQ, MOE_TAIL_WS_SX, MOE_TAIL_WS_HQ, MOE_TAIL_WS_SH, MOE_TAIL_WS_Y, MOE_TAIL_WS_RN, \
     MOE_TAIL_WS_HS, MOE_TAIL_WS_S = range(8)
@@ -29,7 +30,7 @@ MOE_TAIL_NUM_STAGES = 7
 
 EXPORTED = ("moe_tail_workspace_bytes", "moe_tail_workspace_layout", "moe_tail_route", "moe_tail_forward",
             "moe_tail_forward_add3", "moe_tail_forward_fused", "moe_tail_forward_profiled", "moe_tail_quant_fp8_1x128",
-            "moe_tail_strerror")
+            "moe_tail_pack_mxfp4_scales", "moe_tail_strerror")
 
 
 class MoeTailError(RuntimeError):
@@ -83,6 +84,9 @@ def lib() -> C.CDLL:
         L.moe_tail_quant_fp8_1x128.restype = C.c_int
         L.moe_tail_quant_fp8_1x128.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
                                                C.c_void_p, C.c_void_p]
+        L.moe_tail_pack_mxfp4_scales.restype = C.c_int
+        L.moe_tail_pack_mxfp4_scales.argtypes = [C.POINTER(Dims), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                                 C.c_void_p]
         L.moe_tail_strerror.restype = C.c_char_p
         L.moe_tail_strerror.argtypes = [C.c_int]
         _lib = L
@@ -172,6 +176,11 @@ def moe_tail_forward_profiled(dims: Dims, weights: Weights, x_lat, Mr: int, x_hi
     _check(lib().moe_tail_forward_profiled(C.byref(dims), C.byref(weights), ptr(x_lat), Mr, ptr(x_hid), Ms,
                                            C.byref(routing), ptr(out), ptr(shared_out), ptr(workspace), ws_bytes,
                                            stream_handle(stream), arr), "moe_tail_forward_profiled")
+
+
+def moe_tail_pack_mxfp4_scales(dims: Dims, w1_scale, w2_scale, w1_scale_packed, w2_scale_packed, stream=None) -> None:
+    _check(lib().moe_tail_pack_mxfp4_scales(C.byref(dims), ptr(w1_scale), ptr(w2_scale), ptr(w1_scale_packed),
+                                            ptr(w2_scale_packed), stream_handle(stream)), "moe_tail_pack_mxfp4_scales")
 
 
 def moe_tail_quant_fp8_1x128(x, x_is_bf16: bool, rows: int, cols: int, codes, scales, stream=None) -> None:

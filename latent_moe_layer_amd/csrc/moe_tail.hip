@@ -35,7 +35,8 @@ int check_dims(const moe_tail_dims* d) {
     return MOE_TAIL_ERR_INVALID;
   if (d->top_k < 1 || d->top_k > d->num_experts) return MOE_TAIL_ERR_INVALID;
   if (!(d->rms_eps > 0.0f) || !std::isfinite(d->rms_eps)) return MOE_TAIL_ERR_INVALID;
-  if (d->wfmt != MOE_TAIL_W_FP8_BLOCK128 && d->wfmt != MOE_TAIL_W_MXFP4) return MOE_TAIL_ERR_UNSUPPORTED;
+  if (d->wfmt != MOE_TAIL_W_FP8_BLOCK128 && d->wfmt != MOE_TAIL_W_MXFP4 && d->wfmt != MOE_TAIL_W_MXFP4_PACKED)
+    return MOE_TAIL_ERR_UNSUPPORTED;
   if (d->hidden % 256 || d->latent % 256 || d->latent > 256 * kNormMaxCols) return MOE_TAIL_ERR_UNSUPPORTED;
   if (d->inter % 128 || d->shared_inter % 128 || d->inter > 128 * kMaxKBlocks) return MOE_TAIL_ERR_UNSUPPORTED;
   if (d->latent > 128 * kMaxKBlocks) return MOE_TAIL_ERR_UNSUPPORTED;
@@ -110,7 +111,7 @@ bool fuse_shared_reduce(const Plans& p, int32_t Mr, int32_t Ms) { return Mr > 0 
 // kStages - 1 steps ahead (K >= 384 for L1 and L2; MXFP4, whose small tiles
 // take two 128-wide K blocks per step: K a multiple of 256, at least 512).
 bool tiled_ok(const moe_tail_dims& d, int32_t Mr) {
-  const bool fp4_ok = d.wfmt != MOE_TAIL_W_MXFP4 ||
+  const bool fp4_ok = d.wfmt == MOE_TAIL_W_FP8_BLOCK128 ||
                       (d.latent % 256 == 0 && d.inter % 256 == 0 && d.latent >= 512 && d.inter >= 512);
   return d.num_experts <= kTileMaxE && static_cast<size_t>(Mr) * d.latent < (1ull << 31) && d.latent >= 384 &&
          d.inter >= 384 && fp4_ok;
@@ -278,6 +279,7 @@ FusedArgs fused_args(const moe_tail_dims& d, const moe_tail_weights* w, int32_t 
   ta.big_rows = 0x7fffffff;
   ta.huge_rows = 0x7fffffff;
   ta.mid_rows = 0x7fffffff;
+  ta.e8_packed = d.wfmt == MOE_TAIL_W_MXFP4_PACKED;
   f.l1 = ta;
   f.l1.a = at<uint8_t>(ws, lay.xq);
   f.l1.a_scale = at<float>(ws, lay.sx);
@@ -352,6 +354,8 @@ int check_forward(const moe_tail_dims* dims, const moe_tail_weights* w, const ui
   if (residual != nullptr && !ptr_ok(residual, static_cast<size_t>(Mr) * H * 2)) return MOE_TAIL_ERR_INVALID;
   if ((Ms > Mr) != (shared_out != nullptr)) return MOE_TAIL_ERR_INVALID;
   if (shared_out != nullptr && !aligned16(shared_out)) return MOE_TAIL_ERR_INVALID;
+  // packed MXFP4 scales are read by the tiled kernels only
+  if (d.wfmt == MOE_TAIL_W_MXFP4_PACKED && !tiled_ok(d, Mr)) return MOE_TAIL_ERR_UNSUPPORTED;
   *lay = layout_of(d, Mr, Ms);
   if (ws_bytes < lay->total) return MOE_TAIL_ERR_WORKSPACE;
   if (lay->total > 0 && !ptr_ok(ws, 1)) return MOE_TAIL_ERR_INVALID;
@@ -440,6 +444,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   ta.expert_offsets = routing ? routing->expert_offsets : nullptr;
   ta.E = E;
   ta.k = k;
+  ta.e8_packed = d.wfmt == MOE_TAIL_W_MXFP4_PACKED;
   ta.big_rows = big ? kBigMinRows : 0x7fffffff;
   ta.huge_rows = big ? kHugeTM : 0x7fffffff;
   const bool mid = tiled && R > static_cast<size_t>(32) * E;
@@ -731,6 +736,39 @@ int moe_tail_forward_profiled(const moe_tail_dims* dims, const moe_tail_weights*
   if (stage_events == nullptr) return MOE_TAIL_ERR_INVALID;
   return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, nullptr, out, shared_out, ws, ws_bytes, stream,
                       stage_events);
+}
+
+int moe_tail_pack_mxfp4_scales(const moe_tail_dims* dims, const uint8_t* w1_scale, const uint8_t* w2_scale,
+                               uint8_t* w1_scale_packed, uint8_t* w2_scale_packed, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  const moe_tail_dims& d = *dims;
+  if (d.wfmt != MOE_TAIL_W_MXFP4 && d.wfmt != MOE_TAIL_W_MXFP4_PACKED) return MOE_TAIL_ERR_INVALID;
+  if (d.latent % 256 || d.inter % 256) return MOE_TAIL_ERR_UNSUPPORTED;
+  const size_t E = d.num_experts, L = d.latent, I = d.inter;
+  const size_t n1 = E * 2 * I * (L / 32), n2 = E * L * (I / 32);  // bytes of each scale array
+  if ((w1_scale == nullptr) != (w1_scale_packed == nullptr) || (w2_scale == nullptr) != (w2_scale_packed == nullptr))
+    return MOE_TAIL_ERR_INVALID;
+  if ((w1_scale && (!ptr_ok(w1_scale, n1) || !ptr_ok(w1_scale_packed, n1))) ||
+      (w2_scale && (!ptr_ok(w2_scale, n2) || !ptr_ok(w2_scale_packed, n2))))
+    return MOE_TAIL_ERR_INVALID;
+  auto overlap = [](const uint8_t* a, const uint8_t* b, size_t n) { return a < b + n && b < a + n; };
+  if ((w1_scale && overlap(w1_scale, w1_scale_packed, n1)) || (w2_scale && overlap(w2_scale, w2_scale_packed, n2)))
+    return MOE_TAIL_ERR_INVALID;
+  if (w1_scale == nullptr && w2_scale == nullptr) return MOE_TAIL_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (w1_scale) {
+    const size_t words = n1 / 4;
+    hipLaunchKernelGGL(k_pack_e8m0, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, st, w1_scale,
+                       w1_scale_packed, words, static_cast<int>(2 * I), static_cast<int>(L), static_cast<int>(I));
+  }
+  if (w2_scale) {
+    const size_t words = n2 / 4;
+    hipLaunchKernelGGL(k_pack_e8m0, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, st, w2_scale,
+                       w2_scale_packed, words, static_cast<int>(L), static_cast<int>(I), 0);
+  }
+  return launched();
 }
 
 int moe_tail_quant_fp8_1x128(const void* x, int32_t x_is_bf16, int32_t rows, int32_t cols, uint8_t* codes,

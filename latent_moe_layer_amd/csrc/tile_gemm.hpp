@@ -86,7 +86,35 @@ struct TileArgs {
   int big_rows;                   // routed: experts with >= big_rows rows take 128-row tiles, the others 32-row tiles
   int huge_rows;                  // routed: experts with >= huge_rows rows take 256-row tiles instead
   int mid_rows;                   // routed: experts with mid_rows .. big_rows - 1 rows take 64-row tiles
+  int e8_packed;                  // MXFP4: e8m0 scales in the packed tile order (k_pack_e8m0)
 };
+
+// MXFP4 e8m0 scales from the natural order [E][N][K/32] into the tile order
+// P[e][t][s][h][j][g] = S[e][n(t, j)][8 s + 4 h + g] (t: tile of 256 weight
+// rows, s: 256-wide K step, h: 128-wide K block, j: tile row, g: 32-wide
+// group), one 4-byte word (the four groups g) per thread.  Tile row j is
+// weight row 256 t + j, or for the paired L1 matrix (half = I) gate row
+// 128 t + j (j < 128) and up row I + 128 t + j - 128.  The scales of one
+// tile's rows for one K step are then 2 KB in a row, [h][j][g] as the
+// two-K-block stage holds them in LDS; with one K block per step, block
+// 2 s + h is the 1 KB at offset 1024 (2 s + h).
+__global__ __launch_bounds__(256) void k_pack_e8m0(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                   size_t words, int N, int K, int half) {
+  const size_t w = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (w >= words) return;
+  const int j = static_cast<int>(w % 256);
+  size_t rest = w / 256;
+  const int h = static_cast<int>(rest % 2);
+  rest /= 2;
+  const size_t nks = static_cast<size_t>(K) / 256, ntl = static_cast<size_t>(N) / 256;
+  const int s = static_cast<int>(rest % nks);
+  rest /= nks;
+  const size_t t = rest % ntl, e = rest / ntl;
+  const size_t n = half > 0 ? (j < 128 ? 128 * t + j : static_cast<size_t>(half) + 128 * t + (j - 128)) : 256 * t + j;
+  const size_t wpr = static_cast<size_t>(K) / 32;
+  reinterpret_cast<uint32_t*>(dst)[w] =
+      *reinterpret_cast<const uint32_t*>(src + (e * static_cast<size_t>(N) + n) * wpr + 8 * static_cast<size_t>(s) + 4 * h);
+}
 
 // Persistent: one workgroup per CU works through a list of tiles.  Tile t
 // of T: XCD x (workgroups are dealt to the 8 XCDs in turn, b % 8) owns tiles
@@ -322,6 +350,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   struct Iss {
     __amdgpu_buffer_rsrc_t ra, rb, rs, rs2;
     uint32_t a_off[kAL], b_off[kBChunks], s_off, s_off2;
+    int s_step;  // bytes of the first scale load's source per K step (wave-uniform)
   };
   auto make_iss = [&](const Desc& d, int buf) -> Iss {
     // the lane's coordinates, recomputed from an opaque copy of the thread
@@ -364,12 +393,20 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     r.s_off = kNoRow;
     r.rs2 = z_rsrc;
     r.s_off2 = kNoRow;
+    r.s_step = kKH == 2 ? 8 : 4;
+    // packed e8m0 (k_pack_e8m0): this tile's run of K steps
+    const uint32_t pk_tile = static_cast<uint32_t>(d.nt) * static_cast<uint32_t>(p.K / 256) * 2048u;
     if (kScaled && kKH == 2) {
       // e8m0 words of half wv / 4, B row 64 (wv % 4) + lane (8 bytes a row and stage)
       const int j = 64 * (wv & 3) + lane;
       r.rs = make_rsrc(static_cast<const uint8_t*>(p.b_scale) + static_cast<size_t>(d.e) * nbrows * wpr,
                        static_cast<uint32_t>(nbrows * wpr));
-      r.s_off = static_cast<uint32_t>(wrow(d.nt, j) * wpr) + 4u * static_cast<uint32_t>(wv >> 2);
+      if (p.e8_packed) {
+        r.s_off = pk_tile + 1024u * static_cast<uint32_t>(wv >> 2) + 4u * static_cast<uint32_t>(j);
+        r.s_step = 2048;
+      } else {
+        r.s_off = static_cast<uint32_t>(wrow(d.nt, j) * wpr) + 4u * static_cast<uint32_t>(wv >> 2);
+      }
       // activation word q: half q / TM, row q % TM
       const int q = 64 * (wv % kActW2) + lane, hh = q / TM, row = q - hh * TM;
       const float* sbase = (KIND == TK_L1) ? p.a_scale : p.a_scale + static_cast<size_t>(d.row0) * nkb;
@@ -393,7 +430,12 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
         const int j = 64 * (wv - kActW) + lane;
         r.rs = make_rsrc(static_cast<const uint8_t*>(p.b_scale) + static_cast<size_t>(d.e) * nbrows * wpr,
                          static_cast<uint32_t>(nbrows * wpr));
-        r.s_off = static_cast<uint32_t>(wrow(d.nt, j) * wpr);
+        if (p.e8_packed) {
+          r.s_off = pk_tile + 4u * static_cast<uint32_t>(j);
+          r.s_step = 1024;
+        } else {
+          r.s_off = static_cast<uint32_t>(wrow(d.nt, j) * wpr);
+        }
       }
     }
     return r;
@@ -415,10 +457,10 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     }
     if (!(part & 2)) return;
     if (kScaled && kKH == 2) {
-      dma4(live ? r.rs : z_rsrc, st + kSOff + kE8Off + 256 * wv, r.s_off, 8 * k);
+      dma4(live ? r.rs : z_rsrc, st + kSOff + kE8Off + 256 * wv, r.s_off, r.s_step * k);
       dma4(live ? r.rs2 : z_rsrc, st + kSOff + 256 * (wv % kActW2), r.s_off2, 8 * k);
     } else if (kScaled) {
-      dma4(live ? r.rs : z_rsrc, st + kSOff + 256 * wv, r.s_off, 4 * k);
+      dma4(live ? r.rs : z_rsrc, st + kSOff + 256 * wv, r.s_off, r.s_step * k);
     }
   };
   // per-tile data loaded ahead (issued first in a stage's batch, only by the

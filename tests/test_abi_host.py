@@ -67,7 +67,7 @@ def test_invalid_args_size_zero(kw, Mr, Ms):
 
 
 @pytest.mark.parametrize("kw", [dict(hidden=7000), dict(latent=3600), dict(inter=2000), dict(shared_inter=100),
-                                dict(num_experts=1025), dict(top_k=17, num_experts=64), dict(wfmt=2),
+                                dict(num_experts=1025), dict(top_k=17, num_experts=64), dict(wfmt=3),
                                 dict(latent=16384)])
 def test_unsupported_dims(kw):
     offs = (C.c_size_t * B.MOE_TAIL_WS_NUM)()
@@ -183,6 +183,27 @@ def test_forward_fused_rejections():
     needn = B.moe_tail_workspace_bytes(dn, 16, 16)
     assert f(C.byref(dn), C.byref(w), X, 16, X, 16, C.byref(r), None, OUT, None, WS, needn, None) == \
         B.MOE_TAIL_ERR_UNSUPPORTED
+
+
+def test_pack_mxfp4_scales_rejections():
+    pk = B.lib().moe_tail_pack_mxfp4_scales
+    d4 = dims(wfmt=B.MOE_TAIL_W_MXFP4)
+    A, P = 1 << 44, 1 << 45  # placeholders: every call below fails before touching them
+    # FP8 dims have no e8m0 scales
+    assert pk(C.byref(dims()), A, A + (1 << 40), P, P + (1 << 40), None) == B.MOE_TAIL_ERR_INVALID
+    # widths that are not multiples of 256
+    assert pk(C.byref(dims(wfmt=1, inter=640)), A, None, P, None, None) == B.MOE_TAIL_ERR_UNSUPPORTED
+    # an input without its output, misaligned or overlapping buffers
+    assert pk(C.byref(d4), A, None, None, None, None) == B.MOE_TAIL_ERR_INVALID
+    assert pk(C.byref(d4), A + 4, None, P, None, None) == B.MOE_TAIL_ERR_INVALID
+    assert pk(C.byref(d4), A, None, A + 1024, None, None) == B.MOE_TAIL_ERR_INVALID
+    # nothing to do
+    assert pk(C.byref(d4), None, None, None, None, None) == B.MOE_TAIL_OK
+    # a forward on packed scales needs the tiled kernels' shapes
+    w, r = _fake_weights(), _fake_routing()
+    dp = dims(wfmt=B.MOE_TAIL_W_MXFP4_PACKED, inter=640)
+    need = B.moe_tail_workspace_bytes(dp, 16, 16)
+    assert _fwd(dp, w, X, 16, X, 16, r, OUT, None, WS, need) == B.MOE_TAIL_ERR_UNSUPPORTED
 
 
 def test_quant_rejections():
