@@ -92,7 +92,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs the tail on one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is a design note, not part of this build).", file=sys.stderr)
+              "(how the tail would shard over several GPUs is a design note, not code).", file=sys.stderr)
         return 2
 
     import numpy as np

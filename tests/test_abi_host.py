@@ -224,3 +224,13 @@ def test_status_error_type():
     with pytest.raises(B.MoeTailError) as e:
         B._check(B.MOE_TAIL_ERR_UNSUPPORTED, "x")
     assert e.value.status == B.MOE_TAIL_ERR_UNSUPPORTED
+
+
+def test_bench_declines_several_gpus():
+    # one GPU only: more is refused before any device work, with a message
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
