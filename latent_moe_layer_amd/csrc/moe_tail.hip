@@ -423,8 +423,8 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
     const long blocks = static_cast<long>(Mr) * (L / 128);
     hipLaunchKernelGGL(k_quant_1x128<true>, dim3(quant_grid(blocks)), dim3(256), 0, st, x_lat, xq, sx, blocks);
   }
-  // 1, 2: routed L1 and L2 on the persistent LDS-tiled kernel: 128-row tiles
-  // for experts with at least kBigMinRows rows (FP8: 256-row tiles from 256
+  // 1, 2: routed L1 and L2 on the persistent LDS-tiled kernel: FP8 128-row
+  // tiles for experts with at least kBigMinRows rows (256-row tiles from 256
   // rows on, the rows past them in one 128-row tile when at most 128), 32-row
   // tiles for the others;
   // up to kSmallOnlyMr tokens every expert takes 32-row tiles (an expert
@@ -438,9 +438,14 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   // row-streaming kernel for every expert.
   const bool tiled = tiled_ok(d, Mr);
   constexpr int kSmallOnlyMr = 256;
-  const bool big = tiled && Mr > kSmallOnlyMr;
-  const unsigned max_tiles = static_cast<unsigned>((R + kBM - 1) / kBM + E);
   const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
+  // 128- and 256-row tiles for FP8 only.  A 256-row MXFP4 tile fits one
+  // 128-wide K block per step (half-line weight loads) and a 128-row one a
+  // single stage in flight; MXFP4 experts with 33 rows or more take 64-row
+  // tiles (three two-block stages) instead (the 1024-token MXFP4 workload:
+  // 923 -> 866 us on 128-row tiles, 851-859 us on 64-row ones)
+  const bool big = tiled && Mr > kSmallOnlyMr && fp8;
+  const unsigned max_tiles = static_cast<unsigned>((R + kBM - 1) / kBM + E);
   TileArgs ta{};
   ta.sorted_pair = routing ? routing->sorted_pair : nullptr;
   ta.expert_offsets = routing ? routing->expert_offsets : nullptr;
@@ -448,13 +453,8 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   ta.k = k;
   ta.e8_packed = d.wfmt == MOE_TAIL_W_MXFP4_PACKED;
   ta.big_rows = big ? kBigMinRows : 0x7fffffff;
-  // 256-row tiles for FP8 only: a 256-row MXFP4 tile fits one 128-wide K
-  // block per step (64-byte pieces of each weight row, loaded as half lines),
-  // and 128-row MXFP4 tiles with two K blocks per step measured faster for
-  // those experts too (the 1024-token MXFP4 workload: 923 -> 866 us)
-  const bool huge = big && fp8;
-  ta.huge_rows = huge ? kHugeTM : 0x7fffffff;
-  const bool mid = tiled && R > static_cast<size_t>(32) * E;
+  ta.huge_rows = big ? kHugeTM : 0x7fffffff;
+  const bool mid = tiled && (R > static_cast<size_t>(32) * E || (!fp8 && Mr > kSmallOnlyMr));
   ta.mid_rows = mid ? 33 : 0x7fffffff;
   // bounds on the row tiles, which size the grids: ceil(c / 128) <= c / 64
   // for c >= 128, and ceil(c / 32) <= c / 32 + 1 (the launch of the 32- and
@@ -496,10 +496,9 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       }
       if (big) {
         a1.nslots = slots_big;
-        if (fp8) launch_tile<TK_L1, TF_FP8, 0>(a1, st);
-        else launch_tile<TK_L1, TF_FP4, 0>(a1, st);
+        launch_tile<TK_L1, TF_FP8, 0>(a1, st);
         a1.nslots = slots_huge;
-        if (huge) launch_tile<TK_L1, TF_FP8, 0, kHugeTM>(a1, st);
+        launch_tile<TK_L1, TF_FP8, 0, kHugeTM>(a1, st);
       }
     }
   }
@@ -533,10 +532,9 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       }
       if (big) {
         a2.nslots = slots_big;
-        if (fp8) launch_tile<TK_L2, TF_FP8, 0>(a2, st);
-        else launch_tile<TK_L2, TF_FP4, 0>(a2, st);
+        launch_tile<TK_L2, TF_FP8, 0>(a2, st);
         a2.nslots = slots_huge;
-        if (huge) launch_tile<TK_L2, TF_FP8, 0, kHugeTM>(a2, st);
+        launch_tile<TK_L2, TF_FP8, 0, kHugeTM>(a2, st);
       }
     }
   }
