@@ -55,15 +55,13 @@ enum { TF_FP8 = 0, TF_FP4 = 1, TF_BF16 = 2 };
 // per 128 K, and loads of half lines run at a fraction of the rate of whole
 // ones (the 1024-token MXFP4 workload's routed L1 + L2: 460 + 238 us with
 // half-line weight loads, 387 + 199 us in a timing-only variant that moved
-// the same bytes as whole lines), so the 32- and 64-row MXFP4 tiles, which
-// stream weights, take two K blocks (one 128-byte line of every weight row)
-// per stage.  Larger tiles keep one: a 256-K stage of their activation rows
-// would not leave room for two stages.
-constexpr int tile_khalves(int FMT, int TM) { return (FMT == TF_FP4 && TM <= 128) ? 2 : 1; }
+// the same bytes as whole lines), so MXFP4 tiles take two K blocks (one
+// 128-byte line of every weight row) per stage.  MXFP4 tiles have 32 or 64
+// rows: a larger tile's two-block stage would leave at most one stage in
+// flight (every MXFP4 expert on 32- and 64-row tiles measured fastest).
+constexpr int tile_khalves(int FMT, int TM) { return FMT == TF_FP4 ? 2 : 1; }
 // Ring depth: kStages - 1 stages in flight.
-constexpr int tile_stages(int FMT, int TM) {
-  return (TM == 256 || (TM == 128 && tile_khalves(FMT, TM) == 2)) ? 2 : (TM == 32 && tile_khalves(FMT, TM) == 1) ? 4 : 3;
-}
+constexpr int tile_stages(int FMT, int TM) { return TM == 256 ? 2 : (TM == 32 && FMT != TF_FP4) ? 4 : 3; }
 
 struct TileArgs {
   const uint8_t* a;               // L1: xq [Mr, L]; L2: hq [R, I]; dense: bf16 rows [M, K]
@@ -142,8 +140,7 @@ struct TileLds {
   static constexpr bool kRouted = KIND != TK_DENSE;
   static constexpr int kKH = tile_khalves(FMT, TM);
   static constexpr int kStages = tile_stages(FMT, TM);
-  static constexpr int kStage = TM * 128 * kKH + kTN * ((kFP4 && kKH == 1) ? 64 : 128) +
-                                (kScaled ? (kKH == 2 ? 8 * TM + 2048 : 2048) : 0);
+  static constexpr int kStage = TM * 128 * kKH + kTN * 128 + (kScaled ? (kKH == 2 ? 8 * TM + 2048 : 2048) : 0);
   static constexpr int kPairRows = (TM < 64) ? 64 : TM;
   static constexpr int kWavesN = (TM <= 64) ? 8 : 4;
   static constexpr int kRing = 0;
@@ -190,16 +187,15 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   constexpr int kNJ = kTN / (16 * kWavesN);          // 16-column MFMA tiles per wave
   constexpr int kStages = tile_stages(FMT, TM);     // ring depth (kStages - 1 steps in flight)
   constexpr int kKH = tile_khalves(FMT, TM);         // 128-wide K blocks per stage
-  constexpr bool kB64 = kFP4 && kKH == 1;            // B rows of 64 bytes a stage (else 128)
+  static_assert(!kFP4 || TM <= 64, "MXFP4 tiles: 32 or 64 rows");
   constexpr int kABlk = TM / 8;                      // 1 KB blocks of A per stage and K block
   constexpr int kAL = (kABlk + 7) / 8;               // A blocks loaded per wave and K block
   constexpr int kABytes1 = TM * 128;                 // A bytes of one K block: 32, 16, 8 or 4 KB
   constexpr int kABytes = kABytes1 * kKH;
-  constexpr int kBBytes = kTN * (kB64 ? 64 : 128);   // 16 or 32 KB
-  // scale words of a stage.  One K block (2 KB, 256 bytes per wave):
-  // activation scales (one word per row) loaded by waves 0 .. kActW - 1, FP4
-  // e8m0 words (four per B row) by the next four; the other waves load zeros
-  // into their part.  Two K blocks (MXFP4 small tiles): activation words
+  constexpr int kBBytes = kTN * 128;                 // 128 bytes of each of the 256 B rows: 32 KB
+  // scale words of a stage.  FP8 (one K block, 2 KB, 256 bytes per wave):
+  // activation scales (one word per row) loaded by waves 0 .. kActW - 1; the
+  // other waves load zeros into their part.  MXFP4 (two K blocks): activation words
   // [half][row] (8 TM bytes: every wave loads its share of them, waves
   // past the 2 TM words repeating the first ones, the same bytes to the same
   // place), then the e8m0 words [half][B row] (2 KB, wave w: half w / 4,
@@ -211,7 +207,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   static_assert(kKH == 2 || kE8Off + 1024 <= 2048, "scale words");
   constexpr int kSBytes = !kScaled ? 0 : (kKH == 2) ? 8 * TM + 2048 : 2048;
   constexpr int kStage = kSOff + kSBytes;
-  constexpr int kBChunks = kB64 ? 2 : 4;             // 16-byte B loads per thread and stage
+  constexpr int kBChunks = 4;                        // 16-byte B loads per thread and stage
   constexpr int kSLoads = kScaled ? kKH : 0;         // 4-byte scale loads per thread and stage
   constexpr int kLoads = kAL * kKH + kBChunks + kSLoads;  // direct loads per wave and stage
   constexpr uint32_t kNoRow = 0x80000000u;           // offset past any buffer: reads zeros
@@ -336,13 +332,11 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   // Lane l lands at block + 16 l and carries row 8 * block + (l >> 3), chunk
   // (l & 7) ^ (l >> 3): chunk c of row r sits in 16-byte slot c ^ (r & 7) of
   // the row's 128 bytes, so the 8 lanes that read one chunk of 8
-  // consecutive rows hit 8 different slots (no bank conflicts).  FP4 B rows
-  // (64 bytes a step) keep one 16-row block per kilobyte, lane l holding row
-  // l % 16, chunk l / 16.
+  // consecutive rows hit 8 different slots (no bank conflicts).  (MXFP4 B
+  // rows hold two K blocks a step, so they are 128-byte pieces too.)
   const int q8 = lane >> 3;                             // row within a block
   const int st_c = (lane & 7) ^ q8;                     // chunk this lane fetches
   const int st_r0 = 8 * wave + q8;                      // B rows st_r0 + 64 i
-  const int t_r = tid & 15, t_g = (tid >> 4) & 3;       // FP4 B
   // a resource with no valid bytes: loads through it write zeros
   const __amdgpu_buffer_rsrc_t z_rsrc = make_rsrc(p.b, 0u);
 
@@ -360,7 +354,6 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     int tid_o = threadIdx.x;
     asm volatile("" : "+v"(tid_o));
     const int lane = tid_o & 63, wave = tid_o >> 6, q8 = lane >> 3, st_c = (lane & 7) ^ q8, st_r0 = 8 * wave + q8;
-    const int t_r = tid_o & 15, t_g = (tid_o >> 4) & 3;
     Iss r;
     if (KIND == TK_L1)  // gathered token rows of x codes
       r.ra = make_rsrc(p.a, static_cast<uint32_t>(static_cast<size_t>(p.M) * a_row_bytes));
@@ -381,8 +374,8 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     r.rb = make_rsrc(p.b + static_cast<size_t>(d.e) * nbrows * brow_bytes, static_cast<uint32_t>(static_cast<size_t>(nbrows) * brow_bytes));
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i) {
-      const int row = kB64 ? 128 * i + 16 * wave + t_r : st_r0 + 64 * i;
-      const int c = kB64 ? t_g : st_c;
+      const int row = st_r0 + 64 * i;
+      const int c = st_c;
       r.b_off[i] = static_cast<uint32_t>(static_cast<size_t>(wrow(d.nt, row)) * brow_bytes) + 16u * c;
     }
     // scale words, one 4-byte load per lane and stage: waves 0-1 the
@@ -426,16 +419,6 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
           const size_t ar = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
           r.s_off = static_cast<uint32_t>(ar * nkb * 4);
         }
-      } else if (kFP4 && wv >= kActW && wv < kActW + 4) {
-        const int j = 64 * (wv - kActW) + lane;
-        r.rs = make_rsrc(static_cast<const uint8_t*>(p.b_scale) + static_cast<size_t>(d.e) * nbrows * wpr,
-                         static_cast<uint32_t>(nbrows * wpr));
-        if (p.e8_packed) {
-          r.s_off = pk_tile + 4u * static_cast<uint32_t>(j);
-          r.s_step = 1024;
-        } else {
-          r.s_off = static_cast<uint32_t>(wrow(d.nt, j) * wpr);
-        }
       }
     }
     return r;
@@ -453,7 +436,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     if (part & 1) {
 #pragma unroll
       for (int i = 0; i < kBChunks; ++i)
-        dma16(live ? r.rb : z_rsrc, st + kABytes + 8192 * i + 1024 * wv, r.b_off[i], kB64 ? k * 64 : k * 128);
+        dma16(live ? r.rb : z_rsrc, st + kABytes + 8192 * i + 1024 * wv, r.b_off[i], k * 128);
     }
     if (!(part & 2)) return;
     if (kScaled && kKH == 2) {
@@ -518,11 +501,9 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     auto load_b = [&](int j, i32x8& bfj, int& sbj, int h = 0) {
       const int bb = bblk(j);
       if (kFP4) {
-        // 64-byte rows: 16 rows x 16 bytes per chunk, lane l at 16 l; 128-byte
-        // rows (two K blocks): the swizzled layout of the 8-bit operands, K
-        // block h in chunks 4 h .. 4 h + 3
-        const i32x4 v = kB64 ? *reinterpret_cast<const i32x4*>(st + kABytes + bb * 1024 + lane * 16)
-                             : *reinterpret_cast<const i32x4*>(st + kABytes + bb * 2048 + (h ? f_hi : f_lo));
+        // two K blocks of 128-byte rows in the swizzled layout of the 8-bit
+        // operands: K block h in chunks 4 h .. 4 h + 3
+        const i32x4 v = *reinterpret_cast<const i32x4*>(st + kABytes + bb * 2048 + (h ? f_hi : f_lo));
         const i32x4 z = {0, 0, 0, 0};
         bfj = __builtin_shufflevector(v, z, 0, 1, 2, 3, 4, 5, 6, 7);
         sbj = st[kSOff + kE8Off + 1024 * h + (16 * bb + l16) * 4 + g];
