@@ -191,12 +191,14 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": l1_flops / (l1_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = MEASURED_L1_TRAFFIC.get(wl.name)
-    # the routed L1 stage: the persistent tiled kernel with 32-row tiles
-    # (experts under 128 rows) and, past 256 tokens, the 128-row (128 to 255
-    # rows) and 256-row (256 rows and more) launches
+    # the routed L1 stage: the persistent tiled kernel's launches (32-row
+    # tiles, or 32- and 64-row tiles in one launch; past 256 tokens, FP8 also
+    # the 128-row and 256-row launches)
     fmt = "TF_FP8" if wl.wfmt == 0 else "TF_FP4"
-    roof["kernel"] = f"k_tile<TK_L1, {fmt}, 0, 32>" + \
-        ("" if wl.Mr <= 256 else f" + k_tile<TK_L1, {fmt}, 0, 128> + k_tile<TK_L1, {fmt}, 0, 256>")
+    small = f"k_tile<TK_L1, {fmt}, 0, 32>" if wl.Mr * wl.k <= 32 * wl.E and wl.Mr <= 256 \
+        else f"k_tile_small_mid<TK_L1, {fmt}>"
+    roof["kernel"] = small + ("" if wl.Mr <= 256 or wl.wfmt != 0
+                              else f" + k_tile<TK_L1, {fmt}, 0, 128> + k_tile<TK_L1, {fmt}, 0, 256>")
     roof["algorithmic_bytes_per_launch"] = l1_bytes
     roof["avg_launch_us"] = l1_ms * 1e3
     if fused_ms is not None:
