@@ -3,16 +3,29 @@
 One step = one pass of the whole tail (route + forward: router top-k and
 permutation, x quantization, routed L1 + SwiGLU + h quantization, routed L2,
 combine + RMSNorm, shared L1 + SwiGLU, shared L2, up-projection + FP32 shared
-add) over one batch of seeded synthetic input already resident in HBM.  At
-decode sizes moe_tail_forward runs independent stages in shared launches;
-the per-stage breakdown (`stage_us`) comes from moe_tail_forward_profiled,
-which keeps one launch per stage (the same kernels' bodies and bits).
+add) over one batch of seeded synthetic input already resident in HBM,
+captured as one HIP graph and replayed.
 
-Prints ONE JSON line.  `value` is the whole tail's achieved HBM throughput
-(algorithmic bytes / time per layer); `us_per_layer` is the step time.  The
-`roofline` object covers the dominant kernel (the routed L1 launch), timed with HIP events
-recorded on the stream it runs on.  `cpu_baseline` times the CPU oracle on the
-same inputs (rank 0, N = 1 only).
+Prints ONE JSON line.  The headline is the decode workload (128 routed and
+128 shared tokens, 64 experts, top-8, FP8 experts): `value` is the whole
+tail's achieved HBM throughput (algorithmic bytes / mean time per layer over
+the K timed replays).  The same line carries, under `legs`, the other
+workloads timed the same way (by default the prefill workload, the MFMA-bound
+half of the metric, and the tiny workload), and for every workload:
+  - median / p10 / p90 of the per-replay times (events between replays), and
+    the same cache-cold (a 512 MiB streaming read between replays, outside
+    the timed pair, evicts the 256 MB Infinity Cache);
+  - `groups_us`: each launch group of the schedule the plain call runs, from
+    moe_tail_forward_timed (events recorded on the library's stream);
+  - `roofline`: the routed L1 launch(es) against the bound of that workload
+    (HBM for the weight-streaming workloads, FP8 MFMA for prefill), with the
+    other unit alongside.
+`stream_read_gbs` is a plain streaming read of 4 GiB (moe_tail_probe_stream
+_read), the practical HBM read ceiling.  `cpu_baseline` times the CPU oracle
+on the decode workload's tokens (rank 0, N = 1 only).
+
+`--calibrate-copy` instead copies 512 MiB three times with the probe copy
+kernel (for scaling the FETCH_SIZE / WRITE_SIZE counters under rocprofv3).
 """
 from __future__ import annotations
 
@@ -28,15 +41,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "latent-MoE tail µs/layer + achieved HBM GB/s (M<=128) / MFMA TFLOP/s (M>=1024)"
 HBM_PEAK_GBS = 8000.0
-# HBM bytes per launch of the routed L1 kernel from FETCH_SIZE and WRITE_SIZE
-# counter runs, scaled by the same counters' reading of a copy kernel of known
-# size (profiles/decode_routed_traffic.md); taken on the current kernels.
-MEASURED_L1_TRAFFIC = {"decode": 945.7e6}
-# the same for the single-launch forward (quantizer + persistent tail)
-MEASURED_FUSED_TRAFFIC: dict = {}
-FP8_PEAK_TFLOPS = 5000.0
-MXFP4_PEAK_TFLOPS = 10100.0
-STAGES = ["quant_x", "routed_l1", "routed_l2", "combine_rmsnorm", "shared_l1", "shared_l2", "up_proj_add"]
+FP8_PEAK_TFLOPS = 5000.0     # dense FP8 (and FP8 x FP4: the scaled MFMA runs both at the FP8 rate)
+BF16_PEAK_TFLOPS = 2500.0
+# HBM bytes per launch of a routed L1 kernel from FETCH_SIZE and WRITE_SIZE
+# counter runs, each scaled by the same counter's reading of the probe copy
+# of 512 MiB (bench.py --calibrate-copy); see the traffic summaries under
+# profiles/.  Only figures taken on the current kernels are listed.
+MEASURED_L1_TRAFFIC: dict = {}
+# workloads whose routed GEMMs are bound by the matrix cores (the others stream weights)
+MFMA_BOUND = {"prefill"}
 
 
 class HipEvents:
@@ -48,15 +61,11 @@ class HipEvents:
         self.rt.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
         self.rt.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self.rt.hipEventSynchronize.argtypes = [C.c_void_p]
-        self.rt.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
         self.ev = []
         for _ in range(n):
             h = C.c_void_p()
             assert self.rt.hipEventCreate(C.byref(h)) == 0
             self.ev.append(h.value)
-
-    def record(self, i: int, stream) -> None:
-        assert self.rt.hipEventRecord(C.c_void_p(self.ev[i]), C.c_void_p(stream.cuda_stream)) == 0
 
     def elapsed_ms(self, a: int, b: int) -> float:
         ms = C.c_float()
@@ -66,9 +75,9 @@ class HipEvents:
 
 
 def routed_l1_bytes(wl, touched: int) -> int:
-    """Algorithmic bytes of the routed L1 launch: the touched experts' W1 and
-    its scales, the x codes and scales it gathers, the h codes and scales it
-    writes."""
+    """Algorithmic bytes of the routed L1 launch(es): the touched experts' W1
+    and its scales, the x codes and scales it gathers, the h codes and scales
+    it writes."""
     L, I, R = wl.L, wl.I, wl.Mr * wl.k
     if wl.wfmt == 0:
         w = touched * (2 * I * L + 4 * (2 * I // 128) * (L // 128))
@@ -77,18 +86,195 @@ def routed_l1_bytes(wl, touched: int) -> int:
     return w + wl.Mr * (L + 4 * L // 128) + R * (I + 4 * I // 128)
 
 
+def routed_l2_bytes(wl, touched: int) -> int:
+    """Algorithmic bytes of the routed L2 launch(es): W2 and scales of the
+    touched experts, the h codes and scales, the FP32 y rows."""
+    L, I, R = wl.L, wl.I, wl.Mr * wl.k
+    if wl.wfmt == 0:
+        w = touched * (L * I + 4 * (L // 128) * (I // 128))
+    else:
+        w = touched * (L * I // 2 + L * I // 32)
+    return w + R * (I + 4 * I // 128) + R * L * 4
+
+
+def pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs), q))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def stream_read_gbs(torch, B, reps: int = 5) -> float:
+    """Best-of-`reps` rate of one streaming read of 4 GiB."""
+    nbytes = 4 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = 0.0
+    for _ in range(reps + 1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        B.moe_tail_probe_stream_read(src, nbytes, sink, stream=torch.cuda.current_stream())
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src
+    return best
+
+
+def measure(name: str, args, torch, np, B, synth, DeviceTail, to_np, flush) -> dict:
+    wl = synth.WORKLOADS[name]
+    t0 = time.time()
+    inp = synth.make_inputs(wl)
+    gen_s = time.time() - t0
+    # MXFP4 scales go in the tiled kernels' order once, as a server would at load
+    dev = DeviceTail(inp, "cuda:0", pack_scales=wl.wfmt == synth.WFMT_MXFP4)
+    if args.add3:
+        dev.set_residual(synth.make_residual(wl))
+    stream = torch.cuda.Stream()
+    K = args.steps
+
+    def step(st):
+        dev.route(st)
+        dev.forward(st, fused=args.fused)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step(stream)
+    torch.cuda.synchronize()
+
+    # one step (route + forward, all kernels) captured as a HIP graph
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K replays, an event between consecutive replays
+    cur = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(cur)
+    for i in range(K):
+        graph.replay()
+        ev[i + 1].record(cur)
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[K])
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(K)]
+
+    # cache-cold: a 512 MiB streaming read before each replay, outside the pair
+    cold = []
+    if not args.no_cold:
+        a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+        b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+        for i in range(K):
+            B.moe_tail_probe_stream_read(flush["buf"], flush["bytes"], flush["sink"], stream=cur)
+            a[i].record(cur)
+            graph.replay()
+            b[i].record(cur)
+        torch.cuda.synchronize()
+        cold = [a[i].elapsed_time(b[i]) * 1e3 for i in range(K)]
+
+    # launch groups of the schedule the plain call runs (eager, events on its stream)
+    names = B.moe_tail_stage_names(dev.dims, dev.Mr, dev.Ms)
+    nev = B.MOE_TAIL_NUM_STAGES + 1
+    hev = HipEvents(K * nev)
+    groups = None
+    if not args.fused:
+        for i in range(K):
+            dev.route(stream)
+            dev.forward_timed(stream, hev.ev[i * nev:(i + 1) * nev])
+        torch.cuda.synchronize()
+        gsum = np.zeros(len(names))
+        for i in range(K):
+            for g in range(len(names)):
+                gsum[g] += hev.elapsed_ms(i * nev + g, i * nev + g + 1)
+        groups = {n: float(v * 1e3 / K) for n, v in zip(names, gsum)}
+
+    offsets = to_np(dev.offsets)
+    loads = np.diff(offsets)
+    touched = int(np.count_nonzero(loads))
+    nbytes = synth.algorithmic_bytes(wl, touched)["total"] + (wl.Mr * wl.H * 2 if args.add3 else 0)
+    flops = synth.algorithmic_flops(wl)
+    us = total_ms * 1e3 / K
+    leg = {
+        "workload": f"{wl.name}: Mr={wl.Mr} Ms={wl.Ms} E={wl.E} top{wl.k} I={wl.I} I_s={wl.Is} H={wl.H} L={wl.L} "
+                    f"{'FP8 128x128' if wl.wfmt == 0 else 'MXFP4 (e8m0 scales packed)'} routed weights",
+        "us_per_layer": us, "us_median": pct(per, 50), "us_p10": pct(per, 10), "us_p90": pct(per, 90),
+        "cold_us_median": pct(cold, 50) if cold else None, "cold_us_p10": pct(cold, 10) if cold else None,
+        "cold_us_p90": pct(cold, 90) if cold else None,
+        "algorithmic_bytes": nbytes, "flops_lowp": flops["lowp"], "flops_bf16": flops["bf16"],
+        "GBps": nbytes / (us * 1e-6) / 1e9, "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "TFLOPs_lowp": flops["lowp"] / (us * 1e-6) / 1e12, "TFLOPs_bf16": flops["bf16"] / (us * 1e-6) / 1e12,
+        "touched_experts": touched, "expert_rows_min_max": [int(loads.min()), int(loads.max())],
+        "groups_us": groups, "input_gen_s": gen_s,
+    }
+    if groups is not None and "routed_l1" in groups:
+        l1_us = groups["routed_l1"]
+        l1_b = routed_l1_bytes(wl, touched)
+        l1_f = 2 * wl.Mr * wl.k * 2 * wl.I * wl.L
+        gbs = l1_b / (l1_us * 1e-6) / 1e9
+        tfs = l1_f / (l1_us * 1e-6) / 1e12
+        fmt = "TF_FP8" if wl.wfmt == 0 else "TF_FP4"
+        if wl.Mr <= 256 and wl.Mr * wl.k <= 32 * wl.E:
+            kern = f"k_tile<TK_L1, {fmt}, 0, 32>"
+        else:
+            kern = f"k_tile_small_mid<TK_L1, {fmt}>"
+            if wl.Mr > 256 and wl.wfmt == 0:
+                kern += f" + k_tile<TK_L1, {fmt}, 0, 128> + k_tile<TK_L1, {fmt}, 0, 256>"
+        if name in MFMA_BOUND:
+            roof = {"bound": "mfma", "achieved": tfs, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "also": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}}
+        else:
+            roof = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "also": {"achieved": tfs, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": tfs / FP8_PEAK_TFLOPS}}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = MEASURED_L1_TRAFFIC.get(name)
+        roof["kernel"] = kern
+        roof["algorithmic_bytes_per_launch"] = l1_b
+        roof["flops_per_launch"] = l1_f
+        roof["avg_launch_us"] = l1_us
+        roof["timing"] = "HIP events around the routed L1 launch group of moe_tail_forward_timed, on its stream"
+        leg["roofline"] = roof
+        if "routed_l2" in groups:
+            l2_us = groups["routed_l2"]
+            lf = 2 * wl.Mr * wl.k * wl.L * wl.I
+            both = (l1_f + lf) / ((l1_us + l2_us) * 1e-6) / 1e12
+            leg["routed_l1_l2"] = {"us": l1_us + l2_us, "TFLOPs": both, "mfma_frac": both / FP8_PEAK_TFLOPS,
+                                   "GBps": (l1_b + routed_l2_bytes(wl, touched)) / ((l1_us + l2_us) * 1e-6) / 1e9}
+    leg["_inp"] = inp
+    leg["_dev"] = dev
+    return leg
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "mxfp4", "indep"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "mxfp4", "indep"],
+                    help="the headline workload")
+    ap.add_argument("--legs", default="prefill,tiny",
+                    help="other workloads timed on the same line (comma list, 'none', or 'all')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cache-cold replays")
     ap.add_argument("--add3", action="store_true",
                     help="time moe_tail_forward_add3 (the residual joined in the up-projection epilogue)")
     ap.add_argument("--fused", action="store_true",
                     help="time moe_tail_forward_fused (the x quantizer, then one persistent launch for the rest)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="copy 512 MiB three times with the probe copy kernel and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs the tail on one GPU only; --gpus {args.gpus} is not supported "
@@ -98,122 +284,36 @@ def main() -> int:
     import numpy as np
     import torch
 
+    from latent_moe_layer_amd import binding as B
     from latent_moe_layer_amd import synth
     from latent_moe_layer_amd.device import DeviceTail, to_np
 
-    wl = synth.WORKLOADS[args.workload]
-    t0 = time.time()
-    inp = synth.make_inputs(wl)
-    gen_s = time.time() - t0
-    # MXFP4 scales go in the tiled kernels' order once, as a server would at load
-    dev = DeviceTail(inp, "cuda:0", pack_scales=wl.wfmt == synth.WFMT_MXFP4)
-    if args.add3:
-        dev.set_residual(synth.make_residual(wl))
-    stream = torch.cuda.Stream()
-    nst = len(STAGES)
-    hev = HipEvents((args.steps + 1) * (nst + 1) + 2)
-
-    def step(st, events=None):
-        dev.route(st)
-        dev.forward(st, events, fused=args.fused and events is None)
-
-    with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            step(stream)
-    torch.cuda.synchronize()
-
-    if args.eager:
-        run_step = lambda: step(stream)  # noqa: E731
-    else:
-        # one step (route + forward, all kernels) captured as a HIP graph
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step(torch.cuda.current_stream())
+    if args.calibrate_copy:
+        nbytes = 512 << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()
         for _ in range(3):
-            graph.replay()
-        run_step = graph.replay
+            B.moe_tail_probe_copy(src, dst, nbytes)
+        torch.cuda.synchronize()
+        assert torch.equal(src[::4096], dst[::4096])
+        print(json.dumps({"calibration": "k_probe_copy", "bytes_read_per_launch": nbytes,
+                          "bytes_written_per_launch": nbytes, "launches": 3}))
+        return 0
 
-    # timed region: exactly K steps
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(torch.cuda.current_stream() if not args.eager else stream)
-    for _ in range(args.steps):
-        run_step()
-    stop.record(torch.cuda.current_stream() if not args.eager else stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
-
-    # per-stage durations: K more eager steps, the library recording HIP events
-    # on the stream its kernels run on (the profiled entry point has no add3
-    # variant; the stages run the same kernels)
-    residual, dev.residual = getattr(dev, "residual", None), None
-    for i in range(args.steps):
-        step(stream, hev.ev[i * (nst + 1):(i + 1) * (nst + 1)])
-    torch.cuda.synchronize()
-    dev.residual = residual
-    stage_ms = np.zeros(nst)
-    for i in range(args.steps):
-        base = i * (nst + 1)
-        for s in range(nst):
-            stage_ms[s] += hev.elapsed_ms(base + s, base + s + 1)
-    stage_ms /= args.steps
-
-    fused_ms = None
-    if args.fused:
-        # the single-launch forward (x quantizer + persistent tail) bracketed
-        # by HIP events on its stream, route outside the brackets
-        base = args.steps * (nst + 1)
-        tot = 0.0
-        for i in range(args.steps):
-            dev.route(stream)
-            hev.record(base, stream)
-            dev.forward(stream, fused=True)
-            hev.record(base + 1, stream)
-            tot += hev.elapsed_ms(base, base + 1)
-        fused_ms = tot / args.steps
-
-    offsets = to_np(dev.offsets)
-    touched = int(np.count_nonzero(np.diff(offsets)))
-    nbytes = synth.algorithmic_bytes(wl, touched)["total"] + (wl.Mr * wl.H * 2 if args.add3 else 0)
-    flops = synth.algorithmic_flops(wl)
-    us = ms_per_step * 1e3
-    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
-    l1_bytes = routed_l1_bytes(wl, touched)
-    l1_ms = float(stage_ms[1])
-    if wl.Mr <= 128:
-        roof = {"bound": "hbm", "achieved": l1_bytes / (l1_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    else:
-        l1_flops = 2 * wl.Mr * wl.k * 2 * wl.I * wl.L
-        peak = FP8_PEAK_TFLOPS if wl.wfmt == 0 else MXFP4_PEAK_TFLOPS
-        roof = {"bound": "mfma", "achieved": l1_flops / (l1_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = MEASURED_L1_TRAFFIC.get(wl.name)
-    # the routed L1 stage: the persistent tiled kernel's launches (32-row
-    # tiles, or 32- and 64-row tiles in one launch; past 256 tokens, FP8 also
-    # the 128-row and 256-row launches)
-    fmt = "TF_FP8" if wl.wfmt == 0 else "TF_FP4"
-    small = f"k_tile<TK_L1, {fmt}, 0, 32>" if wl.Mr * wl.k <= 32 * wl.E and wl.Mr <= 256 \
-        else f"k_tile_small_mid<TK_L1, {fmt}>"
-    roof["kernel"] = small + ("" if wl.Mr <= 256 or wl.wfmt != 0
-                              else f" + k_tile<TK_L1, {fmt}, 0, 128> + k_tile<TK_L1, {fmt}, 0, 256>")
-    roof["algorithmic_bytes_per_launch"] = l1_bytes
-    roof["avg_launch_us"] = l1_ms * 1e3
-    if fused_ms is not None:
-        # the dominant launch is then the persistent tail itself: every byte of
-        # the forward (all but the router's weights), timed with the quantizer
-        # launch that precedes it
-        fw_bytes = nbytes - 4 * wl.E * wl.L
-        roof = {"bound": "hbm", "achieved": fw_bytes / (fused_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-        roof["frac"] = roof["achieved"] / roof["peak"]
-        roof["traffic"] = MEASURED_FUSED_TRAFFIC.get(wl.name)
-        roof["kernel"] = f"k_quant_clear + k_tail_small<{fmt}>"
-        roof["algorithmic_bytes_per_launch"] = fw_bytes
-        roof["avg_launch_us"] = fused_ms * 1e3
+    flush = None
+    if not args.no_cold:
+        fb = 512 << 20
+        flush = {"buf": torch.empty(fb, dtype=torch.uint8, device="cuda").fill_(3), "bytes": fb,
+                 "sink": torch.zeros(1, dtype=torch.int32, device="cuda")}
+    head = measure(args.workload, args, torch, np, B, synth, DeviceTail, to_np, flush)
+    legs = {}
+    names = [] if args.legs == "none" else \
+        (["tiny", "decode", "prefill", "mxfp4", "indep"] if args.legs == "all" else args.legs.split(","))
+    inp, dev = head.pop("_inp"), head.pop("_dev")
 
     cpu = None
+    wl = synth.WORKLOADS[args.workload]
     if not args.no_cpu_baseline:
         from oracle import oracle as orc
         sample = min(wl.Mr, 128)
@@ -224,29 +324,45 @@ def main() -> int:
         orc.forward(inp, ids, w, sel=sel)
         cpu_s = (time.time() - t1) * wl.Mr / sample
         cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        cpu = {"value": nbytes / cpu_s / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-               "us_per_layer": cpu_s * 1e6,
+        cpu = {"value": head["algorithmic_bytes"] / cpu_s / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+               "us_per_layer": cpu_s * 1e6, "cpu_model": cpu_model(),
                "sample": (f"route + permute + forward of all {wl.Mr} tokens" if sample == wl.Mr else
                           f"route of all tokens + forward of {sample} of {wl.Mr} tokens, scaled to {wl.Mr}")}
+    del inp, dev
+    torch.cuda.empty_cache()
 
+    for n in names:
+        if n and n != args.workload:
+            leg = measure(n, args, torch, np, B, synth, DeviceTail, to_np, flush)
+            leg.pop("_inp")
+            leg.pop("_dev")
+            legs[n] = leg
+            torch.cuda.empty_cache()
+
+    if flush is not None:
+        del flush["buf"]
+        torch.cuda.empty_cache()
+    sread = stream_read_gbs(torch, B)
+
+    us = head["us_per_layer"]
     out = {
-        "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_per_step, "us_per_layer": us, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp8e4m3+bf16" if wl.wfmt == 0 else "mxfp4+fp8e4m3+bf16",
+        "metric": METRIC, "value": head["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": us * 1e-3, "us_per_layer": us, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3+bf16" if wl.wfmt == 0 else "mxfp4+fp8e4m3+bf16",
         "data": "synthetic (seeded; random-init weights of the tail's shapes)",
-        "config": {"workload": f"{wl.name}: Mr={wl.Mr} Ms={wl.Ms} E={wl.E} top{wl.k} I={wl.I} I_s={wl.Is} "
-                               f"H={wl.H} L={wl.L} {'FP8 128x128' if wl.wfmt == 0 else 'MXFP4 (e8m0 scales packed)'} routed weights",
-                   "global_batch": wl.Mr, "parallelism": "single GPU",
+        "config": {"workload": head["workload"], "global_batch": wl.Mr, "parallelism": "single GPU",
                    "epilogue": "add3: up + shared + residual, one rounding" if args.add3 else "up + shared"},
-        "algorithmic_bytes": nbytes, "touched_experts": touched,
-        "tflops_lowp": flops["lowp"] / (ms_per_step * 1e-3) / 1e12,
-        "tflops_bf16": flops["bf16"] / (ms_per_step * 1e-3) / 1e12,
-        "hbm_frac": gbs / HBM_PEAK_GBS,
-        "timing": ("eager launches" if args.eager else "HIP graph replay of route + forward") +
-                  (" (single-launch forward)" if args.fused else ""),
-        "stage_us": {n: float(v * 1e3) for n, v in zip(STAGES, stage_ms)},
-        "stage_timing": "one launch per stage (moe_tail_forward_profiled), HIP events on its stream",
-        "roofline": roof, "cpu_baseline": cpu, "input_gen_s": gen_s,
+        "us_median": head["us_median"], "us_p10": head["us_p10"], "us_p90": head["us_p90"],
+        "cold_us_median": head["cold_us_median"], "cold_us_p10": head["cold_us_p10"],
+        "cold_us_p90": head["cold_us_p90"],
+        "algorithmic_bytes": head["algorithmic_bytes"], "touched_experts": head["touched_experts"],
+        "hbm_frac": head["hbm_frac"], "tflops_lowp": head["TFLOPs_lowp"], "tflops_bf16": head["TFLOPs_bf16"],
+        "stream_read_gbs": sread, "frac_of_stream_read": head["GBps"] / sread,
+        "timing": ("HIP graph replay of route + forward" +
+                   (" (single-launch forward)" if args.fused else "") + "; events between replays"),
+        "groups_us": head["groups_us"],
+        "roofline": head.get("roofline"), "cpu_baseline": cpu, "input_gen_s": head["input_gen_s"],
+        "legs": legs,
     }
     print(json.dumps(out))
     return 0

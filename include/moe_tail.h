@@ -112,10 +112,14 @@ enum {
   MOE_TAIL_WS_RN = 5,   /* [Mr, L] bf16 normalized combined latent */
   MOE_TAIL_WS_HS = 6,   /* [Ms, I_s] bf16 shared intermediate */
   MOE_TAIL_WS_S = 7,    /* [Mr, H] bf16 shared output rows 0..Mr-1 */
-  MOE_TAIL_WS_NUM = 8
+  MOE_TAIL_WS_STATUS = 8, /* int32 status of the last moe_tail_forward_fused call on this workspace:
+                             0 = complete, 1 = a stage wait gave up and out / shared_out hold NaN;
+                             SIZE_MAX where these sizes have no single-launch path */
+  MOE_TAIL_WS_NUM = 9
 };
 
-/* Byte offsets of the intermediates above inside the workspace.
+/* Byte offsets of the intermediates above inside the workspace (SIZE_MAX
+ * for one these sizes do not have).
  * Returns MOE_TAIL_OK or MOE_TAIL_ERR_INVALID / _UNSUPPORTED. */
 int moe_tail_workspace_layout(const moe_tail_dims *dims, int32_t Mr, int32_t Ms, size_t offsets[MOE_TAIL_WS_NUM]);
 
@@ -172,13 +176,26 @@ int moe_tail_forward_add3(const moe_tail_dims *dims, const moe_tail_weights *wei
  *   The persistent launch needs all of its workgroups resident together (its
  *   stages wait on each other): do not run it concurrently with other work
  *   that occupies CUs for long, including another call of this entry point
- *   on another stream.  A stage that waits for more than about a second
- *   gives up and lets the launch finish (with wrong results) instead of
- *   hanging the device. */
+ *   on another stream.
+ *   Fail closed: a stage that waits for more than about a second gives up
+ *   (the launch always finishes); the launch then writes NaN over every
+ *   element of out and shared_out and sets the workspace's status word
+ *   (moe_tail_workspace_layout, MOE_TAIL_WS_STATUS) to 1.  The word is 0
+ *   after a complete launch; read it after the stream has passed the call. */
 int moe_tail_forward_fused(const moe_tail_dims *dims, const moe_tail_weights *weights, const uint16_t *x_lat,
                            int32_t Mr, const uint16_t *x_hid, int32_t Ms, const moe_tail_routing *routing,
                            const uint16_t *residual, uint16_t *out, uint16_t *shared_out, void *workspace,
                            size_t ws_bytes, void *stream);
+
+/* moe_tail_forward_fused with each stage wait polling its counter at most
+ * max_polls times (about 0.1 us apart) before it gives up, for callers that
+ * want a shorter bound and for tests of the failure path: max_polls = 0
+ * gives up every wait at once, which always ends in the NaN outputs and
+ * status 1 described above.  max_polls < 0 is MOE_TAIL_ERR_INVALID. */
+int moe_tail_forward_fused_bounded(const moe_tail_dims *dims, const moe_tail_weights *weights, const uint16_t *x_lat,
+                                   int32_t Mr, const uint16_t *x_hid, int32_t Ms, const moe_tail_routing *routing,
+                                   const uint16_t *residual, uint16_t *out, uint16_t *shared_out, void *workspace,
+                                   size_t ws_bytes, void *stream, int32_t max_polls);
 
 /* Number of stages moe_tail_forward_profiled brackets with events. */
 #define MOE_TAIL_NUM_STAGES 7
@@ -194,6 +211,25 @@ int moe_tail_forward_profiled(const moe_tail_dims *dims, const moe_tail_weights 
                               int32_t Mr, const uint16_t *x_hid, int32_t Ms, const moe_tail_routing *routing,
                               uint16_t *out, uint16_t *shared_out, void *workspace, size_t ws_bytes, void *stream,
                               void *const *stage_events);
+
+/* moe_tail_forward (residual NULL) or moe_tail_forward_add3 (residual
+ * non-NULL), the same launches in the same order, with events[i]
+ * (hipEvent_t) recorded on `stream` right before launch group i of that
+ * schedule and the events after the last group recorded back to back after
+ * it.  events must hold MOE_TAIL_NUM_STAGES + 1 created events.  The groups
+ * are named by moe_tail_stage_name; for measuring each group of the schedule
+ * the plain call runs (every other argument as moe_tail_forward). */
+int moe_tail_forward_timed(const moe_tail_dims *dims, const moe_tail_weights *weights, const uint16_t *x_lat,
+                           int32_t Mr, const uint16_t *x_hid, int32_t Ms, const moe_tail_routing *routing,
+                           const uint16_t *residual, uint16_t *out, uint16_t *shared_out, void *workspace,
+                           size_t ws_bytes, void *stream, void *const *events);
+
+/* Static name of launch group i of the schedule moe_tail_forward runs for
+ * these sizes (decode sizes: "quant_x", "routed_l1", "routed_l2+shared_l1",
+ * "combine_rmsnorm+shared_l1_reduce", "shared_l2+up_proj", "final_join";
+ * otherwise the MOE_TAIL_NUM_STAGES stages of moe_tail_forward_profiled), or
+ * NULL past the last group or for invalid arguments. */
+const char *moe_tail_stage_name(const moe_tail_dims *dims, int32_t Mr, int32_t Ms, int32_t i);
 
 /* The device 1x128 FP8 quantizer the forward pass uses, exported for tests:
  * per row and 128-wide block, s = amax / 448 (1.0 for an all-zero block),

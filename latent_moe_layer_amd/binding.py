@@ -24,12 +24,14 @@ MOE_TAIL_W_MXFP4 = 1
 MOE_TAIL_W_MXFP4_PACKED = 2
 
 MOE_TAIL_WS_XQ, MOE_TAIL_WS_SX, MOE_TAIL_WS_HQ, MOE_TAIL_WS_SH, MOE_TAIL_WS_Y, MOE_TAIL_WS_RN, \
-    MOE_TAIL_WS_HS, MOE_TAIL_WS_S = range(8)
-MOE_TAIL_WS_NUM = 8
+    MOE_TAIL_WS_HS, MOE_TAIL_WS_S, MOE_TAIL_WS_STATUS = range(9)
+MOE_TAIL_WS_NUM = 9
+SIZE_MAX = 2 ** 64 - 1
 MOE_TAIL_NUM_STAGES = 7
 
 EXPORTED = ("moe_tail_workspace_bytes", "moe_tail_workspace_layout", "moe_tail_route", "moe_tail_forward",
-            "moe_tail_forward_add3", "moe_tail_forward_fused", "moe_tail_forward_profiled", "moe_tail_quant_fp8_1x128",
+            "moe_tail_forward_add3", "moe_tail_forward_fused", "moe_tail_forward_fused_bounded",
+            "moe_tail_forward_profiled", "moe_tail_forward_timed", "moe_tail_stage_name", "moe_tail_quant_fp8_1x128",
             "moe_tail_pack_mxfp4_scales", "moe_tail_strerror")
 
 
@@ -79,6 +81,12 @@ def lib() -> C.CDLL:
         L.moe_tail_forward_add3.argtypes = fwd[:7] + [C.c_void_p] + fwd[7:]
         L.moe_tail_forward_fused.restype = C.c_int
         L.moe_tail_forward_fused.argtypes = fwd[:7] + [C.c_void_p] + fwd[7:]
+        L.moe_tail_forward_fused_bounded.restype = C.c_int
+        L.moe_tail_forward_fused_bounded.argtypes = fwd[:7] + [C.c_void_p] + fwd[7:] + [C.c_int32]
+        L.moe_tail_forward_timed.restype = C.c_int
+        L.moe_tail_forward_timed.argtypes = fwd[:7] + [C.c_void_p] + fwd[7:] + [C.POINTER(C.c_void_p)]
+        L.moe_tail_stage_name.restype = C.c_char_p
+        L.moe_tail_stage_name.argtypes = [C.POINTER(Dims), C.c_int32, C.c_int32, C.c_int32]
         L.moe_tail_forward_profiled.restype = C.c_int
         L.moe_tail_forward_profiled.argtypes = fwd + [C.POINTER(C.c_void_p)]
         L.moe_tail_quant_fp8_1x128.restype = C.c_int
@@ -169,6 +177,14 @@ def moe_tail_forward_fused(dims: Dims, weights: Weights, x_lat, Mr: int, x_hid, 
                                         ws_bytes, stream_handle(stream)), "moe_tail_forward_fused")
 
 
+def moe_tail_forward_fused_bounded(dims: Dims, weights: Weights, x_lat, Mr: int, x_hid, Ms: int, routing: Routing,
+                                   residual, out, shared_out, workspace, ws_bytes: int, stream, max_polls: int) -> None:
+    _check(lib().moe_tail_forward_fused_bounded(C.byref(dims), C.byref(weights), ptr(x_lat), Mr, ptr(x_hid), Ms,
+                                                C.byref(routing), ptr(residual), ptr(out), ptr(shared_out),
+                                                ptr(workspace), ws_bytes, stream_handle(stream), max_polls),
+           "moe_tail_forward_fused_bounded")
+
+
 def moe_tail_forward_profiled(dims: Dims, weights: Weights, x_lat, Mr: int, x_hid, Ms: int, routing: Routing, out,
                               shared_out, workspace, ws_bytes: int, stream, events) -> None:
     """``events``: MOE_TAIL_NUM_STAGES + 1 hipEvent_t handles (integers)."""
@@ -176,6 +192,25 @@ def moe_tail_forward_profiled(dims: Dims, weights: Weights, x_lat, Mr: int, x_hi
     _check(lib().moe_tail_forward_profiled(C.byref(dims), C.byref(weights), ptr(x_lat), Mr, ptr(x_hid), Ms,
                                            C.byref(routing), ptr(out), ptr(shared_out), ptr(workspace), ws_bytes,
                                            stream_handle(stream), arr), "moe_tail_forward_profiled")
+
+
+def moe_tail_forward_timed(dims: Dims, weights: Weights, x_lat, Mr: int, x_hid, Ms: int, routing: Routing, residual,
+                           out, shared_out, workspace, ws_bytes: int, stream, events) -> None:
+    """``events``: MOE_TAIL_NUM_STAGES + 1 hipEvent_t handles (integers)."""
+    arr = (C.c_void_p * len(events))(*events)
+    _check(lib().moe_tail_forward_timed(C.byref(dims), C.byref(weights), ptr(x_lat), Mr, ptr(x_hid), Ms,
+                                        C.byref(routing), ptr(residual), ptr(out), ptr(shared_out), ptr(workspace),
+                                        ws_bytes, stream_handle(stream), arr), "moe_tail_forward_timed")
+
+
+def moe_tail_stage_names(dims: Dims, Mr: int, Ms: int) -> list[str]:
+    """Names of the launch groups of moe_tail_forward's schedule for these sizes."""
+    names = []
+    while True:
+        n = lib().moe_tail_stage_name(C.byref(dims), Mr, Ms, len(names))
+        if n is None:
+            return names
+        names.append(n.decode())
 
 
 def moe_tail_pack_mxfp4_scales(dims: Dims, w1_scale, w2_scale, w1_scale_packed, w2_scale_packed, stream=None) -> None:
@@ -186,3 +221,50 @@ def moe_tail_pack_mxfp4_scales(dims: Dims, w1_scale, w2_scale, w1_scale_packed, 
 def moe_tail_quant_fp8_1x128(x, x_is_bf16: bool, rows: int, cols: int, codes, scales, stream=None) -> None:
     _check(lib().moe_tail_quant_fp8_1x128(ptr(x), int(bool(x_is_bf16)), rows, cols, ptr(codes), ptr(scales),
                                           stream_handle(stream)), "moe_tail_quant_fp8_1x128")
+
+
+# ------------------------------------------------------------ probes --
+# libmoe_tail_probes.so (include/moe_tail_probes.h): measurement kernels the
+# tests and the benchmark use; not steps of the tail.
+
+PROBES_PATH = os.path.join(_HERE, "libmoe_tail_probes.so")
+PROBES_EXPORTED = ("moe_tail_probe_mfma_fp8", "moe_tail_probe_copy", "moe_tail_probe_stream_read")
+
+_probes = None
+
+
+def probes() -> C.CDLL:
+    """Load the probe library; fails loudly when it has not been built."""
+    global _probes
+    if _probes is None:
+        if not os.path.exists(PROBES_PATH):
+            raise ImportError(f"{PROBES_PATH} is missing: build it with __graft_entry__.build()")
+        L = C.CDLL(PROBES_PATH)
+        L.moe_tail_probe_mfma_fp8.restype = C.c_int
+        L.moe_tail_probe_mfma_fp8.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p]
+        L.moe_tail_probe_copy.restype = C.c_int
+        L.moe_tail_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+        L.moe_tail_probe_stream_read.restype = C.c_int
+        L.moe_tail_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_uint32, C.c_void_p]
+        _probes = L
+    return _probes
+
+
+def _check_probe(rc: int, where: str) -> None:
+    if rc != 0:
+        raise MoeTailError(rc, where)
+
+
+def moe_tail_probe_mfma_fp8(a, b, c, n: int, stream=None) -> None:
+    _check_probe(probes().moe_tail_probe_mfma_fp8(ptr(a), ptr(b), ptr(c), n, stream_handle(stream)),
+                 "moe_tail_probe_mfma_fp8")
+
+
+def moe_tail_probe_copy(src, dst, nbytes: int, stream=None) -> None:
+    _check_probe(probes().moe_tail_probe_copy(ptr(src), ptr(dst), nbytes, stream_handle(stream)),
+                 "moe_tail_probe_copy")
+
+
+def moe_tail_probe_stream_read(src, nbytes: int, sink, magic: int = 0x9E3779B9, stream=None) -> None:
+    _check_probe(probes().moe_tail_probe_stream_read(ptr(src), nbytes, ptr(sink), magic, stream_handle(stream)),
+                 "moe_tail_probe_stream_read")

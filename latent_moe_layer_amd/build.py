@@ -1,4 +1,5 @@
-"""Builds ``libmoe_tail.so`` in-tree with hipcc for gfx950."""
+"""Builds ``libmoe_tail.so`` (the tail) and ``libmoe_tail_probes.so`` (the
+measurement probes) in-tree with hipcc for gfx950."""
 from __future__ import annotations
 
 import glob
@@ -8,6 +9,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc", "moe_tail.hip")
 OUT = os.path.join(HERE, "libmoe_tail.so")
+PROBES_SRC = os.path.join(HERE, "csrc", "probes.hip")
+PROBES_OUT = os.path.join(HERE, "libmoe_tail_probes.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
@@ -25,12 +28,17 @@ def sources() -> list[str]:
         [os.path.join(os.path.dirname(HERE), "include", "moe_tail.h")]
 
 
-def build() -> str:
+def _hipcc(src: str, out: str) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = OUT + ".tmp"
-    subprocess.run([hipcc, *HIPCC_FLAGS, SRC, "-o", tmp], check=True)
-    os.replace(tmp, OUT)
-    return OUT
+    tmp = out + ".tmp"
+    subprocess.run([hipcc, *HIPCC_FLAGS, src, "-o", tmp], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build() -> str:
+    _hipcc(PROBES_SRC, PROBES_OUT)
+    return _hipcc(SRC, OUT)
 
 
 if __name__ == "__main__":

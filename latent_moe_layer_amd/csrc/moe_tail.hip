@@ -128,6 +128,7 @@ struct Layout {
   size_t xq, sx, hq, sh, y, rn, hs, s, partial;     // forward intermediates
   size_t partial_s;                                 // the shared L2's partials when a later step reduces them
   size_t sync;                                      // completion counters of the single-launch tail
+  size_t sync_bytes;
   size_t total;
 };
 
@@ -161,7 +162,8 @@ Layout layout_of(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   l.partial = take(partial);
   const bool keep_s2 = fuse_shared_reduce(p, Mr, Ms) || fused_ok(d, p, Mr, Ms);
   l.partial_s = take(keep_s2 ? static_cast<size_t>(p.s2.splits) * Ms * H * 4 : 0);
-  l.sync = take(fused_ok(d, p, Mr, Ms) ? kSyncWords * 4 : 0);
+  l.sync_bytes = fused_ok(d, p, Mr, Ms) ? kSyncWords * 4 : 0;
+  l.sync = take(l.sync_bytes);
   l.total = o;
   return l;
 }
@@ -331,6 +333,7 @@ FusedArgs fused_args(const moe_tail_dims& d, const moe_tail_weights* w, int32_t 
   f.shared_out = shared_out;
   f.resid = residual;
   f.sync = at<int>(ws, lay.sync);
+  f.max_polls = kSpinLimit;
   return f;
 }
 
@@ -362,9 +365,22 @@ int check_forward(const moe_tail_dims* dims, const moe_tail_weights* w, const ui
   return MOE_TAIL_OK;
 }
 
+// Event modes of forward_impl: none; one launch per stage with an event
+// before each stage (moe_tail_forward_profiled); the schedule moe_tail_forward
+// runs with an event before each of its launch groups (moe_tail_forward_timed).
+enum { EV_NONE = 0, EV_PER_STAGE = 1, EV_SCHEDULE = 2 };
+
+// Launch groups of the schedule moe_tail_forward runs for these sizes.
+const char* const kStagedNames[MOE_TAIL_NUM_STAGES] = {"quant_x", "routed_l1", "routed_l2", "combine_rmsnorm",
+                                                       "shared_l1", "shared_l2", "up_proj_add"};
+const char* const kDecodeNames[6] = {"quant_x",          "routed_l1",
+                                     "routed_l2+shared_l1", "combine_rmsnorm+shared_l1_reduce",
+                                     "shared_l2+up_proj", "final_join"};
+
 int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
                  const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, const uint16_t* residual,
-                 uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream, void* const* events) {
+                 uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream, void* const* events,
+                 int ev_mode = EV_NONE) {
   Layout lay;
   int rc = check_forward(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, &lay);
   if (rc) return rc;
@@ -394,26 +410,33 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   // Decode sizes (every dense GEMM small-M, every expert on 32-row tiles):
   // six launches, independent work sharing a launch (the profiled variant
   // keeps one launch per stage so that each stage can be timed)
-  if (events == nullptr && fused_ok(d, plans, Mr, Ms)) {
+  if (ev_mode != EV_PER_STAGE && fused_ok(d, plans, Mr, Ms)) {
     const FusedArgs f = fused_args(d, w, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, lay, plans);
     const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
     const long qblocks = static_cast<long>(Mr) * (L / 128);
+    mark(0);
     hipLaunchKernelGGL(k_quant_clear, dim3(quant_grid(qblocks)), dim3(256), 0, st, x_lat, xq, sx, qblocks, f.sync,
                        kSyncWords);
+    mark(1);
     if (fp8) launch_tile<TK_L1, TF_FP8, 0, 32>(f.l1, st);
     else launch_tile<TK_L1, TF_FP4, 0, 32>(f.l1, st);
+    mark(2);
     const unsigned pgrid = std::max(8u, num_cus() / 8 * 8);  // persistent: one workgroup per CU
     if (fp8) hipLaunchKernelGGL(k_l2_shared1<TF_FP8>, dim3(pgrid), dim3(512), 0, st, f);
     else hipLaunchKernelGGL(k_l2_shared1<TF_FP4>, dim3(pgrid), dim3(512), 0, st, f);
+    mark(3);
     const long r_groups = static_cast<long>(Ms) * (Is / 4);
     const unsigned cgrid = static_cast<unsigned>(Mr + (r_groups + 255) / 256);
     const int nc4 = (L / 4 + 255) / 256;
     auto kc = (nc4 <= 2) ? k_combine_shared1r<2> : (nc4 <= 4) ? k_combine_shared1r<4> : k_combine_shared1r<8>;
     hipLaunchKernelGGL(kc, dim3(cgrid), dim3(256), 0, st, f);
+    mark(4);
     const unsigned dgrid = static_cast<unsigned>(plans.s2.nt * plans.s2.splits + plans.up.nt * plans.up.splits);
     hipLaunchKernelGGL(k_shared2_up, dim3(dgrid), dim3(512), 0, st, f);
+    mark(5);
     const long f_groups = static_cast<long>(Ms) * (H / 4);
     hipLaunchKernelGGL(k_final_join, dim3(static_cast<unsigned>((f_groups + 255) / 256)), dim3(256), 0, st, f);
+    for (int i = 6; i <= MOE_TAIL_NUM_STAGES; ++i) mark(i);
     return launched();
   }
 
@@ -593,7 +616,8 @@ unsigned fused_grid() {
 
 int fused_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
                const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, const uint16_t* residual,
-               uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream) {
+               uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream, int32_t max_polls) {
+  if (max_polls < 0) return MOE_TAIL_ERR_INVALID;
   Layout lay;
   int rc = check_forward(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, &lay);
   if (rc) return rc;
@@ -610,7 +634,8 @@ int fused_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint1
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // launch errors below are ours, not an earlier call's
-  const FusedArgs f = fused_args(d, w, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, lay, plans);
+  FusedArgs f = fused_args(d, w, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, lay, plans);
+  f.max_polls = max_polls;
   {
     const long blocks = static_cast<long>(Mr) * (L / 128);
     hipLaunchKernelGGL(k_quant_clear, dim3(quant_grid(blocks)), dim3(256), 0, st, x_lat, at<uint8_t>(ws, lay.xq),
@@ -655,6 +680,7 @@ int moe_tail_workspace_layout(const moe_tail_dims* dims, int32_t Mr, int32_t Ms,
   offsets[MOE_TAIL_WS_RN] = l.rn;
   offsets[MOE_TAIL_WS_HS] = l.hs;
   offsets[MOE_TAIL_WS_S] = l.s;
+  offsets[MOE_TAIL_WS_STATUS] = l.sync_bytes > 0 ? l.sync + 4 * kSyncErr : SIZE_MAX;
   return MOE_TAIL_OK;
 }
 
@@ -729,7 +755,16 @@ int moe_tail_forward_add3(const moe_tail_dims* dims, const moe_tail_weights* w, 
 int moe_tail_forward_fused(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
                            const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, const uint16_t* residual,
                            uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream) {
-  return fused_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, stream);
+  return fused_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, stream,
+                    kSpinLimit);
+}
+
+int moe_tail_forward_fused_bounded(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat,
+                                   int32_t Mr, const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing,
+                                   const uint16_t* residual, uint16_t* out, uint16_t* shared_out, void* ws,
+                                   size_t ws_bytes, void* stream, int32_t max_polls) {
+  return fused_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, stream,
+                    max_polls);
 }
 
 int moe_tail_forward_profiled(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat,
@@ -738,7 +773,23 @@ int moe_tail_forward_profiled(const moe_tail_dims* dims, const moe_tail_weights*
                               void* const* stage_events) {
   if (stage_events == nullptr) return MOE_TAIL_ERR_INVALID;
   return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, nullptr, out, shared_out, ws, ws_bytes, stream,
-                      stage_events);
+                      stage_events, EV_PER_STAGE);
+}
+
+int moe_tail_forward_timed(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
+                           const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing,
+                           const uint16_t* residual, uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes,
+                           void* stream, void* const* events) {
+  if (events == nullptr) return MOE_TAIL_ERR_INVALID;
+  return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, stream, events,
+                      EV_SCHEDULE);
+}
+
+const char* moe_tail_stage_name(const moe_tail_dims* dims, int32_t Mr, int32_t Ms, int32_t i) {
+  if (check_dims(dims) || check_counts(Mr, Ms) || i < 0) return nullptr;
+  const Plans plans = plan_all(*dims, Mr, Ms);
+  if (fused_ok(*dims, plans, Mr, Ms)) return i < 6 ? kDecodeNames[i] : nullptr;
+  return i < MOE_TAIL_NUM_STAGES ? kStagedNames[i] : nullptr;
 }
 
 int moe_tail_pack_mxfp4_scales(const moe_tail_dims* dims, const uint8_t* w1_scale, const uint8_t* w2_scale,

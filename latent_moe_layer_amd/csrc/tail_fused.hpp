@@ -30,8 +30,11 @@
 //
 // Every workgroup must be resident at once (the waits are on all of them):
 // the grid is at most one workgroup per CU and the kernel's LDS allows no
-// second.  A wait that does not end within kSpinLimit polls sets the error
-// word and goes on, so every wave always exits.
+// second.  A wait that does not end within its poll limit sets the error
+// word and goes on, so every wave always exits; the launch then fails
+// closed: the last workgroup to finish (a completion count after the final
+// stage) finds the error word set and overwrites out and shared_out with
+// NaN, and the word stays set for the host to read.
 #pragma once
 
 #include "common.hpp"
@@ -41,10 +44,11 @@
 
 namespace moe_tail {
 
-enum { SEG_S1 = 0, SEG_L1, SEG_S1R, SEG_L2, SEG_S2, SEG_CMB, SEG_UP, kSegs };
+enum { SEG_S1 = 0, SEG_L1, SEG_S1R, SEG_L2, SEG_S2, SEG_CMB, SEG_UP, SEG_FIN, kSegs };
 constexpr int kSyncWords = 16;  // segment counters + error word (cleared before the launch)
-constexpr int kSyncErr = 15;
+constexpr int kSyncErr = 15;    // 0: every wait ended; 1: a wait gave up (outputs are NaN)
 constexpr int kSpinLimit = 1 << 20;
+constexpr uint16_t kBf16NaN = 0x7FC0;
 
 struct DenseItems {
   int nt, splits, kps;  // weight-row blocks, K splits, K steps per split
@@ -73,6 +77,7 @@ struct FusedArgs {
   uint16_t* shared_out;              // [Ms - Mr, H] or null
   const uint16_t* resid;             // [Mr, H] or null
   int* sync;                         // kSyncWords words, zero at launch
+  int max_polls;                     // polls of a stage wait before it gives up (0: give up at once)
 };
 
 template <int FMT>
@@ -93,19 +98,48 @@ __device__ __forceinline__ void seg_done(int* ctr) {
 
 // Wait until `target` workgroups have finished the segment of `ctr`; the
 // acquire then invalidates this CU's stale lines before any wave reads.
-__device__ __forceinline__ void seg_wait(const int* ctr, int target, int* err) {
+// After max_polls polls (at once for max_polls == 0) the wait gives up and
+// sets the error word.
+__device__ __forceinline__ void seg_wait(const int* ctr, int target, int* err, int max_polls) {
   if (threadIdx.x == 0) {
     int n = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      if (++n == kSpinLimit) {
+    for (;;) {
+      if (n == max_polls) {
         __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
+      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
+      ++n;
       __builtin_amdgcn_s_sleep(4);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
+}
+
+// The end of the launch: every workgroup counts itself out after its final
+// stores; the last one (which sees every other workgroup's count) reads the
+// error word and, if a wait gave up anywhere, overwrites out and shared_out
+// with NaN, so that a result of an incomplete hand-off is never returned as
+// numbers.
+__device__ __forceinline__ void fused_fail_closed(const FusedArgs& f, int nwg, int* s_flag) {
+  vm_wait<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int before = __hip_atomic_fetch_add(f.sync + SEG_FIN, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    int poison = 0;
+    if (before == nwg - 1) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      poison = __hip_atomic_load(f.sync + kSyncErr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    }
+    *s_flag = poison;
+  }
+  __syncthreads();
+  if (*s_flag == 0) return;
+  const size_t n_out = static_cast<size_t>(f.Mr) * f.H, n_so = static_cast<size_t>(f.Ms - f.Mr) * f.H;
+  for (size_t i = threadIdx.x; i < n_out; i += blockDim.x) f.out[i] = kBf16NaN;
+  if (f.shared_out != nullptr)
+    for (size_t i = threadIdx.x; i < n_so; i += blockDim.x) f.shared_out[i] = kBf16NaN;
 }
 
 template <int NC4>
@@ -159,13 +193,13 @@ __device__ __forceinline__ void fused_final_group(const FusedArgs& f, long idx) 
 // activations (dep: null for none), which the weights do not depend on.
 __device__ __forceinline__ void fused_dense_items(const uint16_t* A, const uint16_t* B, int M, int nbrows, int K,
                                                   const DenseItems& it, float* part, uint8_t* smem, int wg, int nwg,
-                                                  const int* dep, int* err) {
+                                                  const int* dep, int* err, int max_polls) {
   const int n = it.nt * it.splits;
   if (dep != nullptr) {
     if (wg < n)
       dense_small_run<kSkinnyBStages, kSkinnyAStages, 1>(A, B, M, nbrows, K, it.kps, part, smem, wg % it.nt,
                                                          wg / it.nt);
-    seg_wait(dep, nwg, err);
+    seg_wait(dep, nwg, err, max_polls);
   }
   for (int i = wg; i < n; i += nwg) {
     if (dep != nullptr && i == wg)
@@ -180,11 +214,13 @@ __device__ __forceinline__ void fused_dense_items(const uint16_t* A, const uint1
 template <int FMT>
 __global__ __launch_bounds__(512) void k_tail_small(FusedArgs f) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[fused_lds<FMT>()];
+  __shared__ int s_flag;
   const int wg = blockIdx.x, nwg = gridDim.x, tid = threadIdx.x;
   int* err = f.sync + kSyncErr;
+  const int mp = f.max_polls;
 
   // S1: shared L1 split-K items (weight block, K split)
-  fused_dense_items(f.x_hid, f.ws1, f.Ms, 2 * f.Is, f.H, f.s1, f.part_s1, smem, wg, nwg, nullptr, err);
+  fused_dense_items(f.x_hid, f.ws1, f.Ms, 2 * f.Is, f.H, f.s1, f.part_s1, smem, wg, nwg, nullptr, err, mp);
   seg_done(f.sync + SEG_S1);
 
   // L1: routed L1 tiles (x codes quantized by the launch before)
@@ -192,7 +228,7 @@ __global__ __launch_bounds__(512) void k_tail_small(FusedArgs f) {
   seg_done(f.sync + SEG_L1);
 
   // S1R: hs = bf16(silu(gate) * up) from the S1 partials
-  seg_wait(f.sync + SEG_S1, nwg, err);
+  seg_wait(f.sync + SEG_S1, nwg, err, mp);
   {
     const DenseEpi ep{f.Mr, f.Is, f.hs, nullptr, nullptr, nullptr};
     const long n = static_cast<long>(f.Ms) * (f.Is / 4);
@@ -202,16 +238,16 @@ __global__ __launch_bounds__(512) void k_tail_small(FusedArgs f) {
   seg_done(f.sync + SEG_S1R);
 
   // L2: routed L2 tiles -> y
-  seg_wait(f.sync + SEG_L1, nwg, err);
+  seg_wait(f.sync + SEG_L1, nwg, err, mp);
   tile_run<TK_L2, FMT, 0, 32>(f.l2, tile_smem_in<TK_L2, FMT, 32>(smem), wg, nwg);
   seg_done(f.sync + SEG_L2);
 
   // S2: shared L2 split-K items, after every S1R
-  fused_dense_items(f.hs, f.ws2, f.Ms, f.H, f.Is, f.s2, f.part_s2, smem, wg, nwg, f.sync + SEG_S1R, err);
+  fused_dense_items(f.hs, f.ws2, f.Ms, f.H, f.Is, f.s2, f.part_s2, smem, wg, nwg, f.sync + SEG_S1R, err, mp);
   seg_done(f.sync + SEG_S2);
 
   // CMB: top-k combine + RMSNorm -> rn
-  seg_wait(f.sync + SEG_L2, nwg, err);
+  seg_wait(f.sync + SEG_L2, nwg, err, mp);
   {
     float* s_part = reinterpret_cast<float*>(smem);
     const int nc4 = (f.L / 4 + 255) / 256;
@@ -223,16 +259,17 @@ __global__ __launch_bounds__(512) void k_tail_small(FusedArgs f) {
 
   // UP: up-projection split-K items (S1's partials are consumed: reuse
   // them), after every CMB
-  fused_dense_items(f.rn, f.w_up, f.Mr, f.H, f.L, f.up, f.part_up, smem, wg, nwg, f.sync + SEG_CMB, err);
+  fused_dense_items(f.rn, f.w_up, f.Mr, f.H, f.L, f.up, f.part_up, smem, wg, nwg, f.sync + SEG_CMB, err, mp);
   seg_done(f.sync + SEG_UP);
 
   // FIN (every workgroup finished S2 before it started UP)
-  seg_wait(f.sync + SEG_UP, nwg, err);
+  seg_wait(f.sync + SEG_UP, nwg, err, mp);
   {
     const long n = static_cast<long>(f.Ms) * (f.H / 4);
     for (long idx = static_cast<long>(wg) * 512 + tid; idx < n; idx += static_cast<long>(nwg) * 512)
       fused_final_group(f, idx);
   }
+  fused_fail_closed(f, nwg, &s_flag);
 }
 
 // ----------------------------------------------------------------------

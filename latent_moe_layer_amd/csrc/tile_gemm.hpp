@@ -334,9 +334,9 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   // the row's 128 bytes, so the 8 lanes that read one chunk of 8
   // consecutive rows hit 8 different slots (no bank conflicts).  (MXFP4 B
   // rows hold two K blocks a step, so they are 128-byte pieces too.)
-  const int q8 = lane >> 3;                             // row within a block
-  const int st_c = (lane & 7) ^ q8;                     // chunk this lane fetches
-  const int st_r0 = 8 * wave + q8;                      // B rows st_r0 + 64 i
+  // (each lane's row within a block, lane >> 3, its chunk (lane & 7) ^ (lane
+  // >> 3) and its B rows 8 wave + (lane >> 3) + 64 i are recomputed where
+  // the loads are set up, make_iss)
   // a resource with no valid bytes: loads through it write zeros
   const __amdgpu_buffer_rsrc_t z_rsrc = make_rsrc(p.b, 0u);
 

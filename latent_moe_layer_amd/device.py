@@ -99,6 +99,13 @@ class DeviceTail:
         else:
             B.moe_tail_forward_profiled(*args, events)
 
+    def forward_timed(self, stream, events) -> None:
+        """moe_tail_forward's schedule (add3 if a residual is set) with an event
+        before each launch group (moe_tail_forward_timed)."""
+        B.moe_tail_forward_timed(self.dims, self.weights, self.t["x_lat"], self.Mr, self.t["x_hid"], self.Ms,
+                                 self.routing, getattr(self, "residual", None), self.out, self.shared_out, self.ws,
+                                 self.ws_bytes, stream, events)
+
     # -------- views of the materialized intermediates (tests) --------
     def _view(self, idx: int, dtype, shape):
         n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()

@@ -323,6 +323,11 @@ void oracle_permute(int E, int k, int Mr, const int32_t* ids, int32_t* offsets, 
 //   y[s, k, L]                               routed L2 output per slot
 //   rn[s, L]                                 normalised latent (bf16)
 //   hs[s, Is], sbf[s, H]                     shared intermediate and output (bf16)
+// hq_in / sh_in (optional, [n_sel, k, I] codes and [n_sel, k, I/128] scales,
+// rows in sel order): h codes and scales given instead of computed; the
+// routed L1 and SwiGLU are then skipped (h_out reads 0) and every later step
+// runs on the given codes.  This is how a test checks the steps after the h
+// quantization on exactly the codes another implementation produced.
 int oracle_forward(int H, int L, int E, int k, int I, int Is, int wfmt, float eps,
                    const uint8_t* w1, const void* w1s, const uint8_t* w2, const void* w2s,
                    const uint16_t* gamma, const uint16_t* w_up, const uint16_t* ws1, const uint16_t* ws2,
@@ -331,7 +336,9 @@ int oracle_forward(int H, int L, int E, int k, int I, int Is, int wfmt, float ep
                    int n_sel, const int32_t* sel,
                    float* out_f32, uint16_t* out_bf16,
                    uint8_t* xq_out, float* sx_out, uint8_t* hq_out, float* sh_out, float* h_out,
-                   float* y_out, uint16_t* rn_out, uint16_t* hs_out, uint16_t* sbf_out) {
+                   float* y_out, uint16_t* rn_out, uint16_t* hs_out, uint16_t* sbf_out,
+                   const uint8_t* hq_in, const float* sh_in) {
+  if ((hq_in == nullptr) != (sh_in == nullptr)) return 1;
   if (L % 128 || H % 128 || I % 128 || Is % 128 || k < 1 || k > E || Mr < 0 || Mr > Ms) return 1;
   for (int s = 0; s < n_sel; ++s)
     if (sel[s] < 0 || sel[s] >= Ms) return 1;
@@ -358,7 +365,8 @@ int oracle_forward(int H, int L, int E, int k, int I, int Is, int wfmt, float ep
   }
 
   // --- routed L1: g[a, j, n] = sum_c x_hat[a, c] * W1_hat[e, n, c] ---
-  std::vector<float> g(static_cast<size_t>(nr) * k * 2 * I);
+  std::vector<float> g(hq_in ? 0 : static_cast<size_t>(nr) * k * 2 * I);
+  if (!hq_in)
 #pragma omp parallel
   {
     std::vector<float> wrow(L);
@@ -379,10 +387,17 @@ int oracle_forward(int H, int L, int E, int k, int I, int Is, int wfmt, float ep
   std::vector<float> sh(static_cast<size_t>(nr) * k * (I / 128));
 #pragma omp parallel for schedule(static)
   for (int aj = 0; aj < nr * k; ++aj) {
-    const float* ga = &g[static_cast<size_t>(aj) * 2 * I];
     float* ha = &h[static_cast<size_t>(aj) * I];
-    for (int n = 0; n < I; ++n) ha[n] = silu_mul(ga[n], ga[I + n]);
-    quant_row_1x128(ha, I, &hq[static_cast<size_t>(aj) * I], &sh[static_cast<size_t>(aj) * (I / 128)]);
+    if (hq_in) {
+      // the given codes of selected token rsel[aj / k], slot aj % k
+      const size_t src = static_cast<size_t>(rsel[aj / k]) * k + aj % k;
+      std::memcpy(&hq[static_cast<size_t>(aj) * I], hq_in + src * I, I);
+      std::memcpy(&sh[static_cast<size_t>(aj) * (I / 128)], sh_in + src * (I / 128), (I / 128) * 4);
+    } else {
+      const float* ga = &g[static_cast<size_t>(aj) * 2 * I];
+      for (int n = 0; n < I; ++n) ha[n] = silu_mul(ga[n], ga[I + n]);
+      quant_row_1x128(ha, I, &hq[static_cast<size_t>(aj) * I], &sh[static_cast<size_t>(aj) * (I / 128)]);
+    }
     for (int n = 0; n < I; ++n)
       hhat[static_cast<size_t>(aj) * I + n] = e4m3_value(hq[static_cast<size_t>(aj) * I + n]) * sh[static_cast<size_t>(aj) * (I / 128) + n / 128];
   }

@@ -156,10 +156,13 @@ class ForwardResult:
     sbf: np.ndarray         # [n, H] bf16 bits
 
 
-def forward(inp, topk_ids, topk_w, sel=None, Mr=None, Ms=None, residual=None) -> ForwardResult:
+def forward(inp, topk_ids, topk_w, sel=None, Mr=None, Ms=None, residual=None, h_codes=None) -> ForwardResult:
     """Run the oracle on ``synth.Inputs`` for the tokens in ``sel`` (default all).
     ``residual`` ([Mr, H] bf16 bits, row t for token t) is added to the routed
-    rows after the shared add, before the one rounding ("add3")."""
+    rows after the shared add, before the one rounding ("add3").
+    ``h_codes`` (optional ``(hq [n, k, I] u8, sh [n, k, I/128] f32)``, rows in
+    ``sel`` order): the h codes and scales to continue from instead of the
+    oracle's own (the routed L1 is skipped; ``h`` then reads 0)."""
     wl = inp.wl
     Mr = inp.x_lat.shape[0] if Mr is None else Mr
     Ms = inp.x_hid.shape[0] if Ms is None else Ms
@@ -180,6 +183,11 @@ def forward(inp, topk_ids, topk_w, sel=None, Mr=None, Ms=None, residual=None) ->
             _c(inp.ws1, np.uint16), _c(inp.ws2, np.uint16), _c(inp.x_lat, np.uint16), _c(inp.x_hid, np.uint16),
             _c(topk_ids, np.int32), _c(topk_w, np.float32)]
     res = None if residual is None else _c(residual, np.uint16)
+    hq_in = sh_in = None
+    if h_codes is not None:
+        hq_in, sh_in = _c(h_codes[0], np.uint8), _c(h_codes[1], np.float32)
+        if hq_in.shape != (n, k, I) or sh_in.shape != (n, k, I // 128):
+            raise ValueError("h_codes must be [n, k, I] codes and [n, k, I/128] scales")
     if res is not None and res.shape != (Mr, H):
         raise ValueError("residual must be [Mr, H]")
     rc = lib().oracle_forward(
@@ -189,7 +197,7 @@ def forward(inp, topk_ids, topk_w, sel=None, Mr=None, Ms=None, residual=None) ->
         _p(arrs[8]), C.c_int(Mr), _p(arrs[9]), C.c_int(Ms), _p(arrs[10]), _p(arrs[11]), _p(res),
         C.c_int(n), _p(sel),
         _p(r.out_f32), _p(r.out_bf16), _p(r.xq), _p(r.sx), _p(r.hq), _p(r.sh), _p(r.h), _p(r.y), _p(r.rn),
-        _p(r.hs), _p(r.sbf))
+        _p(r.hs), _p(r.sbf), _p(hq_in), _p(sh_in))
     if rc != 0:
         raise ValueError("oracle_forward rejected its arguments")
     return r

@@ -1,17 +1,29 @@
 """Parity metrics shared by the GPU tests.
 
-Relative error of token t's output vector against the oracle's FP32 output:
-    rel_t = ||g_t - o_t||_2 / ||o_t||_2
-The bar: max_t rel_t <= 2e-2 and mean_t rel_t <= 3e-3.
+Two statistics of an output g against the oracle's FP32 output o, with the
+bar max <= 2e-2 and mean <= 3e-3:
 
-Why per token and not per element: the re-quantized activation h has
-legitimately different codes where it sits within the two summation
-procedures' disagreement of a rounding midpoint (see H_TOL); one such flip of a
-top-binade code moves single output elements by several percent of the output
-rms at I = 512 (about 0.07 * (amax/rms of h) * 3.5 / sqrt(I)), while it moves
-the token's output vector by about 1 %.  An elementwise max cannot tell a valid
-tie-break from an error; the vector norm can.  The elementwise statistic
-|g_i - o_i| / max(|o_i|, rms(o)) is still reported (rel_errors).
+* elementwise: rel_i = |g_i - o_i| / max(|o_i|, rms(o)) over every compared
+  element (the floor rms(o) keeps the ratio defined where the routed and the
+  shared parts cancel);
+* per token, normwise: rel_t = ||g_t - o_t||_2 / ||o_t||_2.
+
+The GPU and the oracle sum the routed L1 in different orders, so h differs
+by a few 1e-5 of its block amax and its FP8 codes differ where h lies that
+close to a rounding midpoint (check_h_codes states and checks the rule).  Each
+such flip moves whole output rows: a single element of out by up to about 1 %,
+so the largest elementwise error over a workload grows with the number of
+elements compared, while the per-token error and the mean stay put.  The
+outputs are therefore compared twice:
+
+* directly with the oracle's own pipeline: per token (max and mean) and
+  elementwise mean against the bar; the elementwise max is reported;
+* with the oracle continuing from the GPU's own h codes (oracle.forward's
+  h_codes): every step after the h quantization, checked elementwise and per
+  token against the full bar, with the h-code flips taken out.
+
+Intermediates downstream of h (the routed L2 output y of one (token, slot)
+row, the normalized latent rn) are compared per row with the same bar.
 """
 from __future__ import annotations
 
@@ -19,12 +31,7 @@ import numpy as np
 
 MAX_REL = 2e-2
 MEAN_REL = 3e-3
-# Intermediates downstream of h (the routed L2 output y of one (token, slot)
-# row and the normalized latent) inherit the h-code flips undiluted by the
-# other slots: one top-binade flip moves a y row by about (amax/14) /
-# (rms(h) sqrt(I)) ~ 2 % of its norm at I = 512, and a row can hold a few.
-# They get this looser max bound; the mean bound is unchanged.
-MAX_REL_INTERMEDIATE = 1e-1
+MAX_REL_INTERMEDIATE = MAX_REL
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -42,7 +49,7 @@ def row_rel_errors(got: np.ndarray, want: np.ndarray) -> tuple[float, float]:
 
 
 def rel_errors(got: np.ndarray, want: np.ndarray) -> tuple[float, float]:
-    """Elementwise (max, mean) of |g - o| / max(|o|, rms(o)) (reported only)."""
+    """Elementwise (max, mean) of |g - o| / max(|o|, rms(o))."""
     g = np.asarray(got, np.float64)
     o = np.asarray(want, np.float64)
     if o.size == 0:
@@ -60,12 +67,29 @@ def e4m3_value(code: np.ndarray) -> np.ndarray:
 
 
 # h is computed twice by different summation procedures: the oracle's
-# sequential FP32 loop and the matrix cores, whose FP8 products are summed in
-# groups with an internal precision of about 2^-14 of the group's largest
-# product (measured on gfx950: 2^-9 addends beside a 448 product are dropped,
-# 2^-5 ones kept).  Over K = 3584 that moves h by a few 1e-5 of the block
-# amax (observed up to 7e-5 on the scales); the bar below leaves 7x margin.
+# sequential FP32 loop and the matrix cores, which sum the 128 FP8 products of
+# one block instruction with an internal precision coarser than FP32 (see
+# tests/test_gpu_mfma_precision.py, which measures it and checks that on the
+# workloads' own operands it moves h by at most H_TOL / 5 of the block amax).
 H_TOL = 5e-4
+
+
+def assert_output_gate(got: np.ndarray, want: np.ndarray, what: str, elementwise_max: bool = True) -> dict:
+    """Both output statistics against the bar (the elementwise max only when
+    `elementwise_max`); returns them."""
+    emax, emean = rel_errors(got, want)
+    tmax, tmean = row_rel_errors(got, want)
+    st = {f"{what}_elementwise": (emax, emean), f"{what}_per_token": (tmax, tmean)}
+    assert emean <= MEAN_REL and (emax <= MAX_REL or not elementwise_max), st
+    assert tmax <= MAX_REL and tmean <= MEAN_REL, st
+    return st
+
+
+def e4m3_ordinal(code: np.ndarray) -> np.ndarray:
+    """Position of an e4m3 code on the number line (+0 and -0 both 0)."""
+    c = np.asarray(code, np.int64)
+    mag = c & 0x7F
+    return np.where(c >> 7 == 1, -mag, mag)
 
 
 def e4m3_encode_np(x: np.ndarray) -> np.ndarray:
@@ -81,22 +105,36 @@ def e4m3_encode_np(x: np.ndarray) -> np.ndarray:
     return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
 
 
+def e4m3_spacing(code: np.ndarray) -> np.ndarray:
+    """Distance from an e4m3 code's magnitude to the next larger one (in
+    units of the scale)."""
+    mag = np.asarray(code, np.int64) & 0x7F
+    return e4m3_value(np.minimum(mag + 1, 126)) - e4m3_value(np.minimum(mag, 125))
+
+
 def check_h_codes(gpu_hq, gpu_sh, orc_hq, orc_sh, orc_h, tol=H_TOL):
     """The rule for re-quantized activations computed by two different
     summation procedures: scales agree to `tol` relative, and every GPU code
     is the rounding (with the GPU's scale) of some value within tol * block
     amax of the oracle's h -- so codes differ only where h sits that close to
-    a rounding midpoint.  Returns (n_mismatch, n_total)."""
+    a rounding midpoint.  Where that band is narrower than the code spacing
+    (every normal code of the larger values) a differing code is exactly one
+    step from the oracle's; near zero, where the subnormal codes are spaced
+    2^-9 of the scale apart, the band spans several codes and the band rule
+    alone applies.  Returns (n_mismatch, n_total, max scale deviation,
+    n_mismatch more than one step apart)."""
     gpu_hq = np.asarray(gpu_hq)
     orc_hq = np.asarray(orc_hq)
     rs = np.abs(np.asarray(gpu_sh, np.float64) - orc_sh) / np.abs(orc_sh)
     assert np.all(rs <= tol), f"h scale mismatch {rs.max():.3e}"
-    mism = gpu_hq != orc_hq
+    mism = (gpu_hq != orc_hq) & (e4m3_ordinal(gpu_hq) != e4m3_ordinal(orc_hq))  # (+0 and -0 are equal)
     n = int(mism.sum())
+    multi = 0
     if n:
         ncol = gpu_hq.shape[-1]
         rows, cols = np.nonzero(mism.reshape(-1, ncol))
         g = gpu_hq.reshape(-1, ncol)[rows, cols]
+        o = orc_hq.reshape(-1, ncol)[rows, cols]
         h = np.asarray(orc_h, np.float64).reshape(-1, ncol)[rows, cols]
         s_orc = np.asarray(orc_sh, np.float64).reshape(-1, ncol // 128)[rows, cols // 128]
         s_gpu = np.asarray(gpu_sh, np.float64).reshape(-1, ncol // 128)[rows, cols // 128]
@@ -105,4 +143,8 @@ def check_h_codes(gpu_hq, gpu_sh, orc_hq, orc_sh, orc_h, tol=H_TOL):
         hi = e4m3_value(e4m3_encode_np((h + band) / s_gpu))
         gv = e4m3_value(g)
         assert np.all((gv >= lo) & (gv <= hi)), "h code flip away from a rounding midpoint"
-    return n, gpu_hq.size
+        step = np.abs(e4m3_ordinal(g) - e4m3_ordinal(o))
+        narrow = 2.0 * band < e4m3_spacing(np.minimum(g & 0x7F, o & 0x7F)) * s_orc
+        assert np.all(step[narrow] == 1), f"h codes more than one step apart: {np.bincount(step[narrow])}"
+        multi = int(np.count_nonzero(step > 1))
+    return n, gpu_hq.size, float(rs.max(initial=0.0)), multi

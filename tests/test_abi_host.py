@@ -12,20 +12,26 @@ from latent_moe_layer_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    names = set()
-    for fn in os.listdir(os.path.join(ROOT, "include")):
-        if fn.endswith(".h"):
-            text = open(os.path.join(ROOT, "include", fn)).read()
-            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            names |= set(re.findall(r"\b(moe_tail_\w+)\s*\(", text))
-    return names
+def _declared_functions(header):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(moe_tail_\w+)\s*\(", text))
 
 
-def test_library_exports_every_declared_function():
-    lib = B.lib()
-    declared = _declared_functions()
-    assert declared >= set(B.EXPORTED)
+# every header under include/ and the library that implements it
+HEADERS = {"moe_tail.h": (B.lib, B.EXPORTED), "moe_tail_probes.h": (B.probes, B.PROBES_EXPORTED)}
+
+
+def test_every_header_has_a_library():
+    assert sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h")) == sorted(HEADERS)
+
+
+@pytest.mark.parametrize("header", sorted(HEADERS))
+def test_library_exports_every_declared_function(header):
+    load, exported = HEADERS[header]
+    lib = load()
+    declared = _declared_functions(header)
+    assert declared == set(exported)
     for name in declared:
         assert hasattr(lib, name), name
 
@@ -43,8 +49,13 @@ def test_workspace_bytes_and_layout():
     d = dims()
     n = B.moe_tail_workspace_bytes(d, 128, 128)
     offs = B.moe_tail_workspace_layout(d, 128, 128)
-    assert n > 0 and all(o % 256 == 0 for o in offs) and max(offs) < n
-    assert sorted(offs) == offs
+    regions, status = offs[:B.MOE_TAIL_WS_STATUS], offs[B.MOE_TAIL_WS_STATUS]
+    assert n > 0 and all(o % 256 == 0 for o in regions) and max(regions) < n
+    assert sorted(regions) == regions
+    # decode sizes have the single-launch path: its status word is the last word of the workspace's counters
+    assert status % 4 == 0 and max(regions) < status <= n - 4
+    # sizes without that path have no status word
+    assert B.moe_tail_workspace_layout(d, 2048, 2048)[B.MOE_TAIL_WS_STATUS] == B.SIZE_MAX
     # y holds Mr*k rows of fp32 latent
     assert offs[B.MOE_TAIL_WS_RN] - offs[B.MOE_TAIL_WS_Y] >= 128 * 8 * 3584 * 4
     # the independent-count case (more shared than routed tokens)
@@ -183,6 +194,33 @@ def test_forward_fused_rejections():
     needn = B.moe_tail_workspace_bytes(dn, 16, 16)
     assert f(C.byref(dn), C.byref(w), X, 16, X, 16, C.byref(r), None, OUT, None, WS, needn, None) == \
         B.MOE_TAIL_ERR_UNSUPPORTED
+
+
+def test_forward_fused_bounded_rejections():
+    d, w, r = dims(), _fake_weights(), _fake_routing()
+    f = B.lib().moe_tail_forward_fused_bounded
+    need = B.moe_tail_workspace_bytes(d, 16, 16)
+    assert f(C.byref(d), C.byref(w), X, 16, X, 16, C.byref(r), None, OUT, None, WS, need, None, -1) == \
+        B.MOE_TAIL_ERR_INVALID
+    assert f(C.byref(d), C.byref(w), X, 16, X, 16, C.byref(r), None, OUT, None, WS, need - 1, None, 0) == \
+        B.MOE_TAIL_ERR_WORKSPACE
+    need129 = B.moe_tail_workspace_bytes(d, 16, 129)
+    assert f(C.byref(d), C.byref(w), X, 16, X, 129, C.byref(r), None, OUT, SOUT, WS, need129, None, 0) == \
+        B.MOE_TAIL_ERR_UNSUPPORTED
+
+
+def test_probe_rejections():
+    p = B.probes()
+    assert p.moe_tail_probe_mfma_fp8(X, X, OUT, 0, None) == 1
+    assert p.moe_tail_probe_mfma_fp8(X, X, OUT, 65537, None) == 1
+    assert p.moe_tail_probe_mfma_fp8(X + 4, X, OUT, 1, None) == 1
+    assert p.moe_tail_probe_copy(X, OUT, 100, None) == 1
+    assert p.moe_tail_probe_copy(X, X + 16, 4096, None) == 1  # overlapping
+    assert p.moe_tail_probe_copy(None, OUT, 4096, None) == 1
+    assert p.moe_tail_probe_copy(X, OUT, 0, None) == 0
+    assert p.moe_tail_probe_stream_read(X, 4000, OUT, 0, None) == 1
+    assert p.moe_tail_probe_stream_read(X, 4096, None, 0, None) == 1
+    assert p.moe_tail_probe_stream_read(X, 0, OUT, 0, None) == 0
 
 
 def test_pack_mxfp4_scales_rejections():

@@ -17,11 +17,13 @@ from tests.test_gpu_parity import check_forward
 
 pytestmark = pytest.mark.gpu
 
-# The launch's counters: the last 256 bytes of the workspace, one word per
-# segment (the workgroups that finished it) and the error word.
-SYNC_BYTES = 256
-SEGMENTS = 7
+# The launch's counters: 16 words of the workspace ending with the status word
+# (moe_tail_workspace_layout, MOE_TAIL_WS_STATUS): one word per stage (the
+# workgroups that finished it, the last one the count of finished workgroups)
+# and the error word.
+SEGMENTS = 8
 SYNC_ERR = 15
+BF16_NAN = 0x7FC0
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -31,13 +33,18 @@ def _gpu():
     B.lib()
 
 
+def _sync_base(dev):
+    return dev.layout[B.MOE_TAIL_WS_STATUS] - 4 * SYNC_ERR
+
+
 def _poison(dev):
     """Fill outputs and intermediates with a pattern no result has (0xFFFF
     bf16 is a NaN, 0xFF codes and all-ones floats too)."""
     dev.out.fill_(-1)
     if dev.shared_out is not None:
         dev.shared_out.fill_(-1)
-    dev.ws[: dev.ws_bytes - SYNC_BYTES].fill_(255)
+    end = _sync_base(dev) if dev.layout[B.MOE_TAIL_WS_STATUS] != B.SIZE_MAX else dev.ws_bytes
+    dev.ws[:end].fill_(255)
 
 
 def _snapshot(dev):
@@ -50,8 +57,8 @@ def _snapshot(dev):
 
 
 def _sync_words(dev):
-    w = dev.ws[dev.ws_bytes - SYNC_BYTES: dev.ws_bytes - SYNC_BYTES + 64].view(torch.int32)
-    return to_np(w)
+    base = _sync_base(dev)
+    return to_np(dev.ws[base: base + 64].view(torch.int32))
 
 
 def _grid():
@@ -220,6 +227,36 @@ def test_coscheduled_forward_equals_one_launch_per_stage(case):
     dev.forward(events=_hip_events(B.MOE_TAIL_NUM_STAGES + 1))
     torch.cuda.synchronize()
     assert_same(co, _snapshot(dev))
+
+
+@pytest.mark.parametrize("case", ["ragged", "decode"])
+def test_fused_wait_given_up_fails_closed(case):
+    # Every stage wait forced to give up from the host (max_polls = 0): the
+    # launch still finishes, out and shared_out hold NaN in every element and
+    # the status word reads 1.  The next complete call on the same workspace
+    # clears the word and gives the staged forward's bits again.
+    wl = synth.WORKLOADS["decode"] if case == "decode" else CASES[case]
+    inp = synth.make_inputs(wl)
+    dev = DeviceTail(inp, "cuda:0")
+    dev.route()
+    dev.forward()
+    torch.cuda.synchronize()
+    ref = _snapshot(dev)
+    print(f"[{case}] fused launch with every wait given up", flush=True)
+    B.moe_tail_forward_fused_bounded(dev.dims, dev.weights, dev.t["x_lat"], dev.Mr, dev.t["x_hid"], dev.Ms,
+                                     dev.routing, None, dev.out, dev.shared_out, dev.ws, dev.ws_bytes, None, 0)
+    torch.cuda.synchronize()
+    words = _sync_words(dev)
+    assert words[SYNC_ERR] == 1
+    assert words[SEGMENTS - 1] == _grid()  # every workgroup finished
+    assert np.all(to_np(dev.out) == BF16_NAN)
+    if dev.shared_out is not None:
+        assert np.all(to_np(dev.shared_out) == BF16_NAN)
+    dev.forward(fused=True)
+    torch.cuda.synchronize()
+    assert _sync_words(dev)[SYNC_ERR] == 0
+    assert_same(ref, _snapshot(dev), keys=["out"] + (["shared_out"] if dev.shared_out is not None else []))
+    assert_counters(dev)
 
 
 def test_fused_declines_large_token_counts():

@@ -1,7 +1,10 @@
 """Parity at the five full workload sizes, in the launch configuration the
 benchmark times.  Routing, permutation and x codes are compared bit for bit on
-every token; outputs, h codes, y and the normalized latent on a sample of
-tokens that the oracle computes one by one.  MI355X only (marker ``gpu``)."""
+every token; outputs, h codes, y and the normalized latent on every token up
+to 128 tokens, and beyond that on a sample the oracle computes one by one: the
+tokens of every touched expert's first and last row (so each expert's first
+and last row tile is checked), and random tokens up to at least 128.  MI355X
+only (marker ``gpu``)."""
 import numpy as np
 import pytest
 import torch
@@ -26,9 +29,22 @@ def _sample(n, m, seed):
     return s.astype(np.int32)
 
 
-@pytest.mark.parametrize("name,n_routed,n_shared", [("tiny", None, 0), ("decode", None, 0), ("prefill", 12, 0),
-                                                   ("mxfp4", 12, 0), ("indep", 10, 10)])
-def test_workload(name, n_routed, n_shared):
+def boundary_tokens(offsets, sorted_pair, k, n_min, seed):
+    """The tokens of each touched expert's first and last row, topped up with
+    random tokens to at least n_min."""
+    Mr = sorted_pair.size // k
+    first = offsets[:-1][np.diff(offsets) > 0]
+    last = offsets[1:][np.diff(offsets) > 0] - 1
+    toks = np.unique(sorted_pair[np.concatenate([first, last])] // k)
+    if toks.size < n_min:
+        rng = np.random.default_rng(seed)
+        rest = np.setdiff1d(np.arange(Mr), toks)
+        toks = np.union1d(toks, rng.choice(rest, size=min(rest.size, n_min - toks.size), replace=False))
+    return np.union1d(toks, [0, Mr - 1]).astype(np.int32)
+
+
+@pytest.mark.parametrize("name,n_shared", [("tiny", 0), ("decode", 0), ("prefill", 0), ("mxfp4", 0), ("indep", 32)])
+def test_workload(name, n_shared):
     wl = synth.WORKLOADS[name]
     print(f"[{name}] generating inputs", flush=True)
     inp = synth.make_inputs(wl)
@@ -45,14 +61,16 @@ def test_workload(name, n_routed, n_shared):
     inter = dev.intermediates()
     assert np.array_equal(to_np(inter["xq"]), xq)
     assert np.array_equal(to_np(inter["sx"]), sx)
-    if n_routed is None:
-        sel = None
+    offsets, sorted_pair = to_np(dev.offsets), to_np(dev.sorted_pair)
+    if wl.Mr <= 128:
+        sel = np.arange(wl.Ms, dtype=np.int32) if n_shared == 0 else None
     else:
-        sel = _sample(wl.Mr, n_routed, wl.seed)
-        if n_shared:
-            sel = np.concatenate([sel, wl.Mr + _sample(wl.Ms - wl.Mr, n_shared, wl.seed + 1)]).astype(np.int32)
-    print(f"[{name}] oracle on {'all' if sel is None else len(sel)} tokens", flush=True)
+        sel = boundary_tokens(offsets, sorted_pair, wl.k, 128, wl.seed)
+    if n_shared:
+        base = np.arange(wl.Mr, dtype=np.int32) if sel is None else sel
+        sel = np.concatenate([base, wl.Mr + _sample(wl.Ms - wl.Mr, n_shared, wl.seed + 1)]).astype(np.int32)
+    loads = np.diff(offsets)
+    print(f"[{name}] oracle on {len(sel)} tokens ({np.count_nonzero(sel < wl.Mr)} routed)", flush=True)
     stats = check_forward(dev, inp, sel=sel)
-    loads = np.diff(to_np(dev.offsets))
     print(f"[{name}] expert loads min/max {loads.min()}/{loads.max()}, touched {np.count_nonzero(loads)}; {stats}",
           flush=True)

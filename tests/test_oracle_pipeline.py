@@ -210,3 +210,33 @@ def test_subset_selection_matches_full_run():
     part = orc.forward(inp, ids, w, sel=sel)
     assert np.array_equal(part.out_bf16, full.out_bf16[sel])
     assert np.array_equal(part.hq, full.hq[sel])
+
+
+def test_given_h_codes_continue_the_same_pipeline():
+    # Given the oracle's own h codes back, every later step is bit for bit the
+    # plain run's; given one code moved by a step, only that (token, slot)'s y
+    # row changes, by the moved value times the W2 column (float64 check).
+    inp = synth.make_inputs(PIN)
+    ids, w = orc.route(inp.x_lat, inp.gate, inp.gate_bias, PIN.k)
+    sel = np.array([4, 0, 2, 6], np.int32)
+    plain = orc.forward(inp, ids, w, sel=sel)
+    same = orc.forward(inp, ids, w, sel=sel, h_codes=(plain.hq, plain.sh))
+    for name in ("y", "rn", "out_f32", "out_bf16", "hq", "sh", "sbf"):
+        assert np.array_equal(getattr(same, name), getattr(plain, name)), name
+    assert np.all(same.h == 0)  # the L1 is skipped
+    hq = plain.hq.copy()
+    s_, j_, i_ = 2, 1, 37          # token 2 (row 2 of sel), slot 1, h column 37
+    old = hq[s_, j_, i_]
+    hq[s_, j_, i_] = (old & 0x80) | ((old & 0x7F) + 1)
+    moved = orc.forward(inp, ids, w, sel=sel, h_codes=(hq, plain.sh))
+    dy = moved.y.astype(np.float64) - plain.y
+    mask = np.zeros(dy.shape, bool)
+    mask[s_, j_] = True
+    assert np.all(dy[~mask] == 0)
+    W2 = _dequant(inp, "w2")
+    dh = (ref.E4M3[hq[s_, j_, i_]] - ref.E4M3[old]) * np.float64(plain.sh[s_, j_, i_ // 128])
+    want = dh * W2[ids[sel[s_], j_]][:, i_]
+    # (dy is the difference of two FP32 sums: compare at the scale of the y row)
+    yscale = np.sqrt(np.mean(plain.y[s_, j_].astype(np.float64) ** 2))
+    assert np.max(np.abs(dy[s_, j_] - want)) <= 1e-5 * yscale
+    assert np.max(np.abs(dy[s_, j_] - want)) <= 1e-2 * np.max(np.abs(want))
