@@ -152,9 +152,16 @@ def measure(name: str, args, torch, np, B, synth, DeviceTail, to_np, flush) -> d
     torch.cuda.synchronize()
 
     # one step (route + forward, all kernels) captured as a HIP graph
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step(torch.cuda.current_stream())
+    if args.eager:
+        class _Eager:
+            @staticmethod
+            def replay():
+                step(torch.cuda.current_stream())
+        graph = _Eager()
+    else:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(torch.cuda.current_stream())
     torch.cuda.synchronize()
     for _ in range(3):
         graph.replay()
@@ -269,6 +276,7 @@ def main() -> int:
                     help="other workloads timed on the same line (comma list, 'none', or 'all')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-cold replays")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--add3", action="store_true",
                     help="time moe_tail_forward_add3 (the residual joined in the up-projection epilogue)")
     ap.add_argument("--fused", action="store_true",
@@ -358,7 +366,7 @@ def main() -> int:
         "algorithmic_bytes": head["algorithmic_bytes"], "touched_experts": head["touched_experts"],
         "hbm_frac": head["hbm_frac"], "tflops_lowp": head["TFLOPs_lowp"], "tflops_bf16": head["TFLOPs_bf16"],
         "stream_read_gbs": sread, "frac_of_stream_read": head["GBps"] / sread,
-        "timing": ("HIP graph replay of route + forward" +
+        "timing": (("eager launches" if args.eager else "HIP graph replay") + " of route + forward" +
                    (" (single-launch forward)" if args.fused else "") + "; events between replays"),
         "groups_us": head["groups_us"],
         "roofline": head.get("roofline"), "cpu_baseline": cpu, "input_gen_s": head["input_gen_s"],
