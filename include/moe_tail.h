@@ -159,6 +159,28 @@ int moe_tail_forward_add3(const moe_tail_dims *dims, const moe_tail_weights *wei
                           const uint16_t *residual, uint16_t *out, uint16_t *shared_out, void *workspace,
                           size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture that must not call the allocator, tight serving loops, harnesses
+ * that forbid it): moe_tail_forward without a workspace argument.  The
+ * library keeps one workspace of MOE_TAIL_NOALLOC_MAX_BYTES in device memory
+ * for the whole process (a static device array, one per GPU it runs on) and
+ * the call uses that; it allocates nothing and frees nothing.
+ *   Sizes whose moe_tail_workspace_bytes exceeds MOE_TAIL_NOALLOC_MAX_BYTES
+ *   return MOE_TAIL_ERR_WORKSPACE with nothing enqueued (48 MiB covers the
+ *   decode sizes: 128 routed and 128 shared tokens with 64..1024 experts,
+ *   top-8, I = I_s = 2048 at the served widths take about 43 MiB).
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents: calls that overlap on one GPU (other streams, other
+ *   threads) race and must be serialized by the caller.  Whatever must start
+ *   at zero is cleared by the call's own kernels.
+ *   Results are bit for bit those of moe_tail_forward; every other argument
+ *   and error is moe_tail_forward's.  MOE_TAIL_ERR_DEVICE also reports that
+ *   the runtime could not give this device's copy of the array. */
+#define MOE_TAIL_NOALLOC_MAX_BYTES ((size_t)48 << 20)
+int moe_tail_forward_noalloc(const moe_tail_dims *dims, const moe_tail_weights *weights, const uint16_t *x_lat,
+                             int32_t Mr, const uint16_t *x_hid, int32_t Ms, const moe_tail_routing *routing,
+                             uint16_t *out, uint16_t *shared_out, void *stream);
+
 /* moe_tail_forward (residual NULL) or moe_tail_forward_add3 (residual
  * non-NULL) as two launches: the x quantizer, then ONE persistent launch
  * that runs the routed experts, the shared expert, combine + RMSNorm and the

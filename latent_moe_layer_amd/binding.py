@@ -30,7 +30,7 @@ SIZE_MAX = 2 ** 64 - 1
 MOE_TAIL_NUM_STAGES = 7
 
 EXPORTED = ("moe_tail_workspace_bytes", "moe_tail_workspace_layout", "moe_tail_route", "moe_tail_forward",
-            "moe_tail_forward_add3", "moe_tail_forward_fused", "moe_tail_forward_fused_bounded",
+            "moe_tail_forward_add3", "moe_tail_forward_noalloc", "moe_tail_forward_fused", "moe_tail_forward_fused_bounded",
             "moe_tail_forward_profiled", "moe_tail_forward_timed", "moe_tail_stage_name", "moe_tail_quant_fp8_1x128",
             "moe_tail_pack_mxfp4_scales", "moe_tail_strerror")
 
@@ -77,6 +77,8 @@ def lib() -> C.CDLL:
                C.POINTER(Routing), C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
         L.moe_tail_forward.restype = C.c_int
         L.moe_tail_forward.argtypes = fwd
+        L.moe_tail_forward_noalloc.restype = C.c_int
+        L.moe_tail_forward_noalloc.argtypes = fwd[:9] + [C.c_void_p]
         L.moe_tail_forward_add3.restype = C.c_int
         L.moe_tail_forward_add3.argtypes = fwd[:7] + [C.c_void_p] + fwd[7:]
         L.moe_tail_forward_fused.restype = C.c_int
@@ -160,6 +162,16 @@ def moe_tail_forward(dims: Dims, weights: Weights, x_lat, Mr: int, x_hid, Ms: in
     _check(lib().moe_tail_forward(C.byref(dims), C.byref(weights), ptr(x_lat), Mr, ptr(x_hid), Ms,
                                   C.byref(routing), ptr(out), ptr(shared_out), ptr(workspace), ws_bytes,
                                   stream_handle(stream)), "moe_tail_forward")
+
+
+MOE_TAIL_NOALLOC_MAX_BYTES = 48 << 20
+
+
+def moe_tail_forward_noalloc(dims: Dims, weights: Weights, x_lat, Mr: int, x_hid, Ms: int, routing: Routing, out,
+                             shared_out, stream=None) -> None:
+    _check(lib().moe_tail_forward_noalloc(C.byref(dims), C.byref(weights), ptr(x_lat), Mr, ptr(x_hid), Ms,
+                                          C.byref(routing), ptr(out), ptr(shared_out), stream_handle(stream)),
+           "moe_tail_forward_noalloc")
 
 
 def moe_tail_forward_add3(dims: Dims, weights: Weights, x_lat, Mr: int, x_hid, Ms: int, routing: Routing, residual,

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/moe_tail.h"
 #include "dense_gemm.hpp"
@@ -646,6 +647,29 @@ int fused_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint1
   return launched();
 }
 
+// Scratch of moe_tail_forward_noalloc: the workspace of one call, held by
+// the library in device memory for as long as the process runs (one copy per
+// GPU, each at its own address).  Host code never uses the array's name as
+// an address: scratch_base() asks the runtime for this device's copy.
+constexpr size_t kScratchBytes = MOE_TAIL_NOALLOC_MAX_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The current device's copy of `scratch`, looked up once per device (with
+// that device current); nullptr if the runtime cannot give it.
+void* scratch_base() {
+  static std::mutex mu;
+  static void* base[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (base[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    base[dev] = p;
+  }
+  return base[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -743,6 +767,22 @@ int moe_tail_forward(const moe_tail_dims* dims, const moe_tail_weights* w, const
                      const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, uint16_t* out,
                      uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, nullptr, out, shared_out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_tail_forward_noalloc(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
+                             const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, uint16_t* out,
+                             uint16_t* shared_out, void* stream) {
+  // every check first, with a stand-in for the scratch address (nothing is
+  // dereferenced on the host), then the one runtime lookup
+  Layout lay;
+  void* const stand_in = reinterpret_cast<void*>(kAlign);
+  int rc = check_forward(dims, w, x_lat, Mr, x_hid, Ms, routing, nullptr, out, shared_out, stand_in, kScratchBytes,
+                         &lay);
+  if (rc) return rc;
+  void* base = scratch_base();
+  if (base == nullptr) return MOE_TAIL_ERR_DEVICE;
+  return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, nullptr, out, shared_out, base, kScratchBytes, stream,
+                      nullptr);
 }
 
 int moe_tail_forward_add3(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,

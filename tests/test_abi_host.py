@@ -209,6 +209,20 @@ def test_forward_fused_bounded_rejections():
         B.MOE_TAIL_ERR_UNSUPPORTED
 
 
+def test_forward_noalloc_rejections():
+    # every check runs before the runtime is asked for the scratch address
+    f = B.lib().moe_tail_forward_noalloc
+    w, r = _fake_weights(), _fake_routing()
+    big = dims(num_experts=8, inter=512, shared_inter=256)
+    assert B.moe_tail_workspace_bytes(big, 512, 512) > B.MOE_TAIL_NOALLOC_MAX_BYTES
+    assert f(C.byref(big), C.byref(w), X, 512, X, 512, C.byref(r), OUT, None, None) == B.MOE_TAIL_ERR_WORKSPACE
+    d = dims()
+    assert f(C.byref(d), C.byref(w), X, 17, X, 16, C.byref(r), OUT, None, None) == B.MOE_TAIL_ERR_INVALID
+    assert f(C.byref(d), C.byref(w), X, 16, X, 32, C.byref(r), OUT, None, None) == B.MOE_TAIL_ERR_INVALID
+    assert f(C.byref(dims(hidden=7040)), C.byref(w), X, 16, X, 16, C.byref(r), OUT, None, None) == \
+        B.MOE_TAIL_ERR_UNSUPPORTED
+
+
 def test_probe_rejections():
     p = B.probes()
     assert p.moe_tail_probe_mfma_fp8(X, X, OUT, 0, None) == 1
