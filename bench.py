@@ -47,7 +47,10 @@ BF16_PEAK_TFLOPS = 2500.0
 # counter runs, each scaled by the same counter's reading of the probe copy
 # of 512 MiB (bench.py --calibrate-copy); see the traffic summaries under
 # profiles/.  Only figures taken on the current kernels are listed.
-MEASURED_L1_TRAFFIC: dict = {}
+MEASURED_L1_TRAFFIC = {
+    "decode": 945.7e6,    # k_tile<0, 0, 0, 32>: 943.5 MB fetched + 2.2 MB written (profiles/decode_tail_traffic.md)
+    "prefill": 1589.5e6,  # k_tile<0, 0, 0, 256> 1129.4 MB + k_tile<0, 0, 0, 128> 460.0 MB (profiles/prefill_tail_traffic.md)
+}
 # workloads whose routed GEMMs are bound by the matrix cores (the others stream weights)
 MFMA_BOUND = {"prefill"}
 
