@@ -287,27 +287,49 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   struct Desc {
     int e, row0, rows, nt;
   };
-  // tile j of this workgroup
+  // tile j of this workgroup.  Routed tiles are numbered expert by expert;
+  // within an expert (ns row slots x ntn n tiles) in blocks of kNBlk n tiles,
+  // slot-major inside a block, so that the workgroups of an XCD working on
+  // neighbouring tiles share both the weight rows (same n tile, different
+  // slots) and the gathered activation rows (same slot, different n tiles)
+  // in the XCD's L2: an expert with many row slots is streamed about ns /
+  // (slots per round) times instead of once per slot.
+  constexpr int kNBlk = 4;
   auto desc = [&](int j) -> Desc {
     const int t = lo + lb + j * nbx;
-    const int slot = t / p.ntn;
     Desc d;
-    d.nt = t - slot * p.ntn;
     if (kRouted) {
-      int a = 0, b = p.E;  // s_pre[a] <= slot < s_pre[b]
+      int a = 0, b = p.E;  // s_pre[a] * ntn <= t < s_pre[b] * ntn
       while (b - a > 1) {
         const int m = (a + b) >> 1;
-        if (s_pre[m] <= slot) a = m;
+        if (s_pre[m] * p.ntn <= t) a = m;
         else b = m;
       }
       d.e = a;
+      const int ns = s_pre[a + 1] - s_pre[a];
+      const int local = t - s_pre[a] * p.ntn;
+      const int full = p.ntn / kNBlk;
+      int blk = local / (kNBlk * ns), n0, w, rem;
+      if (blk < full) {
+        n0 = blk * kNBlk;
+        w = kNBlk;
+        rem = local - blk * kNBlk * ns;
+      } else {
+        n0 = full * kNBlk;
+        w = p.ntn - n0;
+        rem = local - full * kNBlk * ns;
+      }
+      const int slot = rem / w;
+      d.nt = n0 + (rem - slot * w);
       // 128-row tiles of an expert with 256-row tiles cover only the rows
       // past its full 256-row tiles
       const int c = s_eoff[a + 1] - s_eoff[a];
       const int base = (TM == 128 && use256(c, p.huge_rows)) ? c / 256 * 256 : 0;
-      d.row0 = s_eoff[a] + base + (slot - s_pre[a]) * TM;
+      d.row0 = s_eoff[a] + base + slot * TM;
       d.rows = min(TM, s_eoff[a + 1] - d.row0);
     } else {
+      const int slot = t / p.ntn;
+      d.nt = t - slot * p.ntn;
       d.e = 0;
       d.row0 = slot * TM;
       d.rows = min(TM, p.M - d.row0);
