@@ -48,6 +48,7 @@ LATENT = 3584
 
 WFMT_FP8 = 0
 WFMT_MXFP4 = 1
+WFMT_NVFP4 = 3
 
 # tensor tags for the per-tensor seed streams
 _T_XLAT, _T_WG, _T_W1, _T_W2, _T_GAMMA, _T_WUP, _T_XHID, _T_WS1, _T_WS2 = range(1, 10)
@@ -82,6 +83,9 @@ WORKLOADS = {
     "mxfp4": Workload("mxfp4", Mr=1024, Ms=1024, E=128, k=8, I=2048, Is=2048, wfmt=WFMT_MXFP4, seed=3,
                       zipf_s=1.2),
     "indep": Workload("indep", Mr=2048, Ms=8192, E=384, k=8, I=2048, Is=2048, wfmt=WFMT_FP8, seed=4),
+    # the decode shape with NVFP4 routed weights (e2m1, an e4m3 scale per 16
+    # along K and an fp32 scale per expert matrix)
+    "nvfp4": Workload("nvfp4", Mr=128, Ms=128, E=64, k=8, I=2048, Is=2048, wfmt=WFMT_NVFP4, seed=5),
 }
 
 
@@ -115,6 +119,41 @@ def _quant_fp8_block128(w: np.ndarray):
     return codes, scale
 
 
+def _e2m1_codes(v: np.ndarray) -> np.ndarray:
+    """Nearest e2m1 code of each value (ties to the even code), saturating at
+    6, sign in bit 3: the grid has spacing 0.5 below 2, 1 in [2, 4) and 2 from
+    4 on, so the nearest code is an integer rounding (numpy's rint: ties to
+    even) per range."""
+    mag = np.abs(v)
+    code = np.where(mag < 2, np.rint(mag * 2),
+                    np.where(mag < 4, np.rint(mag) + 2, np.minimum(np.rint(mag * 0.5), 3) + 4)).astype(np.uint8)
+    return code | (np.signbit(v).astype(np.uint8) << 3)
+
+
+def _quant_nvfp4(w: np.ndarray):
+    """w [N, K] fp32 -> (packed [N, K/2] u8 e2m1, scales [N, K/16] u8 e4m3,
+    tensor scale fp32).
+
+    NVFP4 as served with --quantization nvfp4: one fp32 scale g for the whole
+    matrix, g = amax / (448 * 6), so that each 16-element block's scale
+    amax16 / (6 g) fits the e4m3 range; that block scale is rounded to e4m3
+    (nearest, torch's cast), and each element w / (s16 g) to the nearest e2m1
+    (saturating at 6; 0 where the block scale rounded to 0)."""
+    n, kk = w.shape
+    amax = np.float32(np.abs(w).max())
+    g = np.float32(1.0) if amax == 0 else np.float32(amax / np.float32(448.0 * 6.0))
+    blocks = w.reshape(n, kk // 16, 16)
+    bmax = np.abs(blocks).max(axis=2)
+    sv = np.minimum(bmax / (np.float32(6.0) * g), np.float32(448.0)).astype(np.float32)
+    scodes = torch.from_numpy(np.ascontiguousarray(sv)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    sdec = torch.from_numpy(scodes.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    den = (sdec * g).astype(np.float32)
+    v = np.where(den[:, :, None] > 0, blocks / np.where(den > 0, den, 1)[:, :, None], 0).astype(np.float32)
+    code = _e2m1_codes(v).reshape(n, kk)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scodes, g
+
+
 def _quant_mxfp4(w: np.ndarray):
     """w [N, K] fp32 -> (packed [N, K/2] u8, e8m0 scales [N, K/32] u8).
 
@@ -131,11 +170,7 @@ def _quant_mxfp4(w: np.ndarray):
     X = np.clip(X, -127, 127)
     e8m0 = (X + 127).astype(np.uint8)
     v = blocks * np.ldexp(np.float32(1.0), -X)[:, :, None].astype(np.float32)
-    mag = np.abs(v)
-    code = np.where(mag < 2, np.rint(mag * 2),
-                    np.where(mag < 4, np.rint(mag) + 2, np.minimum(np.rint(mag * 0.5), 3) + 4)).astype(np.uint8)
-    code |= (np.signbit(v).astype(np.uint8) << 3)
-    code = code.reshape(n, kk)
+    code = _e2m1_codes(v).reshape(n, kk)
     packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
     return packed, e8m0
 
@@ -147,15 +182,17 @@ class Inputs:
     x_hid: np.ndarray            # [Ms, H] bf16 bits
     gate: np.ndarray             # [E, L] fp32
     gate_bias: np.ndarray        # [E] fp32
-    w1: np.ndarray               # FP8 [E, 2I, L] u8 | MXFP4 [E, 2I, L/2] u8
-    w1_scale: np.ndarray         # FP8 [E, 2I/128, L/128] f32 | MXFP4 [E, 2I, L/32] u8
-    w2: np.ndarray               # FP8 [E, L, I] u8 | MXFP4 [E, L, I/2] u8
-    w2_scale: np.ndarray         # FP8 [E, L/128, I/128] f32 | MXFP4 [E, L, I/32] u8
+    w1: np.ndarray               # FP8 [E, 2I, L] u8 | MXFP4, NVFP4 [E, 2I, L/2] u8
+    w1_scale: np.ndarray         # FP8 [E, 2I/128, L/128] f32 | MXFP4 [E, 2I, L/32] u8 e8m0 | NVFP4 [E, 2I, L/16] u8 e4m3
+    w2: np.ndarray               # FP8 [E, L, I] u8 | MXFP4, NVFP4 [E, L, I/2] u8
+    w2_scale: np.ndarray         # FP8 [E, L/128, I/128] f32 | MXFP4 [E, L, I/32] u8 e8m0 | NVFP4 [E, L, I/16] u8 e4m3
     gamma: np.ndarray            # [L] bf16 bits
     w_up: np.ndarray             # [H, L] bf16 bits
     ws1: np.ndarray              # [2 Is, H] bf16 bits
     ws2: np.ndarray              # [H, Is] bf16 bits
     extra: dict = field(default_factory=dict)
+    w1_tscale: np.ndarray = field(default_factory=lambda: np.zeros(0, np.float32))  # NVFP4: [E] fp32
+    w2_tscale: np.ndarray = field(default_factory=lambda: np.zeros(0, np.float32))  # NVFP4: [E] fp32
 
 
 def _normal(seed, tag, idx, shape, std):
@@ -166,11 +203,14 @@ def _normal(seed, tag, idx, shape, std):
     return a
 
 
-def _expert_weights(wl: Workload, tag: int, e: int, n: int, kk: int, out_codes, out_scales):
+def _expert_weights(wl: Workload, tag: int, e: int, n: int, kk: int, out_codes, out_scales, out_tscale):
     src = 0 if wl.identical_experts else e
     w = _normal(wl.seed, tag, src, (n, kk), 1.0 / np.sqrt(kk))
     if wl.wfmt == WFMT_FP8:
         c, s = _quant_fp8_block128(w)
+    elif wl.wfmt == WFMT_NVFP4:
+        c, s, g = _quant_nvfp4(w)
+        out_tscale[e] = g
     else:
         c, s = _quant_mxfp4(w)
     out_codes[e] = c
@@ -201,18 +241,25 @@ def make_inputs(wl: Workload | str, Mr: int | None = None, Ms: int | None = None
         e8, e16 = np.zeros(0, np.uint8), np.zeros(0, np.uint16)
         return Inputs(wl, x_lat, e16, gate, gate_bias, e8, np.zeros(0, np.float32), e8, np.zeros(0, np.float32),
                       e16, e16, e16, e16)
+    w1t = np.zeros(E if wl.wfmt == WFMT_NVFP4 else 0, np.float32)
+    w2t = np.zeros(E if wl.wfmt == WFMT_NVFP4 else 0, np.float32)
     if wl.wfmt == WFMT_FP8:
         w1 = np.empty((E, 2 * I, L), np.uint8)
         w1s = np.empty((E, 2 * I // 128, L // 128), np.float32)
         w2 = np.empty((E, L, I), np.uint8)
         w2s = np.empty((E, L // 128, I // 128), np.float32)
+    elif wl.wfmt == WFMT_NVFP4:
+        w1 = np.empty((E, 2 * I, L // 2), np.uint8)
+        w1s = np.empty((E, 2 * I, L // 16), np.uint8)
+        w2 = np.empty((E, L, I // 2), np.uint8)
+        w2s = np.empty((E, L, I // 16), np.uint8)
     else:
         w1 = np.empty((E, 2 * I, L // 2), np.uint8)
         w1s = np.empty((E, 2 * I, L // 32), np.uint8)
         w2 = np.empty((E, L, I // 2), np.uint8)
         w2s = np.empty((E, L, I // 32), np.uint8)
-    jobs = [(_T_W1, e, 2 * I, L, w1, w1s) for e in range(E)] + \
-           [(_T_W2, e, L, I, w2, w2s) for e in range(E)]
+    jobs = [(_T_W1, e, 2 * I, L, w1, w1s, w1t) for e in range(E)] + \
+           [(_T_W2, e, L, I, w2, w2s, w2t) for e in range(E)]
     with ThreadPoolExecutor(_workers()) as ex:
         list(ex.map(lambda j: _expert_weights(wl, *j), jobs))
     r = _rng(wl.seed, _T_GAMMA, 0)
@@ -225,7 +272,8 @@ def make_inputs(wl: Workload | str, Mr: int | None = None, Ms: int | None = None
     else:
         ws1 = f32_to_bf16_bits(_normal(wl.seed, _T_WS1, 0, (2 * Is, H), 1.0 / np.sqrt(H)))
         ws2 = f32_to_bf16_bits(_normal(wl.seed, _T_WS2, 0, (H, Is), 1.0 / np.sqrt(Is)))
-    return Inputs(wl, x_lat, x_hid, gate, gate_bias, w1, w1s, w2, w2s, gamma, w_up, ws1, ws2)
+    return Inputs(wl, x_lat, x_hid, gate, gate_bias, w1, w1s, w2, w2s, gamma, w_up, ws1, ws2,
+                  w1_tscale=w1t, w2_tscale=w2t)
 
 
 def make_residual(wl: Workload | str, Mr: int | None = None) -> np.ndarray:
@@ -244,6 +292,8 @@ def algorithmic_bytes(wl: Workload, touched_experts: int | None = None) -> dict:
     L, H, I, Is = wl.L, wl.H, wl.I, wl.Is
     if wl.wfmt == WFMT_FP8:
         routed = E * (2 * I * L + L * I) + E * 4 * ((2 * I // 128) * (L // 128) + (L // 128) * (I // 128))
+    elif wl.wfmt == WFMT_NVFP4:
+        routed = E * (2 * I * L // 2 + L * I // 2) + E * (2 * I * L // 16 + L * I // 16) + E * 8
     else:
         routed = E * (2 * I * L // 2 + L * I // 2) + E * (2 * I * L // 32 + L * I // 32)
     dense = 2 * (H * L + 2 * Is * H + H * Is) + 4 * wl.E * L + 2 * L

@@ -12,7 +12,8 @@
 //             ("top-k weighted expert combine", tokenspeed PR 1062, Summary)
 //   permute   histogram -> exclusive scan -> stable scatter by (expert, token)
 //   routed    x_lat quantized to e4m3 with one fp32 scale per 1x128 block;
-//             L1 gate/up with 128x128 block-scaled e4m3 weights (or MXFP4);
+//             L1 gate/up with 128x128 block-scaled e4m3 weights (or MXFP4, or
+//             NVFP4: tokenspeed recipe, Allocation and launch);
 //             SwiGLU; h re-quantized per 1x128; L2 down to the 3584-wide latent
 //             ("[Kimi K3][Kernel] Fuse BF16 shared experts into latent MegaMoE
 //             tail", Summary: routed FP8/FP4 MegaMoE producing a 3584-wide latent)
@@ -155,7 +156,24 @@ float silu_mul(float gate, float up) { return (gate / (1.0f + std::exp(-gate))) 
 // Dequantized routed weight row n of expert e of a [N, K] matrix.
 //   FP8: W = RN(e4m3(code) * S[n/128, c/128])
 //   MXFP4: W = e2m1(nibble) * 2^(e8m0 - 127)   (exact)
-void dequant_row(int wfmt, const uint8_t* w, const void* ws, int e, int N, int K, int n, float* out) {
+//   NVFP4: W = RN((e2m1(nibble) * e4m3(S[n, c/16])) * g[e]), the inner product
+//          exact (at most five significant bits), g the matrix's fp32 scale.
+//          (Reading: the pages name NVFP4 only as the served quantization;
+//          this is the format as published: e2m1 elements, an e4m3 scale per
+//          16 along K, an fp32 scale per tensor, here per expert matrix.)
+void dequant_row(int wfmt, const uint8_t* w, const void* ws, const float* tscale, int e, int N, int K, int n,
+                 float* out) {
+  if (wfmt == 3) {
+    const uint8_t* row = w + (static_cast<size_t>(e) * N + n) * (K / 2);
+    const uint8_t* S = static_cast<const uint8_t*>(ws) + (static_cast<size_t>(e) * N + n) * (K / 16);
+    const float g = tscale[e];
+    for (int c = 0; c < K; ++c) {
+      uint8_t byte = row[c / 2];
+      uint8_t nib = (c % 2 == 0) ? (byte & 0xf) : (byte >> 4);
+      out[c] = (e2m1_decode(nib) * e4m3_value(S[c / 16])) * g;
+    }
+    return;
+  }
   if (wfmt == 0) {
     const uint8_t* row = w + (static_cast<size_t>(e) * N + n) * K;
     const float* S = static_cast<const float*>(ws) + static_cast<size_t>(e) * (N / 128) * (K / 128) +
@@ -323,6 +341,8 @@ void oracle_permute(int E, int k, int Mr, const int32_t* ids, int32_t* offsets, 
 //   y[s, k, L]                               routed L2 output per slot
 //   rn[s, L]                                 normalised latent (bf16)
 //   hs[s, Is], sbf[s, H]                     shared intermediate and output (bf16)
+// w1_tscale / w2_tscale: [E] fp32 scales of the NVFP4 matrices (wfmt 3; NULL
+// otherwise).
 // hq_in / sh_in (optional, [n_sel, k, I] codes and [n_sel, k, I/128] scales,
 // rows in sel order): h codes and scales given instead of computed; the
 // routed L1 and SwiGLU are then skipped (h_out reads 0) and every later step
@@ -337,8 +357,10 @@ int oracle_forward(int H, int L, int E, int k, int I, int Is, int wfmt, float ep
                    float* out_f32, uint16_t* out_bf16,
                    uint8_t* xq_out, float* sx_out, uint8_t* hq_out, float* sh_out, float* h_out,
                    float* y_out, uint16_t* rn_out, uint16_t* hs_out, uint16_t* sbf_out,
-                   const uint8_t* hq_in, const float* sh_in) {
+                   const uint8_t* hq_in, const float* sh_in, const float* w1_tscale, const float* w2_tscale) {
   if ((hq_in == nullptr) != (sh_in == nullptr)) return 1;
+  if (wfmt != 0 && wfmt != 1 && wfmt != 3) return 1;
+  if (wfmt == 3 && (w1_tscale == nullptr || w2_tscale == nullptr)) return 1;
   if (L % 128 || H % 128 || I % 128 || Is % 128 || k < 1 || k > E || Mr < 0 || Mr > Ms) return 1;
   for (int s = 0; s < n_sel; ++s)
     if (sel[s] < 0 || sel[s] >= Ms) return 1;
@@ -376,7 +398,7 @@ int oracle_forward(int H, int L, int E, int k, int I, int Is, int wfmt, float ep
         const int a = aj / k, j = aj % k;
         const int t = sel[rsel[a]];
         const int e = topk_ids[static_cast<size_t>(t) * k + j];
-        dequant_row(wfmt, w1, w1s, e, 2 * I, L, n, wrow.data());
+        dequant_row(wfmt, w1, w1s, w1_tscale, e, 2 * I, L, n, wrow.data());
         g[static_cast<size_t>(aj) * 2 * I + n] = dot(&xhat[static_cast<size_t>(a) * L], wrow.data(), L);
       }
   }
@@ -413,7 +435,7 @@ int oracle_forward(int H, int L, int E, int k, int I, int Is, int wfmt, float ep
         const int a = aj / k, j = aj % k;
         const int t = sel[rsel[a]];
         const int e = topk_ids[static_cast<size_t>(t) * k + j];
-        dequant_row(wfmt, w2, w2s, e, L, I, n, wrow.data());
+        dequant_row(wfmt, w2, w2s, w2_tscale, e, L, I, n, wrow.data());
         y[static_cast<size_t>(aj) * L + n] = dot(&hhat[static_cast<size_t>(aj) * I], wrow.data(), I);
       }
   }

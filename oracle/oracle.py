@@ -197,7 +197,9 @@ def forward(inp, topk_ids, topk_w, sel=None, Mr=None, Ms=None, residual=None, h_
         _p(arrs[8]), C.c_int(Mr), _p(arrs[9]), C.c_int(Ms), _p(arrs[10]), _p(arrs[11]), _p(res),
         C.c_int(n), _p(sel),
         _p(r.out_f32), _p(r.out_bf16), _p(r.xq), _p(r.sx), _p(r.hq), _p(r.sh), _p(r.h), _p(r.y), _p(r.rn),
-        _p(r.hs), _p(r.sbf), _p(hq_in), _p(sh_in))
+        _p(r.hs), _p(r.sbf), _p(hq_in), _p(sh_in),
+        _p(_c(inp.w1_tscale, np.float32) if wl.wfmt == 3 else None),
+        _p(_c(inp.w2_tscale, np.float32) if wl.wfmt == 3 else None))
     if rc != 0:
         raise ValueError("oracle_forward rejected its arguments")
     return r

@@ -88,5 +88,16 @@ def dequant_mxfp4(packed: np.ndarray, e8m0: np.ndarray) -> np.ndarray:
     return v * s
 
 
+def dequant_nvfp4(packed: np.ndarray, s16: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """[E, N, K/2] e2m1 pairs, [E, N, K/16] e4m3 scales, [E] fp32 matrix
+    scales -> fp64 weights e2m1 * e4m3 * g (exact in fp64)."""
+    lo = packed & 0xF
+    hi = packed >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(*packed.shape[:-1], packed.shape[-1] * 2)
+    v = e2m1_values()[nib]
+    s = np.repeat(E4M3[s16], 16, axis=-1)
+    return v * s * np.asarray(g, np.float64)[:, None, None]
+
+
 def silu_mul(g, u):
     return g / (1 + np.exp(-g)) * u

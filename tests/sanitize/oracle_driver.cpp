@@ -1,7 +1,7 @@
 // Runs the CPU oracle's entry points on small random inputs under the
 // address and undefined-behaviour sanitizers (built by
 // tests/test_sanitizers.py): the decoders over every code, the quantizer,
-// routing, the permutation and the forward pass for FP8 and MXFP4 weights,
+// routing, the permutation and the forward pass for FP8, MXFP4 and NVFP4 weights,
 // with token subsets, shared-only rows, the residual join and given h codes.
 // Exit status 0 when every call accepted its arguments; a sanitizer report
 // aborts the process.
@@ -46,7 +46,8 @@ int run(int wfmt) {
 
   // routed weights
   std::vector<uint8_t> w1, w2, w1s8, w2s8;
-  std::vector<float> w1s, w2s;
+  std::vector<float> w1s, w2s, tsc(E);
+  for (auto& v : tsc) v = unif(1e-4f, 1e-3f);
   if (wfmt == 0) {
     w1.resize(static_cast<size_t>(E) * 2 * I * L);
     w2.resize(static_cast<size_t>(E) * L * I);
@@ -61,10 +62,11 @@ int run(int wfmt) {
     w2.resize(static_cast<size_t>(E) * L * I / 2);
     for (auto& v : w1) v = static_cast<uint8_t>(rng() & 0xFF);
     for (auto& v : w2) v = static_cast<uint8_t>(rng() & 0xFF);
-    w1s8.resize(static_cast<size_t>(E) * 2 * I * L / 32);
-    w2s8.resize(static_cast<size_t>(E) * L * I / 32);
-    for (auto& v : w1s8) v = static_cast<uint8_t>(118 + rng() % 8);
-    for (auto& v : w2s8) v = static_cast<uint8_t>(118 + rng() % 8);
+    const int grp = wfmt == 3 ? 16 : 32;  // NVFP4: e4m3 scale per 16, MXFP4: e8m0 per 32
+    w1s8.resize(static_cast<size_t>(E) * 2 * I * L / grp);
+    w2s8.resize(static_cast<size_t>(E) * L * I / grp);
+    for (auto& v : w1s8) v = wfmt == 3 ? static_cast<uint8_t>(rng() & 0x7E) : static_cast<uint8_t>(118 + rng() % 8);
+    for (auto& v : w2s8) v = wfmt == 3 ? static_cast<uint8_t>(rng() & 0x7E) : static_cast<uint8_t>(118 + rng() % 8);
   }
   const void* w1s_p = wfmt == 0 ? static_cast<const void*>(w1s.data()) : w1s8.data();
   const void* w2s_p = wfmt == 0 ? static_cast<const void*>(w2s.data()) : w2s8.data();
@@ -87,7 +89,8 @@ int run(int wfmt) {
   int rc = oracle_forward(H, L, E, k, I, Is, wfmt, eps, w1.data(), w1s_p, w2.data(), w2s_p, gamma.data(), w_up.data(),
                           ws1.data(), ws2.data(), x_lat.data(), Mr, x_hid.data(), Ms, ids.data(), w.data(), nullptr,
                           n_all, sel_all.data(), out_f32.data(), out_bf16.data(), xq.data(), sx.data(), hq.data(),
-                          sh.data(), h.data(), y.data(), rn.data(), hs.data(), sbf.data(), nullptr, nullptr);
+                          sh.data(), h.data(), y.data(), rn.data(), hs.data(), sbf.data(), nullptr, nullptr,
+                          tsc.data(), tsc.data());
   if (rc) return 10 + rc;
   const std::vector<int32_t> sel = {6, 0, 3};
   const int n = static_cast<int>(sel.size());
@@ -101,13 +104,13 @@ int run(int wfmt) {
   rc = oracle_forward(H, L, E, k, I, Is, wfmt, eps, w1.data(), w1s_p, w2.data(), w2s_p, gamma.data(), w_up.data(),
                       ws1.data(), ws2.data(), x_lat.data(), Mr, x_hid.data(), Ms, ids.data(), w.data(), resid.data(),
                       n, sel.data(), o2.data(), nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                      nullptr, nullptr, hq_in.data(), sh_in.data());
+                      nullptr, nullptr, hq_in.data(), sh_in.data(), tsc.data(), tsc.data());
   if (rc) return 20 + rc;
   // a rejected call: h codes without scales
   if (oracle_forward(H, L, E, k, I, Is, wfmt, eps, w1.data(), w1s_p, w2.data(), w2s_p, gamma.data(), w_up.data(),
                      ws1.data(), ws2.data(), x_lat.data(), Mr, x_hid.data(), Ms, ids.data(), w.data(), nullptr, n,
                      sel.data(), o2.data(), nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     nullptr, nullptr, hq_in.data(), nullptr) == 0)
+                     nullptr, nullptr, hq_in.data(), nullptr, tsc.data(), tsc.data()) == 0)
     return 30;
   return 0;
 }
@@ -130,7 +133,7 @@ int main() {
   std::vector<uint8_t> q(4096);
   std::vector<float> s(32);
   oracle_quant_1x128(vals.data(), 4, 1024, q.data(), s.data());
-  for (int wfmt = 0; wfmt <= 1; ++wfmt) {
+  for (int wfmt : {0, 1, 3}) {
     const int rc = run(wfmt);
     if (rc) {
       std::printf("oracle driver: format %d failed (%d)\n", wfmt, rc);

@@ -20,10 +20,12 @@ def _rel_close(got, want, tol):
 def _dequant(inp, which):
     if inp.wl.wfmt == synth.WFMT_FP8:
         return ref.dequant_fp8(getattr(inp, which), getattr(inp, which + "_scale"))
+    if inp.wl.wfmt == synth.WFMT_NVFP4:
+        return ref.dequant_nvfp4(getattr(inp, which), getattr(inp, which + "_scale"), getattr(inp, which + "_tscale"))
     return ref.dequant_mxfp4(getattr(inp, which), getattr(inp, which + "_scale"))
 
 
-@pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4])
+@pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4, synth.WFMT_NVFP4])
 def test_pipeline_against_float64_stagewise(wfmt):
     wl = replace(PIN, wfmt=wfmt, zipf_s=1.2 if wfmt else 0.0)
     inp = synth.make_inputs(wl)
@@ -240,3 +242,52 @@ def test_given_h_codes_continue_the_same_pipeline():
     yscale = np.sqrt(np.mean(plain.y[s_, j_].astype(np.float64) ** 2))
     assert np.max(np.abs(dy[s_, j_] - want)) <= 1e-5 * yscale
     assert np.max(np.abs(dy[s_, j_] - want)) <= 1e-2 * np.max(np.abs(want))
+
+
+def test_nvfp4_with_power_of_two_scales_is_mxfp4():
+    # NVFP4 whose e4m3 block scales are powers of two, equal over each
+    # 32-wide group, and whose matrix scale is a power of two, encodes the same
+    # weights as MXFP4 with e8m0 = log2(block scale * matrix scale) + 127: every
+    # output of the pipeline is then bit for bit the MXFP4 one
+    wl4 = replace(PIN, wfmt=synth.WFMT_MXFP4, zipf_s=0.7)
+    inp4 = synth.make_inputs(wl4)
+    ids, w = orc.route(inp4.x_lat, inp4.gate, inp4.gate_bias, wl4.k)
+    base = orc.forward(inp4, ids, w)
+    nv = synth.make_inputs(replace(wl4, wfmt=synth.WFMT_NVFP4))
+    nv.w1, nv.w2 = inp4.w1, inp4.w2
+    for which, src in (("w1", inp4.w1_scale), ("w2", inp4.w2_scale)):
+        X = src.astype(np.int64) - 127 + 3          # block exponent against a matrix scale of 2^-3
+        assert np.all((X >= -9) & (X <= 8))         # a power of two e4m3 can hold
+        s16 = np.repeat(P_E4M3_POW2[X + 9], 2, axis=-1)
+        setattr(nv, which + "_scale", s16.astype(np.uint8))
+        setattr(nv, which + "_tscale", np.full(wl4.E, 2.0 ** -3, np.float32))
+    got = orc.forward(nv, ids, w)
+    for name in ("hq", "sh", "y", "rn", "out_f32", "out_bf16"):
+        assert np.array_equal(getattr(got, name), getattr(base, name)), name
+
+
+# e4m3 codes of 2^-9 .. 2^8 (index X + 9): subnormal 2^-9 .. 2^-7 (mantissa
+# 1, 2, 4), normal 2^-6 .. 2^8 (exponent field X + 7, mantissa 0)
+P_E4M3_POW2 = np.array([1, 2, 4] + [(x + 7) << 3 for x in range(-6, 9)], np.int64)
+
+
+def test_nvfp4_dequantization_against_float64():
+    wl = replace(PIN, wfmt=synth.WFMT_NVFP4)
+    inp = synth.make_inputs(wl)
+    assert inp.w1.shape == (wl.E, 2 * wl.I, wl.L // 2) and inp.w1_scale.shape == (wl.E, 2 * wl.I, wl.L // 16)
+    assert inp.w1_scale.dtype == np.uint8 and inp.w1_tscale.shape == (wl.E,)
+    # the oracle's L1 output of one token and expert against float64 from the codes
+    ids, w = orc.route(inp.x_lat, inp.gate, inp.gate_bias, wl.k)
+    res = orc.forward(inp, ids, w, sel=np.array([0], np.int32))
+    W1 = _dequant(inp, "w1")
+    xq, sx = ref.quant_1x128(ref.bf16_val(inp.x_lat[:1]).astype(np.float32))
+    xhat = ref.E4M3[xq[0]] * np.repeat(sx[0].astype(np.float64), 128)
+    for j in range(wl.k):
+        g = W1[ids[0, j]] @ xhat
+        h64 = ref.silu_mul(g[:wl.I], g[wl.I:])
+        amax = np.abs(h64).reshape(-1, 128).max(axis=1)
+        err = np.abs(res.h[0, j] - h64).reshape(-1, 128).max(axis=1)
+        assert np.all(err <= 1e-5 * amax)
+    # the generator's scales: every block scale times the matrix scale covers the block
+    w64 = _dequant(inp, "w1")
+    assert np.all(np.isfinite(w64)) and np.abs(w64).max() > 0
