@@ -51,6 +51,8 @@ MEASURED_L1_TRAFFIC = {
     "decode": 945.7e6,    # k_tile<0, 0, 0, 32>: 943.5 MB fetched + 2.2 MB written (profiles/decode_tail_traffic.md)
     "prefill": 1589.5e6,  # k_tile<0, 0, 0, 256> 1129.4 MB + k_tile<0, 0, 0, 128> 460.0 MB (profiles/prefill_tail_traffic.md)
 }
+FORMATS = {0: "FP8 128x128", 1: "MXFP4 (e8m0 scales packed)", 3: "NVFP4 (e4m3 scale per 16, fp32 per matrix)"}
+DTYPES = {0: "fp8e4m3+bf16", 1: "mxfp4+fp8e4m3+bf16", 3: "nvfp4+fp8e4m3+fp16+bf16"}
 # workloads whose routed GEMMs are bound by the matrix cores (the others stream weights)
 MFMA_BOUND = {"prefill"}
 
@@ -84,6 +86,8 @@ def routed_l1_bytes(wl, touched: int) -> int:
     L, I, R = wl.L, wl.I, wl.Mr * wl.k
     if wl.wfmt == 0:
         w = touched * (2 * I * L + 4 * (2 * I // 128) * (L // 128))
+    elif wl.wfmt == 3:
+        w = touched * (2 * I * L // 2 + 2 * I * L // 16 + 4)
     else:
         w = touched * (2 * I * L // 2 + 2 * I * L // 32)
     return w + wl.Mr * (L + 4 * L // 128) + R * (I + 4 * I // 128)
@@ -95,6 +99,8 @@ def routed_l2_bytes(wl, touched: int) -> int:
     L, I, R = wl.L, wl.I, wl.Mr * wl.k
     if wl.wfmt == 0:
         w = touched * (L * I + 4 * (L // 128) * (I // 128))
+    elif wl.wfmt == 3:
+        w = touched * (L * I // 2 + L * I // 16 + 4)
     else:
         w = touched * (L * I // 2 + L * I // 32)
     return w + R * (I + 4 * I // 128) + R * L * 4
@@ -219,7 +225,7 @@ def measure(name: str, args, torch, np, B, synth, DeviceTail, to_np, flush) -> d
     us = total_ms * 1e3 / K
     leg = {
         "workload": f"{wl.name}: Mr={wl.Mr} Ms={wl.Ms} E={wl.E} top{wl.k} I={wl.I} I_s={wl.Is} H={wl.H} L={wl.L} "
-                    f"{'FP8 128x128' if wl.wfmt == 0 else 'MXFP4 (e8m0 scales packed)'} routed weights",
+                    f"{FORMATS[wl.wfmt]} routed weights",
         "us_per_layer": us, "us_median": pct(per, 50), "us_p10": pct(per, 10), "us_p90": pct(per, 90),
         "cold_us_median": pct(cold, 50) if cold else None, "cold_us_p10": pct(cold, 10) if cold else None,
         "cold_us_p90": pct(cold, 90) if cold else None,
@@ -236,7 +242,9 @@ def measure(name: str, args, torch, np, B, synth, DeviceTail, to_np, flush) -> d
         gbs = l1_b / (l1_us * 1e-6) / 1e9
         tfs = l1_f / (l1_us * 1e-6) / 1e12
         fmt = "TF_FP8" if wl.wfmt == 0 else "TF_FP4"
-        if wl.Mr <= 256 and wl.Mr * wl.k <= 32 * wl.E:
+        if wl.wfmt == 3:
+            kern = "k_routed_l1<FMT_NVFP4>"
+        elif wl.Mr <= 256 and wl.Mr * wl.k <= 32 * wl.E:
             kern = f"k_tile<TK_L1, {fmt}, 0, 32>"
         else:
             kern = f"k_tile_small_mid<TK_L1, {fmt}>"
@@ -273,7 +281,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "mxfp4", "indep"],
+    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "mxfp4", "indep", "nvfp4"],
                     help="the headline workload")
     ap.add_argument("--legs", default="prefill,tiny",
                     help="other workloads timed on the same line (comma list, 'none', or 'all')")
@@ -320,7 +328,7 @@ def main() -> int:
     head = measure(args.workload, args, torch, np, B, synth, DeviceTail, to_np, flush)
     legs = {}
     names = [] if args.legs == "none" else \
-        (["tiny", "decode", "prefill", "mxfp4", "indep"] if args.legs == "all" else args.legs.split(","))
+        (["tiny", "decode", "prefill", "mxfp4", "indep", "nvfp4"] if args.legs == "all" else args.legs.split(","))
     inp, dev = head.pop("_inp"), head.pop("_dev")
 
     cpu = None
@@ -359,7 +367,7 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": head["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": us * 1e-3, "us_per_layer": us, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3+bf16" if wl.wfmt == 0 else "mxfp4+fp8e4m3+bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPES[wl.wfmt],
         "data": "synthetic (seeded; random-init weights of the tail's shapes)",
         "config": {"workload": head["workload"], "global_batch": wl.Mr, "parallelism": "single GPU",
                    "epilogue": "add3: up + shared + residual, one rounding" if args.add3 else "up + shared"},

@@ -52,7 +52,8 @@ typedef enum {
 typedef enum {
   MOE_TAIL_W_FP8_BLOCK128 = 0,   /* e4m3 codes + fp32 scale per 128 (N) x 128 (K) block */
   MOE_TAIL_W_MXFP4 = 1,          /* e2m1 pairs (even K in the low nibble) + e8m0 scale per 32 along K */
-  MOE_TAIL_W_MXFP4_PACKED = 2    /* MXFP4 with the e8m0 scales in the tile order of moe_tail_pack_mxfp4_scales */
+  MOE_TAIL_W_MXFP4_PACKED = 2,   /* MXFP4 with the e8m0 scales in the tile order of moe_tail_pack_mxfp4_scales */
+  MOE_TAIL_W_NVFP4 = 3           /* e2m1 pairs + e4m3 scale per 16 along K + fp32 scale per expert matrix */
 } moe_tail_wfmt;
 
 /* Sizes of one tail.  hidden (H) and latent (L) are the shared and routed
@@ -73,18 +74,26 @@ typedef struct {
 } moe_tail_dims;
 
 /* Weights (device, read-only).  Row r of w1 for r < I is the gate projection,
- * r >= I the up projection; the same split holds for ws1 with I_s. */
+ * r >= I the up projection; the same split holds for ws1 with I_s.
+ * NVFP4 (MOE_TAIL_W_NVFP4): the routed weights as served with NVFP4
+ * quantization (tokenspeed recipe "Kimi-K3 DEP16 with sharded shared
+ * experts", Allocation and launch): W = e2m1 * e4m3 block scale (one per 16
+ * weights along K) * the expert matrix's fp32 scale.  The gfx950 scaled
+ * matrix cores take e8m0 scales per 32 only, so these weights run on the
+ * FP16 matrix cores, dequantized exactly in registers. */
 typedef struct {
   const float *gate;          /* [E, L] fp32 router weights */
   const float *gate_bias;     /* [E] fp32 router bias, or NULL for none */
-  const uint8_t *w1;          /* FP8: [E, 2I, L] e4m3      | MXFP4: [E, 2I, L/2] packed e2m1 */
-  const void *w1_scale;       /* FP8: [E, 2I/128, L/128] f32 | MXFP4: [E, 2I, L/32] e8m0 */
-  const uint8_t *w2;          /* FP8: [E, L, I] e4m3       | MXFP4: [E, L, I/2] packed e2m1 */
-  const void *w2_scale;       /* FP8: [E, L/128, I/128] f32  | MXFP4: [E, L, I/32] e8m0 */
+  const uint8_t *w1;          /* FP8: [E, 2I, L] e4m3      | MXFP4, NVFP4: [E, 2I, L/2] packed e2m1 */
+  const void *w1_scale;       /* FP8: [E, 2I/128, L/128] f32 | MXFP4: [E, 2I, L/32] e8m0 | NVFP4: [E, 2I, L/16] e4m3 */
+  const uint8_t *w2;          /* FP8: [E, L, I] e4m3       | MXFP4, NVFP4: [E, L, I/2] packed e2m1 */
+  const void *w2_scale;       /* FP8: [E, L/128, I/128] f32  | MXFP4: [E, L, I/32] e8m0 | NVFP4: [E, L, I/16] e4m3 */
   const uint16_t *rms_gamma;  /* [L] bf16 */
   const uint16_t *w_up;       /* [H, L] bf16 up-projection */
   const uint16_t *ws1;        /* [2 I_s, H] bf16 shared gate/up */
   const uint16_t *ws2;        /* [H, I_s] bf16 shared down */
+  const float *w1_tensor_scale;  /* NVFP4: [E] fp32 scale of each expert's w1; ignored by the other formats */
+  const float *w2_tensor_scale;  /* NVFP4: [E] fp32 scale of each expert's w2; ignored by the other formats */
 } moe_tail_weights;
 
 /* Routing produced by moe_tail_route (device buffers owned by the caller). */

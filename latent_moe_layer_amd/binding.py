@@ -22,6 +22,7 @@ MOE_TAIL_ERR_DEVICE = 4
 MOE_TAIL_W_FP8_BLOCK128 = 0
 MOE_TAIL_W_MXFP4 = 1
 MOE_TAIL_W_MXFP4_PACKED = 2
+MOE_TAIL_W_NVFP4 = 3
 
 MOE_TAIL_WS_XQ, MOE_TAIL_WS_SX, MOE_TAIL_WS_HQ, MOE_TAIL_WS_SH, MOE_TAIL_WS_Y, MOE_TAIL_WS_RN, \
     MOE_TAIL_WS_HS, MOE_TAIL_WS_S, MOE_TAIL_WS_STATUS = range(9)
@@ -48,7 +49,7 @@ class Dims(C.Structure):
 
 class Weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("gate", "gate_bias", "w1", "w1_scale", "w2", "w2_scale", "rms_gamma",
-                                          "w_up", "ws1", "ws2")]
+                                          "w_up", "ws1", "ws2", "w1_tensor_scale", "w2_tensor_scale")]
 
 
 class Routing(C.Structure):

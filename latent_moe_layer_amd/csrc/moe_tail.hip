@@ -36,7 +36,8 @@ int check_dims(const moe_tail_dims* d) {
     return MOE_TAIL_ERR_INVALID;
   if (d->top_k < 1 || d->top_k > d->num_experts) return MOE_TAIL_ERR_INVALID;
   if (!(d->rms_eps > 0.0f) || !std::isfinite(d->rms_eps)) return MOE_TAIL_ERR_INVALID;
-  if (d->wfmt != MOE_TAIL_W_FP8_BLOCK128 && d->wfmt != MOE_TAIL_W_MXFP4 && d->wfmt != MOE_TAIL_W_MXFP4_PACKED)
+  if (d->wfmt != MOE_TAIL_W_FP8_BLOCK128 && d->wfmt != MOE_TAIL_W_MXFP4 && d->wfmt != MOE_TAIL_W_MXFP4_PACKED &&
+      d->wfmt != MOE_TAIL_W_NVFP4)
     return MOE_TAIL_ERR_UNSUPPORTED;
   if (d->hidden % 256 || d->latent % 256 || d->latent > 256 * kNormMaxCols) return MOE_TAIL_ERR_UNSUPPORTED;
   if (d->inter % 128 || d->shared_inter % 128 || d->inter > 128 * kMaxKBlocks) return MOE_TAIL_ERR_UNSUPPORTED;
@@ -112,6 +113,7 @@ bool fuse_shared_reduce(const Plans& p, int32_t Mr, int32_t Ms) { return Mr > 0 
 // kStages - 1 steps ahead (K >= 384 for L1 and L2; MXFP4, whose small tiles
 // take two 128-wide K blocks per step: K a multiple of 256, at least 512).
 bool tiled_ok(const moe_tail_dims& d, int32_t Mr) {
+  if (d.wfmt == MOE_TAIL_W_NVFP4) return false;  // NVFP4 runs on the row-streaming kernels
   const bool fp4_ok = d.wfmt == MOE_TAIL_W_FP8_BLOCK128 ||
                       (d.latent % 256 == 0 && d.inter % 256 == 0 && d.latent >= 512 && d.inter >= 512);
   return d.num_experts <= kTileMaxE && static_cast<size_t>(Mr) * d.latent < (1ull << 31) && d.latent >= 384 &&
@@ -188,6 +190,8 @@ int check_weights(const moe_tail_dims& d, const moe_tail_weights* w, bool need_r
     if (!ptr_ok(w->w1, 1) || !ptr_ok(w->w1_scale, 1) || !ptr_ok(w->w2, 1) || !ptr_ok(w->w2_scale, 1))
       return MOE_TAIL_ERR_INVALID;
     if (!ptr_ok(w->rms_gamma, L * 2)) return MOE_TAIL_ERR_INVALID;
+    if (d.wfmt == MOE_TAIL_W_NVFP4 && (!ptr_ok(w->w1_tensor_scale, E * 4) || !ptr_ok(w->w2_tensor_scale, E * 4)))
+      return MOE_TAIL_ERR_INVALID;
   }
   if (need_shared && (!ptr_ok(w->ws1, 2 * Is * H * 2) || !ptr_ok(w->ws2, H * Is * 2))) return MOE_TAIL_ERR_INVALID;
   if (need_up && !ptr_ok(w->w_up, H * L * 2)) return MOE_TAIL_ERR_INVALID;
@@ -463,6 +467,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   const bool tiled = tiled_ok(d, Mr);
   constexpr int kSmallOnlyMr = 256;
   const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
+  const bool nvfp4 = d.wfmt == MOE_TAIL_W_NVFP4;
   // 128- and 256-row tiles for FP8 only.  A 256-row MXFP4 tile fits one
   // 128-wide K block per step (half-line weight loads) and a 128-row one a
   // single stage in flight; MXFP4 experts with 33 rows or more take 64-row
@@ -489,14 +494,10 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   mark(1);
   if (Mr > 0) {
     if (!tiled) {
-      if (fp8)
-        hipLaunchKernelGGL(k_routed_l1<FMT_FP8>, dim3(max_tiles, I / 128), dim3(256), 0, st, xq, sx,
-                           routing->sorted_pair, routing->expert_offsets, w->w1, w->w1_scale, hq, sh, E, k, L, I,
-                           0x7fffffff);
-      else
-        hipLaunchKernelGGL(k_routed_l1<FMT_MXFP4>, dim3(max_tiles, I / 128), dim3(256), 0, st, xq, sx,
-                           routing->sorted_pair, routing->expert_offsets, w->w1, w->w1_scale, hq, sh, E, k, L, I,
-                           0x7fffffff);
+      auto kl1 = fp8 ? k_routed_l1<FMT_FP8> : nvfp4 ? k_routed_l1<FMT_NVFP4> : k_routed_l1<FMT_MXFP4>;
+      hipLaunchKernelGGL(kl1, dim3(max_tiles, I / 128), dim3(256), 0, st, xq, sx, routing->sorted_pair,
+                         routing->expert_offsets, w->w1, w->w1_scale, w->w1_tensor_scale, hq, sh, E, k, L, I,
+                         0x7fffffff);
     } else {
       TileArgs a1 = ta;
       a1.a = xq;
@@ -529,12 +530,9 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   mark(2);
   if (Mr > 0) {
     if (!tiled) {
-      if (fp8)
-        hipLaunchKernelGGL(k_routed_l2<FMT_FP8>, dim3(max_tiles, L / 128), dim3(256), 0, st, hq, sh,
-                           routing->expert_offsets, w->w2, w->w2_scale, y, E, L, I, 0x7fffffff);
-      else
-        hipLaunchKernelGGL(k_routed_l2<FMT_MXFP4>, dim3(max_tiles, L / 128), dim3(256), 0, st, hq, sh,
-                           routing->expert_offsets, w->w2, w->w2_scale, y, E, L, I, 0x7fffffff);
+      auto kl2 = fp8 ? k_routed_l2<FMT_FP8> : nvfp4 ? k_routed_l2<FMT_NVFP4> : k_routed_l2<FMT_MXFP4>;
+      hipLaunchKernelGGL(kl2, dim3(max_tiles, L / 128), dim3(256), 0, st, hq, sh, routing->expert_offsets, w->w2,
+                         w->w2_scale, w->w2_tensor_scale, y, E, L, I, 0x7fffffff);
     } else {
       TileArgs a2 = ta;
       a2.a = hq;

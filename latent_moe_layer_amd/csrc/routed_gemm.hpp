@@ -23,6 +23,9 @@
 // promoted with (activation scale of the row) x (weight scale of the 128x128
 // block) and accumulated in FP32.  For MXFP4 the weight scale rides in the
 // MFMA's e8m0 operand and only the activation scale is applied afterwards.
+// NVFP4 (an e4m3 scale per 16 weights, which no scaled MFMA takes) runs on
+// the FP16 matrix cores with the weights dequantized exactly in registers;
+// the matrix's fp32 scale joins the activation scale in the promotion.
 #pragma once
 
 #include "common.hpp"
@@ -32,7 +35,7 @@ namespace moe_tail {
 constexpr int kBM = 32;           // rows per routed tile (two 16-row MFMA tiles)
 constexpr int kMaxKBlocks = 64;   // K <= 8192 for the LDS copy of activation scales
 
-enum { FMT_FP8 = 0, FMT_MXFP4 = 1 };
+enum { FMT_FP8 = 0, FMT_MXFP4 = 1, FMT_NVFP4 = 2 };
 
 // Finds the tile `mt` among the row tiles of the experts with fewer than
 // `skip_at` rows (the others go to the tiled kernel).  Run by one wave;
@@ -94,13 +97,25 @@ __device__ __forceinline__ i32x8 load_fp8_frag(const uint8_t* __restrict__ row_p
 // Weight fragment of one 128-wide K step of row `row` of a [N, K] matrix.
 // FP8: the two-half layout above.  MXFP4: the 4-bit operand takes 32
 // consecutive K elements per lane group, K [32 g, 32 g + 32) = 16 packed bytes,
-// and the lane's e8m0 scale covers exactly those 32 elements.
+// and the lane's e8m0 scale covers exactly those 32 elements.  NVFP4 (FP16
+// matrix cores, mfma_fp8_nvfp4): the K of the FP8 layout, K [16 g, +16) and
+// [64 + 16 g, +16) = packed bytes [8 g, +8) and [32 + 8 g, +8) of the step,
+// with the e4m3 scales of those two 16-element blocks.
 template <int kFmt>
 __device__ __forceinline__ void load_weight_frag(const uint8_t* __restrict__ w, const void* __restrict__ ws,
                                                  size_t row, int K, int k0, i32x8& frag, int& scale) {
   if (kFmt == FMT_FP8) {
     frag = load_fp8_frag(w + row * K, k0);
     scale = 127;
+  } else if (kFmt == FMT_NVFP4) {
+    const int g = (threadIdx.x & 63) >> 4;
+    const uint8_t* rp = w + row * (K / 2) + k0 / 2;
+    const uint2 lo = *reinterpret_cast<const uint2*>(rp + 8 * g);
+    const uint2 hi = *reinterpret_cast<const uint2*>(rp + 32 + 8 * g);
+    frag = i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(hi.x), static_cast<int>(hi.y),
+                 0, 0, 0, 0};
+    const uint8_t* sp = static_cast<const uint8_t*>(ws) + row * (K / 16) + k0 / 16;
+    scale = static_cast<int>(sp[g]) | (static_cast<int>(sp[4 + g]) << 8);
   } else {
     const int g = (threadIdx.x & 63) >> 4;
     const uint4 v = *reinterpret_cast<const uint4*>(w + row * (K / 2) + (k0 + 32 * g) / 2);
@@ -117,6 +132,7 @@ __device__ __forceinline__ i32x8 load_act_frag(const uint8_t* __restrict__ row_p
 template <int kFmt>
 __device__ __forceinline__ f32x4 mfma_lowp(const i32x8& a, const i32x8& b, int scale_b) {
   if (kFmt == FMT_FP8) return mfma_fp8(a, b);
+  if (kFmt == FMT_NVFP4) return mfma_fp8_nvfp4(a, b, scale_b);
   return mfma_fp8_fp4(a, b, scale_b);
 }
 
@@ -129,8 +145,8 @@ __global__ __launch_bounds__(256, 2) void k_routed_l1(const uint8_t* __restrict_
                                                    const int32_t* __restrict__ sorted_pair,
                                                    const int32_t* __restrict__ expert_offsets,
                                                    const uint8_t* __restrict__ w1, const void* __restrict__ w1s,
-                                                   uint8_t* __restrict__ hq, float* __restrict__ sh, int E, int k,
-                                                   int L, int I, int skip_at) {
+                                                   const float* __restrict__ w1t, uint8_t* __restrict__ hq,
+                                                   float* __restrict__ sh, int E, int k, int L, int I, int skip_at) {
   __shared__ int s_tile[3];
   __shared__ int s_tok[kBM];
   __shared__ float s_sx[kBM * kMaxKBlocks];
@@ -203,6 +219,8 @@ __global__ __launch_bounds__(256, 2) void k_routed_l1(const uint8_t* __restrict_
     if (kFmt == FMT_FP8) {
       swg = S1[static_cast<size_t>(nb) * nkb + kb];
       swu = S1[static_cast<size_t>(I / 128 + nb) * nkb + kb];
+    } else if (kFmt == FMT_NVFP4) {
+      swg = swu = w1t[e];  // the matrix's fp32 scale
     }
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms) {
@@ -271,7 +289,8 @@ template <int kFmt>
 __global__ __launch_bounds__(256, 2) void k_routed_l2(const uint8_t* __restrict__ hq, const float* __restrict__ sh,
                                                    const int32_t* __restrict__ expert_offsets,
                                                    const uint8_t* __restrict__ w2, const void* __restrict__ w2s,
-                                                   float* __restrict__ y, int E, int L, int I, int skip_at) {
+                                                   const float* __restrict__ w2t, float* __restrict__ y, int E, int L,
+                                                   int I, int skip_at) {
   __shared__ int s_tile[3];
   __shared__ float s_sh[kBM * kMaxKBlocks];
 
@@ -326,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void k_routed_l2(const uint8_t* __restrict_
     for (int ms = 0; ms < 2; ++ms) fa[set][ms] = load_act_frag(arow[ms], kb * 128, avalid[ms]);
   };
   auto mma_step = [&](int set, int kb) {
-    const float sw = (kFmt == FMT_FP8) ? S2[kb] : 1.0f;
+    const float sw = (kFmt == FMT_FP8) ? S2[kb] : (kFmt == FMT_NVFP4) ? w2t[e] : 1.0f;
 #pragma unroll
     for (int ms = 0; ms < 2; ++ms) {
       float sa[4];

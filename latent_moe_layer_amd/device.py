@@ -32,7 +32,7 @@ class DeviceTail:
         d = self.device
         self.t = {name: _dev(getattr(inp, name), d) for name in
                   ("x_lat", "x_hid", "gate", "gate_bias", "w1", "w1_scale", "w2", "w2_scale", "gamma", "w_up",
-                   "ws1", "ws2")}
+                   "ws1", "ws2", "w1_tscale", "w2_tscale")}
         t = self.t
         if pack_scales:
             if wl.wfmt != synth.WFMT_MXFP4:
@@ -44,7 +44,9 @@ class DeviceTail:
             self.dims.wfmt = B.MOE_TAIL_W_MXFP4_PACKED
         self.weights = B.make_weights(gate=t["gate"], gate_bias=t["gate_bias"], w1=t["w1"], w1_scale=t["w1_scale"],
                                       w2=t["w2"], w2_scale=t["w2_scale"], rms_gamma=t["gamma"], w_up=t["w_up"],
-                                      ws1=t["ws1"], ws2=t["ws2"])
+                                      ws1=t["ws1"], ws2=t["ws2"],
+                                      w1_tensor_scale=t["w1_tscale"] if wl.wfmt == synth.WFMT_NVFP4 else None,
+                                      w2_tensor_scale=t["w2_tscale"] if wl.wfmt == synth.WFMT_NVFP4 else None)
         self.alloc(self.Mr, self.Ms)
 
     def alloc(self, Mr: int, Ms: int) -> None:

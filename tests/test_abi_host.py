@@ -78,7 +78,7 @@ def test_invalid_args_size_zero(kw, Mr, Ms):
 
 
 @pytest.mark.parametrize("kw", [dict(hidden=7000), dict(latent=3600), dict(inter=2000), dict(shared_inter=100),
-                                dict(num_experts=1025), dict(top_k=17, num_experts=64), dict(wfmt=3),
+                                dict(num_experts=1025), dict(top_k=17, num_experts=64), dict(wfmt=4),
                                 dict(latent=16384)])
 def test_unsupported_dims(kw):
     offs = (C.c_size_t * B.MOE_TAIL_WS_NUM)()
@@ -153,6 +153,23 @@ def test_forward_rejections():
     assert _fwd(d, wn, X, 16, X, 32, r, OUT, SOUT, WS, need) == B.MOE_TAIL_ERR_INVALID
     assert B.lib().moe_tail_forward_profiled(C.byref(d), C.byref(w), X, 16, X, 32, C.byref(r), OUT, SOUT, WS, need,
                                              None, None) == B.MOE_TAIL_ERR_INVALID
+
+
+def test_forward_nvfp4_needs_its_matrix_scales():
+    d, r = dims(wfmt=B.MOE_TAIL_W_NVFP4), _fake_routing()
+    need = B.moe_tail_workspace_bytes(d, 16, 16)
+    w = _fake_weights()
+    assert _fwd(d, w, X, 16, X, 16, r, OUT, None, WS, need) == B.MOE_TAIL_ERR_INVALID  # no matrix scales
+    w.w1_tensor_scale, w.w2_tensor_scale = 1 << 47, (1 << 47) + 4096
+    assert _fwd(d, w, X, 16, X, 16, r, OUT, None, WS, need - 1) == B.MOE_TAIL_ERR_WORKSPACE
+    w.w2_tensor_scale += 4  # misaligned
+    assert _fwd(d, w, X, 16, X, 16, r, OUT, None, WS, need) == B.MOE_TAIL_ERR_INVALID
+    # the single launch and the packed-scale entry points decline NVFP4
+    w.w2_tensor_scale -= 4
+    f = B.lib().moe_tail_forward_fused
+    assert f(C.byref(d), C.byref(w), X, 16, X, 16, C.byref(r), None, OUT, None, WS, need, None) == \
+        B.MOE_TAIL_ERR_UNSUPPORTED
+    assert B.lib().moe_tail_pack_mxfp4_scales(C.byref(d), X, None, OUT, None, None) == B.MOE_TAIL_ERR_INVALID
 
 
 def test_forward_add3_rejections():

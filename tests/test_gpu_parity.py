@@ -174,14 +174,14 @@ def test_forward_tiny_full():
     check_forward(dev, inp)
 
 
-@pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4])
+@pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4, synth.WFMT_NVFP4])
 def test_forward_ragged(wfmt):
     # several tiles and a ragged tail in every dimension the grid splits.  I is
     # the smallest workload's 512: one legitimate h-code flip moves the output
     # by about 1/sqrt(I) of its rms, so much narrower experts would need a
     # looser bar than the workloads' 2e-2.
     wl = synth.Workload("ragged", Mr=37, Ms=53, E=8, k=3, I=512, Is=384, wfmt=wfmt, seed=21,
-                        zipf_s=1.2 if wfmt else 0.0)
+                        zipf_s=1.2 if wfmt == synth.WFMT_MXFP4 else 0.0)
     inp = synth.make_inputs(wl)
     dev = run(inp)
     check_forward(dev, inp)
@@ -197,14 +197,14 @@ def test_forward_mxfp4_width_not_a_multiple_of_256():
     check_forward(dev, inp)
 
 
-@pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4])
+@pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4, synth.WFMT_NVFP4])
 def test_forward_tiled_path(wfmt):
     # Mr * k >= 2048 turns on the LDS-tiled routed kernel for experts with >= 128
     # rows (here most experts, ~150 rows each: full and partial 128-row tiles),
     # the others stay on the row-streaming kernel; M > 128 takes the tiled
     # dense kernel for the shared expert and the up-projection.
-    wl = synth.Workload("tiled", Mr=300, Ms=333, E=18 if wfmt == 0 else 16, k=8, I=512, Is=512, wfmt=wfmt, seed=30,
-                        zipf_s=0.3 if wfmt else 0.0)
+    wl = synth.Workload("tiled", Mr=300, Ms=333, E=16 if wfmt == synth.WFMT_MXFP4 else 18, k=8, I=512, Is=512, wfmt=wfmt, seed=30,
+                        zipf_s=0.3 if wfmt == synth.WFMT_MXFP4 else 0.0)
     inp = synth.make_inputs(wl)
     dev = run(inp)
     loads = np.diff(to_np(dev.offsets))
@@ -329,6 +329,17 @@ def test_forward_heavy_expert_many_row_tiles():
     wl = synth.Workload("heavy", Mr=100, Ms=100, E=6, k=2, I=512, Is=128, wfmt=0, seed=22, zero_router=True)
     inp = synth.make_inputs(wl)
     dev = run(inp)
+    check_forward(dev, inp)
+
+
+def test_forward_nvfp4_skewed_and_narrow():
+    # NVFP4 weights on skewed loads (a few heavy experts, many empty ones) at
+    # the served widths, with more shared than routed tokens
+    wl = synth.Workload("nv", Mr=96, Ms=120, E=32, k=4, I=384, Is=256, wfmt=synth.WFMT_NVFP4, seed=91, zipf_s=1.2)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    loads = np.diff(to_np(dev.offsets))
+    assert np.any(loads == 0) and loads.max() > 32, loads
     check_forward(dev, inp)
 
 

@@ -43,7 +43,8 @@ def boundary_tokens(offsets, sorted_pair, k, n_min, seed):
     return np.union1d(toks, [0, Mr - 1]).astype(np.int32)
 
 
-@pytest.mark.parametrize("name,n_shared", [("tiny", 0), ("decode", 0), ("prefill", 0), ("mxfp4", 0), ("indep", 32)])
+@pytest.mark.parametrize("name,n_shared", [("tiny", 0), ("decode", 0), ("prefill", 0), ("mxfp4", 0), ("indep", 32),
+                                           ("nvfp4", 0)])
 def test_workload(name, n_shared):
     wl = synth.WORKLOADS[name]
     print(f"[{name}] generating inputs", flush=True)
