@@ -72,6 +72,10 @@ class HipEvents:
             assert self.rt.hipEventCreate(C.byref(h)) == 0
             self.ev.append(h.value)
 
+    def record(self, i: int, stream) -> None:
+        self.rt.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        assert self.rt.hipEventRecord(C.c_void_p(self.ev[i]), C.c_void_p(stream.cuda_stream)) == 0
+
     def elapsed_ms(self, a: int, b: int) -> float:
         ms = C.c_float()
         assert self.rt.hipEventSynchronize(C.c_void_p(self.ev[b])) == 0
@@ -202,20 +206,24 @@ def measure(name: str, args, torch, np, B, synth, DeviceTail, to_np, flush) -> d
         cold = [a[i].elapsed_time(b[i]) * 1e3 for i in range(K)]
 
     # launch groups of the schedule the plain call runs (eager, events on its stream)
+    # (the route, moe_tail_route's launches, from an event before it to the
+    # forward's first event)
     names = B.moe_tail_stage_names(dev.dims, dev.Mr, dev.Ms)
     nev = B.MOE_TAIL_NUM_STAGES + 1
-    hev = HipEvents(K * nev)
+    per_step = nev + 1
+    hev = HipEvents(K * per_step)
     groups = None
     if not args.fused:
         for i in range(K):
+            hev.record(i * per_step, stream)
             dev.route(stream)
-            dev.forward_timed(stream, hev.ev[i * nev:(i + 1) * nev])
+            dev.forward_timed(stream, hev.ev[i * per_step + 1:(i + 1) * per_step])
         torch.cuda.synchronize()
-        gsum = np.zeros(len(names))
+        gsum = np.zeros(len(names) + 1)
         for i in range(K):
-            for g in range(len(names)):
-                gsum[g] += hev.elapsed_ms(i * nev + g, i * nev + g + 1)
-        groups = {n: float(v * 1e3 / K) for n, v in zip(names, gsum)}
+            for g in range(len(names) + 1):
+                gsum[g] += hev.elapsed_ms(i * per_step + g, i * per_step + g + 1)
+        groups = {n: float(v * 1e3 / K) for n, v in zip(["route"] + names, gsum)}
 
     offsets = to_np(dev.offsets)
     loads = np.diff(offsets)
@@ -276,6 +284,28 @@ def measure(name: str, args, torch, np, B, synth, DeviceTail, to_np, flush) -> d
     return leg
 
 
+def oracle_timing(inp, leg, np) -> dict:
+    """The CPU oracle on this workload's inputs: route and permutation of every
+    routed token, the forward of at most 128 of the Ms tokens (evenly spread
+    over routed and shared-only ones), the forward's time scaled to all Ms."""
+    from oracle import oracle as orc
+    wl = inp.wl
+    sample = min(wl.Ms, 128)
+    sel = np.linspace(0, wl.Ms - 1, sample).astype(np.int32) if sample < wl.Ms else None
+    t1 = time.time()
+    ids, w = orc.route(inp.x_lat, inp.gate, inp.gate_bias, wl.k)
+    orc.permute(ids, wl.E)
+    t2 = time.time()
+    orc.forward(inp, ids, w, sel=sel)
+    cpu_s = (t2 - t1) + (time.time() - t2) * wl.Ms / sample
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": leg["algorithmic_bytes"] / cpu_s / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "us_per_layer": cpu_s * 1e6, "cpu_model": cpu_model(),
+            "sample": (f"route + permute + forward of all {wl.Ms} tokens" if sample == wl.Ms else
+                       f"route + permute of all {wl.Mr} routed tokens, forward of {sample} of the {wl.Ms} tokens "
+                       f"(evenly spread), scaled to {wl.Ms}")}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,6 +316,7 @@ def main() -> int:
     ap.add_argument("--legs", default="prefill,tiny",
                     help="other workloads timed on the same line (comma list, 'none', or 'all')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-all", action="store_true", help="also time the CPU oracle on every leg's tokens")
     ap.add_argument("--no-cold", action="store_true", help="skip the cache-cold replays")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--add3", action="store_true",
@@ -331,30 +362,19 @@ def main() -> int:
         (["tiny", "decode", "prefill", "mxfp4", "indep", "nvfp4"] if args.legs == "all" else args.legs.split(","))
     inp, dev = head.pop("_inp"), head.pop("_dev")
 
-    cpu = None
     wl = synth.WORKLOADS[args.workload]
-    if not args.no_cpu_baseline:
-        from oracle import oracle as orc
-        sample = min(wl.Mr, 128)
-        sel = np.linspace(0, wl.Mr - 1, sample).astype(np.int32) if sample < wl.Mr else None
-        t1 = time.time()
-        ids, w = orc.route(inp.x_lat, inp.gate, inp.gate_bias, wl.k)
-        orc.permute(ids, wl.E)
-        orc.forward(inp, ids, w, sel=sel)
-        cpu_s = (time.time() - t1) * wl.Mr / sample
-        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        cpu = {"value": head["algorithmic_bytes"] / cpu_s / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-               "us_per_layer": cpu_s * 1e6, "cpu_model": cpu_model(),
-               "sample": (f"route + permute + forward of all {wl.Mr} tokens" if sample == wl.Mr else
-                          f"route of all tokens + forward of {sample} of {wl.Mr} tokens, scaled to {wl.Mr}")}
+    cpu = None if args.no_cpu_baseline else oracle_timing(inp, head, np)
     del inp, dev
     torch.cuda.empty_cache()
 
     for n in names:
         if n and n != args.workload:
             leg = measure(n, args, torch, np, B, synth, DeviceTail, to_np, flush)
-            leg.pop("_inp")
+            linp = leg.pop("_inp")
             leg.pop("_dev")
+            if args.cpu_all:
+                leg["cpu_baseline"] = oracle_timing(linp, leg, np)
+            del linp
             legs[n] = leg
             torch.cuda.empty_cache()
 
