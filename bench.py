@@ -51,7 +51,7 @@ MEASURED_L1_TRAFFIC = {
     "decode": 945.7e6,    # k_tile<0, 0, 0, 32>: 943.5 MB fetched + 2.2 MB written (profiles/decode_tail_traffic.md)
     "prefill": 1589.5e6,  # k_tile<0, 0, 0, 256> 1129.4 MB + k_tile<0, 0, 0, 128> 460.0 MB (profiles/prefill_tail_traffic.md)
 }
-FORMATS = {0: "FP8 128x128", 1: "MXFP4 (e8m0 scales packed)", 3: "NVFP4 (e4m3 scale per 16, fp32 per matrix)"}
+FORMATS = {0: "FP8 128x128", 1: "MXFP4 (e8m0 scales packed)", 3: "NVFP4 (e4m3 scale per 16 packed, fp32 per matrix)"}
 DTYPES = {0: "fp8e4m3+bf16", 1: "mxfp4+fp8e4m3+bf16", 3: "nvfp4+fp8e4m3+fp16+bf16"}
 # workloads whose routed GEMMs are bound by the matrix cores (the others stream weights)
 MFMA_BOUND = {"prefill"}
@@ -148,8 +148,8 @@ def measure(name: str, args, torch, np, B, synth, DeviceTail, to_np, flush) -> d
     t0 = time.time()
     inp = synth.make_inputs(wl)
     gen_s = time.time() - t0
-    # MXFP4 scales go in the tiled kernels' order once, as a server would at load
-    dev = DeviceTail(inp, "cuda:0", pack_scales=wl.wfmt == synth.WFMT_MXFP4)
+    # FP4 block scales go in the tiled kernels' order once, as a server would at load
+    dev = DeviceTail(inp, "cuda:0", pack_scales=wl.wfmt in (synth.WFMT_MXFP4, synth.WFMT_NVFP4))
     if args.add3:
         dev.set_residual(synth.make_residual(wl))
     stream = torch.cuda.Stream()
@@ -249,9 +249,9 @@ def measure(name: str, args, torch, np, B, synth, DeviceTail, to_np, flush) -> d
         l1_f = 2 * wl.Mr * wl.k * 2 * wl.I * wl.L
         gbs = l1_b / (l1_us * 1e-6) / 1e9
         tfs = l1_f / (l1_us * 1e-6) / 1e12
-        fmt = "TF_FP8" if wl.wfmt == 0 else "TF_FP4"
+        fmt = {0: "TF_FP8", 1: "TF_FP4", 3: "TF_NV4"}[wl.wfmt]
         if wl.wfmt == 3:
-            kern = "k_routed_l1<FMT_NVFP4>"
+            kern = f"k_tile<TK_L1, {fmt}, 0, 32>"
         elif wl.Mr <= 256 and wl.Mr * wl.k <= 32 * wl.E:
             kern = f"k_tile<TK_L1, {fmt}, 0, 32>"
         else:

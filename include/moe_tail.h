@@ -53,7 +53,8 @@ typedef enum {
   MOE_TAIL_W_FP8_BLOCK128 = 0,   /* e4m3 codes + fp32 scale per 128 (N) x 128 (K) block */
   MOE_TAIL_W_MXFP4 = 1,          /* e2m1 pairs (even K in the low nibble) + e8m0 scale per 32 along K */
   MOE_TAIL_W_MXFP4_PACKED = 2,   /* MXFP4 with the e8m0 scales in the tile order of moe_tail_pack_mxfp4_scales */
-  MOE_TAIL_W_NVFP4 = 3           /* e2m1 pairs + e4m3 scale per 16 along K + fp32 scale per expert matrix */
+  MOE_TAIL_W_NVFP4 = 3,          /* e2m1 pairs + e4m3 scale per 16 along K + fp32 scale per expert matrix */
+  MOE_TAIL_W_NVFP4_PACKED = 4    /* NVFP4 with the e4m3 scales in the tile order of moe_tail_pack_nvfp4_scales */
 } moe_tail_wfmt;
 
 /* Sizes of one tail.  hidden (H) and latent (L) are the shared and routed
@@ -295,6 +296,35 @@ int moe_tail_quant_fp8_1x128(const void *x, int32_t x_is_bf16, int32_t rows, int
  * multiples of 256, at least 512, num_experts <= 512), else it returns
  * MOE_TAIL_ERR_UNSUPPORTED. */
 int moe_tail_pack_mxfp4_scales(const moe_tail_dims *dims, const uint8_t *w1_scale, const uint8_t *w2_scale,
+                               uint8_t *w1_scale_packed, uint8_t *w2_scale_packed, void *stream);
+
+/* NVFP4 weight scales rearranged for the tiled kernels (same values, same
+ * byte count per matrix), to be done once when the weights are loaded.  The
+ * NVFP4 recipe the pages serve (tokenspeed recipe "Kimi-K3 DEP16 with
+ * sharded shared experts", Allocation and launch) fixes the format (an e4m3
+ * scale per 16 weights along K), not the order of the scales in memory; in
+ * this order the scales of one tile's 256 weight rows for one 256-wide K
+ * step are one contiguous 4 KB run (whole-line loads instead of 16 bytes
+ * from each of 256 rows), and the four scales one lane of the FP16 matrix
+ * cores needs for a K step are one 4-byte word.
+ *   For each expert e and each weight matrix W [N, K] with natural scales
+ *   S[n][K/16] (w1: N = 2I, K = L; w2: N = L, K = I), the packed scales are
+ *   P[e][t][s][j][g][h][c] = S[e][n(t, j)][16 s + 8 h + 4 c + g] with
+ *   t < N/256 (tile), s < K/256 (K step), j < 256 (tile row), g < 4 (lane
+ *   group), h < 2 (128-wide K block), c < 2 (the first or second 64 of the
+ *   block); tile row j of w1 is gate row 128 t + j for j < 128 and up row
+ *   I + 128 t + (j - 128) otherwise, of w2 row 256 t + j.
+ * dims->wfmt is MOE_TAIL_W_NVFP4 or _PACKED; L and I must be multiples of
+ * 256 (else MOE_TAIL_ERR_UNSUPPORTED).  w1_scale / w2_scale are the natural
+ * [E, 2I, L/16] / [E, L, I/16] e4m3 arrays, the packed outputs the same sizes
+ * (device, caller-owned, not overlapping the inputs).  Either pair may be
+ * NULL to skip that matrix.  A forward with dims->wfmt =
+ * MOE_TAIL_W_NVFP4_PACKED takes the packed arrays in weights->w1_scale /
+ * w2_scale (and the matrix scales as for MOE_TAIL_W_NVFP4) and gives bit for
+ * bit the results of MOE_TAIL_W_NVFP4 with the natural ones; it needs the
+ * shapes the tiled kernels cover (L and I multiples of 256, at least 512,
+ * num_experts <= 512), else it returns MOE_TAIL_ERR_UNSUPPORTED. */
+int moe_tail_pack_nvfp4_scales(const moe_tail_dims *dims, const uint8_t *w1_scale, const uint8_t *w2_scale,
                                uint8_t *w1_scale_packed, uint8_t *w2_scale_packed, void *stream);
 
 /* Static description of a status code. */

@@ -23,6 +23,7 @@ MOE_TAIL_W_FP8_BLOCK128 = 0
 MOE_TAIL_W_MXFP4 = 1
 MOE_TAIL_W_MXFP4_PACKED = 2
 MOE_TAIL_W_NVFP4 = 3
+MOE_TAIL_W_NVFP4_PACKED = 4
 
 MOE_TAIL_WS_XQ, MOE_TAIL_WS_SX, MOE_TAIL_WS_HQ, MOE_TAIL_WS_SH, MOE_TAIL_WS_Y, MOE_TAIL_WS_RN, \
     MOE_TAIL_WS_HS, MOE_TAIL_WS_S, MOE_TAIL_WS_STATUS = range(9)
@@ -33,7 +34,7 @@ MOE_TAIL_NUM_STAGES = 7
 EXPORTED = ("moe_tail_workspace_bytes", "moe_tail_workspace_layout", "moe_tail_route", "moe_tail_forward",
             "moe_tail_forward_add3", "moe_tail_forward_noalloc", "moe_tail_forward_fused", "moe_tail_forward_fused_bounded",
             "moe_tail_forward_profiled", "moe_tail_forward_timed", "moe_tail_stage_name", "moe_tail_quant_fp8_1x128",
-            "moe_tail_pack_mxfp4_scales", "moe_tail_strerror")
+            "moe_tail_pack_mxfp4_scales", "moe_tail_pack_nvfp4_scales", "moe_tail_strerror")
 
 
 class MoeTailError(RuntimeError):
@@ -97,6 +98,9 @@ def lib() -> C.CDLL:
                                                C.c_void_p, C.c_void_p]
         L.moe_tail_pack_mxfp4_scales.restype = C.c_int
         L.moe_tail_pack_mxfp4_scales.argtypes = [C.POINTER(Dims), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                                 C.c_void_p]
+        L.moe_tail_pack_nvfp4_scales.restype = C.c_int
+        L.moe_tail_pack_nvfp4_scales.argtypes = [C.POINTER(Dims), C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                                  C.c_void_p]
         L.moe_tail_strerror.restype = C.c_char_p
         L.moe_tail_strerror.argtypes = [C.c_int]
@@ -224,6 +228,11 @@ def moe_tail_stage_names(dims: Dims, Mr: int, Ms: int) -> list[str]:
         if n is None:
             return names
         names.append(n.decode())
+
+
+def moe_tail_pack_nvfp4_scales(dims: Dims, w1_scale, w2_scale, w1_scale_packed, w2_scale_packed, stream=None) -> None:
+    _check(lib().moe_tail_pack_nvfp4_scales(C.byref(dims), ptr(w1_scale), ptr(w2_scale), ptr(w1_scale_packed),
+                                            ptr(w2_scale_packed), stream_handle(stream)), "moe_tail_pack_nvfp4_scales")
 
 
 def moe_tail_pack_mxfp4_scales(dims: Dims, w1_scale, w2_scale, w1_scale_packed, w2_scale_packed, stream=None) -> None:

@@ -82,21 +82,20 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, con
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-// One 128-wide K block of an FP8 (A) x NVFP4 (B) product on the FP16 matrix
-// cores (16x16x32, FP32 accumulation), without the activation and matrix
-// scales.  The FP8 fragment `a` is the 8-bit operand layout (lane group g:
-// K [16 g, 16 g + 16) in registers 0-3, K [64 + 16 g, +16) in 4-7); `b`
-// holds the same K of the lane's weight row as e2m1 pairs (registers 0-1:
-// K [16 g, +16), 2-3: K [64 + 16 g, +16), the even K in the low nibble) and
-// `scales` the e4m3 scales of those two 16-element blocks (bytes 0 and 1).
-// Every conversion is exact: e4m3 and e2m1 are FP16 values, and an e2m1 times
-// an e4m3 has at most five significant bits within the FP16 range.  Chunk m
-// (eight K elements) of the block is the m-th MFMA for both operands.
-__device__ __forceinline__ f32x4 mfma_fp8_nvfp4(const i32x8& a, const i32x8& b, int scales) {
-  const f16x2 s_lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<unsigned>(scales) & 0xffu, 1.0f, false);
-  const f16x2 s_hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((static_cast<unsigned>(scales) >> 8) & 0xffu, 1.0f, false);
-  const f16x2 slo = {s_lo.x, s_lo.x}, shi = {s_hi.x, s_hi.x};
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+// FP8 x NVFP4 on the FP16 matrix cores (16x16x32, FP32 accumulation).  The
+// FP8 fragment `a` is the 8-bit operand layout (lane group g: K [16 g,
+// 16 g + 16) in registers 0-3, K [64 + 16 g, +16) in 4-7); the weight
+// fragment `b` holds the same K of the lane's weight row as e2m1 pairs
+// (registers 0-1: K [16 g, +16), 2-3: K [64 + 16 g, +16), the even K in the
+// low nibble) and `scales` the e4m3 scales of those two 16-element blocks
+// (bytes 0 and 1).  Every conversion is exact: e4m3 and e2m1 values are FP16
+// values, and an e2m1 times an e4m3 has at most six significant bits, within
+// the FP16 range (2^-10 .. 2688).  Chunk m (eight K elements, registers 2m
+// and 2m + 1 of `a`, register m of `b`) of the block is the m-th MFMA for
+// both operands.
+
+// the four FP16 chunks of an FP8 fragment
+__device__ __forceinline__ void fp8_frag_f16(const i32x8& a, f16x8 x[4]) {
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const unsigned a0 = static_cast<unsigned>(a[2 * m]), a1 = static_cast<unsigned>(a[2 * m + 1]);
@@ -104,17 +103,44 @@ __device__ __forceinline__ f32x4 mfma_fp8_nvfp4(const i32x8& a, const i32x8& b, 
     const f16x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a0, 1.0f, true);
     const f16x2 x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a1, 1.0f, false);
     const f16x2 x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(a1, 1.0f, true);
-    const unsigned w = static_cast<unsigned>(b[m]);
-    const f16x2 s = (m < 2) ? slo : shi;
-    const f16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
-    const f16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
-    const f16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
-    const f16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
-    const f16x8 av = {x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
-    const f16x8 bv = {w0.x, w0.y, w1.x, w1.y, w2.x, w2.y, w3.x, w3.y};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+    x[m] = f16x8{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
   }
+}
+
+// the four FP16 chunks of an NVFP4 fragment: e2m1 times its e4m3 block scale
+__device__ __forceinline__ void nvfp4_frag_f16(const i32x8& b, int scales, f16x8 w[4]) {
+  const f16x2 s_lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<unsigned>(scales) & 0xffu, 1.0f, false);
+  const f16x2 s_hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((static_cast<unsigned>(scales) >> 8) & 0xffu, 1.0f, false);
+  const f16x2 slo = {s_lo.x, s_lo.x}, shi = {s_hi.x, s_hi.x};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const unsigned v = static_cast<unsigned>(b[m]);
+    const f16x2 s = (m < 2) ? slo : shi;
+    const f16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0) * s;
+    const f16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1) * s;
+    const f16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2) * s;
+    const f16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3) * s;
+    w[m] = f16x8{w0.x, w0.y, w1.x, w1.y, w2.x, w2.y, w3.x, w3.y};
+  }
+}
+
+// one 128-wide K block from converted chunks, the activation block as A
+// (acc[i]: activation row 4 g + i, weight row l16) or, with the operands
+// swapped, the weight block as A (weight row 4 g + i, activation row l16);
+// no activation or matrix scale
+__device__ __forceinline__ f32x4 mfma_f16_block(const f16x8 a[4], const f16x8 b[4]) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[m], b[m], acc, 0, 0, 0);
   return acc;
+}
+
+// FP8 activations (A) x NVFP4 weights (B) for one 128-wide K block
+__device__ __forceinline__ f32x4 mfma_fp8_nvfp4(const i32x8& a, const i32x8& b, int scales) {
+  f16x8 x[4], w[4];
+  fp8_frag_f16(a, x);
+  nvfp4_frag_f16(b, scales, w);
+  return mfma_f16_block(x, w);
 }
 
 // ------------------------------------------------ direct global -> LDS loads

@@ -30,6 +30,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // required pointer: non-null and 16-byte aligned when the tensor is non-empty
 bool ptr_ok(const void* p, size_t bytes) { return bytes == 0 || (p != nullptr && aligned16(p)); }
 
+bool is_nvfp4(const moe_tail_dims& d) { return d.wfmt == MOE_TAIL_W_NVFP4 || d.wfmt == MOE_TAIL_W_NVFP4_PACKED; }
+
 int check_dims(const moe_tail_dims* d) {
   if (d == nullptr) return MOE_TAIL_ERR_INVALID;
   if (d->hidden <= 0 || d->latent <= 0 || d->inter <= 0 || d->shared_inter <= 0 || d->num_experts <= 0)
@@ -37,7 +39,7 @@ int check_dims(const moe_tail_dims* d) {
   if (d->top_k < 1 || d->top_k > d->num_experts) return MOE_TAIL_ERR_INVALID;
   if (!(d->rms_eps > 0.0f) || !std::isfinite(d->rms_eps)) return MOE_TAIL_ERR_INVALID;
   if (d->wfmt != MOE_TAIL_W_FP8_BLOCK128 && d->wfmt != MOE_TAIL_W_MXFP4 && d->wfmt != MOE_TAIL_W_MXFP4_PACKED &&
-      d->wfmt != MOE_TAIL_W_NVFP4)
+      d->wfmt != MOE_TAIL_W_NVFP4 && d->wfmt != MOE_TAIL_W_NVFP4_PACKED)
     return MOE_TAIL_ERR_UNSUPPORTED;
   if (d->hidden % 256 || d->latent % 256 || d->latent > 256 * kNormMaxCols) return MOE_TAIL_ERR_UNSUPPORTED;
   if (d->inter % 128 || d->shared_inter % 128 || d->inter > 128 * kMaxKBlocks) return MOE_TAIL_ERR_UNSUPPORTED;
@@ -110,10 +112,10 @@ bool fuse_shared_reduce(const Plans& p, int32_t Mr, int32_t Ms) { return Mr > 0 
 
 // Shapes of the routed tiled kernel: expert tables in LDS (E <= kTileMaxE),
 // gathered x rows addressed with 32-bit offsets, a tile's side data loaded
-// kStages - 1 steps ahead (K >= 384 for L1 and L2; MXFP4, whose small tiles
-// take two 128-wide K blocks per step: K a multiple of 256, at least 512).
+// kStages - 1 steps ahead (K >= 384 for L1 and L2; MXFP4 and NVFP4, whose
+// small tiles take two 128-wide K blocks per step: K a multiple of 256, at
+// least 512).
 bool tiled_ok(const moe_tail_dims& d, int32_t Mr) {
-  if (d.wfmt == MOE_TAIL_W_NVFP4) return false;  // NVFP4 runs on the row-streaming kernels
   const bool fp4_ok = d.wfmt == MOE_TAIL_W_FP8_BLOCK128 ||
                       (d.latent % 256 == 0 && d.inter % 256 == 0 && d.latent >= 512 && d.inter >= 512);
   return d.num_experts <= kTileMaxE && static_cast<size_t>(Mr) * d.latent < (1ull << 31) && d.latent >= 384 &&
@@ -190,7 +192,7 @@ int check_weights(const moe_tail_dims& d, const moe_tail_weights* w, bool need_r
     if (!ptr_ok(w->w1, 1) || !ptr_ok(w->w1_scale, 1) || !ptr_ok(w->w2, 1) || !ptr_ok(w->w2_scale, 1))
       return MOE_TAIL_ERR_INVALID;
     if (!ptr_ok(w->rms_gamma, L * 2)) return MOE_TAIL_ERR_INVALID;
-    if (d.wfmt == MOE_TAIL_W_NVFP4 && (!ptr_ok(w->w1_tensor_scale, E * 4) || !ptr_ok(w->w2_tensor_scale, E * 4)))
+    if (is_nvfp4(d) && (!ptr_ok(w->w1_tensor_scale, E * 4) || !ptr_ok(w->w2_tensor_scale, E * 4)))
       return MOE_TAIL_ERR_INVALID;
   }
   if (need_shared && (!ptr_ok(w->ws1, 2 * Is * H * 2) || !ptr_ok(w->ws2, H * Is * 2))) return MOE_TAIL_ERR_INVALID;
@@ -286,13 +288,14 @@ FusedArgs fused_args(const moe_tail_dims& d, const moe_tail_weights* w, int32_t 
   ta.big_rows = 0x7fffffff;
   ta.huge_rows = 0x7fffffff;
   ta.mid_rows = 0x7fffffff;
-  ta.e8_packed = d.wfmt == MOE_TAIL_W_MXFP4_PACKED;
+  ta.scales_packed = d.wfmt == MOE_TAIL_W_MXFP4_PACKED || d.wfmt == MOE_TAIL_W_NVFP4_PACKED;
   f.l1 = ta;
   f.l1.a = at<uint8_t>(ws, lay.xq);
   f.l1.a_scale = at<float>(ws, lay.sx);
   f.l1.M = Mr;
   f.l1.b = w->w1;
   f.l1.b_scale = w->w1_scale;
+  f.l1.b_tscale = w->w1_tensor_scale;
   f.l1.hq = at<uint8_t>(ws, lay.hq);
   f.l1.sh = at<float>(ws, lay.sh);
   f.l1.K = L;
@@ -305,6 +308,7 @@ FusedArgs fused_args(const moe_tail_dims& d, const moe_tail_weights* w, int32_t 
   f.l2.a_scale = at<float>(ws, lay.sh);
   f.l2.b = w->w2;
   f.l2.b_scale = w->w2_scale;
+  f.l2.b_tscale = w->w2_tensor_scale;
   f.l2.y = at<float>(ws, lay.y);
   f.l2.K = I;
   f.l2.N = L;
@@ -363,7 +367,8 @@ int check_forward(const moe_tail_dims* dims, const moe_tail_weights* w, const ui
   if ((Ms > Mr) != (shared_out != nullptr)) return MOE_TAIL_ERR_INVALID;
   if (shared_out != nullptr && !aligned16(shared_out)) return MOE_TAIL_ERR_INVALID;
   // packed MXFP4 scales are read by the tiled kernels only
-  if (d.wfmt == MOE_TAIL_W_MXFP4_PACKED && !tiled_ok(d, Mr)) return MOE_TAIL_ERR_UNSUPPORTED;
+  if ((d.wfmt == MOE_TAIL_W_MXFP4_PACKED || d.wfmt == MOE_TAIL_W_NVFP4_PACKED) && !tiled_ok(d, Mr))
+    return MOE_TAIL_ERR_UNSUPPORTED;
   *lay = layout_of(d, Mr, Ms);
   if (ws_bytes < lay->total) return MOE_TAIL_ERR_WORKSPACE;
   if (lay->total > 0 && !ptr_ok(ws, 1)) return MOE_TAIL_ERR_INVALID;
@@ -417,17 +422,19 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   // keeps one launch per stage so that each stage can be timed)
   if (ev_mode != EV_PER_STAGE && fused_ok(d, plans, Mr, Ms)) {
     const FusedArgs f = fused_args(d, w, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, lay, plans);
-    const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
+    const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128, nv4 = is_nvfp4(d);
     const long qblocks = static_cast<long>(Mr) * (L / 128);
     mark(0);
     hipLaunchKernelGGL(k_quant_clear, dim3(quant_grid(qblocks)), dim3(256), 0, st, x_lat, xq, sx, qblocks, f.sync,
                        kSyncWords);
     mark(1);
     if (fp8) launch_tile<TK_L1, TF_FP8, 0, 32>(f.l1, st);
+    else if (nv4) launch_tile<TK_L1, TF_NV4, 0, 32>(f.l1, st);
     else launch_tile<TK_L1, TF_FP4, 0, 32>(f.l1, st);
     mark(2);
     const unsigned pgrid = std::max(8u, num_cus() / 8 * 8);  // persistent: one workgroup per CU
     if (fp8) hipLaunchKernelGGL(k_l2_shared1<TF_FP8>, dim3(pgrid), dim3(512), 0, st, f);
+    else if (nv4) hipLaunchKernelGGL(k_l2_shared1<TF_NV4>, dim3(pgrid), dim3(512), 0, st, f);
     else hipLaunchKernelGGL(k_l2_shared1<TF_FP4>, dim3(pgrid), dim3(512), 0, st, f);
     mark(3);
     const long r_groups = static_cast<long>(Ms) * (Is / 4);
@@ -467,12 +474,14 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   const bool tiled = tiled_ok(d, Mr);
   constexpr int kSmallOnlyMr = 256;
   const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
-  const bool nvfp4 = d.wfmt == MOE_TAIL_W_NVFP4;
+  const bool nvfp4 = is_nvfp4(d);
   // 128- and 256-row tiles for FP8 only.  A 256-row MXFP4 tile fits one
   // 128-wide K block per step (half-line weight loads) and a 128-row one a
   // single stage in flight; MXFP4 experts with 33 rows or more take 64-row
   // tiles (three two-block stages) instead (the 1024-token MXFP4 workload:
-  // 923 -> 866 us on 128-row tiles, 851-859 us on 64-row ones)
+  // 923 -> 866 us on 128-row tiles, 851-859 us on 64-row ones).  NVFP4
+  // takes 32-row tiles for every expert (its block scales leave no room for
+  // a 64-row tile's three stages).
   const bool big = tiled && Mr > kSmallOnlyMr && fp8;
   const unsigned max_tiles = static_cast<unsigned>((R + kBM - 1) / kBM + E);
   TileArgs ta{};
@@ -480,10 +489,10 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   ta.expert_offsets = routing ? routing->expert_offsets : nullptr;
   ta.E = E;
   ta.k = k;
-  ta.e8_packed = d.wfmt == MOE_TAIL_W_MXFP4_PACKED;
+  ta.scales_packed = d.wfmt == MOE_TAIL_W_MXFP4_PACKED || d.wfmt == MOE_TAIL_W_NVFP4_PACKED;
   ta.big_rows = big ? kBigMinRows : 0x7fffffff;
   ta.huge_rows = big ? kHugeTM : 0x7fffffff;
-  const bool mid = tiled && (R > static_cast<size_t>(32) * E || (!fp8 && Mr > kSmallOnlyMr));
+  const bool mid = tiled && !nvfp4 && (R > static_cast<size_t>(32) * E || (!fp8 && Mr > kSmallOnlyMr));
   ta.mid_rows = mid ? 33 : 0x7fffffff;
   // bounds on the row tiles, which size the grids: ceil(c / 128) <= c / 64
   // for c >= 128, and ceil(c / 32) <= c / 32 + 1 (the launch of the 32- and
@@ -505,6 +514,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       a1.M = Mr;
       a1.b = w->w1;
       a1.b_scale = w->w1_scale;
+      a1.b_tscale = w->w1_tensor_scale;
       a1.hq = hq;
       a1.sh = sh;
       a1.K = L;
@@ -517,6 +527,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
         else launch_small_mid<TK_L1, TF_FP4>(a1, st);
       } else {
         if (fp8) launch_tile<TK_L1, TF_FP8, 0, 32>(a1, st);
+        else if (nvfp4) launch_tile<TK_L1, TF_NV4, 0, 32>(a1, st);
         else launch_tile<TK_L1, TF_FP4, 0, 32>(a1, st);
       }
       if (big) {
@@ -539,6 +550,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       a2.a_scale = sh;
       a2.b = w->w2;
       a2.b_scale = w->w2_scale;
+      a2.b_tscale = w->w2_tensor_scale;
       a2.y = y;
       a2.K = I;
       a2.N = L;
@@ -550,6 +562,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
         else launch_small_mid<TK_L2, TF_FP4>(a2, st);
       } else {
         if (fp8) launch_tile<TK_L2, TF_FP8, 0, 32>(a2, st);
+        else if (nvfp4) launch_tile<TK_L2, TF_NV4, 0, 32>(a2, st);
         else launch_tile<TK_L2, TF_FP4, 0, 32>(a2, st);
       }
       if (big) {
@@ -627,8 +640,8 @@ int fused_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint1
     return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, stream,
                         nullptr);
   if (!fused_ok(d, plans, Mr, Ms)) return MOE_TAIL_ERR_UNSUPPORTED;
-  const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128;
-  const unsigned grid = fp8 ? fused_grid<TF_FP8>() : fused_grid<TF_FP4>();
+  const bool fp8 = d.wfmt == MOE_TAIL_W_FP8_BLOCK128, nv4 = is_nvfp4(d);
+  const unsigned grid = fp8 ? fused_grid<TF_FP8>() : nv4 ? fused_grid<TF_NV4>() : fused_grid<TF_FP4>();
   if (grid < 8) return MOE_TAIL_ERR_UNSUPPORTED;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -641,6 +654,7 @@ int fused_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint1
                        at<float>(ws, lay.sx), blocks, f.sync, kSyncWords);
   }
   if (fp8) hipLaunchKernelGGL(k_tail_small<TF_FP8>, dim3(grid), dim3(512), 0, st, f);
+  else if (nv4) hipLaunchKernelGGL(k_tail_small<TF_NV4>, dim3(grid), dim3(512), 0, st, f);
   else hipLaunchKernelGGL(k_tail_small<TF_FP4>, dim3(grid), dim3(512), 0, st, f);
   return launched();
 }
@@ -859,6 +873,39 @@ int moe_tail_pack_mxfp4_scales(const moe_tail_dims* dims, const uint8_t* w1_scal
     const size_t words = n2 / 4;
     hipLaunchKernelGGL(k_pack_e8m0, dim3(static_cast<unsigned>((words + 255) / 256)), dim3(256), 0, st, w2_scale,
                        w2_scale_packed, words, static_cast<int>(L), static_cast<int>(I), 0);
+  }
+  return launched();
+}
+
+int moe_tail_pack_nvfp4_scales(const moe_tail_dims* dims, const uint8_t* w1_scale, const uint8_t* w2_scale,
+                               uint8_t* w1_scale_packed, uint8_t* w2_scale_packed, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  const moe_tail_dims& d = *dims;
+  if (!is_nvfp4(d)) return MOE_TAIL_ERR_INVALID;
+  if (d.latent % 256 || d.inter % 256) return MOE_TAIL_ERR_UNSUPPORTED;
+  const size_t E = d.num_experts, L = d.latent, I = d.inter;
+  const size_t n1 = E * 2 * I * (L / 16), n2 = E * L * (I / 16);  // bytes of each scale array
+  if ((w1_scale == nullptr) != (w1_scale_packed == nullptr) || (w2_scale == nullptr) != (w2_scale_packed == nullptr))
+    return MOE_TAIL_ERR_INVALID;
+  if ((w1_scale && (!ptr_ok(w1_scale, n1) || !ptr_ok(w1_scale_packed, n1))) ||
+      (w2_scale && (!ptr_ok(w2_scale, n2) || !ptr_ok(w2_scale_packed, n2))))
+    return MOE_TAIL_ERR_INVALID;
+  auto overlap = [](const uint8_t* a, const uint8_t* b, size_t n) { return a < b + n && b < a + n; };
+  if ((w1_scale && overlap(w1_scale, w1_scale_packed, n1)) || (w2_scale && overlap(w2_scale, w2_scale_packed, n2)))
+    return MOE_TAIL_ERR_INVALID;
+  if (w1_scale == nullptr && w2_scale == nullptr) return MOE_TAIL_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (w1_scale) {
+    const size_t runs = n1 / 16;
+    hipLaunchKernelGGL(k_pack_e4m3_16, dim3(static_cast<unsigned>((runs + 255) / 256)), dim3(256), 0, st, w1_scale,
+                       w1_scale_packed, runs, static_cast<int>(2 * I), static_cast<int>(L), static_cast<int>(I));
+  }
+  if (w2_scale) {
+    const size_t runs = n2 / 16;
+    hipLaunchKernelGGL(k_pack_e4m3_16, dim3(static_cast<unsigned>((runs + 255) / 256)), dim3(256), 0, st, w2_scale,
+                       w2_scale_packed, runs, static_cast<int>(L), static_cast<int>(I), 0);
   }
   return launched();
 }

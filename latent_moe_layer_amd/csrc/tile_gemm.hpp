@@ -49,7 +49,7 @@ __host__ __device__ __forceinline__ bool tail128(int c) { return (c % 256) > 0 &
 constexpr int kTileMaxE = 512;    // expert tables of the routed kinds live in LDS
 
 enum { TK_L1 = 0, TK_L2 = 1, TK_DENSE = 2 };
-enum { TF_FP8 = 0, TF_FP4 = 1, TF_BF16 = 2 };
+enum { TF_FP8 = 0, TF_FP4 = 1, TF_BF16 = 2, TF_NV4 = 3 };  // TF_NV4: NVFP4 weights (FP16 matrix cores)
 
 // K halves (128-wide blocks) per stage.  An MXFP4 weight row holds 64 bytes
 // per 128 K, and loads of half lines run at a fraction of the rate of whole
@@ -59,9 +59,11 @@ enum { TF_FP8 = 0, TF_FP4 = 1, TF_BF16 = 2 };
 // 128-byte line of every weight row) per stage.  MXFP4 tiles have 32 or 64
 // rows: a larger tile's two-block stage would leave at most one stage in
 // flight (every MXFP4 expert on 32- and 64-row tiles measured fastest).
-constexpr int tile_khalves(int FMT, int TM) { return FMT == TF_FP4 ? 2 : 1; }
+// NVFP4 weights are staged like MXFP4 ones (the same e2m1 bytes) and take
+// 32-row tiles only: their e4m3 block scales add 4 KB to a stage.
+constexpr int tile_khalves(int FMT, int TM) { return (FMT == TF_FP4 || FMT == TF_NV4) ? 2 : 1; }
 // Ring depth: kStages - 1 stages in flight.
-constexpr int tile_stages(int FMT, int TM) { return TM == 256 ? 2 : (TM == 32 && FMT != TF_FP4) ? 4 : 3; }
+constexpr int tile_stages(int FMT, int TM) { return TM == 256 ? 2 : (TM == 32 && FMT == TF_FP8) ? 4 : 3; }
 
 struct TileArgs {
   const uint8_t* a;               // L1: xq [Mr, L]; L2: hq [R, I]; dense: bf16 rows [M, K]
@@ -69,7 +71,8 @@ struct TileArgs {
   const int32_t* sorted_pair;     // L1: row -> token * k + slot
   const int32_t* expert_offsets;  // routed
   const uint8_t* b;               // weights (bytes)
-  const void* b_scale;            // FP8: [E, N/128, K/128] f32; FP4: [E, N, K/32] e8m0
+  const void* b_scale;            // FP8: [E, N/128, K/128] f32; FP4: [E, N, K/32] e8m0; NV4: [E, N, K/16] e4m3
+  const float* b_tscale;          // NV4: [E] the fp32 scale of each expert's matrix
   uint8_t* hq;                    // L1 out
   float* sh;                      // L1 out
   float* y;                       // L2 out [R, L]
@@ -84,7 +87,7 @@ struct TileArgs {
   int big_rows;                   // routed: experts with >= big_rows rows take 128-row tiles, the others 32-row tiles
   int huge_rows;                  // routed: experts with >= huge_rows rows take 256-row tiles instead
   int mid_rows;                   // routed: experts with mid_rows .. big_rows - 1 rows take 64-row tiles
-  int e8_packed;                  // MXFP4: e8m0 scales in the packed tile order (k_pack_e8m0)
+  int scales_packed;              // MXFP4 / NV4: block scales in the packed tile order (k_pack_e8m0 / k_pack_e4m3_16)
 };
 
 // MXFP4 e8m0 scales from the natural order [E][N][K/32] into the tile order
@@ -114,6 +117,37 @@ __global__ __launch_bounds__(256) void k_pack_e8m0(const uint8_t* __restrict__ s
       *reinterpret_cast<const uint32_t*>(src + (e * static_cast<size_t>(N) + n) * wpr + 8 * static_cast<size_t>(s) + 4 * h);
 }
 
+// NVFP4 e4m3 scales from the natural order [E][N][K/16] into the tile order
+// P[e][t][s][j][g][h][c] = S[e][n(t, j)][16 s + 8 h + 4 c + g] (t: tile of
+// 256 weight rows, s: 256-wide K step, j: tile row, g: lane group, h:
+// 128-wide K block, c: first or second 64 of the block), one 16-byte run
+// (t, s, j) per thread; tile rows as for k_pack_e8m0.  The scales of one
+// tile's rows for one K step are then 4 KB in a row, and lane group g of
+// the FP16 matrix cores finds the four scales it needs in one word.
+__global__ __launch_bounds__(256) void k_pack_e4m3_16(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                      size_t runs, int N, int K, int half) {
+  const size_t w = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (w >= runs) return;
+  const int j = static_cast<int>(w % 256);
+  size_t rest = w / 256;
+  const size_t nks = static_cast<size_t>(K) / 256, ntl = static_cast<size_t>(N) / 256;
+  const int s = static_cast<int>(rest % nks);
+  rest /= nks;
+  const size_t t = rest % ntl, e = rest / ntl;
+  const size_t n = half > 0 ? (j < 128 ? 128 * t + j : static_cast<size_t>(half) + 128 * t + (j - 128)) : 256 * t + j;
+  const uint8_t* in = src + (e * static_cast<size_t>(N) + n) * (static_cast<size_t>(K) / 16) + 16 * static_cast<size_t>(s);
+  const uint4 v = *reinterpret_cast<const uint4*>(in);
+  const uint8_t* b = reinterpret_cast<const uint8_t*>(&v);
+  uint8_t o[16];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) o[4 * g + 2 * h + c] = b[8 * h + 4 * c + g];
+  *reinterpret_cast<uint4*>(dst + 16 * w) = *reinterpret_cast<const uint4*>(o);
+}
+
 // Persistent: one workgroup per CU works through a list of tiles.  Tile t
 // of T: XCD x (workgroups are dealt to the 8 XCDs in turn, b % 8) owns tiles
 // [x * per, (x + 1) * per), per = ceil(T / 8), and its workgroups take them
@@ -140,7 +174,8 @@ struct TileLds {
   static constexpr bool kRouted = KIND != TK_DENSE;
   static constexpr int kKH = tile_khalves(FMT, TM);
   static constexpr int kStages = tile_stages(FMT, TM);
-  static constexpr int kStage = TM * 128 * kKH + kTN * 128 + (kScaled ? (kKH == 2 ? 8 * TM + 2048 : 2048) : 0);
+  static constexpr int kStage =
+      TM * 128 * kKH + kTN * 128 + (kScaled ? (FMT == TF_NV4 ? 8 * TM + 4096 : kKH == 2 ? 8 * TM + 2048 : 2048) : 0);
   static constexpr int kPairRows = (TM < 64) ? 64 : TM;
   static constexpr int kWavesN = (TM <= 64) ? 8 : 4;
   static constexpr int kRing = 0;
@@ -176,6 +211,8 @@ __device__ __forceinline__ TileSmem tile_smem_in(uint8_t* base) {
 template <int KIND, int FMT, int EPI, int TM = kTM>
 __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, int wg, int nwg) {
   constexpr bool kFP4 = FMT == TF_FP4;
+  constexpr bool kNV4 = FMT == TF_NV4;
+  constexpr bool kNib = kFP4 || kNV4;                // 4-bit weights, 64 bytes per row and K block
   constexpr bool kBF16 = FMT == TF_BF16;
   constexpr bool kScaled = !kBF16;
   constexpr bool kRouted = KIND != TK_DENSE;
@@ -188,6 +225,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   constexpr int kStages = tile_stages(FMT, TM);     // ring depth (kStages - 1 steps in flight)
   constexpr int kKH = tile_khalves(FMT, TM);         // 128-wide K blocks per stage
   static_assert(!kFP4 || TM <= 64, "MXFP4 tiles: 32 or 64 rows");
+  static_assert(!kNV4 || TM == 32, "NVFP4 tiles: 32 rows");
   constexpr int kABlk = TM / 8;                      // 1 KB blocks of A per stage and K block
   constexpr int kAL = (kABlk + 7) / 8;               // A blocks loaded per wave and K block
   constexpr int kABytes1 = TM * 128;                 // A bytes of one K block: 32, 16, 8 or 4 KB
@@ -199,17 +237,27 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   // [half][row] (8 TM bytes: every wave loads its share of them, waves
   // past the 2 TM words repeating the first ones, the same bytes to the same
   // place), then the e8m0 words [half][B row] (2 KB, wave w: half w / 4,
-  // B rows 64 (w % 4) + lane).
+  // B rows 64 (w % 4) + lane).  NVFP4 (two K blocks): waves 0-3 the e4m3
+  // scales of B rows 64 w + lane (16 bytes: 8 per K block), waves 4-7 the
+  // activation words (each wave all 2 TM of them, to the same place).
   constexpr int kActW = (TM + 63) / 64 < 2 ? 2 : (TM + 63) / 64;
   constexpr int kActW2 = (2 * TM) / 64;              // two K blocks: waves with distinct activation words
   constexpr int kSOff = kABytes + kBBytes;
   constexpr int kE8Off = (kKH == 2) ? 8 * TM : 256 * kActW;
   static_assert(kKH == 2 || kE8Off + 1024 <= 2048, "scale words");
-  constexpr int kSBytes = !kScaled ? 0 : (kKH == 2) ? 8 * TM + 2048 : 2048;
+  constexpr int kSBytes = !kScaled ? 0 : kNV4 ? 8 * TM + 4096 : (kKH == 2) ? 8 * TM + 2048 : 2048;
+  static_assert(!kNV4 || 2 * TM <= 64, "NVFP4: one wave's 64 lanes carry every activation word");
   constexpr int kStage = kSOff + kSBytes;
   constexpr int kBChunks = 4;                        // 16-byte B loads per thread and stage
-  constexpr int kSLoads = kScaled ? kKH : 0;         // 4-byte scale loads per thread and stage
-  constexpr int kLoads = kAL * kKH + kBChunks + kSLoads;  // direct loads per wave and stage
+  constexpr int kSLoads = kNV4 ? 1 : kScaled ? kKH : 0;  // scale loads per thread and stage
+  // A pieces of a stage (1 KB each): with two K blocks of 32 rows there are
+  // eight, one per wave (wave w: K block w / 4, block w % 4); otherwise wave
+  // w loads blocks (w + 8 i) % kABlk of every K block (TM = 32 with one K
+  // block: waves 4-7 load the same blocks as waves 0-3, the same bytes to the
+  // same place)
+  constexpr bool kASplit = kABlk * kKH == 8 && kKH == 2;
+  constexpr int kAPerWave = kASplit ? 1 : kAL * kKH;   // A loads per wave and stage
+  constexpr int kLoads = kAPerWave + kBChunks + kSLoads;  // direct loads per wave and stage
   constexpr uint32_t kNoRow = 0x80000000u;           // offset past any buffer: reads zeros
   using Lds = TileLds<KIND, FMT, TM>;
   static_assert(Lds::kStage == kStage && Lds::kStages == kStages && Lds::kWavesN == kWavesN, "LDS plan");
@@ -235,7 +283,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   const int elem = kBF16 ? 2 : 1;                  // bytes per A element
   const int nbrows = kPaired ? 2 * p.half : p.N;  // B rows of one expert / of the dense matrix
   const size_t a_row_bytes = static_cast<size_t>(p.K) * elem;
-  const size_t brow_bytes = kFP4 ? static_cast<size_t>(p.K) / 2 : static_cast<size_t>(p.K) * elem;
+  const size_t brow_bytes = kNib ? static_cast<size_t>(p.K) / 2 : static_cast<size_t>(p.K) * elem;
   const size_t wpr = static_cast<size_t>(p.K) / 32;  // FP4: e8m0 bytes per weight row
 
   // ---- this workgroup's tiles
@@ -381,8 +429,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       r.ra = make_rsrc(p.a, static_cast<uint32_t>(static_cast<size_t>(p.M) * a_row_bytes));
     else
       r.ra = make_rsrc(p.a + static_cast<size_t>(d.row0) * a_row_bytes, static_cast<uint32_t>(static_cast<size_t>(d.rows) * a_row_bytes));
-    // A block (wave + 8 i) % kABlk (TM = 32: waves 4-7 load the same blocks as
-    // waves 0-3, the same bytes to the same place)
+    // A block (wave + 8 i) % kABlk (see kASplit)
 #pragma unroll
     for (int i = 0; i < kAL; ++i) {
       const int row = 8 * ((wave + 8 * i) % kABlk) + q8;
@@ -411,12 +458,37 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     r.s_step = kKH == 2 ? 8 : 4;
     // packed e8m0 (k_pack_e8m0): this tile's run of K steps
     const uint32_t pk_tile = static_cast<uint32_t>(d.nt) * static_cast<uint32_t>(p.K / 256) * 2048u;
-    if (kScaled && kKH == 2) {
+    if (kNV4) {
+      if (wv < 4) {
+        // e4m3 scales of B row j = 64 wv + lane: 16 bytes a row and step
+        const int j = 64 * wv + lane;
+        r.rs = make_rsrc(static_cast<const uint8_t*>(p.b_scale) + static_cast<size_t>(d.e) * nbrows * (p.K / 16),
+                         static_cast<uint32_t>(static_cast<size_t>(nbrows) * (p.K / 16)));
+        if (p.scales_packed) {  // k_pack_e4m3_16: this tile's 4 KB runs, one per K step
+          r.s_off = static_cast<uint32_t>(d.nt) * static_cast<uint32_t>(p.K / 256) * 4096u + 16u * static_cast<uint32_t>(j);
+          r.s_step = 4096;
+        } else {
+          r.s_off = static_cast<uint32_t>(wrow(d.nt, j) * (p.K / 16));
+          r.s_step = 16;
+        }
+      } else {
+        // activation word q = lane: half q / TM, row q % TM
+        const int hh = lane / TM, row = lane - hh * TM;
+        const float* sbase = (KIND == TK_L1) ? p.a_scale : p.a_scale + static_cast<size_t>(d.row0) * nkb;
+        const size_t srows = (KIND == TK_L1) ? static_cast<size_t>(p.M) : static_cast<size_t>(d.rows);
+        r.rs = make_rsrc(sbase, static_cast<uint32_t>(srows * nkb * 4));
+        if (hh < 2 && row < d.rows) {
+          const size_t ar = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
+          r.s_off = static_cast<uint32_t>(ar * nkb * 4) + 4u * static_cast<uint32_t>(hh);
+        }
+        r.s_step = 8;
+      }
+    } else if (kScaled && kKH == 2) {
       // e8m0 words of half wv / 4, B row 64 (wv % 4) + lane (8 bytes a row and stage)
       const int j = 64 * (wv & 3) + lane;
       r.rs = make_rsrc(static_cast<const uint8_t*>(p.b_scale) + static_cast<size_t>(d.e) * nbrows * wpr,
                        static_cast<uint32_t>(nbrows * wpr));
-      if (p.e8_packed) {
+      if (p.scales_packed) {
         r.s_off = pk_tile + 1024u * static_cast<uint32_t>(wv >> 2) + 4u * static_cast<uint32_t>(j);
         r.s_step = 2048;
       } else {
@@ -449,11 +521,17 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   // traffic).  part: 1 = the B rows, 2 = the A rows and the scale words, 3 = all
   auto issue = [&](uint8_t* st, const Iss& r, int k, bool live, int part = 3) {
     if (part & 2) {
+      if (kASplit) {
+        const int h = wv / kABlk;
+        dma16(live ? r.ra : z_rsrc, st + kABytes1 * h + 1024 * (wv % kABlk), r.a_off[0], (k * kKH + h) * 128);
+      } else {
 #pragma unroll
-      for (int h = 0; h < kKH; ++h)
+        for (int h = 0; h < kKH; ++h)
 #pragma unroll
-        for (int i = 0; i < kAL; ++i)
-          dma16(live ? r.ra : z_rsrc, st + kABytes1 * h + 1024 * ((wv + 8 * i) % kABlk), r.a_off[i], (k * kKH + h) * 128);
+          for (int i = 0; i < kAL; ++i)
+            dma16(live ? r.ra : z_rsrc, st + kABytes1 * h + 1024 * ((wv + 8 * i) % kABlk), r.a_off[i],
+                  (k * kKH + h) * 128);
+      }
     }
     if (part & 1) {
 #pragma unroll
@@ -461,7 +539,10 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
         dma16(live ? r.rb : z_rsrc, st + kABytes + 8192 * i + 1024 * wv, r.b_off[i], k * 128);
     }
     if (!(part & 2)) return;
-    if (kScaled && kKH == 2) {
+    if (kNV4) {
+      if (wv < 4) dma16(live ? r.rs : z_rsrc, st + kSOff + kE8Off + 1024 * wv, r.s_off, r.s_step * k);
+      else dma4(live ? r.rs : z_rsrc, st + kSOff, r.s_off, r.s_step * k);
+    } else if (kScaled && kKH == 2) {
       dma4(live ? r.rs : z_rsrc, st + kSOff + kE8Off + 256 * wv, r.s_off, r.s_step * k);
       dma4(live ? r.rs2 : z_rsrc, st + kSOff + 256 * (wv % kActW2), r.s_off2, 8 * k);
     } else if (kScaled) {
@@ -478,6 +559,9 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     if (KIND == TK_L1 && wv < kPairRows / 64) {
       dma4(make_rsrc(p.sorted_pair + d.row0, static_cast<uint32_t>(d.rows) * 4u), reinterpret_cast<uint8_t*>(&s_pair[buf][64 * wv]),
            4u * (64 * wv + lane), 0);
+    } else if (kNV4 && wv == kWscW) {
+      // the matrix's fp32 scale into word 0 (the other lanes read zeros)
+      dma4(make_rsrc(p.b_tscale + d.e, 4u), reinterpret_cast<uint8_t*>(&s_wsc[buf][0][0]), 4u * lane, 0);
     } else if (FMT == TF_FP8 && (wv == kWscW || wv == kWscW + 1)) {
       const int q = wv - kWscW;
       const int wr = wrow(d.nt, 128 * q);
@@ -518,11 +602,27 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     if (FMT == TF_FP8) {
       sw_lo = s_wsc[buf][(16 * bblk(0)) / 128][ks];
       sw_hi = s_wsc[buf][(16 * bblk(kNJ - 1)) / 128][ks];
+    } else if (kNV4) {
+      sw_lo = sw_hi = s_wsc[buf][0][0];  // the matrix's fp32 scale
     }
     // weight fragments of K block h of the step (FP4: with their e8m0 scales)
     auto load_b = [&](int j, i32x8& bfj, int& sbj, int h = 0) {
       const int bb = bblk(j);
-      if (kFP4) {
+      if (kNV4) {
+        // K block h of the 128-byte row: packed bytes [8 g, +8) and [32 + 8 g,
+        // +8) of its 64, i.e. half g & 1 of chunks 4 h + g / 2 and 4 h + 2 + g / 2
+        const uint8_t* rp = st + kABytes + bb * 2048 + fr;
+        const int sw = l16 & 7, c0 = 4 * h + (g >> 1);
+        const uint2 lo = *reinterpret_cast<const uint2*>(rp + 16 * (c0 ^ sw) + 8 * (g & 1));
+        const uint2 hi = *reinterpret_cast<const uint2*>(rp + 16 * ((c0 + 2) ^ sw) + 8 * (g & 1));
+        bfj = i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(hi.x), static_cast<int>(hi.y),
+                    0, 0, 0, 0};
+        const uint8_t* sp = st + kSOff + kE8Off + 16 * (16 * bb + l16);
+        if (p.scales_packed)  // word g of the row: (block 0: c = 0, 1), (block 1: c = 0, 1)
+          sbj = static_cast<int>((*reinterpret_cast<const uint32_t*>(sp + 4 * g) >> (16 * h)) & 0xffffu);
+        else
+          sbj = static_cast<int>(sp[8 * h + g]) | (static_cast<int>(sp[8 * h + 4 + g]) << 8);
+      } else if (kFP4) {
         // two K blocks of 128-byte rows in the swizzled layout of the 8-bit
         // operands: K block h in chunks 4 h .. 4 h + 3
         const i32x4 v = *reinterpret_cast<const i32x4*>(st + kABytes + bb * 2048 + (h ? f_hi : f_lo));
@@ -681,6 +781,54 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
             }
           }
         }
+      }
+      if constexpr (kNV4) {
+        // FP16 matrix cores: the activation chunks converted once per K
+        // block, each weight block's when it is read
+        f16x8 xa[kMT][4];
+  #pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) fp8_frag_f16(af[mt], xa[mt]);
+        if (kTrans) {
+          // as below: group j - 1 is promoted after group j is issued
+          f32x4 pr[2][kMT];
+  #pragma unroll
+          for (int j = 0; j <= kNJ; ++j) {
+            if (j < kNJ) {
+              i32x8 bf;
+              int sb;
+              load_b(j, bf, sb, h);
+              f16x8 wb[4];
+              nvfp4_frag_f16(bf, sb, wb);
+  #pragma unroll
+              for (int mt = 0; mt < kMT; ++mt) pr[j & 1][mt] = mfma_f16_block(wb, xa[mt]);
+            }
+            if (j > 0) {
+              const int jp = j - 1;
+              const int hsel = (kPaired && jp >= kNJ / 2) ? 1 : 0;
+  #pragma unroll
+              for (int mt = 0; mt < kMT; ++mt)
+  #pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mt][jp][i] += pr[jp & 1][mt][i] * sc[hsel][mt][0];
+            }
+          }
+        } else {
+  #pragma unroll
+          for (int j = 0; j < kNJ; ++j) {
+            i32x8 bf;
+            int sb;
+            load_b(j, bf, sb, h);
+            f16x8 wb[4];
+            nvfp4_frag_f16(bf, sb, wb);
+            const int hsel = (kPaired && j >= kNJ / 2) ? 1 : 0;
+  #pragma unroll
+            for (int mt = 0; mt < kMT; ++mt) {
+              const f32x4 pr = mfma_f16_block(xa[mt], wb);
+  #pragma unroll
+              for (int i = 0; i < 4; ++i) acc[mt][j][i] += pr[i] * sc[hsel][mt][i];
+            }
+          }
+        }
+        continue;
       }
       if (kTrans) {
         // kNJ groups of kMT block products; group j - 1 is promoted (FP32

@@ -21,8 +21,9 @@ class DeviceTail:
 
     def __init__(self, inp: synth.Inputs, device="cuda:0", Mr: int | None = None, Ms: int | None = None,
                  pack_scales: bool = False):
-        """``pack_scales`` (MXFP4 weights): rearrange the e8m0 scales once with
-        moe_tail_pack_mxfp4_scales and run the forward on the packed order."""
+        """``pack_scales`` (MXFP4 or NVFP4 weights): rearrange the block scales
+        once with moe_tail_pack_mxfp4_scales / moe_tail_pack_nvfp4_scales and
+        run the forward on the packed order."""
         wl = inp.wl
         self.inp = inp
         self.device = torch.device(device)
@@ -35,13 +36,17 @@ class DeviceTail:
                    "ws1", "ws2", "w1_tscale", "w2_tscale")}
         t = self.t
         if pack_scales:
-            if wl.wfmt != synth.WFMT_MXFP4:
-                raise ValueError("packed scales are an MXFP4 layout")
+            if wl.wfmt not in (synth.WFMT_MXFP4, synth.WFMT_NVFP4):
+                raise ValueError("packed scales are an MXFP4 or NVFP4 layout")
             t["w1_scale"], natural1 = torch.empty_like(t["w1_scale"]), t["w1_scale"]
             t["w2_scale"], natural2 = torch.empty_like(t["w2_scale"]), t["w2_scale"]
-            B.moe_tail_pack_mxfp4_scales(self.dims, natural1, natural2, t["w1_scale"], t["w2_scale"])
+            if wl.wfmt == synth.WFMT_MXFP4:
+                B.moe_tail_pack_mxfp4_scales(self.dims, natural1, natural2, t["w1_scale"], t["w2_scale"])
+                self.dims.wfmt = B.MOE_TAIL_W_MXFP4_PACKED
+            else:
+                B.moe_tail_pack_nvfp4_scales(self.dims, natural1, natural2, t["w1_scale"], t["w2_scale"])
+                self.dims.wfmt = B.MOE_TAIL_W_NVFP4_PACKED
             torch.cuda.synchronize(d)
-            self.dims.wfmt = B.MOE_TAIL_W_MXFP4_PACKED
         self.weights = B.make_weights(gate=t["gate"], gate_bias=t["gate_bias"], w1=t["w1"], w1_scale=t["w1_scale"],
                                       w2=t["w2"], w2_scale=t["w2_scale"], rms_gamma=t["gamma"], w_up=t["w_up"],
                                       ws1=t["ws1"], ws2=t["ws2"],

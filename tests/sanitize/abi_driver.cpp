@@ -59,7 +59,7 @@ int main() {
   const int shapes[][4] = {{8, 2, 16, 16}, {64, 8, 128, 128}, {64, 8, 4096, 4096}, {128, 8, 1024, 1024},
                            {384, 8, 2048, 8192}, {1024, 16, 200, 300}, {5, 5, 0, 70}, {9, 3, 1, 1}};
   for (const auto& sh : shapes) {
-    for (int wfmt = 0; wfmt <= 2; ++wfmt) {
+    for (int wfmt = 0; wfmt <= 4; ++wfmt) {
       const moe_tail_dims d = dims(sh[0], sh[1], 2048, 2048, wfmt);
       const size_t need = moe_tail_workspace_bytes(&d, sh[2], sh[3]);
       size_t off[MOE_TAIL_WS_NUM];
@@ -120,6 +120,11 @@ int main() {
          "pack(no output)");
   expect(moe_tail_pack_mxfp4_scales(&d4, nullptr, nullptr, nullptr, nullptr, nullptr), MOE_TAIL_OK,
          "pack(nothing)");
+  const moe_tail_dims dn = dims(64, 8, 2048, 2048, MOE_TAIL_W_NVFP4);
+  expect(moe_tail_pack_nvfp4_scales(&d4, A, nullptr, P, nullptr, nullptr), MOE_TAIL_ERR_INVALID, "pack_nv(mxfp4 dims)");
+  expect(moe_tail_pack_nvfp4_scales(&dn, P, nullptr, P + 64, nullptr, nullptr), MOE_TAIL_ERR_INVALID,
+         "pack_nv(overlap)");
+  expect(moe_tail_pack_nvfp4_scales(&dn, nullptr, nullptr, nullptr, nullptr, nullptr), MOE_TAIL_OK, "pack_nv(nothing)");
   expect(moe_tail_quant_fp8_1x128(X, 1, 4, 100, static_cast<uint8_t*>(addr(1ull << 43)),
                                   static_cast<float*>(addr(1ull << 44)), nullptr),
          MOE_TAIL_ERR_INVALID, "quant(cols 100)");

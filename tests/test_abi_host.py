@@ -78,7 +78,7 @@ def test_invalid_args_size_zero(kw, Mr, Ms):
 
 
 @pytest.mark.parametrize("kw", [dict(hidden=7000), dict(latent=3600), dict(inter=2000), dict(shared_inter=100),
-                                dict(num_experts=1025), dict(top_k=17, num_experts=64), dict(wfmt=4),
+                                dict(num_experts=1025), dict(top_k=17, num_experts=64), dict(wfmt=5),
                                 dict(latent=16384)])
 def test_unsupported_dims(kw):
     offs = (C.c_size_t * B.MOE_TAIL_WS_NUM)()
@@ -273,6 +273,32 @@ def test_pack_mxfp4_scales_rejections():
     dp = dims(wfmt=B.MOE_TAIL_W_MXFP4_PACKED, inter=640)
     need = B.moe_tail_workspace_bytes(dp, 16, 16)
     assert _fwd(dp, w, X, 16, X, 16, r, OUT, None, WS, need) == B.MOE_TAIL_ERR_UNSUPPORTED
+
+
+def test_pack_nvfp4_scales_rejections():
+    pk = B.lib().moe_tail_pack_nvfp4_scales
+    dn = dims(wfmt=B.MOE_TAIL_W_NVFP4)
+    A, P = 1 << 44, 1 << 45  # placeholders: every call below fails before touching them
+    # FP8 and MXFP4 dims have no e4m3 block scales
+    assert pk(C.byref(dims()), A, None, P, None, None) == B.MOE_TAIL_ERR_INVALID
+    assert pk(C.byref(dims(wfmt=B.MOE_TAIL_W_MXFP4)), A, None, P, None, None) == B.MOE_TAIL_ERR_INVALID
+    # widths that are not multiples of 256
+    assert pk(C.byref(dims(wfmt=B.MOE_TAIL_W_NVFP4, inter=640)), A, None, P, None, None) == B.MOE_TAIL_ERR_UNSUPPORTED
+    # an input without its output, misaligned or overlapping buffers
+    assert pk(C.byref(dn), None, A, None, None, None) == B.MOE_TAIL_ERR_INVALID
+    assert pk(C.byref(dn), A + 4, None, P, None, None) == B.MOE_TAIL_ERR_INVALID
+    assert pk(C.byref(dn), A, None, A + 1024, None, None) == B.MOE_TAIL_ERR_INVALID
+    assert pk(C.byref(dn), None, None, None, None, None) == B.MOE_TAIL_OK
+    # a forward on packed scales needs the tiled kernels' shapes and the matrix scales
+    w, r = _fake_weights(), _fake_routing()
+    dp = dims(wfmt=B.MOE_TAIL_W_NVFP4_PACKED, inter=640)
+    need = B.moe_tail_workspace_bytes(dp, 16, 16)
+    w.w1_tensor_scale = w.w2_tensor_scale = 1 << 46
+    assert _fwd(dp, w, X, 16, X, 16, r, OUT, None, WS, need) == B.MOE_TAIL_ERR_UNSUPPORTED
+    dp = dims(wfmt=B.MOE_TAIL_W_NVFP4_PACKED)
+    need = B.moe_tail_workspace_bytes(dp, 16, 16)
+    w.w1_tensor_scale = None
+    assert _fwd(dp, w, X, 16, X, 16, r, OUT, None, WS, need) == B.MOE_TAIL_ERR_INVALID
 
 
 def test_quant_rejections():

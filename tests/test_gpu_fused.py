@@ -98,6 +98,9 @@ CASES = {
     "ragged": synth.Workload("ragged", Mr=37, Ms=53, E=8, k=3, I=512, Is=384, wfmt=0, seed=21, H=1024, L=512),
     "ragged_fp4": synth.Workload("ragged4", Mr=37, Ms=53, E=8, k=3, I=512, Is=384, wfmt=1, seed=21, H=1024, L=512,
                                  zipf_s=1.2),
+    # NVFP4 weights on skewed loads (experts past 32 rows take several tiles)
+    "ragged_nv4": synth.Workload("raggednv", Mr=37, Ms=53, E=8, k=3, I=512, Is=384, wfmt=synth.WFMT_NVFP4, seed=27,
+                                 H=1024, L=512, zipf_s=1.2),
     # all-equal logits: two experts with 100 rows each, four 32-row tiles apiece
     "heavy": synth.Workload("heavy", Mr=100, Ms=100, E=6, k=2, I=512, Is=128, wfmt=0, seed=22, zero_router=True,
                             H=1024, L=512),
@@ -116,7 +119,7 @@ def test_fused_equals_staged_bitwise(case):
     assert_counters(dev)
 
 
-@pytest.mark.parametrize("case", ["tiny", "ragged", "ragged_fp4"])
+@pytest.mark.parametrize("case", ["tiny", "ragged", "ragged_fp4", "ragged_nv4"])
 def test_fused_against_oracle(case):
     inp = synth.make_inputs(CASES[case])
     dev = DeviceTail(inp, "cuda:0")
@@ -208,7 +211,7 @@ def _hip_events(n):
     return out
 
 
-@pytest.mark.parametrize("case", ["tiny", "ragged", "ragged_fp4", "ms128", "decode"])
+@pytest.mark.parametrize("case", ["tiny", "ragged", "ragged_fp4", "ragged_nv4", "ms128", "decode"])
 def test_coscheduled_forward_equals_one_launch_per_stage(case):
     # At decode sizes moe_tail_forward runs the tail as six launches with
     # independent stages sharing a launch (routed L2 with the shared L1's

@@ -1,10 +1,12 @@
-"""MXFP4 scales in the tiled kernels' order (moe_tail_pack_mxfp4_scales): the
-pack kernel against the order written out here from its definition, and the
-forward on packed scales bit for bit the forward on natural ones, on every
-path that reads them (one launch per stage with every tile size, the
-six-launch decode forward, the single-launch tail, add3).  The pages' routed
-FP8/FP4 experts (DeepGEMM PR 416 mirror, Summary) fix the scale format, not
-its order in memory.  MI355X only (marker ``gpu``)."""
+"""MXFP4 and NVFP4 scales in the tiled kernels' order
+(moe_tail_pack_mxfp4_scales, moe_tail_pack_nvfp4_scales): the pack kernels
+against the orders written out here from their definitions, and the forward
+on packed scales bit for bit the forward on natural ones, on every path that
+reads them (one launch per stage with every tile size, the six-launch decode
+forward, the single-launch tail, add3).  The pages' routed FP8/FP4 experts
+(DeepGEMM PR 416 mirror, Summary) and the NVFP4 recipe (tokenspeed recipe
+"Kimi-K3 DEP16 with sharded shared experts", Allocation and launch) fix the
+scale formats, not their order in memory.  MI355X only (marker ``gpu``)."""
 from dataclasses import replace
 
 import numpy as np
@@ -60,6 +62,40 @@ def test_pack_kernel_matches_the_order(E, I, L):
     assert np.array_equal(to_np(p2), packed_order(s2, 0))
 
 
+def packed_order_nv(S: np.ndarray, paired_half: int) -> np.ndarray:
+    """P[e][t][s][j][g][h][c] = S[e][n(t, j)][16 s + 8 h + 4 c + g] for natural
+    e4m3 scales S [E, N, K/16]; tile rows as in packed_order."""
+    E, N, KB = S.shape
+    T, NS = N // 256, KB // 16
+    t = np.arange(T)[:, None]
+    j = np.arange(256)[None, :]
+    if paired_half:
+        rows = np.where(j < 128, 128 * t + j, paired_half + 128 * t + (j - 128))
+    else:
+        rows = 256 * t + j
+    out = np.empty((E, T, NS, 256, 4, 2, 2), np.uint8)
+    for s in range(NS):
+        for g in range(4):
+            for h in range(2):
+                for c in range(2):
+                    out[:, :, s, :, g, h, c] = S[:, rows, 16 * s + 8 * h + 4 * c + g]
+    return out.reshape(E, N, KB)
+
+
+@pytest.mark.parametrize("E,I,L", [(3, 512, 768), (2, 256, 512)])
+def test_pack_nvfp4_kernel_matches_the_order(E, I, L):
+    rng = np.random.default_rng(E * 1000 + I + 7)
+    s1 = rng.integers(0, 256, (E, 2 * I, L // 16), dtype=np.uint8)
+    s2 = rng.integers(0, 256, (E, L, I // 16), dtype=np.uint8)
+    d = B.make_dims(1024, L, E, 2, I, 256, B.MOE_TAIL_W_NVFP4, 1e-6)
+    t1, t2 = torch.from_numpy(s1).cuda(), torch.from_numpy(s2).cuda()
+    p1, p2 = torch.empty_like(t1), torch.empty_like(t2)
+    B.moe_tail_pack_nvfp4_scales(d, t1, t2, p1, p2)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(p1), packed_order_nv(s1, I))
+    assert np.array_equal(to_np(p2), packed_order_nv(s2, 0))
+
+
 def _forward(inp, pack, residual=None, fused=False, events=None):
     dev = DeviceTail(inp, "cuda:0", pack_scales=pack)
     dev.set_residual(residual)
@@ -85,6 +121,12 @@ CASES = {
     # several tiles per persistent workgroup on the 128- and 256-row tiles
     "multi": synth.Workload("multi", Mr=1024, Ms=1184, E=8, k=4, I=2048, Is=256, wfmt=1, seed=31, H=2048,
                             L=2048, zipf_s=0.4),
+    # NVFP4: the six-launch decode forward, and the 32-row tiles of the
+    # one-launch-per-stage path with several tiles per expert
+    "ragged_nv4": synth.Workload("raggednv", Mr=37, Ms=53, E=8, k=3, I=512, Is=384, wfmt=synth.WFMT_NVFP4, seed=27,
+                                 H=1024, L=512, zipf_s=1.2),
+    "skewed_nv4": synth.Workload("skewnv", Mr=300, Ms=320, E=16, k=4, I=512, Is=256, wfmt=synth.WFMT_NVFP4, seed=88,
+                                 H=1024, L=768, zipf_s=1.2),
 }
 
 
@@ -94,8 +136,9 @@ def test_packed_forward_equals_natural(case):
     _same(_forward(inp, False), _forward(inp, True))
 
 
-def test_packed_single_launch_and_add3():
-    wl = CASES["ragged"]
+@pytest.mark.parametrize("case", ["ragged", "ragged_nv4"])
+def test_packed_single_launch_and_add3(case):
+    wl = CASES[case]
     inp = synth.make_inputs(wl)
     _same(_forward(inp, False, fused=True), _forward(inp, True, fused=True))
     r = synth.make_residual(wl)
@@ -107,6 +150,12 @@ def test_packed_mxfp4_workload():
     inp = synth.make_inputs(synth.WORKLOADS["mxfp4"])
     a, b = _forward(inp, False), _forward(inp, True)
     _same(a, b)
+
+
+def test_packed_nvfp4_workload():
+    # the decode-shape NVFP4 workload: bit for bit the natural order
+    inp = synth.make_inputs(synth.WORKLOADS["nvfp4"])
+    _same(_forward(inp, False), _forward(inp, True))
 
 
 def test_packed_declines_other_widths():

@@ -199,10 +199,11 @@ def test_forward_mxfp4_width_not_a_multiple_of_256():
 
 @pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4, synth.WFMT_NVFP4])
 def test_forward_tiled_path(wfmt):
-    # Mr * k >= 2048 turns on the LDS-tiled routed kernel for experts with >= 128
-    # rows (here most experts, ~150 rows each: full and partial 128-row tiles),
-    # the others stay on the row-streaming kernel; M > 128 takes the tiled
-    # dense kernel for the shared expert and the up-projection.
+    # Past 256 tokens FP8 experts with >= 128 rows take 128-row tiles (here
+    # most experts, ~150 rows each: full and partial 128-row tiles), the
+    # others 32- or 64-row tiles; MXFP4 experts take 32- and 64-row tiles,
+    # NVFP4 experts several 32-row tiles; M > 128 takes the tiled dense
+    # kernel for the shared expert and the up-projection.
     wl = synth.Workload("tiled", Mr=300, Ms=333, E=16 if wfmt == synth.WFMT_MXFP4 else 18, k=8, I=512, Is=512, wfmt=wfmt, seed=30,
                         zipf_s=0.3 if wfmt == synth.WFMT_MXFP4 else 0.0)
     inp = synth.make_inputs(wl)
@@ -333,8 +334,9 @@ def test_forward_heavy_expert_many_row_tiles():
 
 
 def test_forward_nvfp4_skewed_and_narrow():
-    # NVFP4 weights on skewed loads (a few heavy experts, many empty ones) at
-    # the served widths, with more shared than routed tokens
+    # NVFP4 weights on skewed loads (a few heavy experts, many empty ones),
+    # with more shared than routed tokens; experts 384 wide (not a multiple
+    # of 256) keep the routed GEMMs on the row-streaming kernels
     wl = synth.Workload("nv", Mr=96, Ms=120, E=32, k=4, I=384, Is=256, wfmt=synth.WFMT_NVFP4, seed=91, zipf_s=1.2)
     inp = synth.make_inputs(wl)
     dev = run(inp)

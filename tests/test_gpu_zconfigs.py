@@ -49,9 +49,9 @@ def test_workload(name, n_shared):
     wl = synth.WORKLOADS[name]
     print(f"[{name}] generating inputs", flush=True)
     inp = synth.make_inputs(wl)
-    # (MXFP4 on packed scales, as the benchmark runs it; the natural order is
-    # bit for bit the same, test_gpu_packed)
-    dev = DeviceTail(inp, "cuda:0", pack_scales=wl.wfmt == synth.WFMT_MXFP4)
+    # (MXFP4 and NVFP4 on packed scales, as the benchmark runs them; the
+    # natural order is bit for bit the same, test_gpu_packed)
+    dev = DeviceTail(inp, "cuda:0", pack_scales=wl.wfmt in (synth.WFMT_MXFP4, synth.WFMT_NVFP4))
     stream = torch.cuda.Stream()
     print(f"[{name}] route + forward on the GPU", flush=True)
     dev.route(stream)
