@@ -60,10 +60,11 @@ int check_counts(int32_t Mr, int32_t Ms) {
 // Plan of one dense BF16 GEMM.  Up to kSmallMaxM rows: k_dense_small (all
 // rows per workgroup, kSkinnyN B rows per workgroup) with K split until the grid
 // holds about 256 workgroups, always through FP32 partials.  More rows: the
-// LDS-tiled kernel (128 x 256 tiles, epilogue fused, no split).
+// LDS-tiled kernel (256- or 128-row tiles, epilogue fused unless K is split).
 struct DensePlan {
   bool small;
   int mt, nt, splits, kps;
+  int tm;  // tiled: rows per tile (256 or 128)
 };
 
 constexpr int kPlanCUs = 256;
@@ -71,6 +72,7 @@ constexpr int kPlanCUs = 256;
 DensePlan plan_dense(int M, int nbrows, int ntiles, int K, int cus = kPlanCUs) {
   DensePlan p;
   p.small = M <= kSmallMaxM;
+  p.tm = 0;
   const int nk = p.small ? K / 64 : K / 128;  // K steps of the kernel
   int s = 1;
   if (p.small) {
@@ -80,8 +82,20 @@ DensePlan plan_dense(int M, int nbrows, int ntiles, int K, int cus = kPlanCUs) {
     p.nt = nbrows / kSkinnyN;
     if (p.nt > 0) s = std::min(nk, std::max(1, cus / p.nt));
   } else {
-    p.mt = (M + kTM - 1) / kTM;
+    // 256-row tiles once they alone fill the chip; else 128-row tiles, and
+    // while those fill at most half of it, K split in two more ranges (FP32
+    // partials reduced in split order, as for small M) down to 16 K steps a
+    // range (the 1024-token shared L1: 128 tiles of 112 K steps, split in 2)
     p.nt = ntiles;
+    const bool huge = static_cast<long>((M + kHugeTM - 1) / kHugeTM) * ntiles >= cus;
+    p.tm = huge ? kHugeTM : kTM;
+    p.mt = (M + p.tm - 1) / p.tm;
+    const int steps = K / 64;  // 64-wide BF16 K steps of the tiled kernel
+    if (!huge)
+      while (static_cast<long>(p.mt) * p.nt * s * 2 <= cus && steps % (2 * s) == 0 && steps / (2 * s) >= 16) s *= 2;
+    p.kps = steps / s;
+    p.splits = s;
+    return p;
   }
   p.kps = (nk + s - 1) / s;
   p.splits = (nk + p.kps - 1) / p.kps;
@@ -99,9 +113,10 @@ Plans plan_all(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   // partial sums to write and reduce).  The shared expert's plan depends on
   // Ms only, so its rows come out the same whatever Mr is.
   const int pair = Ms <= kSmallMaxM ? 2 : 1;
-  p.s1 = plan_dense(Ms, 2 * d.shared_inter, d.shared_inter / 64, d.hidden);
-  p.s2 = plan_dense(Ms, d.hidden, d.hidden / 128, d.shared_inter, kPlanCUs / pair);
-  p.up = plan_dense(Mr, d.hidden, d.hidden / 128, d.latent, kPlanCUs / pair);
+  // (tiles of the tiled kernel: 128 gate + 128 up rows, or 256 rows)
+  p.s1 = plan_dense(Ms, 2 * d.shared_inter, d.shared_inter / 128, d.hidden);
+  p.s2 = plan_dense(Ms, d.hidden, d.hidden / kTN, d.shared_inter, kPlanCUs / pair);
+  p.up = plan_dense(Mr, d.hidden, d.hidden / kTN, d.latent, kPlanCUs / pair);
   return p;
 }
 
@@ -143,7 +158,7 @@ Layout layout_of(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   const size_t ng = (static_cast<size_t>(Mr) + kGroup - 1) / kGroup;
   const Plans p = plan_all(d, Mr, Ms);
   size_t partial = 0;
-  auto need = [](const DensePlan& q) { return q.small; };
+  auto need = [](const DensePlan& q) { return q.small || q.splits > 1; };
   if (need(p.s1)) partial = std::max(partial, static_cast<size_t>(p.s1.splits) * Ms * 2 * Is * 4);
   if (need(p.s2)) partial = std::max(partial, static_cast<size_t>(p.s2.splits) * Ms * H * 4);
   if (need(p.up)) partial = std::max(partial, static_cast<size_t>(p.up.splits) * Mr * H * 4);
@@ -225,7 +240,8 @@ unsigned num_cus() {
 
 template <int KIND, int FMT, int EPI, int TM = kTM>
 void launch_tile(const TileArgs& a, hipStream_t st) {
-  const unsigned T = static_cast<unsigned>(a.nslots) * static_cast<unsigned>(a.ntn);
+  const unsigned T = static_cast<unsigned>(a.nslots) * static_cast<unsigned>(a.ntn) *
+                     static_cast<unsigned>(KIND == TK_DENSE && a.ksplit > 1 ? a.ksplit : 1);
   if (T == 0) return;
   // persistent: one workgroup per CU (the kernel's LDS allows no second),
   // whole rounds of 8 so that every XCD gets the same number
@@ -263,13 +279,16 @@ void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int 
   a.N = N;
   a.half = ep.half;
   a.ntn = (kEpi == EPI_SWIGLU) ? ep.half / 128 : N / kTN;
-  if (static_cast<unsigned>((M + kHugeTM - 1) / kHugeTM) * static_cast<unsigned>(a.ntn) >= num_cus()) {
-    // 256-row tiles once they alone fill the chip
-    a.nslots = (M + kHugeTM - 1) / kHugeTM;
-    launch_tile<TK_DENSE, TF_BF16, kEpi, kHugeTM>(a, st);
-  } else {
-    a.nslots = (M + kTM - 1) / kTM;
-    launch_tile<TK_DENSE, TF_BF16, kEpi>(a, st);
+  a.nslots = p.mt;
+  a.ksplit = p.splits;
+  a.partial = p.splits > 1 ? partial : nullptr;
+  if (p.tm == kHugeTM) launch_tile<TK_DENSE, TF_BF16, kEpi, kHugeTM>(a, st);
+  else launch_tile<TK_DENSE, TF_BF16, kEpi>(a, st);
+  if (p.splits > 1) {
+    const int ncols = (kEpi == EPI_SWIGLU) ? ep.half : N;
+    const long n = static_cast<long>(M) * (ncols / 4);
+    hipLaunchKernelGGL(k_dense_reduce<kEpi>, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,
+                       partial, M, N, p.splits, ep);
   }
 }
 

@@ -88,6 +88,8 @@ struct TileArgs {
   int huge_rows;                  // routed: experts with >= huge_rows rows take 256-row tiles instead
   int mid_rows;                   // routed: experts with mid_rows .. big_rows - 1 rows take 64-row tiles
   int scales_packed;              // MXFP4 / NV4: block scales in the packed tile order (k_pack_e8m0 / k_pack_e4m3_16)
+  int ksplit;                     // dense: K ranges (each tile's K steps split evenly; 0 or 1: none)
+  float* partial;                 // dense, ksplit > 1: FP32 partials [ksplit, M, B rows], reduced by k_dense_reduce
 };
 
 // MXFP4 e8m0 scales from the natural order [E][N][K/32] into the tile order
@@ -278,7 +280,8 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int l16 = lane & 15, g = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int nk = kBF16 ? p.K / 64 : p.K / (128 * kKH);  // K steps (stages of the stream) of a tile
+  const int nsplit = (!kRouted && p.ksplit > 1) ? p.ksplit : 1;
+  const int nk = kBF16 ? p.K / 64 / nsplit : p.K / (128 * kKH);  // K steps (stages of the stream) of a tile
   const int nkb = p.K / 128;                       // scale blocks along K (scaled formats)
   const int elem = kBF16 ? 2 : 1;                  // bytes per A element
   const int nbrows = kPaired ? 2 * p.half : p.N;  // B rows of one expert / of the dense matrix
@@ -325,7 +328,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     __syncthreads();
     T = s_pre[p.E] * p.ntn;
   } else {
-    T = p.nslots * p.ntn;
+    T = p.nslots * p.ntn * nsplit;
   }
   const int xcd = wg & 7, lb = wg >> 3, nbx = nwg >> 3;
   const int per = (T + 7) / 8, lo = xcd * per, hi = min(T, lo + per);
@@ -333,7 +336,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   if (n_my == 0) return;  // uniform
 
   struct Desc {
-    int e, row0, rows, nt;
+    int e, row0, rows, nt, kz;  // kz: the dense tile's K range
   };
   // tile j of this workgroup.  Routed tiles are numbered expert by expert;
   // within an expert (ns row slots x ntn n tiles) in blocks of kNBlk n tiles,
@@ -346,6 +349,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   auto desc = [&](int j) -> Desc {
     const int t = lo + lb + j * nbx;
     Desc d;
+    d.kz = 0;
     if (kRouted) {
       int a = 0, b = p.E;  // s_pre[a] * ntn <= t < s_pre[b] * ntn
       while (b - a > 1) {
@@ -376,8 +380,11 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       d.row0 = s_eoff[a] + base + slot * TM;
       d.rows = min(TM, s_eoff[a + 1] - d.row0);
     } else {
-      const int slot = t / p.ntn;
-      d.nt = t - slot * p.ntn;
+      // K range slowest: an XCD's run of tiles shares K range and rows
+      const int per_z = p.nslots * p.ntn;
+      d.kz = t / per_z;
+      const int slot = (t - d.kz * per_z) / p.ntn;
+      d.nt = t - d.kz * per_z - slot * p.ntn;
       d.e = 0;
       d.row0 = slot * TM;
       d.rows = min(TM, p.M - d.row0);
@@ -386,6 +393,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     d.row0 = __builtin_amdgcn_readfirstlane(d.row0);
     d.rows = __builtin_amdgcn_readfirstlane(d.rows);
     d.nt = __builtin_amdgcn_readfirstlane(d.nt);
+    d.kz = __builtin_amdgcn_readfirstlane(d.kz);
     return d;
   };
   // B row j of a tile (0..255) -> weight row: paired kinds take 128 gate
@@ -425,6 +433,8 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     asm volatile("" : "+v"(tid_o));
     const int lane = tid_o & 63, wave = tid_o >> 6, q8 = lane >> 3, st_c = (lane & 7) ^ q8, st_r0 = 8 * wave + q8;
     Iss r;
+    // bytes along a row before this tile's K range (split dense tiles)
+    const uint32_t kbase = kRouted ? 0u : static_cast<uint32_t>(d.kz) * static_cast<uint32_t>(nk) * 128u;
     if (KIND == TK_L1)  // gathered token rows of x codes
       r.ra = make_rsrc(p.a, static_cast<uint32_t>(static_cast<size_t>(p.M) * a_row_bytes));
     else
@@ -436,7 +446,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       uint32_t o = kNoRow;
       if (row < d.rows) {
         const size_t rr = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
-        o = static_cast<uint32_t>(rr * a_row_bytes) + 16u * st_c;
+        o = static_cast<uint32_t>(rr * a_row_bytes) + 16u * st_c + kbase;
       }
       r.a_off[i] = o;
     }
@@ -445,7 +455,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     for (int i = 0; i < kBChunks; ++i) {
       const int row = st_r0 + 64 * i;
       const int c = st_c;
-      r.b_off[i] = static_cast<uint32_t>(static_cast<size_t>(wrow(d.nt, row)) * brow_bytes) + 16u * c;
+      r.b_off[i] = static_cast<uint32_t>(static_cast<size_t>(wrow(d.nt, row)) * brow_bytes) + 16u * c + kbase;
     }
     // scale words, one 4-byte load per lane and stage: waves 0-1 the
     // activation scales of tile rows 64 w + lane (w < kActW), waves kActW ..
@@ -938,6 +948,21 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
             float* yr = p.y + static_cast<size_t>(d.row0 + r) * p.N + kTN * d.nt + 16 * kNJ * wn + l16;
 #pragma unroll
             for (int j = 0; j < kNJ; ++j) yr[16 * j] = acc[mt][j][i];
+          }
+        }
+    } else if (nsplit > 1) {
+      // one K range of a split dense tile: FP32 partial sums by B row
+      // (k_dense_reduce adds the ranges in order and applies the epilogue)
+      float* part = p.partial + static_cast<size_t>(d.kz) * p.M * nbrows;
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * kMT * wm + 16 * mt + 4 * g + i;
+          if (r < d.rows) {
+            float* pr = part + static_cast<size_t>(d.row0 + r) * nbrows;
+#pragma unroll
+            for (int j = 0; j < kNJ; ++j) pr[wrow(d.nt, 16 * bblk(j) + l16)] = acc[mt][j][i];
           }
         }
     } else {
