@@ -117,7 +117,7 @@ enum {
   MOE_TAIL_WS_XQ = 0,   /* [Mr, L] u8 e4m3 codes of x_lat */
   MOE_TAIL_WS_SX = 1,   /* [Mr, L/128] f32 scales of x_lat */
   MOE_TAIL_WS_HQ = 2,   /* [Mr*k, I] u8 e4m3 codes of h, rows in sorted order */
-  MOE_TAIL_WS_SH = 3,   /* [Mr*k, I/128] f32 scales of h */
+  MOE_TAIL_WS_SH = 3,   /* [I/128, Mr*k] f32 scales of h, K-block-major: block b of sorted row r at b*Mr*k + r */
   MOE_TAIL_WS_Y = 4,    /* [Mr*k, L] f32 routed L2 output, rows in sorted order */
   MOE_TAIL_WS_RN = 5,   /* [Mr, L] bf16 normalized combined latent */
   MOE_TAIL_WS_HS = 6,   /* [Ms, I_s] bf16 shared intermediate */

@@ -145,7 +145,7 @@ bool fused_ok(const moe_tail_dims& d, const Plans& p, int32_t Mr, int32_t Ms) {
 
 struct Layout {
   size_t logits, hist;                              // routing scratch
-  size_t xq, sx, hq, sh, y, rn, hs, s, partial;     // forward intermediates
+  size_t xq, sx, sxr, hq, sh, y, rn, hs, s, partial;  // forward intermediates
   size_t partial_s;                                 // the shared L2's partials when a later step reduces them
   size_t sync;                                      // completion counters of the single-launch tail
   size_t sync_bytes;
@@ -173,6 +173,7 @@ Layout layout_of(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   l.hist = take(E * ng * 4);
   l.xq = take(static_cast<size_t>(Mr) * L);
   l.sx = take(static_cast<size_t>(Mr) * (L / 128) * 4);
+  l.sxr = take(R * (L / 128) * 4);  // sx per routed row, K-block-major (RowScales)
   l.hq = take(R * I);
   l.sh = take(R * (I / 128) * 4);
   l.y = take(R * L * 4);
@@ -194,6 +195,18 @@ T* at(void* ws, size_t off) {
 }
 
 int launched() { return hipGetLastError() == hipSuccess ? MOE_TAIL_OK : MOE_TAIL_ERR_DEVICE; }
+
+// The x quantizer's second copy of the scales, by routed row (read by the
+// tiled routed L1)
+RowScales row_scales(const moe_tail_dims& d, const Layout& lay, void* ws, const moe_tail_routing* routing, int32_t Mr) {
+  RowScales rs{};
+  rs.pair_to_row = routing->pair_to_row;
+  rs.out = at<float>(ws, lay.sxr);
+  rs.k = d.top_k;
+  rs.nkb = d.latent / 128;
+  rs.R = static_cast<long>(Mr) * d.top_k;
+  return rs;
+}
 
 int check_weights(const moe_tail_dims& d, const moe_tail_weights* w, bool need_router, bool need_routed,
                   bool need_shared, bool need_up) {
@@ -310,7 +323,7 @@ FusedArgs fused_args(const moe_tail_dims& d, const moe_tail_weights* w, int32_t 
   ta.scales_packed = d.wfmt == MOE_TAIL_W_MXFP4_PACKED || d.wfmt == MOE_TAIL_W_NVFP4_PACKED;
   f.l1 = ta;
   f.l1.a = at<uint8_t>(ws, lay.xq);
-  f.l1.a_scale = at<float>(ws, lay.sx);
+  f.l1.a_scale = at<float>(ws, lay.sxr);
   f.l1.M = Mr;
   f.l1.b = w->w1;
   f.l1.b_scale = w->w1_scale;
@@ -445,7 +458,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
     const long qblocks = static_cast<long>(Mr) * (L / 128);
     mark(0);
     hipLaunchKernelGGL(k_quant_clear, dim3(quant_grid(qblocks)), dim3(256), 0, st, x_lat, xq, sx, qblocks, f.sync,
-                       kSyncWords);
+                       kSyncWords, row_scales(d, lay, ws, routing, Mr));
     mark(1);
     if (fp8) launch_tile<TK_L1, TF_FP8, 0, 32>(f.l1, st);
     else if (nv4) launch_tile<TK_L1, TF_NV4, 0, 32>(f.l1, st);
@@ -475,7 +488,8 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   mark(0);
   if (Mr > 0) {
     const long blocks = static_cast<long>(Mr) * (L / 128);
-    hipLaunchKernelGGL(k_quant_1x128<true>, dim3(quant_grid(blocks)), dim3(256), 0, st, x_lat, xq, sx, blocks);
+    hipLaunchKernelGGL(k_quant_1x128<true>, dim3(quant_grid(blocks)), dim3(256), 0, st, x_lat, xq, sx, blocks,
+                       tiled_ok(d, Mr) ? row_scales(d, lay, ws, routing, Mr) : RowScales{});
   }
   // 1, 2: routed L1 and L2 on the persistent LDS-tiled kernel: FP8 128-row
   // tiles for experts with at least kBigMinRows rows (256-row tiles from 256
@@ -529,7 +543,7 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
     } else {
       TileArgs a1 = ta;
       a1.a = xq;
-      a1.a_scale = sx;
+      a1.a_scale = at<float>(ws, lay.sxr);
       a1.M = Mr;
       a1.b = w->w1;
       a1.b_scale = w->w1_scale;
@@ -670,7 +684,7 @@ int fused_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint1
   {
     const long blocks = static_cast<long>(Mr) * (L / 128);
     hipLaunchKernelGGL(k_quant_clear, dim3(quant_grid(blocks)), dim3(256), 0, st, x_lat, at<uint8_t>(ws, lay.xq),
-                       at<float>(ws, lay.sx), blocks, f.sync, kSyncWords);
+                       at<float>(ws, lay.sx), blocks, f.sync, kSyncWords, row_scales(d, lay, ws, routing, Mr));
   }
   if (fp8) hipLaunchKernelGGL(k_tail_small<TF_FP8>, dim3(grid), dim3(512), 0, st, f);
   else if (nv4) hipLaunchKernelGGL(k_tail_small<TF_NV4>, dim3(grid), dim3(512), 0, st, f);
@@ -940,9 +954,9 @@ int moe_tail_quant_fp8_1x128(const void* x, int32_t x_is_bf16, int32_t rows, int
   const long blocks = static_cast<long>(rows) * (cols / 128);
   const dim3 grid(quant_grid(blocks));
   if (x_is_bf16)
-    hipLaunchKernelGGL(k_quant_1x128<true>, grid, dim3(256), 0, st, x, codes, scales, blocks);
+    hipLaunchKernelGGL(k_quant_1x128<true>, grid, dim3(256), 0, st, x, codes, scales, blocks, RowScales{});
   else
-    hipLaunchKernelGGL(k_quant_1x128<false>, grid, dim3(256), 0, st, x, codes, scales, blocks);
+    hipLaunchKernelGGL(k_quant_1x128<false>, grid, dim3(256), 0, st, x, codes, scales, blocks, RowScales{});
   return launched();
 }
 

@@ -14,9 +14,22 @@ namespace moe_tail {
 // neighbouring elements each (16-byte loads).
 constexpr int kQuantBlocksPerWave = 4;
 
+// Optional second copy of the scales for the routed GEMMs: block kb of
+// token t also goes to out[kb * R + pair_to_row[t * k + j]] for every slot j,
+// i.e. K-block-major over the sorted routed rows, so that the tiled kernels
+// read a tile's row scales for one K block as one contiguous run (instead of
+// one 4-byte load from each row's own line, once per weight tile).
+struct RowScales {
+  const int32_t* pair_to_row;  // [tokens * k], or null: no copy
+  float* out;                  // [cols / 128, R]
+  int k, nkb;                  // slots per token (<= 16), scale blocks per row
+  long R;                      // routed rows (tokens * k)
+};
+
 template <bool kBf16In>
 __device__ __forceinline__ void quant_wave(const void* __restrict__ x, uint8_t* __restrict__ codes,
-                                           float* __restrict__ scales, long nblocks, long w, int lane) {
+                                           float* __restrict__ scales, long nblocks, long w, int lane,
+                                           const RowScales& rs) {
   const long blk = w * kQuantBlocksPerWave + (lane >> 4);
   if (w * kQuantBlocksPerWave >= nblocks) return;  // wave-uniform
   const bool live = blk < nblocks;                 // uniform within a block's 16 lanes
@@ -50,14 +63,18 @@ __device__ __forceinline__ void quant_wave(const void* __restrict__ x, uint8_t* 
   if (live) {
     *reinterpret_cast<uint2*>(codes + e0) = make_uint2(lo, hi);
     if ((lane & 15) == 0) scales[blk] = s;
+    if (rs.out != nullptr && (lane & 15) < rs.k) {  // lane j of the block: slot j's row
+      const long t = blk / rs.nkb, kb = blk - t * rs.nkb;
+      rs.out[kb * rs.R + rs.pair_to_row[t * rs.k + (lane & 15)]] = s;
+    }
   }
 }
 
 template <bool kBf16In>
 __global__ __launch_bounds__(256) void k_quant_1x128(const void* __restrict__ x, uint8_t* __restrict__ codes,
-                                                     float* __restrict__ scales, long nblocks) {
+                                                     float* __restrict__ scales, long nblocks, RowScales rs) {
   quant_wave<kBf16In>(x, codes, scales, nblocks, static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6),
-                      threadIdx.x & 63);
+                      threadIdx.x & 63, rs);
 }
 
 // Workgroups of 256 threads for nblocks 1x128 blocks.
@@ -70,11 +87,11 @@ inline unsigned quant_grid(long nblocks) {
 // `zero` (the completion counters of the single-launch tail that follows).
 __global__ __launch_bounds__(256) void k_quant_clear(const uint16_t* __restrict__ x, uint8_t* __restrict__ codes,
                                                      float* __restrict__ scales, long nblocks,
-                                                     int* __restrict__ zero, int n) {
+                                                     int* __restrict__ zero, int n, RowScales rs) {
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < n; i += 256) zero[i] = 0;
   quant_wave<true>(x, codes, scales, nblocks, static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6),
-                   threadIdx.x & 63);
+                   threadIdx.x & 63, rs);
 }
 
 // One workgroup (256 threads) per routed token: z = sum_j w_j * y[row(t, j)]

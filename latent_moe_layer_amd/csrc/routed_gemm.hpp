@@ -171,6 +171,7 @@ __global__ __launch_bounds__(256, 2) void k_routed_l1(const uint8_t* __restrict_
   if (e < 0) return;  // uniform over the workgroup
   const int row0 = __builtin_amdgcn_readfirstlane(s_tile[1]), rows = __builtin_amdgcn_readfirstlane(s_tile[2]);
   const int nkb = L / 128;
+  const int n_rows = expert_offsets[E];  // routed rows: the stride of sh, which is K-block-major
   if (tid < kBM) s_tok[tid] = (tid < rows) ? sorted_pair[row0 + tid] / k : -1;
   __syncthreads();
   for (int i = tid; i < kBM * nkb; i += 256) {
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void k_routed_l1(const uint8_t* __restrict_
       const float inv = 1.0f / s;
 #pragma unroll
       for (int c = 0; c < 2; ++c) s_q[r][32 * wave + 16 * c + l16] = static_cast<uint8_t>(f32_to_e4m3(h[ms][c][i] * inv));
-      if (wave == 0 && l16 == 0 && r < rows) sh[static_cast<size_t>(row0 + r) * (I / 128) + nb] = s;
+      if (wave == 0 && l16 == 0 && r < rows) sh[static_cast<size_t>(nb) * n_rows + row0 + r] = s;
     }
   __syncthreads();
   {
@@ -310,9 +311,10 @@ __global__ __launch_bounds__(256, 2) void k_routed_l2(const uint8_t* __restrict_
   if (e < 0) return;
   const int row0 = __builtin_amdgcn_readfirstlane(s_tile[1]), rows = __builtin_amdgcn_readfirstlane(s_tile[2]);
   const int nkb = I / 128;
+  const int n_rows = expert_offsets[E];  // routed rows: the stride of sh, which is K-block-major
   for (int i = tid; i < kBM * nkb; i += 256) {
     const int r = i / nkb, kb = i % nkb;
-    s_sh[i] = (r < rows) ? sh[static_cast<size_t>(row0 + r) * nkb + kb] : 0.0f;
+    s_sh[i] = (r < rows) ? sh[static_cast<size_t>(kb) * n_rows + row0 + r] : 0.0f;
   }
   __syncthreads();
 

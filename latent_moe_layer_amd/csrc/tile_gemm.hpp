@@ -67,7 +67,8 @@ constexpr int tile_stages(int FMT, int TM) { return TM == 256 ? 2 : (TM == 32 &&
 
 struct TileArgs {
   const uint8_t* a;               // L1: xq [Mr, L]; L2: hq [R, I]; dense: bf16 rows [M, K]
-  const float* a_scale;           // L1: sx [Mr, L/128]; L2: sh [R, I/128]
+  const float* a_scale;           // routed: scales of the A rows by routed row, K-block-major: L1 the x scales
+                                  // [L/128, R] (RowScales), L2 sh [I/128, R]
   const int32_t* sorted_pair;     // L1: row -> token * k + slot
   const int32_t* expert_offsets;  // routed
   const uint8_t* b;               // weights (bytes)
@@ -291,6 +292,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
 
   // ---- this workgroup's tiles
   int T;
+  int n_rows = 0;  // routed: rows of the sorted routed segment (the stride of the K-block-major scales)
   if (kRouted) {
     for (int i = tid; i <= p.E; i += 512) s_eoff[i] = p.expert_offsets[i];
     __syncthreads();
@@ -327,6 +329,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     }
     __syncthreads();
     T = s_pre[p.E] * p.ntn;
+    n_rows = __builtin_amdgcn_readfirstlane(s_eoff[p.E]);
   } else {
     T = p.nslots * p.ntn * nsplit;
   }
@@ -422,7 +425,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   struct Iss {
     __amdgpu_buffer_rsrc_t ra, rb, rs, rs2;
     uint32_t a_off[kAL], b_off[kBChunks], s_off, s_off2;
-    int s_step;  // bytes of the first scale load's source per K step (wave-uniform)
+    int s_step, s_step2;  // bytes of the scale loads' sources per K step (wave-uniform)
   };
   auto make_iss = [&](const Desc& d, int buf) -> Iss {
     // the lane's coordinates, recomputed from an opaque copy of the thread
@@ -466,6 +469,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     r.rs2 = z_rsrc;
     r.s_off2 = kNoRow;
     r.s_step = kKH == 2 ? 8 : 4;
+    r.s_step2 = 0;
     // packed e8m0 (k_pack_e8m0): this tile's run of K steps
     const uint32_t pk_tile = static_cast<uint32_t>(d.nt) * static_cast<uint32_t>(p.K / 256) * 2048u;
     if (kNV4) {
@@ -482,16 +486,12 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
           r.s_step = 16;
         }
       } else {
-        // activation word q = lane: half q / TM, row q % TM
+        // activation word q = lane: half q / TM, row q % TM (as for MXFP4)
         const int hh = lane / TM, row = lane - hh * TM;
-        const float* sbase = (KIND == TK_L1) ? p.a_scale : p.a_scale + static_cast<size_t>(d.row0) * nkb;
-        const size_t srows = (KIND == TK_L1) ? static_cast<size_t>(p.M) : static_cast<size_t>(d.rows);
-        r.rs = make_rsrc(sbase, static_cast<uint32_t>(srows * nkb * 4));
-        if (hh < 2 && row < d.rows) {
-          const size_t ar = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
-          r.s_off = static_cast<uint32_t>(ar * nkb * 4) + 4u * static_cast<uint32_t>(hh);
-        }
-        r.s_step = 8;
+        r.rs = make_rsrc(p.a_scale, static_cast<uint32_t>(static_cast<size_t>(nkb) * n_rows * 4));
+        if (hh < 2 && row < d.rows)
+          r.s_off = static_cast<uint32_t>((static_cast<size_t>(hh) * n_rows + d.row0 + row) * 4);
+        r.s_step = 8 * n_rows;
       }
     } else if (kScaled && kKH == 2) {
       // e8m0 words of half wv / 4, B row 64 (wv % 4) + lane (8 bytes a row and stage)
@@ -504,25 +504,19 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       } else {
         r.s_off = static_cast<uint32_t>(wrow(d.nt, j) * wpr) + 4u * static_cast<uint32_t>(wv >> 2);
       }
-      // activation word q: half q / TM, row q % TM
+      // activation word q: half q / TM, row q % TM (K block 2 k + hh of routed
+      // row row0 + row: one contiguous run per half)
       const int q = 64 * (wv % kActW2) + lane, hh = q / TM, row = q - hh * TM;
-      const float* sbase = (KIND == TK_L1) ? p.a_scale : p.a_scale + static_cast<size_t>(d.row0) * nkb;
-      const size_t srows = (KIND == TK_L1) ? static_cast<size_t>(p.M) : static_cast<size_t>(d.rows);
-      r.rs2 = make_rsrc(sbase, static_cast<uint32_t>(srows * nkb * 4));
-      if (row < d.rows) {
-        const size_t ar = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
-        r.s_off2 = static_cast<uint32_t>(ar * nkb * 4) + 4u * static_cast<uint32_t>(hh);
-      }
+      r.rs2 = make_rsrc(p.a_scale, static_cast<uint32_t>(static_cast<size_t>(nkb) * n_rows * 4));
+      r.s_step2 = 8 * n_rows;
+      if (row < d.rows) r.s_off2 = static_cast<uint32_t>((static_cast<size_t>(hh) * n_rows + d.row0 + row) * 4);
     } else if (kScaled) {
       if (wv < (TM + 63) / 64) {
+        // K block k of routed rows row0 + 64 w + lane: one contiguous run
         const int row = 64 * wv + lane;
-        const float* sbase = (KIND == TK_L1) ? p.a_scale : p.a_scale + static_cast<size_t>(d.row0) * nkb;
-        const size_t srows = (KIND == TK_L1) ? static_cast<size_t>(p.M) : static_cast<size_t>(d.rows);
-        r.rs = make_rsrc(sbase, static_cast<uint32_t>(srows * nkb * 4));
-        if (row < d.rows) {
-          const size_t ar = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
-          r.s_off = static_cast<uint32_t>(ar * nkb * 4);
-        }
+        r.rs = make_rsrc(p.a_scale, static_cast<uint32_t>(static_cast<size_t>(nkb) * n_rows * 4));
+        r.s_step = 4 * n_rows;
+        if (row < d.rows) r.s_off = static_cast<uint32_t>((static_cast<size_t>(d.row0) + row) * 4);
       }
     }
     return r;
@@ -554,7 +548,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       else dma4(live ? r.rs : z_rsrc, st + kSOff, r.s_off, r.s_step * k);
     } else if (kScaled && kKH == 2) {
       dma4(live ? r.rs : z_rsrc, st + kSOff + kE8Off + 256 * wv, r.s_off, r.s_step * k);
-      dma4(live ? r.rs2 : z_rsrc, st + kSOff + 256 * (wv % kActW2), r.s_off2, 8 * k);
+      dma4(live ? r.rs2 : z_rsrc, st + kSOff + 256 * (wv % kActW2), r.s_off2, r.s_step2 * k);
     } else if (kScaled) {
       dma4(live ? r.rs : z_rsrc, st + kSOff + 256 * wv, r.s_off, r.s_step * k);
     }
@@ -927,7 +921,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
             q4 |= static_cast<uint32_t>(f32_to_e4m3(acc[mt][j][i] * inv)) << (8 * i);
           *reinterpret_cast<uint32_t*>(sq + r * 128 + 16 * (kH * wn + j) + 4 * g) = q4;
         }
-        if (wn == 0 && g == 0 && r < d.rows) p.sh[static_cast<size_t>(d.row0 + r) * (p.half / 128) + d.nt] = s;
+        if (wn == 0 && g == 0 && r < d.rows) p.sh[static_cast<size_t>(d.nt) * n_rows + d.row0 + r] = s;
       }
       lds_barrier();
 #pragma unroll

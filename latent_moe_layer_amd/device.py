@@ -126,7 +126,8 @@ class DeviceTail:
             "xq": self._view(B.MOE_TAIL_WS_XQ, torch.uint8, (Mr, wl.L)),
             "sx": self._view(B.MOE_TAIL_WS_SX, torch.float32, (Mr, wl.L // 128)),
             "hq": self._view(B.MOE_TAIL_WS_HQ, torch.uint8, (R, wl.I)),
-            "sh": self._view(B.MOE_TAIL_WS_SH, torch.float32, (R, wl.I // 128)),
+            # (stored K-block-major, [I/128, R]; viewed here as [R, I/128])
+            "sh": self._view(B.MOE_TAIL_WS_SH, torch.float32, (wl.I // 128, R)).t(),
             "y": self._view(B.MOE_TAIL_WS_Y, torch.float32, (R, wl.L)),
             "rn": self._view(B.MOE_TAIL_WS_RN, torch.int16, (Mr, wl.L)),
             "hs": self._view(B.MOE_TAIL_WS_HS, torch.int16, (Ms, wl.Is)),
