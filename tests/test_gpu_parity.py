@@ -333,6 +333,21 @@ def test_forward_heavy_expert_many_row_tiles():
     check_forward(dev, inp)
 
 
+@pytest.mark.parametrize("wfmt", [synth.WFMT_FP8, synth.WFMT_MXFP4, synth.WFMT_NVFP4])
+def test_forward_top16(wfmt):
+    # the widest routing the kernels take (k = 16): every lane of a 1x128
+    # block's 16 writes its slot's copy of the x scale (the by-row copy the
+    # tiled routed L1 reads), and every token reaches 16 of 24 experts; the
+    # decode-sized schedule, one expert past 32 rows on several tiles
+    wl = synth.Workload("top16", Mr=45, Ms=60, E=24, k=16, I=512, Is=256, wfmt=wfmt, seed=95, H=1024, L=768,
+                        zipf_s=0.8)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    loads = np.diff(to_np(dev.offsets))
+    assert loads.sum() == 45 * 16 and loads.max() > 32, loads
+    check_forward(dev, inp)
+
+
 def test_forward_nvfp4_skewed_and_narrow():
     # NVFP4 weights on skewed loads (a few heavy experts, many empty ones),
     # with more shared than routed tokens; experts 384 wide (not a multiple
