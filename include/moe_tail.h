@@ -305,15 +305,13 @@ int moe_tail_pack_mxfp4_scales(const moe_tail_dims *dims, const uint8_t *w1_scal
  * scale per 16 weights along K), not the order of the scales in memory; in
  * this order the scales of one tile's 256 weight rows for one 256-wide K
  * step are one contiguous 4 KB run (whole-line loads instead of 16 bytes
- * from each of 256 rows), and the four scales one lane of the FP16 matrix
- * cores needs for a K step are one 4-byte word.
+ * from each of 256 rows).
  *   For each expert e and each weight matrix W [N, K] with natural scales
  *   S[n][K/16] (w1: N = 2I, K = L; w2: N = L, K = I), the packed scales are
- *   P[e][t][s][j][g][h][c] = S[e][n(t, j)][16 s + 8 h + 4 c + g] with
- *   t < N/256 (tile), s < K/256 (K step), j < 256 (tile row), g < 4 (lane
- *   group), h < 2 (128-wide K block), c < 2 (the first or second 64 of the
- *   block); tile row j of w1 is gate row 128 t + j for j < 128 and up row
- *   I + 128 t + (j - 128) otherwise, of w2 row 256 t + j.
+ *   P[e][t][s][j][q] = S[e][n(t, j)][16 s + q] with t < N/256 (tile),
+ *   s < K/256 (K step), j < 256 (tile row), q < 16; tile row j of w1 is gate
+ *   row 128 t + j for j < 128 and up row I + 128 t + (j - 128) otherwise, of
+ *   w2 row 256 t + j.
  * dims->wfmt is MOE_TAIL_W_NVFP4 or _PACKED; L and I must be multiples of
  * 256 (else MOE_TAIL_ERR_UNSUPPORTED).  w1_scale / w2_scale are the natural
  * [E, 2I, L/16] / [E, L, I/16] e4m3 arrays, the packed outputs the same sizes

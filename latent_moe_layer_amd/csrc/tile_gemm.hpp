@@ -121,12 +121,11 @@ __global__ __launch_bounds__(256) void k_pack_e8m0(const uint8_t* __restrict__ s
 }
 
 // NVFP4 e4m3 scales from the natural order [E][N][K/16] into the tile order
-// P[e][t][s][j][g][h][c] = S[e][n(t, j)][16 s + 8 h + 4 c + g] (t: tile of
-// 256 weight rows, s: 256-wide K step, j: tile row, g: lane group, h:
-// 128-wide K block, c: first or second 64 of the block), one 16-byte run
-// (t, s, j) per thread; tile rows as for k_pack_e8m0.  The scales of one
-// tile's rows for one K step are then 4 KB in a row, and lane group g of
-// the FP16 matrix cores finds the four scales it needs in one word.
+// P[e][t][s][j][q] = S[e][n(t, j)][16 s + q] (t: tile of 256 weight rows, s:
+// 256-wide K step, j: tile row, q < 16), one 16-byte run (t, s, j) per
+// thread; tile rows as for k_pack_e8m0.  The scales of one tile's rows for
+// one K step are then 4 KB in a row (whole-line loads instead of 16 bytes
+// from each of 256 rows).
 __global__ __launch_bounds__(256) void k_pack_e4m3_16(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                       size_t runs, int N, int K, int half) {
   const size_t w = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -139,16 +138,7 @@ __global__ __launch_bounds__(256) void k_pack_e4m3_16(const uint8_t* __restrict_
   const size_t t = rest % ntl, e = rest / ntl;
   const size_t n = half > 0 ? (j < 128 ? 128 * t + j : static_cast<size_t>(half) + 128 * t + (j - 128)) : 256 * t + j;
   const uint8_t* in = src + (e * static_cast<size_t>(N) + n) * (static_cast<size_t>(K) / 16) + 16 * static_cast<size_t>(s);
-  const uint4 v = *reinterpret_cast<const uint4*>(in);
-  const uint8_t* b = reinterpret_cast<const uint8_t*>(&v);
-  uint8_t o[16];
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) o[4 * g + 2 * h + c] = b[8 * h + 4 * c + g];
-  *reinterpret_cast<uint4*>(dst + 16 * w) = *reinterpret_cast<const uint4*>(o);
+  *reinterpret_cast<uint4*>(dst + 16 * w) = *reinterpret_cast<const uint4*>(in);
 }
 
 // Persistent: one workgroup per CU works through a list of tiles.  Tile t
@@ -587,6 +577,9 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   const int fr = 1024 * (l16 >> 3) + 128 * (l16 & 7);
   const int f_lo = fr + 16 * (g ^ (l16 & 7));
   const int f_hi = fr + 16 * ((4 | g) ^ (l16 & 7));
+  // NVFP4's activation pieces: chunks 2 g and 2 g + 1 (32 consecutive K)
+  const int f_nv0 = fr + 16 * ((2 * g) ^ (l16 & 7));
+  const int f_nv1 = fr + 16 * ((2 * g + 1) ^ (l16 & 7));
 
   // Accumulators.  L1 (kTrans): the weight block is the MFMA's A operand
   // and the activation block its B operand, so acc[mt][j][i] is weight
@@ -613,19 +606,15 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     auto load_b = [&](int j, i32x8& bfj, int& sbj, int h = 0) {
       const int bb = bblk(j);
       if (kNV4) {
-        // K block h of the 128-byte row: packed bytes [8 g, +8) and [32 + 8 g,
-        // +8) of its 64, i.e. half g & 1 of chunks 4 h + g / 2 and 4 h + 2 + g / 2
-        const uint8_t* rp = st + kABytes + bb * 2048 + fr;
-        const int sw = l16 & 7, c0 = 4 * h + (g >> 1);
-        const uint2 lo = *reinterpret_cast<const uint2*>(rp + 16 * (c0 ^ sw) + 8 * (g & 1));
-        const uint2 hi = *reinterpret_cast<const uint2*>(rp + 16 * ((c0 + 2) ^ sw) + 8 * (g & 1));
-        bfj = i32x8{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(hi.x), static_cast<int>(hi.y),
-                    0, 0, 0, 0};
-        const uint8_t* sp = st + kSOff + kE8Off + 16 * (16 * bb + l16);
-        if (p.scales_packed)  // word g of the row: (block 0: c = 0, 1), (block 1: c = 0, 1)
-          sbj = static_cast<int>((*reinterpret_cast<const uint32_t*>(sp + 4 * g) >> (16 * h)) & 0xffffu);
-        else
-          sbj = static_cast<int>(sp[8 * h + g]) | (static_cast<int>(sp[8 * h + 4 + g]) << 8);
+        // lane group g takes K [32 g, 32 g + 32) of K block h (for both
+        // operands, see the activation fragments below): chunk 4 h + g of the
+        // weight row, as for MXFP4, and the e4m3 scales of its two 16-element
+        // groups, bytes 8 h + 2 g and 8 h + 2 g + 1 of the row's 16 (natural
+        // and packed order alike)
+        const i32x4 v = *reinterpret_cast<const i32x4*>(st + kABytes + bb * 2048 + (h ? f_hi : f_lo));
+        const i32x4 z = {0, 0, 0, 0};
+        bfj = __builtin_shufflevector(v, z, 0, 1, 2, 3, 4, 5, 6, 7);
+        sbj = *reinterpret_cast<const uint16_t*>(st + kSOff + kE8Off + 16 * (16 * bb + l16) + 8 * h + 2 * g);
       } else if (kFP4) {
         // two K blocks of 128-byte rows in the swizzled layout of the 8-bit
         // operands: K block h in chunks 4 h .. 4 h + 3
@@ -743,8 +732,10 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
         const uint8_t* ab = st + kABytes1 * h + (kMT * wm + mt) * 2048;
-        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(ab + f_lo);
-        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(ab + f_hi);
+        // NVFP4 (FP16 matrix cores): K [32 g, 32 g + 32) of the block, chunks
+        // 2 g and 2 g + 1; the FP8 MFMA's own layout otherwise
+        const i32x4 lo4 = *reinterpret_cast<const i32x4*>(ab + (kNV4 ? f_nv0 : f_lo));
+        const i32x4 hi4 = *reinterpret_cast<const i32x4*>(ab + (kNV4 ? f_nv1 : f_hi));
         af[mt] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
       }
       if (kBF16) {

@@ -63,8 +63,8 @@ def test_pack_kernel_matches_the_order(E, I, L):
 
 
 def packed_order_nv(S: np.ndarray, paired_half: int) -> np.ndarray:
-    """P[e][t][s][j][g][h][c] = S[e][n(t, j)][16 s + 8 h + 4 c + g] for natural
-    e4m3 scales S [E, N, K/16]; tile rows as in packed_order."""
+    """P[e][t][s][j][q] = S[e][n(t, j)][16 s + q] for natural e4m3 scales
+    S [E, N, K/16]; tile rows as in packed_order."""
     E, N, KB = S.shape
     T, NS = N // 256, KB // 16
     t = np.arange(T)[:, None]
@@ -73,12 +73,9 @@ def packed_order_nv(S: np.ndarray, paired_half: int) -> np.ndarray:
         rows = np.where(j < 128, 128 * t + j, paired_half + 128 * t + (j - 128))
     else:
         rows = 256 * t + j
-    out = np.empty((E, T, NS, 256, 4, 2, 2), np.uint8)
+    out = np.empty((E, T, NS, 256, 16), np.uint8)
     for s in range(NS):
-        for g in range(4):
-            for h in range(2):
-                for c in range(2):
-                    out[:, :, s, :, g, h, c] = S[:, rows, 16 * s + 8 * h + 4 * c + g]
+        out[:, :, s, :, :] = S[:, rows, 16 * s:16 * s + 16]
     return out.reshape(E, N, KB)
 
 
