@@ -141,6 +141,15 @@ __global__ __launch_bounds__(256) void k_pack_e4m3_16(const uint8_t* __restrict_
   *reinterpret_cast<uint4*>(dst + 16 * w) = *reinterpret_cast<const uint4*>(in);
 }
 
+// NVFP4 activation rows in LDS: chunk c of row r at 16-byte slot
+// c ^ nv_swz(r & 7).  Lane group g reads chunks 2 g and 2 g + 1 of row l16;
+// under the plain swizzle (slot c ^ (r & 7)) lane groups 2 i and 2 i + 1
+// read chunks of one parity, and the LDS, serving them in one pass, finds
+// pairs of them on the same banks (1.5 times the read time of a conflict-free
+// pattern, measured).  This swizzle spreads the rows of each parity over
+// both halves of the slots.
+__host__ __device__ __forceinline__ int nv_swz(int r) { return ((r >> 1) & 1) | (r & 4); }
+
 // Persistent: one workgroup per CU works through a list of tiles.  Tile t
 // of T: XCD x (workgroups are dealt to the 8 XCDs in turn, b % 8) owns tiles
 // [x * per, (x + 1) * per), per = ceil(T / 8), and its workgroups take them
@@ -425,6 +434,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     int tid_o = threadIdx.x;
     asm volatile("" : "+v"(tid_o));
     const int lane = tid_o & 63, wave = tid_o >> 6, q8 = lane >> 3, st_c = (lane & 7) ^ q8, st_r0 = 8 * wave + q8;
+    const int st_ca = kNV4 ? (lane & 7) ^ nv_swz(q8) : st_c;  // A rows (NVFP4: their own swizzle)
     Iss r;
     // bytes along a row before this tile's K range (split dense tiles)
     const uint32_t kbase = kRouted ? 0u : static_cast<uint32_t>(d.kz) * static_cast<uint32_t>(nk) * 128u;
@@ -439,7 +449,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       uint32_t o = kNoRow;
       if (row < d.rows) {
         const size_t rr = (KIND == TK_L1) ? static_cast<size_t>(s_pair[buf][row] / p.k) : static_cast<size_t>(row);
-        o = static_cast<uint32_t>(rr * a_row_bytes) + 16u * st_c + kbase;
+        o = static_cast<uint32_t>(rr * a_row_bytes) + 16u * st_ca + kbase;
       }
       r.a_off[i] = o;
     }
@@ -577,9 +587,10 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   const int fr = 1024 * (l16 >> 3) + 128 * (l16 & 7);
   const int f_lo = fr + 16 * (g ^ (l16 & 7));
   const int f_hi = fr + 16 * ((4 | g) ^ (l16 & 7));
-  // NVFP4's activation pieces: chunks 2 g and 2 g + 1 (32 consecutive K)
-  const int f_nv0 = fr + 16 * ((2 * g) ^ (l16 & 7));
-  const int f_nv1 = fr + 16 * ((2 * g + 1) ^ (l16 & 7));
+  // NVFP4's activation pieces: chunks 2 g and 2 g + 1 (32 consecutive K),
+  // in rows swizzled by nv_swz
+  const int f_nv0 = fr + 16 * ((2 * g) ^ nv_swz(l16 & 7));
+  const int f_nv1 = fr + 16 * ((2 * g + 1) ^ nv_swz(l16 & 7));
 
   // Accumulators.  L1 (kTrans): the weight block is the MFMA's A operand
   // and the activation block its B operand, so acc[mt][j][i] is weight
