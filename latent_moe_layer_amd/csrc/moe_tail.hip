@@ -791,13 +791,24 @@ int moe_tail_route(const moe_tail_dims* dims, const moe_tail_weights* w, const u
     else
       hipLaunchKernelGGL(k_router_logits, dim3((Mr + kLogitTok - 1) / kLogitTok, egroups), dim3(256), xtile, st, x_lat,
                          w->gate, w->gate_bias, logits, Mr, L, E);
+  }
+  // one workgroup for the whole permutation while it is short (it walks the
+  // token groups one wave at a time), with the top-k too for up to 16
+  // tokens (one per wave); three grid-wide passes beyond that
+  const bool small_sort = static_cast<int64_t>(ng) * E <= kSortSmall && ng <= kSortSmallGroups;
+  if (Mr > 0 && Mr <= kTopkSortTokens && small_sort) {
+    auto ts = (E <= 64) ? k_router_topk_sort<1> : (E <= 128) ? k_router_topk_sort<2> : (E <= 384) ? k_router_topk_sort<6>
+                                                                                       : k_router_topk_sort<kMaxExpertsPerLane>;
+    hipLaunchKernelGGL(ts, dim3(1), dim3(1024), 0, st, logits, out->topk_ids, out->topk_weights, out->expert_offsets,
+                       out->sorted_pair, out->pair_to_row, Mr, E, k, ng);
+    return launched();
+  }
+  if (Mr > 0) {
     auto topk = (E <= 64) ? k_router_topk<1> : (E <= 128) ? k_router_topk<2> : (E <= 384) ? k_router_topk<6>
                                                                                  : k_router_topk<kMaxExpertsPerLane>;
     hipLaunchKernelGGL(topk, dim3((Mr + 3) / 4), dim3(256), 0, st, logits, out->topk_ids, out->topk_weights, Mr, E, k);
   }
-  // one workgroup for the whole permutation while it is short (it walks the
-  // token groups one wave at a time); three grid-wide passes beyond that
-  if (static_cast<int64_t>(ng) * E <= kSortSmall && ng <= kSortSmallGroups) {
+  if (small_sort) {
     hipLaunchKernelGGL(k_router_sort, dim3(1), dim3(1024), 0, st, out->topk_ids, out->expert_offsets,
                        out->sorted_pair, out->pair_to_row, Mr, E, k, ng);
     return launched();

@@ -144,9 +144,13 @@ def test_quantizer_bit_exact():
     assert np.array_equal(to_np(s), os_)
 
 
+# Shapes of every routing path: top-k and permutation in one workgroup (Mr <= 16: 1, 2, 6 and 16
+# experts per lane), top-k then the one-workgroup permutation (from 17 tokens), and the grid-wide
+# permutation (more than 24 groups of 64 tokens).
 @pytest.mark.parametrize("E,k,Mr,zipf", [(8, 2, 16, 0.0), (64, 8, 128, 0.0), (64, 8, 4096, 0.0), (128, 8, 1024, 1.2),
                                          (384, 8, 2048, 0.0), (1024, 16, 200, 0.0), (5, 5, 70, 0.0), (9, 3, 1, 0.0),
-                                         (16, 4, 130, 0.0), (64, 8, 530, 0.0), (32, 4, 1600, 0.0)])
+                                         (16, 4, 130, 0.0), (64, 8, 530, 0.0), (32, 4, 1600, 0.0),
+                                         (128, 8, 16, 1.2), (384, 8, 13, 0.0), (1024, 16, 16, 0.0), (64, 8, 17, 0.0)])
 def test_route_bit_exact(E, k, Mr, zipf):
     wl = synth.Workload("r", Mr=Mr, Ms=Mr, E=E, k=k, I=128, Is=128, wfmt=0, seed=100 + E, zipf_s=zipf)
     inp = synth.make_inputs(wl, routing_only=True)
