@@ -785,9 +785,8 @@ int moe_tail_route(const moe_tail_dims* dims, const moe_tail_weights* w, const u
       lds_raised = true;
     }
     if (Mr >= kWideMinTokens)
-      hipLaunchKernelGGL((k_router_logits_wide<kWideTok, kWideEW>),
-                         dim3((Mr + kWideTok - 1) / kWideTok, (E + 4 * kWideEW - 1) / (4 * kWideEW)), dim3(256), 0, st,
-                         x_lat, w->gate, w->gate_bias, logits, Mr, L, E);
+      hipLaunchKernelGGL((k_router_logits_tile<8, 8>), dim3((Mr + 15) / 16, (E + 15) / 16), dim3(256), 0, st, x_lat,
+                         w->gate, w->gate_bias, logits, Mr, L, E);
     else
       hipLaunchKernelGGL(k_router_logits, dim3((Mr + kLogitTok - 1) / kLogitTok, egroups), dim3(256), xtile, st, x_lat,
                          w->gate, w->gate_bias, logits, Mr, L, E);

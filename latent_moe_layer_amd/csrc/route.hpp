@@ -100,99 +100,85 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 }
 
 // Many tokens: the 4-token tile above re-reads every gate row once per 4
-// tokens (about 1 GB of L2 traffic at 4096 tokens).  This variant takes
-// kTok tokens x 4 kEW experts per workgroup (wave w: experts e0 + w kEW ..),
-// streams x through LDS in 512-column chunks (double-buffered direct loads)
-// and the gate values of a chunk into registers, and keeps the same order
-// of operations per logit: lane l's fused-multiply-add chain over i of
-// x[64 i + l] * W[e, 64 i + l] (chunk by chunk, i ascending), then the xor
-// butterfly, then the bias.  Measured at 4096 tokens x 64 experts: 104 us
-// for the 4-token kernel, 166 / 88 / 76 us for 32 / 16 / 8-token tiles (the
-// larger tiles hold so many accumulators that one wave per SIMD fits); at
-// 2048 x 384: 307 against 204 us.
-constexpr int kWideTok = 8;
-constexpr int kWideEW = 4;
-constexpr int kWideChunk = 512;  // columns of x per LDS stage
+// tokens (about 1 GB of L2 traffic at 4096 tokens).  Here a workgroup of 4
+// waves takes 2 kTW tokens x 2 kEW experts; wave w computes tokens kTW (w & 1)
+// .. and experts kEW (w >> 1) .. .  Per chunk of kLgC columns one stage holds
+// the x rows (bf16) and the gate rows (fp32), loaded with 1 KB direct loads
+// (6 per wave) and double-buffered, so a lane reads per 64-column step kTW x
+// values and kEW gate values from LDS for kTW x kEW fused multiply-adds.  The
+// order of operations per logit is the one above: lane l's chain over i of
+// x[64 i + l] * W[e, 64 i + l], i ascending, then the xor butterfly, then the
+// bias.  At 2048 tokens x 384 experts: 8 x 8 per wave 142-150 us; 4 x 16 and
+// 16 x 4 171-181, 8 x 16 and 16 x 8 241-260 (fewer waves per SIMD); an
+// earlier form with the gate values loaded into registers (one 4-byte load
+// per value and lane) 188 us.
 constexpr int kWideMinTokens = 512;
+constexpr int kLgC = 256;  // columns per stage (L is a multiple of 256)
 
-template <int kTok, int kEW>
-__global__ __launch_bounds__(256) void k_router_logits_wide(const uint16_t* __restrict__ x_lat,
+template <int kTW, int kEW>
+__global__ __launch_bounds__(256) void k_router_logits_tile(const uint16_t* __restrict__ x_lat,
                                                             const float* __restrict__ gate,
                                                             const float* __restrict__ bias, float* __restrict__ logits,
                                                             int Mr, int L, int E) {
-  constexpr int kU = kWideChunk / 64;  // i values per chunk
-  constexpr int kRowBytes = kWideChunk * 2;
-  static_assert(kRowBytes == 1024 && kTok % 4 == 0, "one 1 KB direct load per token row and chunk");
-  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kTok * kRowBytes];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kRowsX = 2 * kTW, kRowsG = 2 * kEW;
+  constexpr int kXBytes = kRowsX * kLgC * 2, kGBytes = kRowsG * kLgC * 4;
+  constexpr int kStage = kXBytes + kGBytes;
+  constexpr int kPieces = kStage / 1024;  // 1 KB direct loads per stage
+  static_assert(kLgC == 256 && kRowsX % 2 == 0 && kPieces % 4 == 0, "x pieces: two 512-byte rows; 4 waves");
+  __shared__ __attribute__((aligned(16))) uint8_t st[2][kStage];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int t0 = blockIdx.x * kTok;
-  const int e0 = (blockIdx.y * 4 + wave) * kEW;
-  const int nch = (L + kWideChunk - 1) / kWideChunk;
-  const size_t row_bytes = static_cast<size_t>(L) * 2;
-  // x rows t0 .. t0 + kTok - 1 (rows past Mr read zeros; columns past a
-  // row's end read the next row's values, which no lane uses)
-  const int nrows = max(0, min(kTok, Mr - t0));
+  const int tw = wv & 1, ew = wv >> 1;
+  const int t0 = blockIdx.x * kRowsX, e0 = blockIdx.y * kRowsG;
+  const int nx = max(0, min(kRowsX, Mr - t0)), ng = max(0, min(kRowsG, E - e0));
+  // rows past Mr / E read zeros
   const __amdgpu_buffer_rsrc_t rx =
-      make_rsrc(x_lat + static_cast<size_t>(t0) * L, static_cast<uint32_t>(static_cast<size_t>(nrows) * row_bytes));
-  __amdgpu_buffer_rsrc_t rw[kEW];
+      make_rsrc(x_lat + static_cast<size_t>(t0) * L, static_cast<uint32_t>(nx) * static_cast<uint32_t>(L) * 2u);
+  const __amdgpu_buffer_rsrc_t rg =
+      make_rsrc(gate + static_cast<size_t>(e0) * L, static_cast<uint32_t>(ng) * static_cast<uint32_t>(L) * 4u);
+  // piece q of chunk c: q < kRowsX / 2: x rows 2q, 2q + 1 (32 lanes each);
+  // else gate row q - kRowsX / 2
+  auto load = [&](int c, int b) {
 #pragma unroll
-  for (int e = 0; e < kEW; ++e)
-    rw[e] = make_rsrc(gate + static_cast<size_t>(min(e0 + e, E - 1)) * L, static_cast<uint32_t>(L) * 4);
-  // chunk c: this wave's token rows wv + 4 j into stage b, and its gate values
-  auto load_x = [&](int c, int b) {
-#pragma unroll
-    for (int j = 0; j < kTok / 4; ++j) {
-      const int r = wv + 4 * j;
-      const size_t off = static_cast<size_t>(r) * row_bytes + static_cast<size_t>(c) * kRowBytes;
-      dma16(rx, xs[b] + r * kRowBytes, static_cast<uint32_t>(off) + 16u * lane, 0);
-    }
-  };
-  auto load_w = [&](int c, float (&dst)[kEW][kU]) {
-#pragma unroll
-    for (int e = 0; e < kEW; ++e)
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-        dst[e][u] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rw[e], 4 * lane, 4 * (c * kWideChunk + 64 * u), 0));
-  };
-  float acc[kTok][kEW];
-#pragma unroll
-  for (int t = 0; t < kTok; ++t)
-#pragma unroll
-    for (int e = 0; e < kEW; ++e) acc[t][e] = 0.0f;
-
-  // chunk c from stage `cur` with gate values wc; chunk c + 1's loads go to
-  // the other stage and wn (two register sets, so no index is dynamic)
-  float w0[kEW][kU], w1[kEW][kU];
-  auto step = [&](int c, float (&wc)[kEW][kU], float (&wn)[kEW][kU], int cur) {
-    vm_wait<0>();   // this wave's loads of chunk c (x rows and gate values)
-    lds_barrier();  // every wave's x rows of chunk c; every wave done with chunk c - 1
-    if (c + 1 < nch) {
-      load_x(c + 1, cur ^ 1);
-      load_w(c + 1, wn);
-    }
-    const uint16_t* xr = reinterpret_cast<const uint16_t*>(xs[cur]);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (c * kWideChunk + 64 * u < L) {
-#pragma unroll
-        for (int t = 0; t < kTok; ++t) {
-          const float xv = bf16_bits_to_f32(xr[t * kWideChunk + 64 * u + lane]);
-#pragma unroll
-          for (int e = 0; e < kEW; ++e) acc[t][e] = __builtin_fmaf(xv, wc[e][u], acc[t][e]);
-        }
+    for (int j = 0; j < kPieces / 4; ++j) {
+      const int q = wv + 4 * j;
+      if (q < kRowsX / 2) {
+        const uint32_t r = 2u * q + (lane >> 5);
+        dma16(rx, st[b] + 1024 * q, r * static_cast<uint32_t>(L) * 2u + static_cast<uint32_t>(c) * (kLgC * 2) + 16u * (lane & 31), 0);
+      } else {
+        const uint32_t r = q - kRowsX / 2;
+        dma16(rg, st[b] + 1024 * q, r * static_cast<uint32_t>(L) * 4u + static_cast<uint32_t>(c) * (kLgC * 4) + 16u * lane, 0);
       }
     }
   };
-  load_x(0, 0);
-  load_w(0, w0);
-  for (int c = 0; c < nch; c += 2) {
-    step(c, w0, w1, 0);
-    if (c + 1 < nch) step(c + 1, w1, w0, 1);
+  float acc[kTW][kEW];
+#pragma unroll
+  for (int t = 0; t < kTW; ++t)
+#pragma unroll
+    for (int e = 0; e < kEW; ++e) acc[t][e] = 0.0f;
+  const int nch = L / kLgC;
+  load(0, 0);
+  for (int c = 0; c < nch; ++c) {
+    const int b = c & 1;
+    ring_barrier<0>();  // this wave's loads of chunk c, then every wave's; every wave done with chunk c - 1
+    if (c + 1 < nch) load(c + 1, b ^ 1);
+    const uint16_t* xr = reinterpret_cast<const uint16_t*>(st[b]) + kTW * tw * kLgC;
+    const float* gr = reinterpret_cast<const float*>(st[b] + kXBytes) + kEW * ew * kLgC;
+#pragma unroll
+    for (int u = 0; u < kLgC / 64; ++u) {
+      float xv[kTW], gv[kEW];
+#pragma unroll
+      for (int t = 0; t < kTW; ++t) xv[t] = bf16_bits_to_f32(xr[t * kLgC + 64 * u + lane]);
+#pragma unroll
+      for (int e = 0; e < kEW; ++e) gv[e] = gr[e * kLgC + 64 * u + lane];
+#pragma unroll
+      for (int t = 0; t < kTW; ++t)
+#pragma unroll
+        for (int e = 0; e < kEW; ++e) acc[t][e] = __builtin_fmaf(xv[t], gv[e], acc[t][e]);
+    }
   }
 #pragma unroll
-  for (int t = 0; t < kTok; ++t)
+  for (int t = 0; t < kTW; ++t)
 #pragma unroll
     for (int e = 0; e < kEW; ++e) {
       float p = acc[t][e];
@@ -200,13 +186,14 @@ __global__ __launch_bounds__(256) void k_router_logits_wide(const uint16_t* __re
       for (int off = 32; off >= 1; off >>= 1) p = p + __shfl_xor(p, off);
       acc[t][e] = p;
     }
-  // lane t stores token t0 + t's logits of this wave's experts
+  // lane t stores token t's logits of this wave's experts
+  const int tb = t0 + kTW * tw, eb = e0 + kEW * ew;
 #pragma unroll
-  for (int t = 0; t < kTok; ++t)
-    if (lane == t && t0 + t < Mr) {
+  for (int t = 0; t < kTW; ++t)
+    if (lane == t && tb + t < Mr) {
 #pragma unroll
       for (int e = 0; e < kEW; ++e)
-        if (e0 + e < E) logits[static_cast<size_t>(t0 + t) * E + e0 + e] = acc[t][e] + (bias ? bias[e0 + e] : 0.0f);
+        if (eb + e < E) logits[static_cast<size_t>(tb + t) * E + eb + e] = acc[t][e] + (bias ? bias[eb + e] : 0.0f);
     }
 }
 
