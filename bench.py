@@ -16,7 +16,10 @@ half of the metric, and the tiny workload), and for every workload:
     the same cache-cold (a 512 MiB streaming read between replays, outside
     the timed pair, evicts the 256 MB Infinity Cache);
   - `groups_us`: each launch group of the schedule the plain call runs, from
-    moe_tail_forward_timed (events recorded on the library's stream);
+    moe_tail_forward_timed (events recorded on the library's stream; where
+    the plain call runs the shared L1 and L2 on a second stream beside the
+    routed GEMMs, the timed call keeps them on one stream, so its groups
+    time each stage alone);
   - `roofline`: the routed L1 launch(es) against the bound of that workload
     (HBM for the weight-streaming workloads, FP8 MFMA for prefill), with the
     other unit alongside.

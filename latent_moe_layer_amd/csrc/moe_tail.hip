@@ -253,27 +253,59 @@ unsigned num_cus() {
   return cache[dev];
 }
 
+// Workgroups of a persistent launch: one per CU (the tiled kernels' LDS
+// allows no second), whole rounds of 8 so that every XCD gets the same
+// number; `share` > 0 caps them at that many CUs (a multiple of 8), the
+// rest of the chip running a concurrent launch.
+unsigned persistent_wgs(unsigned share) {
+  const unsigned all = std::max(8u, num_cus() / 8 * 8);
+  return share > 0 ? std::min(all, share) : all;
+}
+
 template <int KIND, int FMT, int EPI, int TM = kTM>
-void launch_tile(const TileArgs& a, hipStream_t st) {
+void launch_tile(const TileArgs& a, hipStream_t st, unsigned share = 0) {
   const unsigned T = static_cast<unsigned>(a.nslots) * static_cast<unsigned>(a.ntn) *
                      static_cast<unsigned>(KIND == TK_DENSE && a.ksplit > 1 ? a.ksplit : 1);
   if (T == 0) return;
-  // persistent: one workgroup per CU (the kernel's LDS allows no second),
-  // whole rounds of 8 so that every XCD gets the same number
-  const unsigned wg = std::min((T + 7) / 8 * 8, std::max(8u, num_cus() / 8 * 8));
+  const unsigned wg = std::min((T + 7) / 8 * 8, persistent_wgs(share));
   hipLaunchKernelGGL((k_tile<KIND, FMT, EPI, TM>), dim3(wg), dim3(512), 0, st, a);
 }
 
 // The 32-row and 64-row tiles in one persistent launch (one workgroup per CU)
 template <int KIND, int FMT>
-void launch_small_mid(const TileArgs& a, hipStream_t st) {
-  const unsigned wg = std::max(8u, num_cus() / 8 * 8);
-  hipLaunchKernelGGL((k_tile_small_mid<KIND, FMT>), dim3(wg), dim3(512), 0, st, a);
+void launch_small_mid(const TileArgs& a, hipStream_t st, unsigned share = 0) {
+  hipLaunchKernelGGL((k_tile_small_mid<KIND, FMT>), dim3(persistent_wgs(share)), dim3(512), 0, st, a);
+}
+
+// A second stream of the calling host thread on the current device, with the
+// two events that fork work onto it from a caller's stream and join it back
+// (created on first use at the default priority and kept until the process
+// ends; one per host thread, so that concurrent callers never share events).
+struct SideStream {
+  hipStream_t s;
+  hipEvent_t fork, join;
+};
+const SideStream* side_stream() {
+  thread_local SideStream cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  SideStream& c = cache[dev];
+  if (c.s == nullptr) {
+    SideStream n{};
+    if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
+      (void)hipStreamDestroy(n.s);
+      return nullptr;
+    }
+    c = n;
+  }
+  return &c;
 }
 
 template <int kEpi>
 void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int M, int N, int K, float* partial,
-                  const DenseEpi& ep, hipStream_t st, bool reduce = true) {
+                  const DenseEpi& ep, hipStream_t st, bool reduce = true, unsigned share = 0) {
   if (M == 0) return;
   const int nbrows = (kEpi == EPI_SWIGLU) ? 2 * ep.half : N;
   if (p.small) {
@@ -297,8 +329,8 @@ void launch_dense(const DensePlan& p, const uint16_t* A, const uint16_t* B, int 
   a.nslots = p.mt;
   a.ksplit = p.splits;
   a.partial = p.splits > 1 ? partial : nullptr;
-  if (p.tm == kHugeTM) launch_tile<TK_DENSE, TF_BF16, kEpi, kHugeTM>(a, st);
-  else launch_tile<TK_DENSE, TF_BF16, kEpi>(a, st);
+  if (p.tm == kHugeTM) launch_tile<TK_DENSE, TF_BF16, kEpi, kHugeTM>(a, st, share);
+  else launch_tile<TK_DENSE, TF_BF16, kEpi>(a, st, share);
   if (p.splits > 1) {
     const int ncols = (kEpi == EPI_SWIGLU) ? ep.half : N;
     const long n = static_cast<long>(M) * (ncols / 4);
@@ -424,7 +456,7 @@ const char* const kDecodeNames[6] = {"quant_x",          "routed_l1",
 int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,
                  const uint16_t* x_hid, int32_t Ms, const moe_tail_routing* routing, const uint16_t* residual,
                  uint16_t* out, uint16_t* shared_out, void* ws, size_t ws_bytes, void* stream, void* const* events,
-                 int ev_mode = EV_NONE) {
+                 int ev_mode = EV_NONE, bool side_ok = true) {
   Layout lay;
   int rc = check_forward(dims, w, x_lat, Mr, x_hid, Ms, routing, residual, out, shared_out, ws, ws_bytes, &lay);
   if (rc) return rc;
@@ -486,13 +518,6 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
     return launched();
   }
 
-  // 0: quantize x_lat
-  mark(0);
-  if (Mr > 0) {
-    const long blocks = static_cast<long>(Mr) * (L / 128);
-    hipLaunchKernelGGL(k_quant_1x128<true>, dim3(quant_grid(blocks)), dim3(256), 0, st, x_lat, xq, sx, blocks,
-                       tiled_ok(d, Mr) ? row_scales(d, lay, ws, routing, Mr) : RowScales{});
-  }
   // 1, 2: routed L1 and L2 on the persistent LDS-tiled kernel: FP8 128-row
   // tiles for experts with at least kBigMinRows rows (256-row tiles from 256
   // rows on, the rows past them in one 128-row tile when at most 128), 32-row
@@ -518,6 +543,58 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   // takes 32-row tiles for every expert (its block scales leave no room for
   // a 64-row tile's three stages).
   const bool big = tiled && Mr > kSmallOnlyMr && fp8;
+  const bool mid = tiled && !nvfp4 && (R > static_cast<size_t>(32) * E || (!fp8 && Mr > kSmallOnlyMr));
+  // The shared expert on a second stream, beside the routed work: with FP8
+  // weights and the experts averaging at most 64 rows (32/64-row tiles) the
+  // routed GEMMs stream weights and keep HBM busy from fewer CUs (the
+  // 2048-token, 384-expert workload's routed L1 + L2: 1580 us on 256 CUs,
+  // 1726 on 192, 1923 on 160), while the shared L1 and L2 are bound by the
+  // matrix cores of the CUs they run on.  So the routed launches take 10/16
+  // of the CUs and the shared L1 and L2 the rest, concurrently; the
+  // up-projection, which needs both, runs after the join on the whole chip.
+  // Every tile computes what it computes in one stream, so the result is the
+  // same bit for bit.  (That workload: 2571 -> 2475 us.  The shared GEMMs
+  // then run 1.3-1.4 times slower than their share of the CUs predicts,
+  // their one-stage 256-row tiles waiting longer for loads beside the routed
+  // stream; 80, 104 or 112 CUs for them, or 128-row tiles, measured slower.)
+  const SideStream* side = nullptr;
+  unsigned r_share = 0, d_share = 0;
+  if (side_ok && ev_mode == EV_NONE && Mr > 0 && fp8 && mid && R <= static_cast<size_t>(64) * E && Ms >= 2 * Mr &&
+      !plans.s1.small && !plans.s2.small && (side = side_stream()) != nullptr) {
+    const unsigned cus = persistent_wgs(0);
+    d_share = std::max(8u, cus * 6 / 16 / 8 * 8);
+    r_share = cus - d_share;
+    if (r_share < 8 || hipEventRecord(side->fork, st) != hipSuccess ||
+        hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+      side = nullptr;
+  }
+  const bool fuse_s = fuse_shared_reduce(plans, Mr, Ms);
+  float* partial_s = at<float>(ws, lay.partial_s);
+  // 4: shared L1 + SwiGLU, 5: shared L2 -> s (rows < Mr) and shared_out
+  // (rows >= Mr), on `sst`
+  auto shared_l1_l2 = [&](hipStream_t sst, unsigned share) {
+    mark(4);
+    {
+      DenseEpi ep{Mr, Is, hs, nullptr, nullptr, nullptr};
+      launch_dense<EPI_SWIGLU>(plans.s1, x_hid, w->ws1, Ms, Is, H, partial, ep, sst, true, share);
+    }
+    mark(5);
+    DenseEpi ep{Mr, Is, s, shared_out, nullptr, nullptr};
+    if (fuse_s) launch_dense<EPI_SHARED>(plans.s2, hs, w->ws2, Ms, H, Is, partial_s, ep, sst, false, share);
+    else launch_dense<EPI_SHARED>(plans.s2, hs, w->ws2, Ms, H, Is, partial, ep, sst, true, share);
+  };
+  if (side != nullptr) {
+    shared_l1_l2(side->s, d_share);
+    if (hipEventRecord(side->join, side->s) != hipSuccess) return MOE_TAIL_ERR_DEVICE;
+  }
+
+  // 0: quantize x_lat
+  mark(0);
+  if (Mr > 0) {
+    const long blocks = static_cast<long>(Mr) * (L / 128);
+    hipLaunchKernelGGL(k_quant_1x128<true>, dim3(quant_grid(blocks)), dim3(256), 0, st, x_lat, xq, sx, blocks,
+                       tiled_ok(d, Mr) ? row_scales(d, lay, ws, routing, Mr) : RowScales{});
+  }
   const unsigned max_tiles = static_cast<unsigned>((R + kBM - 1) / kBM + E);
   TileArgs ta{};
   ta.sorted_pair = routing ? routing->sorted_pair : nullptr;
@@ -527,7 +604,6 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
   ta.scales_packed = d.wfmt == MOE_TAIL_W_MXFP4_PACKED || d.wfmt == MOE_TAIL_W_NVFP4_PACKED;
   ta.big_rows = big ? kBigMinRows : 0x7fffffff;
   ta.huge_rows = big ? kHugeTM : 0x7fffffff;
-  const bool mid = tiled && !nvfp4 && (R > static_cast<size_t>(32) * E || (!fp8 && Mr > kSmallOnlyMr));
   ta.mid_rows = mid ? 33 : 0x7fffffff;
   // bounds on the row tiles, which size the grids: ceil(c / 128) <= c / 64
   // for c >= 128, and ceil(c / 32) <= c / 32 + 1 (the launch of the 32- and
@@ -558,8 +634,8 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       a1.ntn = I / 128;
       a1.nslots = slots_small;
       if (mid) {
-        if (fp8) launch_small_mid<TK_L1, TF_FP8>(a1, st);
-        else launch_small_mid<TK_L1, TF_FP4>(a1, st);
+        if (fp8) launch_small_mid<TK_L1, TF_FP8>(a1, st, r_share);
+        else launch_small_mid<TK_L1, TF_FP4>(a1, st, r_share);
       } else {
         if (fp8) launch_tile<TK_L1, TF_FP8, 0, 32>(a1, st);
         else if (nvfp4) launch_tile<TK_L1, TF_NV4, 0, 32>(a1, st);
@@ -567,9 +643,9 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       }
       if (big) {
         a1.nslots = slots_big;
-        launch_tile<TK_L1, TF_FP8, 0>(a1, st);
+        launch_tile<TK_L1, TF_FP8, 0>(a1, st, r_share);
         a1.nslots = slots_huge;
-        launch_tile<TK_L1, TF_FP8, 0, kHugeTM>(a1, st);
+        launch_tile<TK_L1, TF_FP8, 0, kHugeTM>(a1, st, r_share);
       }
     }
   }
@@ -593,8 +669,8 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       a2.ntn = L / kTN;
       a2.nslots = slots_small;
       if (mid) {
-        if (fp8) launch_small_mid<TK_L2, TF_FP8>(a2, st);
-        else launch_small_mid<TK_L2, TF_FP4>(a2, st);
+        if (fp8) launch_small_mid<TK_L2, TF_FP8>(a2, st, r_share);
+        else launch_small_mid<TK_L2, TF_FP4>(a2, st, r_share);
       } else {
         if (fp8) launch_tile<TK_L2, TF_FP8, 0, 32>(a2, st);
         else if (nvfp4) launch_tile<TK_L2, TF_NV4, 0, 32>(a2, st);
@@ -602,9 +678,9 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
       }
       if (big) {
         a2.nslots = slots_big;
-        launch_tile<TK_L2, TF_FP8, 0>(a2, st);
+        launch_tile<TK_L2, TF_FP8, 0>(a2, st, r_share);
         a2.nslots = slots_huge;
-        launch_tile<TK_L2, TF_FP8, 0, kHugeTM>(a2, st);
+        launch_tile<TK_L2, TF_FP8, 0, kHugeTM>(a2, st, r_share);
       }
     }
   }
@@ -616,21 +692,9 @@ int forward_impl(const moe_tail_dims* dims, const moe_tail_weights* w, const uin
     hipLaunchKernelGGL(kern, dim3(Mr), dim3(256), 0, st, y, routing->topk_weights, routing->pair_to_row,
                        w->rms_gamma, rn, L, k, d.rms_eps);
   }
-  // 4: shared L1 + SwiGLU
-  mark(4);
-  {
-    DenseEpi ep{Mr, Is, hs, nullptr, nullptr, nullptr};
-    launch_dense<EPI_SWIGLU>(plans.s1, x_hid, w->ws1, Ms, Is, H, partial, ep, st);
-  }
-  // 5: shared L2 -> s (rows < Mr) and shared_out (rows >= Mr)
-  mark(5);
-  const bool fuse_s = fuse_shared_reduce(plans, Mr, Ms);
-  float* partial_s = at<float>(ws, lay.partial_s);
-  {
-    DenseEpi ep{Mr, Is, s, shared_out, nullptr, nullptr};
-    if (fuse_s) launch_dense<EPI_SHARED>(plans.s2, hs, w->ws2, Ms, H, Is, partial_s, ep, st, false);
-    else launch_dense<EPI_SHARED>(plans.s2, hs, w->ws2, Ms, H, Is, partial, ep, st);
-  }
+  // 4, 5: shared L1 and L2 (already on the second stream, or here)
+  if (side == nullptr) shared_l1_l2(st, 0);
+  else if (hipStreamWaitEvent(st, side->join, 0) != hipSuccess) return MOE_TAIL_ERR_DEVICE;
   // 6: up-projection + FP32 shared add (+ FP32 residual add)
   mark(6);
   {
@@ -839,7 +903,7 @@ int moe_tail_forward_noalloc(const moe_tail_dims* dims, const moe_tail_weights* 
   void* base = scratch_base();
   if (base == nullptr) return MOE_TAIL_ERR_DEVICE;
   return forward_impl(dims, w, x_lat, Mr, x_hid, Ms, routing, nullptr, out, shared_out, base, kScratchBytes, stream,
-                      nullptr);
+                      nullptr, EV_NONE, false);
 }
 
 int moe_tail_forward_add3(const moe_tail_dims* dims, const moe_tail_weights* w, const uint16_t* x_lat, int32_t Mr,

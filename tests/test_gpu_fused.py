@@ -232,6 +232,49 @@ def test_coscheduled_forward_equals_one_launch_per_stage(case):
     assert_same(co, _snapshot(dev))
 
 
+# FP8 weights, experts averaging 50 rows (32/64-row tiles) and more than twice
+# as many shared as routed tokens: moe_tail_forward runs the shared L1 and L2
+# on a second stream beside the routed work (each on its share of the CUs).
+COSCHED = synth.Workload("cosched", Mr=300, Ms=700, E=48, k=8, I=512, Is=256, wfmt=0, seed=61, H=1024, L=512)
+
+
+def test_shared_on_second_stream_equals_one_stream():
+    # The forward with the shared expert on a second stream against one
+    # launch per stage on the caller's stream: the same tiles with the same
+    # summation orders, so the same bits; parity with the oracle; the
+    # caller's stream alone orders the outputs (a wait on that stream, not on
+    # the device, finds them complete); graph replays, with eager work in
+    # between, give the same bits each time.
+    inp = synth.make_inputs(COSCHED)
+    dev = DeviceTail(inp, "cuda:0")
+    dev.route()
+    _poison(dev)
+    dev.forward(events=_hip_events(B.MOE_TAIL_NUM_STAGES + 1))
+    torch.cuda.synchronize()
+    ref = _snapshot(dev)
+    check_forward(dev, inp)
+    s = torch.cuda.Stream()
+    for _ in range(2):
+        _poison(dev)
+        torch.cuda.synchronize()
+        dev.forward(stream=s)
+        s.synchronize()
+        assert_same(ref, _snapshot(dev))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            dev.route(stream=s)
+            dev.forward(stream=s)
+    for _ in range(3):
+        _poison(dev)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_same(ref, _snapshot(dev))
+        dev.forward()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("case", ["ragged", "decode"])
 def test_fused_wait_given_up_fails_closed(case):
     # Every stage wait forced to give up from the host (max_polls = 0): the
