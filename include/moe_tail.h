@@ -22,12 +22,17 @@
  *     bit patterns.
  *   - The caller allocates and owns every buffer.  The library allocates no
  *     device memory, keeps no pointer after returning, never synchronizes,
- *     and enqueues all work on `stream` (a hipStream_t; NULL = null stream).
+ *     and enqueues all work on `stream` (a hipStream_t; NULL = null stream),
+ *     or, in moe_tail_forward, partly on a second stream of its own that it
+ *     forks from `stream` and joins back into it (see there): every result
+ *     is ordered on `stream` either way.
  *   - Every argument check runs on the host before anything is enqueued.  On
  *     any error nothing has been enqueued ("fail closed").  A launch failure
  *     reported by the runtime returns MOE_TAIL_ERR_DEVICE.
- *   - The library is stateless and re-entrant; concurrent calls need
- *     disjoint workspaces and outputs.
+ *   - The library keeps no state between calls beyond per-device caches
+ *     (the CU count; per host thread, moe_tail_forward's second stream and
+ *     its two events) and is re-entrant; concurrent calls need disjoint
+ *     workspaces and outputs.
  *   - Behaviour is undefined for non-finite inputs and for a routing that
  *     moe_tail_route did not produce for the same x_lat / Mr.
  */
@@ -148,7 +153,16 @@ int moe_tail_route(const moe_tail_dims *dims, const moe_tail_weights *weights, c
  *   x_hid  [Ms, H] bf16 shared-expert input
  *   routing  from moe_tail_route for this x_lat (read only)
  *   out        [Mr, H] bf16: bf16(up(RMSNorm(routed)) + f32(shared)) for t < Mr
- *   shared_out [Ms-Mr, H] bf16: shared rows t >= Mr at row t-Mr; NULL iff Ms == Mr */
+ *   shared_out [Ms-Mr, H] bf16: shared rows t >= Mr at row t-Mr; NULL iff Ms == Mr
+ * With FP8 routed weights, the experts averaging at most 64 routed rows
+ * (Mr * top_k <= 64 * E, Mr * top_k > 32 * E) and Ms >= 2 * Mr (Ms > 128), the
+ * shared expert's L1 and L2 run on a second stream of the library's own (one
+ * per host thread and device, created on first use at the default priority)
+ * beside the routed GEMMs, each on a share of the CUs: an event recorded on
+ * `stream` at the start forks it, an event recorded on it joins it back into
+ * `stream` before the up-projection.  The outputs are ordered on `stream` as
+ * usual, are the same bits as on one stream, and capturing `stream` into a
+ * graph captures both. */
 int moe_tail_forward(const moe_tail_dims *dims, const moe_tail_weights *weights, const uint16_t *x_lat, int32_t Mr,
                      const uint16_t *x_hid, int32_t Ms, const moe_tail_routing *routing, uint16_t *out,
                      uint16_t *shared_out, void *workspace, size_t ws_bytes, void *stream);
@@ -183,6 +197,8 @@ int moe_tail_forward_add3(const moe_tail_dims *dims, const moe_tail_weights *wei
  *   call's contents: calls that overlap on one GPU (other streams, other
  *   threads) race and must be serialized by the caller.  Whatever must start
  *   at zero is cleared by the call's own kernels.
+ *   It enqueues everything on `stream` (never moe_tail_forward's second
+ *   stream, which it would have to create).
  *   Results are bit for bit those of moe_tail_forward; every other argument
  *   and error is moe_tail_forward's.  MOE_TAIL_ERR_DEVICE also reports that
  *   the runtime could not give this device's copy of the array. */
