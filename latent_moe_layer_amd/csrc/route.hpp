@@ -335,34 +335,72 @@ __global__ __launch_bounds__(64) void k_router_hist(const int32_t* __restrict__ 
 // One workgroup of 1024 threads: exclusive prefix sum of hist laid out
 // [expert][group] (in place), which gives every (expert, group) its first
 // row; expert_offsets[e] is the first row of expert e, expert_offsets[E] = R.
+// Up to kScanLds cells are first copied to LDS with coalesced loads, so that
+// each thread's run of `chunk` cells costs LDS reads rather than one global
+// round trip after another (2048 tokens x 384 experts: 12288 cells).
+constexpr int kScanLds = 16384;
+
 __global__ __launch_bounds__(1024) void k_router_scan(int32_t* __restrict__ hist, int32_t* __restrict__ expert_offsets,
                                                       int E, int ngroups) {
-  __shared__ int s_tot[1024];
+  __shared__ int s_tot[32];  // wave totals, then their inclusive prefixes
+  __shared__ int s_h[kScanLds];
   const int n = E * ngroups;
   const int tid = threadIdx.x;
+  const bool in_lds = n <= kScanLds;
+  if (in_lds) {
+    for (int i = tid; i < n; i += 1024) s_h[i] = hist[i];
+    __syncthreads();
+  }
   const int chunk = (n + 1023) / 1024;
   const int b = tid * chunk;
   const int end = min(b + chunk, n);
   int sum = 0;
-  for (int i = b; i < end; ++i) sum += hist[i];
-  s_tot[tid] = sum;
+  if (in_lds)
+    for (int i = b; i < end; ++i) sum += s_h[i];
+  else
+    for (int i = b; i < end; ++i) sum += hist[i];
+  // inclusive scan of the 1024 chunk totals: within each wave by lane
+  // shifts, then over the 16 wave totals by wave 0
+  const int lane = tid & 63, wave = tid >> 6;
+  int inc = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) s_tot[wave] = inc;
   __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 chunk totals
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int add = (tid >= off) ? s_tot[tid - off] : 0;
+  if (wave == 0) {
+    int w = lane < 16 ? s_tot[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int o = __shfl_up(w, off);
+      if (lane >= off) w += o;
+    }
+    if (lane < 16) s_tot[16 + lane] = w;  // inclusive totals of waves 0..lane
+  }
+  __syncthreads();
+  int run = inc - sum + (wave > 0 ? s_tot[16 + wave - 1] : 0);  // exclusive prefix of this chunk
+  if (in_lds) {
+    // prefixes in place in LDS, then written out with coalesced stores
+    for (int i = b; i < end; ++i) {
+      const int c = s_h[i];
+      s_h[i] = run;
+      run += c;
+    }
     __syncthreads();
-    s_tot[tid] += add;
+    for (int i = tid; i < n; i += 1024) hist[i] = s_h[i];
+  } else {
+    for (int i = b; i < end; ++i) {
+      const int c = hist[i];
+      hist[i] = run;
+      run += c;
+    }
     __syncthreads();
   }
-  int run = (tid == 0) ? 0 : s_tot[tid - 1];
-  for (int i = b; i < end; ++i) {
-    const int c = hist[i];
-    hist[i] = run;
-    run += c;
-  }
-  __syncthreads();
-  const int total = s_tot[1023];
-  for (int e = tid; e <= E; e += 1024) expert_offsets[e] = (e < E) ? (ngroups > 0 ? hist[e * ngroups] : 0) : total;
+  const int total = s_tot[16 + 15];
+  const int* first = in_lds ? s_h : hist;
+  for (int e = tid; e <= E; e += 1024) expert_offsets[e] = (e < E) ? (ngroups > 0 ? first[e * ngroups] : 0) : total;
 }
 
 // --------------------------------------------------------------- scatter --
