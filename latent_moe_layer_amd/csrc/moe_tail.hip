@@ -848,9 +848,12 @@ int moe_tail_route(const moe_tail_dims* dims, const moe_tail_weights* w, const u
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLogitTok * 8192 * 2);
       lds_raised = true;
     }
-    if (Mr >= kWideMinTokens)
-      hipLaunchKernelGGL((k_router_logits_tile<8, 8>), dim3((Mr + 15) / 16, (E + 15) / 16), dim3(256), 0, st, x_lat,
-                         w->gate, w->gate_bias, logits, Mr, L, E);
+    if (Mr >= kWideMinTokens) {
+      const dim3 grid((Mr + 15) / 16, (E + 15) / 16);
+      auto lg = (static_cast<long>(grid.x) * grid.y > 3L * num_cus()) ? k_router_logits_tile<8, 8, 128>
+                                                                        : k_router_logits_tile<8, 8, 256>;
+      hipLaunchKernelGGL(lg, grid, dim3(256), 0, st, x_lat, w->gate, w->gate_bias, logits, Mr, L, E);
+    }
     else
       hipLaunchKernelGGL(k_router_logits, dim3((Mr + kLogitTok - 1) / kLogitTok, egroups), dim3(256), xtile, st, x_lat,
                          w->gate, w->gate_bias, logits, Mr, L, E);

@@ -111,20 +111,27 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
 // bias.  At 2048 tokens x 384 experts: 8 x 8 per wave 142-150 us; 4 x 16 and
 // 16 x 4 171-181, 8 x 16 and 16 x 8 241-260 (fewer waves per SIMD); an
 // earlier form with the gate values loaded into registers (one 4-byte load
-// per value and lane) 188 us.
+// per value and lane) 188 us.  Stages of 256 columns (48 KB of LDS for two)
+// let 3 workgroups share a CU, stages of 128 columns 5 (then the registers
+// limit): the launch takes 128-column stages when its workgroups need more
+// than one round at 3 per CU (4096 x 64: 56.4 -> 51.6 us; 2048 x 384: 149.2
+// -> 146.7), 256-column ones otherwise (half as many barriers; 1024 x 128:
+// 30.4 against 34.6 us).
 constexpr int kWideMinTokens = 512;
-constexpr int kLgC = 256;  // columns per stage (L is a multiple of 256)
-
-template <int kTW, int kEW>
-__global__ __launch_bounds__(256) void k_router_logits_tile(const uint16_t* __restrict__ x_lat,
-                                                            const float* __restrict__ gate,
-                                                            const float* __restrict__ bias, float* __restrict__ logits,
-                                                            int Mr, int L, int E) {
+template <int kTW, int kEW, int kLgC>  // kLgC: columns per stage (128 or 256; L is a multiple of 256)
+__global__ __launch_bounds__(256, kLgC == 128 ? 4 : 1) void k_router_logits_tile(const uint16_t* __restrict__ x_lat,
+                                                               const float* __restrict__ gate,
+                                                               const float* __restrict__ bias,
+                                                               float* __restrict__ logits, int Mr, int L, int E) {
   constexpr int kRowsX = 2 * kTW, kRowsG = 2 * kEW;
   constexpr int kXBytes = kRowsX * kLgC * 2, kGBytes = kRowsG * kLgC * 4;
   constexpr int kStage = kXBytes + kGBytes;
-  constexpr int kPieces = kStage / 1024;  // 1 KB direct loads per stage
-  static_assert(kLgC == 256 && kRowsX % 2 == 0 && kPieces % 4 == 0, "x pieces: two 512-byte rows; 4 waves");
+  constexpr int kPieces = kStage / 1024;   // 1 KB direct loads per stage
+  constexpr int kXRows = 1024 / (2 * kLgC);  // x rows per piece
+  constexpr int kGRows = 1024 / (4 * kLgC);  // gate rows per piece
+  constexpr int kXPieces = kRowsX / kXRows;
+  static_assert(kGRows >= 1 && kRowsX % kXRows == 0 && kRowsG % kGRows == 0 && kPieces % 4 == 0,
+                "whole rows per 1 KB piece; the same number of pieces for each of the 4 waves");
   __shared__ __attribute__((aligned(16))) uint8_t st[2][kStage];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -136,18 +143,22 @@ __global__ __launch_bounds__(256) void k_router_logits_tile(const uint16_t* __re
       make_rsrc(x_lat + static_cast<size_t>(t0) * L, static_cast<uint32_t>(nx) * static_cast<uint32_t>(L) * 2u);
   const __amdgpu_buffer_rsrc_t rg =
       make_rsrc(gate + static_cast<size_t>(e0) * L, static_cast<uint32_t>(ng) * static_cast<uint32_t>(L) * 4u);
-  // piece q of chunk c: q < kRowsX / 2: x rows 2q, 2q + 1 (32 lanes each);
-  // else gate row q - kRowsX / 2
+  // piece q of chunk c: q < kXPieces: x rows kXRows q .. (64 / kXRows lanes
+  // each); else gate rows kGRows (q - kXPieces) .. (64 / kGRows lanes each)
   auto load = [&](int c, int b) {
 #pragma unroll
     for (int j = 0; j < kPieces / 4; ++j) {
       const int q = wv + 4 * j;
-      if (q < kRowsX / 2) {
-        const uint32_t r = 2u * q + (lane >> 5);
-        dma16(rx, st[b] + 1024 * q, r * static_cast<uint32_t>(L) * 2u + static_cast<uint32_t>(c) * (kLgC * 2) + 16u * (lane & 31), 0);
+      if (q < kXPieces) {
+        constexpr int kLanes = 64 / kXRows;
+        const uint32_t r = static_cast<uint32_t>(kXRows * q + lane / kLanes);
+        dma16(rx, st[b] + 1024 * q,
+              r * static_cast<uint32_t>(L) * 2u + static_cast<uint32_t>(c) * (kLgC * 2) + 16u * (lane % kLanes), 0);
       } else {
-        const uint32_t r = q - kRowsX / 2;
-        dma16(rg, st[b] + 1024 * q, r * static_cast<uint32_t>(L) * 4u + static_cast<uint32_t>(c) * (kLgC * 4) + 16u * lane, 0);
+        constexpr int kLanes = 64 / kGRows;
+        const uint32_t r = static_cast<uint32_t>(kGRows * (q - kXPieces) + lane / kLanes);
+        dma16(rg, st[b] + 1024 * q,
+              r * static_cast<uint32_t>(L) * 4u + static_cast<uint32_t>(c) * (kLgC * 4) + 16u * (lane % kLanes), 0);
       }
     }
   };
@@ -177,6 +188,10 @@ __global__ __launch_bounds__(256) void k_router_logits_tile(const uint16_t* __re
         for (int e = 0; e < kEW; ++e) acc[t][e] = __builtin_fmaf(xv[t], gv[e], acc[t][e]);
     }
   }
+  // each logit reduced over the 64 lanes, then stored by lane t (with
+  // 128-column stages, which leave fewer registers, each one as soon as it is
+  // complete)
+  const int tb = t0 + kTW * tw, eb = e0 + kEW * ew;
 #pragma unroll
   for (int t = 0; t < kTW; ++t)
 #pragma unroll
@@ -184,17 +199,22 @@ __global__ __launch_bounds__(256) void k_router_logits_tile(const uint16_t* __re
       float p = acc[t][e];
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) p = p + __shfl_xor(p, off);
-      acc[t][e] = p;
+      if constexpr (kLgC == 128) {
+        if (lane == t && tb + t < Mr && eb + e < E)
+          logits[static_cast<size_t>(tb + t) * E + eb + e] = p + (bias ? bias[eb + e] : 0.0f);
+      } else {
+        acc[t][e] = p;
+      }
     }
-  // lane t stores token t's logits of this wave's experts
-  const int tb = t0 + kTW * tw, eb = e0 + kEW * ew;
+  if constexpr (kLgC != 128) {
 #pragma unroll
-  for (int t = 0; t < kTW; ++t)
-    if (lane == t && tb + t < Mr) {
+    for (int t = 0; t < kTW; ++t)
+      if (lane == t && tb + t < Mr) {
 #pragma unroll
-      for (int e = 0; e < kEW; ++e)
-        if (eb + e < E) logits[static_cast<size_t>(tb + t) * E + eb + e] = acc[t][e] + (bias ? bias[eb + e] : 0.0f);
-    }
+        for (int e = 0; e < kEW; ++e)
+          if (eb + e < E) logits[static_cast<size_t>(tb + t) * E + eb + e] = acc[t][e] + (bias ? bias[eb + e] : 0.0f);
+      }
+  }
 }
 
 // ----------------------------------------------------------------- top-k --
