@@ -275,6 +275,37 @@ def test_shared_on_second_stream_equals_one_stream():
         torch.cuda.synchronize()
 
 
+def test_shared_on_second_stream_add3_and_one_stream_entry_points():
+    # The same sizes through the other entry points: add3 (the shared expert
+    # on the second stream) against the timed entry point with the same
+    # residual (one stream), and the plain forward against the
+    # allocation-free one (one stream, its own scratch): the same bits.
+    inp = synth.make_inputs(COSCHED)
+    dev = DeviceTail(inp, "cuda:0")
+    dev.route()
+    dev.set_residual(synth.make_residual(COSCHED))
+    _poison(dev)
+    dev.forward()
+    torch.cuda.synchronize()
+    two = _snapshot(dev)
+    _poison(dev)
+    dev.forward_timed(None, _hip_events(B.MOE_TAIL_NUM_STAGES + 1))
+    torch.cuda.synchronize()
+    assert_same(two, _snapshot(dev))
+    dev.set_residual(None)
+    _poison(dev)
+    dev.forward()
+    torch.cuda.synchronize()
+    ref = _snapshot(dev)
+    out = torch.full_like(dev.out, -1)
+    shared_out = torch.full_like(dev.shared_out, -1)
+    B.moe_tail_forward_noalloc(dev.dims, dev.weights, dev.t["x_lat"], dev.Mr, dev.t["x_hid"], dev.Ms, dev.routing,
+                               out, shared_out, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(out), ref["out"])
+    assert np.array_equal(to_np(shared_out), ref["shared_out"])
+
+
 @pytest.mark.parametrize("case", ["ragged", "decode"])
 def test_fused_wait_given_up_fails_closed(case):
     # Every stage wait forced to give up from the host (max_polls = 0): the
