@@ -553,6 +553,22 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       dma4(live ? r.rs : z_rsrc, st + kSOff + 256 * wv, r.s_off, r.s_step * k);
     }
   };
+  // load q of issue's batch alone (the same order: the A pieces, the B
+  // chunks, the scale words), for tiles with one K block and one scale load
+  // per stage (the routed L1's 256-row tiles, which spread their batch over
+  // a step)
+  auto issue_one = [&](uint8_t* st, const Iss& r, int k, bool live, int q) {
+    if constexpr (kKH == 1 && !kASplit && !kNV4) {
+      if (q < kAL) {
+        dma16(live ? r.ra : z_rsrc, st + 1024 * ((wv + 8 * q) % kABlk), r.a_off[q], k * 128);
+      } else if (q < kAL + kBChunks) {
+        const int i = q - kAL;
+        dma16(live ? r.rb : z_rsrc, st + kABytes + 8192 * i + 1024 * wv, r.b_off[i], k * 128);
+      } else if (kScaled) {
+        dma4(live ? r.rs : z_rsrc, st + kSOff + 256 * wv, r.s_off, r.s_step * k);
+      }
+    }
+  };
   // per-tile data loaded ahead (issued first in a stage's batch, only by the
   // waves that carry it): L1 sorted pair ids (one wave per 64 rows), FP8 weight-scale
   // rows (waves kWscW, kWscW + 1)
@@ -603,7 +619,9 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   // stores put 16 lanes on one row.
   constexpr bool kTrans = KIND == TK_L1;
   f32x4 acc[kMT][kNJ];
-  auto compute = [&](const uint8_t* st, int ks, int buf) {
+  // `between(mt)` runs after row block mt's products are issued (routed L1
+  // 256-row tiles: it issues load mt of the next stage)
+  auto compute = [&](const uint8_t* st, int ks, int buf, auto&& between) {
     // weight scales of this step (FP8): the wave's B rows lie in the tile's
     // row half 16 * bblk(0) / 128 (paired: its gate rows) and 16 * bblk(3) / 128
     float sw_lo = 1.0f, sw_hi = 1.0f;
@@ -671,6 +689,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
             acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, alo), b0[j], acc[mt][j]);
             acc[mt][j] = mfma_bf16(__builtin_bit_cast(bf16x8, ahi), b1[j], acc[mt][j]);
           }
+          between(mt);
           if (mt + 1 < kMT) a_cur = load_a(mt + 1);
         }
         return;
@@ -692,6 +711,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
 #pragma unroll
             for (int j = 0; j < kNJ; ++j)
               pr[mt & 1][j] = kFP4 ? mfma_fp4_fp8(bf[j], sb[j], a8) : mfma_fp8(bf[j], a8);
+            between(mt);
           }
           if (mt > 0) {
             const int mp = mt - 1;
@@ -719,6 +739,7 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
           f32x4 pr[kNJ];
 #pragma unroll
           for (int j = 0; j < kNJ; ++j) pr[j] = kFP4 ? mfma_fp8_fp4(a_cur, bf[j], sb[j]) : mfma_fp8(a_cur, bf[j]);
+          between(mt);
           i32x8 a_nxt = a_cur;
           f32x4 v_nxt = v_cur;
           if (mt + 1 < kMT) {
@@ -1023,30 +1044,47 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
     ik = 0;
     ij = 1;
   }
-  auto issue_next = [&]() {
-    uint8_t* st = ring + islot * kStage;
-    if (ij >= n_my) {
-      issue(st, is, 0, false);
-    } else {
+  // the next stage to load: its slot, K step and whether it is a real one;
+  // a new tile's load offsets and the per-tile data of the tile after it
+  // are set up here
+  struct Pend {
+    uint8_t* st;
+    int k;
+    bool live;
+  };
+  auto prep_next = [&]() -> Pend {
+    Pend pd{ring + islot * kStage, 0, false};
+    if (ij < n_my) {
       if (ik == 0 && ij != ji) {
         is = make_iss(desc(ij), ij % 3);
         ji = ij;
       }
       if (ik == 0 && ij + 1 < n_my) aux(desc(ij + 1), (ij + 1) % 3);
-      issue(st, is, ik, true);
+      pd.k = ik;
+      pd.live = true;
     }
     if (++ik == nk) {
       ik = 0;
       ++ij;
     }
     if (++islot == kStages) islot = 0;
+    return pd;
   };
+  // The routed L1's 256-row tiles (one stage in flight) issue their batch
+  // spread over the step, one load after each row block's products: issued
+  // at once after the barrier, the batch (66 loads per workgroup) queues in
+  // the vector memory unit while the waves wait to issue it.  (The same for
+  // the routed L2 and the BF16 256-row tiles measured slower: their loads
+  // then land too late for the next step.)
+  constexpr bool kSpread = KIND == TK_L1 && kMT > 4;
+  static_assert(!kSpread || (kKH == 1 && !kASplit && !kNV4 && kLoads >= kMT), "spread batch: one load per row block");
   int j = 0, ks = 0, jb = 0, cslot = 0;  // the computed stage: tile j (buffer jb = j % 3), K step ks, slot
   for (int gg = 0; gg < G; ++gg) {
     if (kStages >= 3 && gg == 0) ring_barrier<kA * (kStages - 2)>();
     else if (kStages >= 4 && gg == 1) ring_barrier<kA * (kStages - 3) + kLoads>();
     else ring_barrier<kLoads * (kStages - 2)>();
-    issue_next();
+    const Pend pd = prep_next();
+    if constexpr (!kSpread) issue(pd.st, is, pd.k, pd.live);
     if (ks == 0) {
       if (j > 0) dc = desc(j);
 #pragma unroll
@@ -1055,7 +1093,14 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
         for (int jj = 0; jj < kNJ; ++jj) acc[mt][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     uint8_t* st = ring + cslot * kStage;
-    compute(st, ks, jb);
+    compute(st, ks, jb, [&](int q) {
+      if constexpr (kSpread)
+        if (q < kLoads) issue_one(pd.st, is, pd.k, pd.live, q);
+    });
+    if constexpr (kSpread) {
+#pragma unroll
+      for (int q = kMT; q < kLoads; ++q) issue_one(pd.st, is, pd.k, pd.live, q);
+    }
     if (ks == nk - 1) epilogue(dc, st);
     if (++ks == nk) {
       ks = 0;
