@@ -146,18 +146,24 @@ def test_quantizer_bit_exact():
 
 # Shapes of every routing path: top-k and permutation in one workgroup (Mr <= 16: 1, 2, 6 and 16
 # experts per lane), top-k then the one-workgroup permutation (from 17 tokens), and the grid-wide
-# permutation (more than 24 groups of 64 tokens).
+# permutation (more than 24 groups of 64 tokens).  Each is routed twice in a row, the outputs
+# poisoned before each call.
 @pytest.mark.parametrize("E,k,Mr,zipf", [(8, 2, 16, 0.0), (64, 8, 128, 0.0), (64, 8, 4096, 0.0), (128, 8, 1024, 1.2),
                                          (384, 8, 2048, 0.0), (1024, 16, 200, 0.0), (5, 5, 70, 0.0), (9, 3, 1, 0.0),
                                          (16, 4, 130, 0.0), (64, 8, 530, 0.0), (32, 4, 1600, 0.0),
-                                         (128, 8, 16, 1.2), (384, 8, 13, 0.0), (1024, 16, 16, 0.0), (64, 8, 17, 0.0)])
+                                         (128, 8, 16, 1.2), (384, 8, 13, 0.0), (1024, 16, 16, 0.0), (64, 8, 17, 0.0),
+                                         (256, 8, 100, 1.2), (64, 8, 511, 0.0)])
 def test_route_bit_exact(E, k, Mr, zipf):
     wl = synth.Workload("r", Mr=Mr, Ms=Mr, E=E, k=k, I=128, Is=128, wfmt=0, seed=100 + E, zipf_s=zipf)
     inp = synth.make_inputs(wl, routing_only=True)
     dev = DeviceTail(inp, "cuda:0", Mr=Mr, Ms=Mr)
-    dev.route()
-    torch.cuda.synchronize()
-    check_routing(dev, inp)
+    for _ in range(2):
+        for t in (dev.topk_ids, dev.offsets, dev.sorted_pair, dev.pair_to_row):
+            t.fill_(-1)
+        dev.topk_w.fill_(float("nan"))
+        dev.route()
+        torch.cuda.synchronize()
+        check_routing(dev, inp)
 
 
 def test_route_all_equal_logits():
