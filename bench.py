@@ -131,6 +131,35 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def probe_paths(torch, B, reps: int = 3) -> dict:
+    """Per-workgroup rates of the staging load paths (moe_tail_probe_stream_paths),
+    best of `reps`: 64 workgroups on private runs (HBM, not saturated), 256 on
+    private runs (HBM, the whole chip) and 256 on one shared run (L2)."""
+    per = 7 << 20  # 16 matrices of 256 rows x 1792 B, 8 of 256 x 3584 B
+    src = torch.empty(256 * per, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    paths = [("lds_ring_contiguous", 0, 128), ("lds_ring_rows_1792B", 1, 1792), ("lds_ring_rows_3584B", 1, 3584),
+             ("regs_whole_lines", 2, 128), ("regs_half_lines", 3, 128)]
+    out = {"per_workgroup_bytes": per, "workgroup_threads": 512,
+           "lds_ring": "4 stages of 32 KB, 3 in flight", "regs": "16 loads of 16 B in flight per lane", "results": []}
+    for grid, shared in ((64, False), (256, False), (256, True)):
+        for name, mode, rb in paths:
+            best = 1e30
+            for _ in range(reps + 1):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                B.moe_tail_probe_stream_paths(src, per, grid, shared, mode, rb, sink,
+                                              stream=torch.cuda.current_stream())
+                b.record()
+                torch.cuda.synchronize()
+                best = min(best, a.elapsed_time(b) * 1e-3)
+            gbs = grid * per / best / 1e9
+            out["results"].append({"path": name, "grid": grid, "source": "L2 (one shared run)" if shared else "HBM",
+                                   "us": round(best * 1e6, 1), "total_GBps": round(gbs), "per_wg_GBps": round(gbs / grid, 1)})
+    del src
+    return out
+
+
 def stream_read_gbs(torch, B, reps: int = 5) -> float:
     """Best-of-`reps` rate of one streaming read of 4 GiB."""
     nbytes = 4 << 30
@@ -330,6 +359,8 @@ def main() -> int:
                     help="time moe_tail_forward_fused (the x quantizer, then one persistent launch for the rest)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="copy 512 MiB three times with the probe copy kernel and exit")
+    ap.add_argument("--probe-paths", action="store_true",
+                    help="time the load-path probes (direct-to-LDS rings, register loads; HBM and L2) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs the tail on one GPU only; --gpus {args.gpus} is not supported "
@@ -354,6 +385,10 @@ def main() -> int:
         assert torch.equal(src[::4096], dst[::4096])
         print(json.dumps({"calibration": "k_probe_copy", "bytes_read_per_launch": nbytes,
                           "bytes_written_per_launch": nbytes, "launches": 3}))
+        return 0
+
+    if args.probe_paths:
+        print(json.dumps(probe_paths(torch, B)))
         return 0
 
     flush = None

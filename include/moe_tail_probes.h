@@ -10,7 +10,10 @@
  *   - a plain copy of known size, which calibrates the HBM byte counters
  *     (FETCH_SIZE, WRITE_SIZE) that the traffic figures are scaled by;
  *   - a streaming read, the practical HBM read ceiling that the bandwidth-bound
- *     kernels are compared with.
+ *     kernels are compared with;
+ *   - the per-workgroup rates of the load paths (direct-to-LDS rings, loads
+ *     into registers) from HBM and from L2, which bound what a tile's staging
+ *     can move.
  *
  * Conventions: device pointers, 16-byte aligned; work is enqueued on `stream`
  * (a hipStream_t; NULL = null stream); nothing is allocated or synchronized.
@@ -44,6 +47,24 @@ int moe_tail_probe_copy(const void *src, void *dst, size_t bytes, void *stream);
  * (a data dependence that keeps the loads; sink is otherwise untouched).
  * bytes % 4096 == 0. */
 int moe_tail_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, uint32_t magic, void *stream);
+
+/* Streaming rate of one load path, nothing computed: `grid` workgroups of 512
+ * threads each read per_wg bytes, workgroup b the run src + b * per_wg (or,
+ * with `shared`, all of them the run at src), and write sink[0] only if what
+ * they read equals `magic` (a data dependence that keeps the loads).  mode:
+ *   0  direct global -> LDS loads into a ring of 4 stages of 32 KB (3 in
+ *      flight), each wave-wide load 1 KB of consecutive bytes;
+ *   1  the same ring, each stage 128 bytes of each of 256 consecutive rows of
+ *      row_bytes bytes (the routed GEMMs' weight-tile pattern: per load 8 rows
+ *      x 128 bytes), the rows of one 256-row matrix after another;
+ *   2  loads into registers, 16 in flight per lane, each wave-wide load 1 KB
+ *      of consecutive bytes;
+ *   3  the same, each wave-wide load 16 rows x 64 bytes (half cache lines).
+ * per_wg: a multiple of 32 KB below 2 GiB (mode 1: also of 256 * row_bytes,
+ * row_bytes a positive multiple of 128); 1 <= grid <= 65535; src holds
+ * (shared ? 1 : grid) * per_wg bytes. */
+int moe_tail_probe_stream_paths(const void *src, size_t per_wg, int32_t grid, int32_t shared, int32_t mode,
+                                int32_t row_bytes, uint32_t *sink, uint32_t magic, void *stream);
 
 #ifdef __cplusplus
 }

@@ -250,7 +250,8 @@ def moe_tail_quant_fp8_1x128(x, x_is_bf16: bool, rows: int, cols: int, codes, sc
 # tests and the benchmark use; not steps of the tail.
 
 PROBES_PATH = os.path.join(_HERE, "libmoe_tail_probes.so")
-PROBES_EXPORTED = ("moe_tail_probe_mfma_fp8", "moe_tail_probe_copy", "moe_tail_probe_stream_read")
+PROBES_EXPORTED = ("moe_tail_probe_mfma_fp8", "moe_tail_probe_copy", "moe_tail_probe_stream_read",
+                   "moe_tail_probe_stream_paths")
 
 _probes = None
 
@@ -268,6 +269,9 @@ def probes() -> C.CDLL:
         L.moe_tail_probe_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
         L.moe_tail_probe_stream_read.restype = C.c_int
         L.moe_tail_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_uint32, C.c_void_p]
+        L.moe_tail_probe_stream_paths.restype = C.c_int
+        L.moe_tail_probe_stream_paths.argtypes = [C.c_void_p, C.c_size_t, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                                  C.c_void_p, C.c_uint32, C.c_void_p]
         _probes = L
     return _probes
 
@@ -290,3 +294,10 @@ def moe_tail_probe_copy(src, dst, nbytes: int, stream=None) -> None:
 def moe_tail_probe_stream_read(src, nbytes: int, sink, magic: int = 0x9E3779B9, stream=None) -> None:
     _check_probe(probes().moe_tail_probe_stream_read(ptr(src), nbytes, ptr(sink), magic, stream_handle(stream)),
                  "moe_tail_probe_stream_read")
+
+
+def moe_tail_probe_stream_paths(src, per_wg: int, grid: int, shared: bool, mode: int, row_bytes: int, sink,
+                                magic: int = 0x9E3779B9, stream=None) -> None:
+    _check_probe(probes().moe_tail_probe_stream_paths(ptr(src), per_wg, grid, int(bool(shared)), mode, row_bytes,
+                                                      ptr(sink), magic, stream_handle(stream)),
+                 "moe_tail_probe_stream_paths")

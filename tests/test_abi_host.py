@@ -252,6 +252,15 @@ def test_probe_rejections():
     assert p.moe_tail_probe_stream_read(X, 4000, OUT, 0, None) == 1
     assert p.moe_tail_probe_stream_read(X, 4096, None, 0, None) == 1
     assert p.moe_tail_probe_stream_read(X, 0, OUT, 0, None) == 0
+    f = p.moe_tail_probe_stream_paths
+    assert f(X, 1 << 20, 64, 0, 4, 128, OUT, 0, None) == 1          # no such mode
+    assert f(X, 1 << 20, 0, 0, 0, 128, OUT, 0, None) == 1           # empty grid
+    assert f(X, (1 << 20) + 1024, 64, 0, 0, 128, OUT, 0, None) == 1  # not whole 32 KB stages
+    assert f(X, 1 << 31, 1, 0, 2, 128, OUT, 0, None) == 1            # past a buffer's 32-bit range
+    assert f(X, 1 << 20, 64, 0, 1, 100, OUT, 0, None) == 1          # rows not whole 128-byte lines
+    assert f(X, 32768 * 5, 64, 0, 1, 1792, OUT, 0, None) == 1       # not whole 256-row matrices
+    assert f(X + 4, 1 << 20, 64, 0, 0, 128, OUT, 0, None) == 1
+    assert f(X, 1 << 20, 64, 0, 0, 128, None, 0, None) == 1
 
 
 def test_pack_mxfp4_scales_rejections():
