@@ -50,8 +50,11 @@ int moe_tail_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, ui
 
 /* Streaming rate of one load path, nothing computed: `grid` workgroups of 512
  * threads each read per_wg bytes, workgroup b the run src + b * per_wg (or,
- * with `shared`, all of them the run at src), and write sink[0] only if what
- * they read equals `magic` (a data dependence that keeps the loads).  mode:
+ * with `shared`, all of them the run at src).  sink[0] = magic is written
+ * only if, for some thread t, what it read equals `magic`: in modes 0 and 1
+ * the 4-byte word t of the last stage in LDS, in modes 2 and 3 the xor of
+ * every 4-byte word it loaded (a data dependence that keeps the loads and lets
+ * a test check what arrived); sink is otherwise untouched.  mode:
  *   0  direct global -> LDS loads into a ring of 4 stages of 32 KB (3 in
  *      flight), each wave-wide load 1 KB of consecutive bytes;
  *   1  the same ring, each stage 128 bytes of each of 256 consecutive rows of

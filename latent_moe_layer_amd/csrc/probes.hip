@@ -108,7 +108,8 @@ __global__ __launch_bounds__(512) void k_probe_path_lds(const uint8_t* __restric
     issue(s + kPathStages - 1);
   }
   ring_barrier<0>();
-  const uint32_t v = reinterpret_cast<const uint32_t*>(ring)[threadIdx.x];
+  // word t of the last stage that read bytes (the trailing stages read none)
+  const uint32_t v = reinterpret_cast<const uint32_t*>(ring + ((nst - 1) % kPathStages) * kPathStage)[threadIdx.x];
   if (v == magic) sink[0] = magic;
 }
 
