@@ -348,6 +348,9 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
   // in the XCD's L2: an expert with many row slots is streamed about ns /
   // (slots per round) times instead of once per slot.
   constexpr int kNBlk = 4;
+  constexpr int kDenseGroup = 4;
+  // dense 128-row tiles (up to about 2048 rows) when every tile of the launch runs at once
+  const bool grouped = !kRouted && TM == 128 && T <= nwg;
   auto desc = [&](int j) -> Desc {
     const int t = lo + lb + j * nbx;
     Desc d;
@@ -382,11 +385,31 @@ __device__ __forceinline__ void tile_run(const TileArgs& p, const TileSmem& sm, 
       d.row0 = s_eoff[a] + base + slot * TM;
       d.rows = min(TM, s_eoff[a + 1] - d.row0);
     } else {
-      // K range slowest: an XCD's run of tiles shares K range and rows
+      // K range slowest.  128-row launches whose tiles all run at once:
+      // within a K range, groups of kDenseGroup row slots, the slots of a
+      // group fastest, so the 32 tiles an XCD's workgroups take side by side
+      // cover kDenseGroup slots x 8 n tiles and each activation row block
+      // and each weight tile they stream serves 8 and kDenseGroup of them
+      // from that XCD's L2 (slot-major runs streamed the weights again for
+      // every slot: the 1024-token up-projection fetched 433 MB for 51 MB of
+      // weights, 147 MB this way).  The 256-row launches (several rounds, or
+      // MFMA-bound at 4096 rows) keep slot-major runs, which measured as
+      // fast or faster there.
       const int per_z = p.nslots * p.ntn;
       d.kz = t / per_z;
-      const int slot = (t - d.kz * per_z) / p.ntn;
-      d.nt = t - d.kz * per_z - slot * p.ntn;
+      const int r = t - d.kz * per_z;
+      int slot;
+      if (grouped) {
+        const int grp = r / (kDenseGroup * p.ntn);
+        const int first = grp * kDenseGroup;
+        const int gsize = min(kDenseGroup, p.nslots - first);
+        const int within = r - grp * kDenseGroup * p.ntn;
+        slot = first + within % gsize;
+        d.nt = within / gsize;
+      } else {
+        slot = r / p.ntn;
+        d.nt = r - slot * p.ntn;
+      }
       d.e = 0;
       d.row0 = slot * TM;
       d.rows = min(TM, p.M - d.row0);
