@@ -53,7 +53,7 @@ BF16_PEAK_TFLOPS = 2500.0
 MEASURED_L1_TRAFFIC = {
     "decode": 945.8e6,    # k_tile<0, 0, 0, 32>: 943.6 MB fetched + 2.2 MB written (profiles/decode_tail_traffic.md)
     "prefill": 1587.2e6,  # k_tile<0, 0, 0, 256> 1127.1 MB + k_tile<0, 0, 0, 128> 460.1 MB (profiles/prefill_tail_traffic.md)
-    "mxfp4": 1082.6e6,    # k_tile_small_mid<0, 1> (profiles/mxfp4_tail_traffic.md)
+    "mxfp4": 1084.5e6,    # k_tile_small_mid<0, 1> (profiles/mxfp4_tail_traffic.md)
     "nvfp4": 534.6e6,     # k_tile<0, 3, 0, 32> (profiles/nvfp4_tail_traffic.md)
 }
 FORMATS = {0: "FP8 128x128", 1: "MXFP4 (e8m0 scales packed)", 3: "NVFP4 (e4m3 scale per 16 packed, fp32 per matrix)"}
