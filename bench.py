@@ -9,12 +9,16 @@ captured as one HIP graph and replayed.
 Prints ONE JSON line.  The headline is the decode workload (128 routed and
 128 shared tokens, 64 experts, top-8, FP8 experts): `value` is the whole
 tail's achieved HBM throughput (algorithmic bytes / mean time per layer over
-the K timed replays).  The same line carries, under `legs`, the other
-workloads timed the same way (by default the prefill workload, the MFMA-bound
-half of the metric, and the tiny workload), and for every workload:
-  - median / p10 / p90 of the per-replay times (events between replays), and
-    the same cache-cold (a 512 MiB streaming read between replays, outside
+the K timed replays, which run back to back between two events).  The same
+line carries, under `legs`, the other workloads timed the same way (by
+default the prefill workload, the MFMA-bound half of the metric, and the
+tiny workload), and for every workload:
+  - median / p10 / p90 of the per-replay times (K replays before those, with
+    an event between consecutive ones; `us_per_layer_evented` is their mean),
+    and the same cache-cold (a 512 MiB streaming read between replays, outside
     the timed pair, evicts the 256 MB Infinity Cache);
+  - `us_per_layer_5_per_graph`: context, the step captured five times in one
+    graph (as a model's graph holds one per layer), per step;
   - `groups_us`: each launch group of the schedule the plain call runs, from
     moe_tail_forward_timed (events recorded on the library's stream; where
     the plain call runs the shared L1 and L2 on a second stream beside the
@@ -214,7 +218,9 @@ def measure(name: str, args, torch, np, B, synth, DeviceTail, to_np, flush) -> d
         graph.replay()
     torch.cuda.synchronize()
 
-    # timed region: exactly K replays, an event between consecutive replays
+    # the distribution over steps: K replays, an event between consecutive
+    # ones (this pass also finishes the warm-up: the first pass after the
+    # capture measured slower)
     cur = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
@@ -223,8 +229,39 @@ def measure(name: str, args, torch, np, B, synth, DeviceTail, to_np, flush) -> d
         graph.replay()
         ev[i + 1].record(cur)
     torch.cuda.synchronize()
-    total_ms = ev[0].elapsed_time(ev[K])
     per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(K)]
+    evented_us = ev[0].elapsed_time(ev[K]) * 1e3 / K
+
+    # timed region: exactly K replays between two events, nothing else
+    # enqueued among them (an event recorded between replays costs about 5 us
+    # a step at decode size)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(cur)
+    for i in range(K):
+        graph.replay()
+    t1.record(cur)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+
+    # context: the step captured 5 times in one graph, as a model's graph
+    # holds one per layer (no graph boundary between them)
+    graph5_us = None
+    if not args.eager:
+        g5 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g5):
+            for _ in range(5):
+                step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        g5.replay()
+        reps = max(1, K // 5)
+        torch.cuda.synchronize()
+        t0.record(cur)
+        for _ in range(reps):
+            g5.replay()
+        t1.record(cur)
+        torch.cuda.synchronize()
+        graph5_us = t0.elapsed_time(t1) * 1e3 / (5 * reps)
+        del g5
 
     # cache-cold: a 512 MiB streaming read before each replay, outside the pair
     cold = []
@@ -269,6 +306,7 @@ def measure(name: str, args, torch, np, B, synth, DeviceTail, to_np, flush) -> d
         "workload": f"{wl.name}: Mr={wl.Mr} Ms={wl.Ms} E={wl.E} top{wl.k} I={wl.I} I_s={wl.Is} H={wl.H} L={wl.L} "
                     f"{FORMATS[wl.wfmt]} routed weights",
         "us_per_layer": us, "us_median": pct(per, 50), "us_p10": pct(per, 10), "us_p90": pct(per, 90),
+        "us_per_layer_evented": evented_us, "us_per_layer_5_per_graph": graph5_us,
         "cold_us_median": pct(cold, 50) if cold else None, "cold_us_p10": pct(cold, 10) if cold else None,
         "cold_us_p90": pct(cold, 90) if cold else None,
         "algorithmic_bytes": nbytes, "flops_lowp": flops["lowp"], "flops_bf16": flops["bf16"],
@@ -432,13 +470,17 @@ def main() -> int:
         "config": {"workload": head["workload"], "global_batch": wl.Mr, "parallelism": "single GPU",
                    "epilogue": "add3: up + shared + residual, one rounding" if args.add3 else "up + shared"},
         "us_median": head["us_median"], "us_p10": head["us_p10"], "us_p90": head["us_p90"],
+        "us_per_layer_evented": head["us_per_layer_evented"],
+        "us_per_layer_5_per_graph": head["us_per_layer_5_per_graph"],
         "cold_us_median": head["cold_us_median"], "cold_us_p10": head["cold_us_p10"],
         "cold_us_p90": head["cold_us_p90"],
         "algorithmic_bytes": head["algorithmic_bytes"], "touched_experts": head["touched_experts"],
         "hbm_frac": head["hbm_frac"], "tflops_lowp": head["TFLOPs_lowp"], "tflops_bf16": head["TFLOPs_bf16"],
         "stream_read_gbs": sread, "frac_of_stream_read": head["GBps"] / sread,
         "timing": (("eager launches" if args.eager else "HIP graph replay") + " of route + forward" +
-                   (" (single-launch forward)" if args.fused else "") + "; events between replays"),
+                   (" (single-launch forward)" if args.fused else "") +
+                   "; value: K replays between two events; median / p10 / p90: K replays before those with an"
+                   " event between consecutive ones (us_per_layer_evented their mean)"),
         "groups_us": head["groups_us"],
         "roofline": head.get("roofline"), "cpu_baseline": cpu, "input_gen_s": head["input_gen_s"],
         "legs": legs,
