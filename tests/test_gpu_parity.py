@@ -358,6 +358,28 @@ def test_forward_top16(wfmt):
     check_forward(dev, inp)
 
 
+@pytest.mark.parametrize("wfmt,E,k,I,L", [(synth.WFMT_FP8, 512, 8, 512, 512), (synth.WFMT_MXFP4, 512, 8, 512, 512),
+                                          (synth.WFMT_FP8, 1024, 16, 512, 256)])
+def test_forward_expert_count_limits(wfmt, E, k, I, L):
+    # 512 experts: the most the tiled kernels hold in their LDS expert tables
+    # (32-row tiles for most experts, 64- and 128-row ones for the heavy ones
+    # of the skewed loads); 1024 experts at top-16: past that limit, every
+    # routed GEMM on the row-streaming kernels (L = 256 keeps them there).
+    # More shared than routed tokens, every token compared.  (Experts at
+    # least 512 wide: at 128, one legitimate h-code flip of a large code
+    # moves its routed row's y by about 2 %, the per-row bar itself.)
+    Mr = 700 if E <= 512 else 300
+    wl = synth.Workload("maxe", Mr=Mr, Ms=Mr + 20, E=E, k=k, I=I, Is=128, wfmt=wfmt, seed=97 + E + wfmt, H=512, L=L,
+                        zipf_s=0.15)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    loads = np.diff(to_np(dev.offsets))
+    assert loads.sum() == Mr * k and np.count_nonzero(loads) > E // 2, loads
+    if E <= 512:
+        assert loads.max() >= 128, loads.max()  # heavy experts on the larger tiles
+    check_forward(dev, inp)
+
+
 def test_forward_nvfp4_skewed_and_narrow():
     # NVFP4 weights on skewed loads (a few heavy experts, many empty ones),
     # with more shared than routed tokens; experts 384 wide (not a multiple
