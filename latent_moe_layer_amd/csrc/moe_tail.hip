@@ -110,15 +110,40 @@ struct Plans {
 
 Plans plan_all(const moe_tail_dims& d, int32_t Mr, int32_t Ms) {
   Plans p;
-  // at decode sizes the shared L2 and the up-projection share one launch:
-  // each gets half of the workgroups (fewer, longer items, and half the
-  // partial sums to write and reduce).  The shared expert's plan depends on
-  // Ms only, so its rows come out the same whatever Mr is.
+  // at decode sizes the shared L2 and the up-projection share one launch,
+  // each on its share of the workgroups (fewer, longer items than one
+  // launch each would take, and fewer partial sums to write and reduce).
+  // The shared expert's plan depends on Ms and the widths only, so its rows
+  // come out the same whatever Mr is.
   const int pair = Ms <= kSmallMaxM ? 2 : 1;
   // (tiles of the tiled kernel: 128 gate + 128 up rows, or 256 rows)
   p.s1 = plan_dense(Ms, 2 * d.shared_inter, d.shared_inter / 128, d.hidden);
-  p.s2 = plan_dense(Ms, d.hidden, d.hidden / kTN, d.shared_inter, kPlanCUs / pair);
-  p.up = plan_dense(Mr, d.hidden, d.hidden / kTN, d.latent, kPlanCUs / pair);
+  if (pair == 2) {
+    // The two share one launch, which ends with its longest item: the
+    // workgroups are split between them so that the larger per-item K range
+    // is as short as it can be (both have H / kSkinnyN weight-row blocks, so
+    // an item's bytes follow its K range), the fewest items among equals.
+    // Decode (I_s = 2048, L = 3584): 2 + 2 splits; 16 tokens with I_s = 512:
+    // 1 + 3 instead of 2 + 2 (the up-projection items 448 -> 304 KB).
+    const int nt = d.hidden / kSkinnyN, n2 = d.shared_inter / 64, nu = d.latent / 64;
+    const int total = std::max(2, kPlanCUs / std::max(1, nt));
+    int best_a = 1, best_b = 1;
+    long best = -1;
+    for (int a = 1; a < total && a <= n2; ++a)
+      for (int b = 1; a + b <= total && b <= nu; ++b) {
+        const long cost = static_cast<long>(std::max((n2 + a - 1) / a, (nu + b - 1) / b)) * 4096 + a + b;
+        if (best < 0 || cost < best) {
+          best = cost;
+          best_a = a;
+          best_b = b;
+        }
+      }
+    p.s2 = plan_dense(Ms, d.hidden, d.hidden / kTN, d.shared_inter, best_a * nt);
+    p.up = plan_dense(Mr, d.hidden, d.hidden / kTN, d.latent, best_b * nt);
+  } else {
+    p.s2 = plan_dense(Ms, d.hidden, d.hidden / kTN, d.shared_inter);
+    p.up = plan_dense(Mr, d.hidden, d.hidden / kTN, d.latent);
+  }
   return p;
 }
 
