@@ -380,6 +380,21 @@ def test_forward_expert_count_limits(wfmt, E, k, I, L):
     check_forward(dev, inp)
 
 
+@pytest.mark.parametrize("wfmt,I,L", [(synth.WFMT_FP8, 512, 8192), (synth.WFMT_FP8, 8192, 512),
+                                      (synth.WFMT_MXFP4, 512, 8192), (synth.WFMT_MXFP4, 8192, 512),
+                                      (synth.WFMT_NVFP4, 384, 8192), (synth.WFMT_NVFP4, 8064, 512)])
+def test_forward_width_limits(wfmt, I, L):
+    # the widest reductions the kernels take: L = 8192 (the routed L1's and
+    # the up-projection's K, and RMSNorm's width) and I = 8192 (the routed
+    # L2's K), 64 scale blocks along K, which fill the kernels' LDS scale
+    # tables; FP8 and MXFP4 on the tiled kernels, NVFP4 with the other
+    # width not a multiple of 256, so on the row-streaming kernels
+    wl = synth.Workload("maxw", Mr=24, Ms=30, E=3, k=2, I=I, Is=256, wfmt=wfmt, seed=131 + wfmt, H=1024, L=L)
+    inp = synth.make_inputs(wl)
+    dev = run(inp)
+    check_forward(dev, inp)
+
+
 def test_forward_nvfp4_skewed_and_narrow():
     # NVFP4 weights on skewed loads (a few heavy experts, many empty ones),
     # with more shared than routed tokens; experts 384 wide (not a multiple
