@@ -59,6 +59,7 @@ MEASURED_L1_TRAFFIC = {
     "prefill": 1587.2e6,  # k_tile<0, 0, 0, 256> 1127.1 MB + k_tile<0, 0, 0, 128> 460.1 MB (profiles/prefill_tail_traffic.md)
     "mxfp4": 1084.5e6,    # k_tile_small_mid<0, 1> (profiles/mxfp4_tail_traffic.md)
     "nvfp4": 534.6e6,     # k_tile<0, 3, 0, 32> (profiles/nvfp4_tail_traffic.md)
+    "indep": 5787.2e6,    # k_tile_small_mid<0, 0>: 5752.5 fetched + 34.8 written (profiles/indep_tail_traffic.md)
 }
 FORMATS = {0: "FP8 128x128", 1: "MXFP4 (e8m0 scales packed)", 3: "NVFP4 (e4m3 scale per 16 packed, fp32 per matrix)"}
 DTYPES = {0: "fp8e4m3+bf16", 1: "mxfp4+fp8e4m3+bf16", 3: "nvfp4+fp8e4m3+fp16+bf16"}
@@ -434,7 +435,11 @@ def main() -> int:
         fb = 512 << 20
         flush = {"buf": torch.empty(fb, dtype=torch.uint8, device="cuda").fill_(3), "bytes": fb,
                  "sink": torch.zeros(1, dtype=torch.int32, device="cuda")}
+    def progress(what):  # one line per finished step of the run, on stderr (stdout carries only the JSON line)
+        print(f"[bench] {what}", file=sys.stderr, flush=True)
+
     head = measure(args.workload, args, torch, np, B, synth, DeviceTail, to_np, flush)
+    progress(f"{args.workload}: {head['us_per_layer']:.1f} us per layer")
     legs = {}
     names = [] if args.legs == "none" else \
         (["tiny", "decode", "prefill", "mxfp4", "indep", "nvfp4"] if args.legs == "all" else args.legs.split(","))
@@ -442,16 +447,20 @@ def main() -> int:
 
     wl = synth.WORKLOADS[args.workload]
     cpu = None if args.no_cpu_baseline else oracle_timing(inp, head, np)
+    if cpu is not None:
+        progress(f"{args.workload}: oracle timed")
     del inp, dev
     torch.cuda.empty_cache()
 
     for n in names:
         if n and n != args.workload:
             leg = measure(n, args, torch, np, B, synth, DeviceTail, to_np, flush)
+            progress(f"{n}: {leg['us_per_layer']:.1f} us per layer")
             linp = leg.pop("_inp")
             leg.pop("_dev")
             if args.cpu_all:
                 leg["cpu_baseline"] = oracle_timing(linp, leg, np)
+                progress(f"{n}: oracle timed")
             del linp
             legs[n] = leg
             torch.cuda.empty_cache()
