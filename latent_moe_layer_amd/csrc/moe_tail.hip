@@ -867,9 +867,10 @@ int moe_tail_route(const moe_tail_dims* dims, const moe_tail_weights* w, const u
   if (Mr > 0) {
     const int egroups = (E + 4 * kLogitExpPerWave - 1) / (4 * kLogitExpPerWave);
     const size_t xtile = static_cast<size_t>(kLogitTok) * L * 2;  // dynamic LDS of the logits kernel
+    const bool few = static_cast<long>((Mr + kLogitTok - 1) / kLogitTok) * egroups < kLogitSmallGrid;
     static bool lds_raised = false;
     if (!lds_raised) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_router_logits),
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_router_logits<kLogitTok, kLogitExpPerWave>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLogitTok * 8192 * 2);
       lds_raised = true;
     }
@@ -879,9 +880,12 @@ int moe_tail_route(const moe_tail_dims* dims, const moe_tail_weights* w, const u
                                                                         : k_router_logits_tile<8, 8, 256>;
       hipLaunchKernelGGL(lg, grid, dim3(256), 0, st, x_lat, w->gate, w->gate_bias, logits, Mr, L, E);
     }
+    else if (few)
+      hipLaunchKernelGGL((k_router_logits<2, 1>), dim3((Mr + 1) / 2, (E + 3) / 4), dim3(256),
+                         static_cast<size_t>(2) * L * 2, st, x_lat, w->gate, w->gate_bias, logits, Mr, L, E);
     else
-      hipLaunchKernelGGL(k_router_logits, dim3((Mr + kLogitTok - 1) / kLogitTok, egroups), dim3(256), xtile, st, x_lat,
-                         w->gate, w->gate_bias, logits, Mr, L, E);
+      hipLaunchKernelGGL((k_router_logits<kLogitTok, kLogitExpPerWave>), dim3((Mr + kLogitTok - 1) / kLogitTok, egroups),
+                         dim3(256), xtile, st, x_lat, w->gate, w->gate_bias, logits, Mr, L, E);
   }
   // one workgroup for the whole permutation while it is short (it walks the
   // token groups one wave at a time), with the top-k too for up to 16

@@ -13,8 +13,8 @@
 namespace moe_tail {
 
 // ---------------------------------------------------------------- logits --
-// One workgroup = 4 waves; tile of kLogitTok tokens x (4 * kLogitExpPerWave)
-// experts.  Lane l of a wave accumulates p[l] = fma-chain over i of
+// One workgroup = 4 waves; tile of kTok tokens x (4 * kEPW) experts
+// (kLogitTok x 4 kLogitExpPerWave unless the launch is small).  Lane l of a wave accumulates p[l] = fma-chain over i of
 // x[64 i + l] * W[e, 64 i + l]; the 64 partials are then combined by an xor
 // butterfly (32, 16, 8, 4, 2, 1), which leaves the same value in every lane.
 // The kernel is latency-bound (a few hundred KB in all), so it waits for
@@ -24,46 +24,52 @@ namespace moe_tail {
 constexpr int kLogitTok = 4;
 constexpr int kLogitExpPerWave = 2;
 constexpr int kLogitChunk = 4096;  // gate columns in registers at once
-// dynamic LDS: the x tile, kLogitTok x L bf16
+// dynamic LDS: the x tile, kTok x L bf16.  Few tokens (a launch of fewer than
+// kLogitSmallGrid workgroups): 2 tokens x 1 expert per wave instead, four
+// times the workgroups, each logit's chain unchanged (the 16-token workload:
+// 4 -> 16 workgroups).
+constexpr int kLogitSmallGrid = 64;
 
+template <int kTok, int kEPW>
 __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restrict__ x_lat,
                                                        const float* __restrict__ gate,
                                                        const float* __restrict__ bias, float* __restrict__ logits,
                                                        int Mr, int L, int E) {
+  static_assert((kTok * 256 * 2) % 1024 == 0, "the x tile in whole 1 KB blocks for every L a multiple of 256");
   extern __shared__ __attribute__((aligned(16))) uint16_t sx[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int t0 = blockIdx.x * kLogitTok;
-  const int e0 = (blockIdx.y * 4 + wave) * kLogitExpPerWave;
+  const int t0 = blockIdx.x * kTok;
+  const int e0 = (blockIdx.y * 4 + wave) * kEPW;
 
-  // x rows t0 .. t0 + kLogitTok - 1 as one linear byte array: 1 KB block j is
+  // x rows t0 .. t0 + kTok - 1 as one linear byte array: 1 KB block j is
   // loaded by wave j % 4, lane l copying bytes [16 (64 j + l), +16) (rows
   // past Mr read as zeros)
   {
     const uint32_t row_bytes = static_cast<uint32_t>(L) * 2;
-    const int nrows = max(0, min(kLogitTok, Mr - t0));
+    const int nrows = max(0, min(kTok, Mr - t0));
     const __amdgpu_buffer_rsrc_t r =
         make_rsrc(x_lat + static_cast<size_t>(t0) * L, static_cast<uint32_t>(nrows) * row_bytes);
-    const int nblocks = (kLogitTok * L * 2) / 1024;  // L is a multiple of 256
+    const int nblocks = (kTok * L * 2) / 1024;  // L is a multiple of 256
     for (int j = wv; j < nblocks; j += 4) dma16(r, reinterpret_cast<uint8_t*>(sx) + 1024 * j, 16u * (64 * j + lane), 0);
   }
 
   // gate row of each expert as a buffer (columns past L read as zeros)
-  __amdgpu_buffer_rsrc_t wr[kLogitExpPerWave];
+  __amdgpu_buffer_rsrc_t wr[kEPW];
 #pragma unroll
-  for (int e = 0; e < kLogitExpPerWave; ++e)
+  for (int e = 0; e < kEPW; ++e)
     wr[e] = make_rsrc(gate + static_cast<size_t>(min(e0 + e, E - 1)) * L, static_cast<uint32_t>(L) * 4);
   constexpr int kPer = kLogitChunk / 64;  // gate values per lane and expert
-  float acc[kLogitTok][kLogitExpPerWave];
+  float acc[kTok][kEPW];
 #pragma unroll
-  for (int t = 0; t < kLogitTok; ++t)
+  for (int t = 0; t < kTok; ++t)
 #pragma unroll
-    for (int e = 0; e < kLogitExpPerWave; ++e) acc[t][e] = 0.0f;
+    for (int e = 0; e < kEPW; ++e) acc[t][e] = 0.0f;
 
   for (int c0 = 0; c0 < L; c0 += kLogitChunk) {  // one pass for L <= kLogitChunk
-    float w[kLogitExpPerWave][kPer];
+    float w[kEPW][kPer];
 #pragma unroll
-    for (int e = 0; e < kLogitExpPerWave; ++e)
+    for (int e = 0; e < kEPW; ++e)
 #pragma unroll
       for (int u = 0; u < kPer; ++u)
         w[e][u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wr[e], 4 * lane, 4 * (c0 + 64 * u), 0));
@@ -72,18 +78,18 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
     for (int u = 0; u < kPer; ++u) {
       if (c0 + 64 * u < L) {
 #pragma unroll
-        for (int t = 0; t < kLogitTok; ++t) {
+        for (int t = 0; t < kTok; ++t) {
           const float xv = bf16_bits_to_f32(sx[t * L + c0 + 64 * u + lane]);
 #pragma unroll
-          for (int e = 0; e < kLogitExpPerWave; ++e) acc[t][e] = __builtin_fmaf(xv, w[e][u], acc[t][e]);
+          for (int e = 0; e < kEPW; ++e) acc[t][e] = __builtin_fmaf(xv, w[e][u], acc[t][e]);
         }
       }
     }
   }
 #pragma unroll
-  for (int t = 0; t < kLogitTok; ++t)
+  for (int t = 0; t < kTok; ++t)
 #pragma unroll
-    for (int e = 0; e < kLogitExpPerWave; ++e) {
+    for (int e = 0; e < kEPW; ++e) {
       float p = acc[t][e];
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) p = p + __shfl_xor(p, off);
@@ -91,9 +97,9 @@ __global__ __launch_bounds__(256) void k_router_logits(const uint16_t* __restric
     }
   if (lane == 0) {
 #pragma unroll
-    for (int t = 0; t < kLogitTok; ++t)
+    for (int t = 0; t < kTok; ++t)
 #pragma unroll
-      for (int e = 0; e < kLogitExpPerWave; ++e)
+      for (int e = 0; e < kEPW; ++e)
         if (t0 + t < Mr && e0 + e < E)
           logits[static_cast<size_t>(t0 + t) * E + e0 + e] = acc[t][e] + (bias ? bias[e0 + e] : 0.0f);
   }
