@@ -166,6 +166,22 @@ def test_route_bit_exact(E, k, Mr, zipf):
         check_routing(dev, inp)
 
 
+@pytest.mark.parametrize("L,Mr,E,k", [(256, 7, 12, 3), (768, 33, 20, 4), (256, 64, 16, 2)])
+def test_route_bit_exact_narrow_latent(L, Mr, E, k):
+    # the few-token logits tiling (2 tokens x 1 expert per wave) at narrow
+    # latents: L = 256 makes its x tile exactly one 1 KB block; odd token and
+    # expert counts leave partial tiles (rows past Mr and experts past E)
+    wl = synth.Workload("rn", Mr=Mr, Ms=Mr, E=E, k=k, I=128, Is=128, wfmt=0, seed=200 + L + E, H=256, L=L)
+    inp = synth.make_inputs(wl, routing_only=True)
+    dev = DeviceTail(inp, "cuda:0", Mr=Mr, Ms=Mr)
+    for t in (dev.topk_ids, dev.offsets, dev.sorted_pair, dev.pair_to_row):
+        t.fill_(-1)
+    dev.topk_w.fill_(float("nan"))
+    dev.route()
+    torch.cuda.synchronize()
+    check_routing(dev, inp)
+
+
 def test_route_all_equal_logits():
     wl = synth.Workload("r", Mr=70, Ms=70, E=16, k=4, I=128, Is=128, wfmt=0, seed=5, zero_router=True)
     inp = synth.make_inputs(wl, routing_only=True)
