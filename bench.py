@@ -11,8 +11,8 @@ Prints ONE JSON line.  The headline is the decode workload (128 routed and
 tail's achieved HBM throughput (algorithmic bytes / mean time per layer over
 the K timed replays, which run back to back between two events).  The same
 line carries, under `legs`, the other workloads timed the same way (by
-default the prefill workload, the MFMA-bound half of the metric, and the
-tiny workload), and for every workload:
+default all of them: prefill, the MFMA-bound half of the metric, tiny,
+mxfp4, the independent-count workload and nvfp4), and for every workload:
   - median / p10 / p90 of the per-replay times (K replays before those, with
     an event between consecutive ones; `us_per_layer_evented` is their mean),
     and the same cache-cold (a 512 MiB streaming read between replays, outside
@@ -386,7 +386,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "mxfp4", "indep", "nvfp4"],
                     help="the headline workload")
-    ap.add_argument("--legs", default="prefill,tiny",
+    ap.add_argument("--legs", default="prefill,tiny,mxfp4,indep,nvfp4",
                     help="other workloads timed on the same line (comma list, 'none', or 'all')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-all", action="store_true", help="also time the CPU oracle on every leg's tokens")
