@@ -192,7 +192,7 @@ int moe_tail_forward_add3(const moe_tail_dims *dims, const moe_tail_weights *wei
  *   Sizes whose moe_tail_workspace_bytes exceeds MOE_TAIL_NOALLOC_MAX_BYTES
  *   return MOE_TAIL_ERR_WORKSPACE with nothing enqueued (48 MiB covers the
  *   decode sizes: 128 routed and 128 shared tokens with 64..1024 experts,
- *   top-8, I = I_s = 2048 at the served widths take about 43 MiB).
+ *   top-8, I = I_s = 2048 at the served widths take about 35 MiB).
  *   Every call on one GPU shares that GPU's array, which keeps the last
  *   call's contents: calls that overlap on one GPU (other streams, other
  *   threads) race and must be serialized by the caller.  Whatever must start
